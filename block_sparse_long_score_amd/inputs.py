@@ -1,0 +1,195 @@
+"""Seeded synthetic inputs for the MSA hot path.
+
+This module only draws random numbers and lays them out; it holds none of
+the method's arithmetic.  Both the GPU path (through the tests and the bench)
+and the CPU oracle read the same bytes produced here.
+
+Workloads.  The pages measure MSA on long-context evaluation suites at 128K
+and on product contexts of 1,048,576 tokens ("MiniMax 模型迭代与竞品分析",
+§1 model table and §2 quality table), with M2's attention shape of 48 query
+heads and 8 KV heads ("深度解读：The MiniMax-M2 Series", §2).  No suite item is
+used: every tensor here is synthetic with those context lengths and head
+shapes.
+
+Value recipe (one sub-stream per tensor, seed = 1000 + workload index):
+  - Q, K, V: float32 N(0, 1), rounded to nearest-even bfloat16.
+  - Q_idx, K_idx: uniform integers in [-4, 4] divided by 4, stored as
+    bfloat16.  Every product is a multiple of 1/16 and every partial sum of
+    at most 64 such products is exact in float32, so index scores are exact
+    in any summation order and block selections can be compared bit for bit.
+  - block table: identity for prefill workloads, a seeded random permutation
+    of the physical blocks for decode workloads.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+
+import numpy as np
+import torch
+
+BLOCK = 128
+TOP_K = 16
+
+# Tensor ids of the sub-streams, in a fixed order.
+_STREAM_Q, _STREAM_K, _STREAM_V, _STREAM_QIDX, _STREAM_KIDX, _STREAM_TABLE = range(6)
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    description: str
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim: int
+    index_dim: int
+    seq_lens: tuple  # tokens per sequence after this step's append
+    q_lens: tuple  # query rows per sequence (its last positions)
+    permuted_table: bool
+    seed: int
+    block_size: int = BLOCK
+    top_k: int = TOP_K
+
+    @property
+    def num_seqs(self) -> int:
+        return len(self.seq_lens)
+
+    @property
+    def total_q(self) -> int:
+        return int(sum(self.q_lens))
+
+    @property
+    def total_tokens(self) -> int:
+        return int(sum(self.seq_lens))
+
+    @property
+    def group_size(self) -> int:
+        return self.num_q_heads // self.num_kv_heads
+
+    @property
+    def max_blocks_per_seq(self) -> int:
+        return max(math.ceil(n / self.block_size) for n in self.seq_lens)
+
+    def with_sizes(self, name: str, seq_lens, q_lens, permuted_table=None, seed=None) -> "Workload":
+        """Same head shapes with other sequence sizes (for parity cases)."""
+        return dataclasses.replace(
+            self, name=name, seq_lens=tuple(int(x) for x in seq_lens), q_lens=tuple(int(x) for x in q_lens),
+            permuted_table=self.permuted_table if permuted_table is None else permuted_table,
+            seed=self.seed if seed is None else seed)
+
+
+_M2 = dict(num_q_heads=48, num_kv_heads=8, head_dim=128, index_dim=64)
+_ONE_M = 1 << 20
+
+WORKLOADS = {
+    "c0": Workload("c0", "tiny MSA prefill, T=4096, 8q/1kv, D=64, d_idx=32",
+                   num_q_heads=8, num_kv_heads=1, head_dim=64, index_dim=32,
+                   seq_lens=(4096,), q_lens=(4096,), permuted_table=False, seed=1000),
+    "c1": Workload("c1", "M2-shaped MSA prefill, T=32768, 48q/8kv, D=128, d_idx=64",
+                   seq_lens=(32768,), q_lens=(32768,), permuted_table=False, seed=1001, **_M2),
+    "c2": Workload("c2", "MSA decode, 32 sequences x 131072 cached tokens, 48q/8kv",
+                   seq_lens=(131072,) * 32, q_lens=(1,) * 32, permuted_table=True, seed=1002, **_M2),
+    "c3": Workload("c3", "long MSA prefill, T=131072, 48q/8kv, D=128, d_idx=64",
+                   seq_lens=(131072,), q_lens=(131072,), permuted_table=False, seed=1003, **_M2),
+    "c4d": Workload("c4d", "1M-context MSA decode, 4 sequences x 1,048,576 cached tokens",
+                    seq_lens=(_ONE_M,) * 4, q_lens=(1,) * 4, permuted_table=True, seed=1004, **_M2),
+    "c4p": Workload("c4p", "8192-token MSA prefill chunk appended to a 1,048,576-token cache",
+                    seq_lens=(_ONE_M + 8192,), q_lens=(8192,), permuted_table=False, seed=1004, **_M2),
+}
+
+
+def _generator(device, seed: int, stream: int) -> torch.Generator:
+    g = torch.Generator(device=device)
+    g.manual_seed(seed * 16 + stream)
+    return g
+
+
+_CHUNK = 1 << 26  # elements drawn per call, bounds the float32 temporary
+
+
+def _normal_bf16(shape, gen, device) -> torch.Tensor:
+    out = torch.empty(shape, dtype=torch.bfloat16, device=device)
+    flat = out.view(-1)
+    for start in range(0, flat.numel(), _CHUNK):
+        n = min(_CHUNK, flat.numel() - start)
+        flat[start:start + n] = torch.randn(n, generator=gen, device=device, dtype=torch.float32).to(torch.bfloat16)
+    return out
+
+
+def _dyadic_bf16(shape, gen, device) -> torch.Tensor:
+    out = torch.empty(shape, dtype=torch.bfloat16, device=device)
+    flat = out.view(-1)
+    for start in range(0, flat.numel(), _CHUNK):
+        n = min(_CHUNK, flat.numel() - start)
+        ints = torch.randint(-4, 5, (n,), generator=gen, device=device, dtype=torch.int32)
+        flat[start:start + n] = ints.to(torch.bfloat16) * 0.25  # exact: a power-of-two scale
+    return out
+
+
+@dataclasses.dataclass
+class Inputs:
+    """Logical (uncached) tensors of one workload.
+
+    k, v     : bf16 [total_tokens, Hkv, D], sequence s at rows tok_off[s]:tok_off[s+1]
+    k_idx    : bf16 [total_tokens, d_idx]
+    q        : bf16 [total_q, Hq, D]
+    q_idx    : bf16 [total_q, Hkv, d_idx]
+    block_table : int32 [num_seqs, max_blocks_per_seq] (physical block ids)
+    """
+    workload: Workload
+    k: torch.Tensor
+    v: torch.Tensor
+    k_idx: torch.Tensor
+    q: torch.Tensor
+    q_idx: torch.Tensor
+    block_table: torch.Tensor
+    num_blocks: int
+
+    @property
+    def tok_off(self):
+        return np.concatenate([[0], np.cumsum(self.workload.seq_lens)]).astype(np.int64)
+
+    @property
+    def cu_q(self):
+        return np.concatenate([[0], np.cumsum(self.workload.q_lens)]).astype(np.int32)
+
+    def positions(self, s: int) -> np.ndarray:
+        """Absolute positions of sequence s's query rows."""
+        n, nq = self.workload.seq_lens[s], self.workload.q_lens[s]
+        return np.arange(n - nq, n, dtype=np.int64)
+
+    def new_token_rows(self) -> torch.Tensor:
+        """Indices into k/v/k_idx of the tokens this step appends (one per query row)."""
+        rows = []
+        off = self.tok_off
+        for s in range(self.workload.num_seqs):
+            n, nq = self.workload.seq_lens[s], self.workload.q_lens[s]
+            rows.append(np.arange(off[s] + n - nq, off[s] + n, dtype=np.int64))
+        return torch.from_numpy(np.concatenate(rows)).to(self.k.device)
+
+
+def make_inputs(w: Workload, device="cpu", seed: int | None = None) -> Inputs:
+    """Draw every tensor of workload `w` on `device` from its seeded sub-streams."""
+    seed = w.seed if seed is None else seed
+    dev = torch.device(device)
+    hkv, d, di = w.num_kv_heads, w.head_dim, w.index_dim
+    q = _normal_bf16((w.total_q, w.num_q_heads, d), _generator(dev, seed, _STREAM_Q), dev)
+    k = _normal_bf16((w.total_tokens, hkv, d), _generator(dev, seed, _STREAM_K), dev)
+    v = _normal_bf16((w.total_tokens, hkv, d), _generator(dev, seed, _STREAM_V), dev)
+    q_idx = _dyadic_bf16((w.total_q, hkv, di), _generator(dev, seed, _STREAM_QIDX), dev)
+    k_idx = _dyadic_bf16((w.total_tokens, di), _generator(dev, seed, _STREAM_KIDX), dev)
+    mb = w.max_blocks_per_seq
+    num_blocks = w.num_seqs * mb
+    if w.permuted_table:
+        perm = torch.randperm(num_blocks, generator=_generator(dev, seed, _STREAM_TABLE), device=dev)
+        table = perm.to(torch.int32).view(w.num_seqs, mb)
+    else:
+        table = torch.arange(num_blocks, device=dev, dtype=torch.int32).view(w.num_seqs, mb)
+    return Inputs(w, k, v, k_idx, q, q_idx, table.contiguous(), num_blocks)
+
+
+def bf16_bits(t: torch.Tensor) -> np.ndarray:
+    """bf16 tensor -> numpy uint16 bit patterns (host copy, no arithmetic)."""
+    if t.dtype != torch.bfloat16:
+        raise TypeError("expected a bfloat16 tensor")
+    return t.detach().contiguous().view(torch.int16).cpu().numpy().view(np.uint16)

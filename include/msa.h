@@ -1,0 +1,231 @@
+/*
+ * msa.h — C ABI of libmsa.so, the MI355X (gfx950) implementation of the
+ * MiniMax Sparse Attention (MSA) hot path over grouped-query attention.
+ *
+ * Sources (web pages; cited by title and section):
+ *   [M3-evo]  "MiniMax 模型迭代与竞品分析：从 Text-01、M1、M2 到 M3", §2
+ *             "从 Lightning Attention 到 MSA": the softmax-attention equation,
+ *             GQA head sharing, and the four inference steps of MSA
+ *             (global index scoring, 128-token block max-pooling, 16 blocks
+ *             per query and GQA group with the local block counted among the
+ *             16, exact softmax over at most 16x128 = 2048 tokens).
+ *   [M-line]  "MiniMax：Text-01 / M1 → M2.7 → M3，注意力选择如何与 Agent RL、
+ *             KV 和内核一起演进", §5: the Index Branch scores KV blocks per GQA
+ *             group and picks Top-k; the Main Branch attends over the picked
+ *             blocks only.
+ *   [FA3-M3]  "前沿架构解码手记（三）：MiniMax M2.7 → M3——稀疏注意力的跨越",
+ *             §2.1 "KV-Block-Major Prefill": the KV cache is nested
+ *             block -> token -> head -> dim so that the tokens of one block
+ *             are contiguous and a selected block is read as one large piece.
+ *   [M2-rep]  "深度解读：The MiniMax-M2 Series", §2: 48 query heads and 8 KV
+ *             heads (GQA 6:1).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Every array argument is a DEVICE pointer unless its name ends in _host.
+ *   Device pointers must be 16-byte aligned.
+ * - bf16 means IEEE-754 binary32 truncated to its upper 16 bits (bfloat16),
+ *   stored as 2-byte little-endian words.
+ * - Every call only validates its arguments on the host and enqueues kernels
+ *   on `stream` (a hipStream_t; NULL = the default stream).  It never
+ *   synchronises, never allocates device or pinned memory, and keeps no
+ *   state between calls; scratch memory is a caller-owned workspace.  The
+ *   caller owns every buffer and keeps it alive until the stream has drained.
+ * - Errors are return codes; the library never aborts and never prints.
+ *   Every check listed under "Errors" runs on the host before the first HIP
+ *   call, so a rejected call has enqueued nothing.  msa_last_error() returns
+ *   a thread-local human-readable detail of the last failure.
+ * - Per-token device metadata (block_table entries, the device copies of
+ *   seq_lens and cu_q) cannot be read by the host without a synchronisation;
+ *   it is a precondition that they equal their host mirrors and that every
+ *   block_table entry a call touches lies in [0, num_blocks).  Kernels guard
+ *   every physical block id against num_blocks and skip out-of-range blocks
+ *   rather than touch memory outside the cache.
+ *
+ * Positions, blocks and groups
+ * ----------------------------
+ * - Sequence s holds seq_lens[s] tokens (after this step's append).  Its
+ *   queries are its LAST nq_s = cu_q[s+1] - cu_q[s] positions, so query row
+ *   r = cu_q[s] + i sits at absolute position t = seq_lens[s] - nq_s + i.
+ *   Prefill of a fresh sequence has nq_s = seq_lens[s]; decode has nq_s = 1;
+ *   a prefill chunk onto an existing cache has 1 <= nq_s < seq_lens[s].
+ *   The new token attends to itself (it is appended before attention).
+ * - Logical block b of a sequence holds absolute positions [128b, 128b+127];
+ *   block_table[s][b] names its physical block in the cache.
+ * - The current ("local") block of a query at position t is c = t / 128.
+ * - Query head h belongs to GQA group g = h / (num_q_heads / num_kv_heads),
+ *   and group g reads KV head g.
+ */
+#ifndef MSA_H_
+#define MSA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MSA_ABI_VERSION 1
+
+typedef enum msa_status {
+  MSA_OK = 0,
+  MSA_ERR_NULL_POINTER = 1, /* a required pointer (struct, array, host mirror) is NULL */
+  MSA_ERR_BAD_SHAPE = 2,    /* inconsistent sizes: Hq % Hkv != 0, cu_q not monotone,
+                               nq_s > seq_lens[s], ld too small, negative counts */
+  MSA_ERR_UNSUPPORTED = 3,  /* a size outside the compiled specialisations: head_dim
+                               not in {64,128}, index_dim not in {32,64}, block_size
+                               != 128, top_k != 16, num_kv_heads not a power of two
+                               in [1,32], group size Hq/Hkv > 16 */
+  MSA_ERR_MISALIGNED = 4,   /* a device pointer is not 16-byte aligned */
+  MSA_ERR_CAPACITY = 5,     /* seq_lens[s] > max_blocks_per_seq * 128, or a size that
+                               overflows the 32-bit indexing the kernels use */
+  MSA_ERR_WORKSPACE = 6,    /* workspace NULL or ws_bytes < msa_workspace_size(...) */
+  MSA_ERR_HIP = 7           /* a HIP launch failed; detail in msa_last_error() */
+} msa_status;
+
+/* Head and block geometry.  softmax_scale <= 0 selects 1/sqrt(head_dim), the
+ * scale of the softmax-attention equation in [M3-evo] §2. */
+typedef struct msa_dims {
+  int32_t num_q_heads;   /* Hq */
+  int32_t num_kv_heads;  /* Hkv = number of GQA groups */
+  int32_t head_dim;      /* D: 64 or 128 */
+  int32_t index_dim;     /* d_idx: width of Q_idx / K_idx, 32 or 64 */
+  int32_t block_size;    /* tokens per KV block: must be 128 ([M3-evo] §2) */
+  int32_t top_k;         /* blocks kept per query and group: must be 16 ([M3-evo] §2) */
+  float softmax_scale;
+} msa_dims;
+
+/* Block-major paged KV cache ([FA3-M3] §2.1).  One physical block holds 128
+ * consecutive tokens; inside it the tokens are contiguous, each token holding
+ * all KV heads, each head holding head_dim values.  K and V are separate
+ * arrays with the same nesting.  The index keys K_idx (one per token, shared
+ * by every group: [M3-evo] §2) live in a third array with the same block
+ * paging. */
+typedef struct msa_cache {
+  void* k;                    /* bf16 [num_blocks][128][Hkv][D] */
+  void* v;                    /* bf16 [num_blocks][128][Hkv][D] */
+  void* k_idx;                /* bf16 [num_blocks][128][d_idx]  */
+  const int32_t* block_table; /* int32 [num_seqs][max_blocks_per_seq], logical -> physical */
+  int32_t num_blocks;
+  int32_t max_blocks_per_seq;
+} msa_cache;
+
+/* A batch of sequences and the query rows this step computes. */
+typedef struct msa_batch {
+  int32_t num_seqs;
+  int32_t total_q;               /* = cu_q[num_seqs] */
+  const int32_t* seq_lens;       /* device int32 [num_seqs]: length after the append */
+  const int32_t* cu_q;           /* device int32 [num_seqs+1]: row offsets, cu_q[0] = 0 */
+  const int32_t* seq_lens_host;  /* host mirror of seq_lens (validation, grid sizing) */
+  const int32_t* cu_q_host;      /* host mirror of cu_q */
+} msa_batch;
+
+/* Which call msa_workspace_size() sizes. */
+typedef enum msa_call {
+  MSA_CALL_SPARSE_ATTN_PREFILL = 1,
+  MSA_CALL_SPARSE_ATTN_DECODE = 2
+} msa_call;
+
+/* ------------------------------------------------------------------------- *
+ * msa_kv_append — store the keys and values of this step's new tokens.
+ * Past K/V are cached for later queries and past queries are not ([M3-evo]
+ * §2, Q/K/V paragraph); the cache is block-major ([FA3-M3] §2.1).
+ *   k_new, v_new : bf16 [total_q][Hkv][D], row r = token at the position of
+ *                  query row r (see "Positions" above).
+ *   k_idx_new    : bf16 [total_q][d_idx], the index key of the same token.
+ * Writes cache.k/v/k_idx at (block_table[s][t/128], t%128) for every new row.
+ * Reads nothing else; other cache slots are left untouched.
+ * Errors: NULL_POINTER, BAD_SHAPE, UNSUPPORTED, MISALIGNED, CAPACITY, HIP.
+ * ------------------------------------------------------------------------- */
+msa_status msa_kv_append(const msa_dims* dims, const msa_cache* cache, const msa_batch* batch,
+                         const void* k_new, const void* v_new, const void* k_idx_new,
+                         void* stream);
+
+/* ------------------------------------------------------------------------- *
+ * msa_index_score — Index Branch scoring plus block max-pooling
+ * ([M3-evo] §2 steps 1–2; [M-line] §5).  For query row r at position t, group
+ * g and every causal block b <= c = t/128:
+ *     s_i          = sum_d q_idx[r][g][d] * k_idx[i][d]      (0 <= i <= t)
+ *     scores[r][g][b] = max { s_i : 128b <= i <= min(128b+127, t) }
+ * computed as bf16 x bf16 products accumulated in fp32; -0.0 is written as
+ * +0.0.  The score is a plain dot product (no scale, no activation): a
+ * positive scale would not change any selection, and the pages name none.
+ *   q_idx        : bf16 [total_q][Hkv][d_idx]
+ *   block_scores : fp32 [total_q][Hkv][ld], ld >= max_s ceil(seq_lens[s]/128).
+ *                  Entries b > c of a row are NOT written.
+ * Errors: NULL_POINTER, BAD_SHAPE (ld too small), UNSUPPORTED, MISALIGNED,
+ *         CAPACITY, HIP.
+ * ------------------------------------------------------------------------- */
+msa_status msa_index_score(const msa_dims* dims, const msa_cache* cache, const msa_batch* batch,
+                           const void* q_idx, float* block_scores, int64_t ld, void* stream);
+
+/* ------------------------------------------------------------------------- *
+ * msa_block_topk — block selection ([M3-evo] §2 step 3).  For row r, group g
+ * with local block c = t/128:
+ *   - if c + 1 <= top_k: sel = {0, 1, ..., c};
+ *   - else sel = {c} plus the top_k - 1 best of blocks 0..c-1, ordered by
+ *     (score descending, block index ascending), so equal scores go to the
+ *     lower block index and the local block takes one of the top_k slots.
+ * No exponential is evaluated: selection only compares scores.
+ *   block_scores : fp32 [total_q][Hkv][ld] as written by msa_index_score
+ *                  (only entries b < c are read).
+ *   sel          : int32 [total_q][Hkv][top_k], logical block ids in
+ *                  ascending order, padded with -1 after the last one.
+ * Errors: NULL_POINTER, BAD_SHAPE, UNSUPPORTED, MISALIGNED, HIP.
+ * ------------------------------------------------------------------------- */
+msa_status msa_block_topk(const msa_dims* dims, const msa_batch* batch, const float* block_scores,
+                          int64_t ld, int32_t* sel, void* stream);
+
+/* ------------------------------------------------------------------------- *
+ * msa_sparse_attn_prefill — Main Branch ([M3-evo] §2 step 4 and the
+ * softmax-attention equation): for query row r at position t and head h of
+ * group g,
+ *     I  = union over b in sel[r][g] of [128b, min(128b+127, t)]
+ *     z_i = softmax_scale * (q[r][h] . k[i][g]),  p = softmax(z over I)
+ *     out[r][h] = sum_{i in I} p_i v[i][g]
+ * in bf16 x bf16 -> fp32 arithmetic, output rounded to bf16.  Designed for
+ * many query rows per sequence (blocks outer, queries inner).
+ *   q    : bf16 [total_q][Hq][D]
+ *   sel  : int32 [total_q][Hkv][top_k] as produced by msa_block_topk
+ *   out  : bf16 [total_q][Hq][D]
+ *   workspace : device scratch of at least
+ *               msa_workspace_size(dims, cache, batch, MSA_CALL_SPARSE_ATTN_PREFILL)
+ *               bytes; its contents on entry are ignored.
+ * Errors: NULL_POINTER, BAD_SHAPE, UNSUPPORTED, MISALIGNED, CAPACITY,
+ *         WORKSPACE, HIP.
+ * ------------------------------------------------------------------------- */
+msa_status msa_sparse_attn_prefill(const msa_dims* dims, const msa_cache* cache,
+                                   const msa_batch* batch, const void* q, const int32_t* sel,
+                                   void* out, void* workspace, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------- *
+ * msa_sparse_attn_decode — the same Main Branch computation for one query
+ * row per sequence (cu_q[s+1] - cu_q[s] == 1 for every s; BAD_SHAPE
+ * otherwise), split across the selected blocks and merged by log-sum-exp.
+ * Arguments and errors as msa_sparse_attn_prefill, workspace sized with
+ * MSA_CALL_SPARSE_ATTN_DECODE.
+ * ------------------------------------------------------------------------- */
+msa_status msa_sparse_attn_decode(const msa_dims* dims, const msa_cache* cache,
+                                  const msa_batch* batch, const void* q, const int32_t* sel,
+                                  void* out, void* workspace, size_t ws_bytes, void* stream);
+
+/* Bytes of workspace `call` needs for this problem; 0 if the arguments are
+ * invalid (the failing check is reported by msa_last_error()). */
+size_t msa_workspace_size(const msa_dims* dims, const msa_cache* cache, const msa_batch* batch,
+                          int32_t call);
+
+/* Static text for a status code; never NULL. */
+const char* msa_status_string(msa_status status);
+
+/* Thread-local detail of the last failing call on this thread; "" if none. */
+const char* msa_last_error(void);
+
+/* MSA_ABI_VERSION of the library that is loaded. */
+int32_t msa_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MSA_H_ */
