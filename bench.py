@@ -1,0 +1,230 @@
+"""Throughput of the MSA hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c3]
+
+A step is one pass of the whole hot path over one batch of synthetic input,
+through the C ABI: append the batch's new K/V/K_idx to the block-major cache,
+index scoring + block max-pool, top-16 block selection, and the Main Branch
+(prefill: every query row of the chunk; decode: one new token per sequence).
+Inputs are resident in HBM before timing starts.  Prints one JSON line.
+
+The default workload is the 131,072-token prefill (48 query heads / 8 KV
+heads, head_dim 128, index dim 64), the context length the metric is quoted
+at; --workload selects another (c0 tiny prefill, c1 32K prefill, c2 decode of
+32 x 128K, c4d decode of 4 x 1M, c4p 8K chunk onto a 1M cache).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0       # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, TFLOP/s
+METRIC = "MSA prefill tokens/s & decode tokens/s at 128K/1M ctx; % MFMA / % HBM peak"
+
+
+def algorithmic_work(w):
+    """Per-step algorithmic flops and bytes of each stage (what the method
+    must compute/move, independent of how the kernels do it)."""
+    B = w.block_size
+    idx_flops = main_flops = 0.0
+    kidx_bytes = kv_bytes = 0.0
+    for n, nq in zip(w.seq_lens, w.q_lens):
+        t = np.arange(n - nq, n, dtype=np.float64)
+        c = np.floor(t / B)
+        # attended tokens: every causal token below 16 blocks, else 15 full blocks + the causal part of the local one
+        lsel = np.where(c + 1 <= w.top_k, t + 1, (w.top_k - 1) * B + (t - c * B + 1))
+        idx_flops += 2.0 * w.index_dim * w.num_kv_heads * float(np.sum(t + 1))
+        main_flops += 4.0 * w.head_dim * w.num_q_heads * float(np.sum(lsel))
+        kidx_bytes += 2.0 * w.index_dim * float(np.sum(t + 1)) if nq == 1 else 2.0 * w.index_dim * n
+        kv_bytes += 2.0 * 2.0 * w.head_dim * w.num_kv_heads * float(np.sum(lsel))
+    nblk = sum((n + B - 1) // B for n in w.seq_lens)
+    rows = w.total_q
+    io_bytes = (rows * w.num_q_heads * w.head_dim * 2 * 2            # q in, out
+                + rows * w.num_kv_heads * w.index_dim * 2            # q_idx
+                + rows * (2 * w.num_kv_heads * w.head_dim + w.index_dim) * 2 * 2  # append: read + write
+                + rows * w.num_kv_heads * w.top_k * 4)               # selections
+    pooled_bytes = 2 * 4 * w.num_kv_heads * sum(nq * (n + B - 1) // B for n, nq in zip(w.seq_lens, w.q_lens))
+    return dict(index_flops=idx_flops, main_flops=main_flops, kidx_bytes=kidx_bytes, kv_bytes=kv_bytes,
+                io_bytes=float(io_bytes), pooled_bytes=float(pooled_bytes), nblk=nblk)
+
+
+def cpu_baseline(inputs, runner, budget_s: float):
+    """The oracle as it stands, on a bounded sample of the same workload's
+    rows, timed on this host's cores.  Host copies are outside the timing."""
+    import oracle
+    from block_sparse_long_score_amd.inputs import bf16_bits
+    import torch
+
+    w = inputs.workload
+    B = w.block_size
+
+    def run_rows(s, positions):
+        rows = torch.from_numpy(inputs.cu_q[s] + positions - (w.seq_lens[s] - w.q_lens[s])).to(inputs.q.device)
+        off = int(inputs.tok_off[s])
+        length = int(positions.max()) + 1
+        k_idx = bf16_bits(inputs.k_idx[off:off + length])
+        q_idx = bf16_bits(inputs.q_idx.index_select(0, rows))
+        q = bf16_bits(inputs.q.index_select(0, rows))
+        t0 = time.perf_counter()
+        pooled = oracle.block_scores(positions, q_idx, k_idx, B, (w.seq_lens[s] + B - 1) // B)
+        sel = oracle.select(positions, pooled, B, w.top_k)
+        t_sel = time.perf_counter() - t0
+        blocks = np.unique(sel[sel >= 0]).astype(np.int64)
+        tok = (blocks[:, None] * B + np.arange(B)[None, :]).ravel()
+        tok = tok[tok < length]
+        shape = (length, w.num_kv_heads, w.head_dim)
+        k_host = np.zeros(shape, np.uint16)
+        v_host = np.zeros(shape, np.uint16)
+        tok_dev = torch.from_numpy(tok + off).to(inputs.k.device)
+        k_host[tok] = bf16_bits(inputs.k.index_select(0, tok_dev))
+        v_host[tok] = bf16_bits(inputs.v.index_select(0, tok_dev))
+        t0 = time.perf_counter()
+        oracle.attend(positions, q, k_host, v_host, sel, B)
+        return t_sel + time.perf_counter() - t0
+
+    decode = runner.decode
+    if decode:
+        # whole decode rows (one per sequence), sequences taken in order until the budget is spent
+        spent, n = 0.0, 0
+        for s in range(w.num_seqs):
+            spent += run_rows(s, np.array([w.seq_lens[s] - 1], np.int64))
+            n += 1
+            if spent >= budget_s:
+                break
+        sample = f"{n} of {w.num_seqs} decode rows (full {w.seq_lens[0]}-token context each)"
+        value = n / spent
+    else:
+        s = 0
+        n_q = w.q_lens[0]
+        first = w.seq_lens[0] - n_q
+        probe = np.linspace(first, w.seq_lens[0] - 1, 8).astype(np.int64)
+        per_row = run_rows(s, probe) / len(probe)
+        n = int(np.clip(budget_s / max(per_row, 1e-9), 8, n_q))
+        pos = np.unique(np.linspace(first, w.seq_lens[0] - 1, n).astype(np.int64))
+        spent = run_rows(s, pos)
+        sample = f"{len(pos)} query rows evenly spaced over positions {first}..{w.seq_lens[0] - 1} (all groups/heads)"
+        value = len(pos) / spent
+    return {"value": value, "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle", "sample": sample,
+            "seconds": round(spent, 2)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="c3", choices=["c0", "c1", "c2", "c3", "c4d", "c4p"])
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for cpu_baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build measures one GPU only; the MSA hot path is not sharded across GPUs "
+              "(see the sharding paragraph of the design notes). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from block_sparse_long_score_amd import _lib
+    from block_sparse_long_score_amd.inputs import WORKLOADS, make_inputs
+    from block_sparse_long_score_amd.pipeline import MsaRunner
+
+    _lib.load()  # fails loudly if the HIP library is not built
+    w = WORKLOADS[args.workload]
+    torch.cuda.set_device(0)
+    inputs = make_inputs(w, "cuda")
+    runner = MsaRunner(inputs)
+    work = algorithmic_work(w)
+    stream = torch.cuda.current_stream()
+
+    stages = ("append", "index_score", "block_topk", "attend")
+    for _ in range(args.warmup):
+        runner.step()
+    torch.cuda.synchronize()
+
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)] for _ in range(args.steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_host = time.perf_counter()
+    start.record(stream)
+    for k in range(args.steps):
+        ev[k][0].record(stream)
+        runner.append()
+        ev[k][1].record(stream)
+        runner.index_score()
+        ev[k][2].record(stream)
+        runner.block_topk()
+        ev[k][3].record(stream)
+        runner.attend()
+        ev[k][4].record(stream)
+    end.record(stream)
+    torch.cuda.synchronize()
+    t_host = time.perf_counter() - t_host
+    total_ms = start.elapsed_time(end)
+    ms_per_step = total_ms / args.steps
+    stage_ms = {name: float(np.mean([ev[k][i].elapsed_time(ev[k][i + 1]) for k in range(args.steps)]))
+                for i, name in enumerate(stages)}
+
+    tokens = w.total_q
+    value = tokens / (ms_per_step / 1e3)
+    if runner.decode:
+        dom = "index_score"
+        algo = work["kidx_bytes"] + work["pooled_bytes"] / 2
+        achieved = algo / (stage_ms[dom] / 1e3) / 1e9
+        roof = {"bound": "hbm", "kernel": "msa_index_score (index_score_kernel, K_idx scan)", "achieved": achieved,
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": None}
+        step_bytes = work["kidx_bytes"] + work["kv_bytes"] + work["io_bytes"] + work["pooled_bytes"]
+        step_frac = step_bytes / (ms_per_step / 1e3) / 1e9 / HBM_PEAK_GBS
+        step_info = {"algorithmic_bytes": step_bytes, "hbm_frac_whole_step": step_frac}
+    else:
+        dom = max(("index_score", "attend"), key=lambda k: stage_ms[k])
+        algo = work["index_flops"] if dom == "index_score" else work["main_flops"]
+        achieved = algo / (stage_ms[dom] / 1e3) / 1e12
+        name = ("msa_index_score (index_score_kernel)" if dom == "index_score"
+                else "msa_sparse_attn_prefill (csr + kvouter + merge_local kernels)")
+        roof = {"bound": "mfma", "kernel": name, "achieved": achieved, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": achieved / BF16_PEAK_TFLOPS, "traffic": None}
+        step_flops = work["index_flops"] + work["main_flops"]
+        step_info = {"algorithmic_flops": step_flops,
+                     "mfma_frac_whole_step": step_flops / (ms_per_step / 1e3) / 1e12 / BF16_PEAK_TFLOPS,
+                     "prefill_tokens_per_s_without_append": tokens / ((ms_per_step - stage_ms["append"]) / 1e3)}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(inputs, runner, args.cpu_budget)
+
+    line = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded; Q/K/V ~ N(0,1) bf16, dyadic-integer Q_idx/K_idx)",
+        "config": {"workload": f"{w.name}: {w.description}", "mode": "decode" if runner.decode else "prefill",
+                   "num_seqs": w.num_seqs, "seq_lens": w.seq_lens[0], "query_tokens_per_step": tokens,
+                   "q_heads": w.num_q_heads, "kv_heads": w.num_kv_heads, "head_dim": w.head_dim,
+                   "index_dim": w.index_dim, "block_size": w.block_size, "top_k": w.top_k},
+        "stage_ms": stage_ms,
+        "step": step_info,
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "host_wall_s_timed_region": t_host,
+    }
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,176 @@
+// block_topk.hip — per (query, group) choice of the blocks the Main Branch
+// attends to.
+//
+// Source: "MiniMax 模型迭代与竞品分析：从 Text-01、M1、M2 到 M3", §2, MSA
+// inference step 3: 16 blocks per query and per GQA group, the local block
+// counted as one of the 16 rather than added as a 17th.  "MiniMax：Text-01 /
+// M1 → M2.7 → M3", §5 names an exp-free Top-k: the choice only compares block
+// scores, so no softmax over them is ever formed.  Equal scores go to the
+// lower block index.
+//
+// One wavefront per (query, group) row; candidates are the blocks b < c of
+// the row (c = the local block).  Scores are compared through a monotone
+// 32-bit key (order_key), which also makes -0 equal to +0.
+//   1. Each lane takes the maximum key of its strided candidates; the 15th
+//      largest of the 64 lane maxima, theta, bounds the answer from below:
+//      the 15 lanes above it each own a candidate >= theta, so every one of
+//      the 15 best candidates is >= theta.
+//   2. Candidates >= theta (usually a few dozen) are compacted into LDS in
+//      ascending block order; if more than 64 survive (massive ties), an
+//      exact search over all candidates is used instead.
+//   3. The exact 15th-largest key T among the survivors is found bit by bit
+//      with wave ballots; every survivor above T is kept, and the lowest-index
+//      survivors equal to T fill the remaining slots.
+//   4. Kept blocks are written in ascending order, then the local block.
+#include "msa_device.h"
+#include "msa_kernels.h"
+
+namespace msa {
+
+struct TopkArgs {
+  Problem p;
+  const float* scores;
+  int64_t ld;
+  int32_t* sel;
+  int hkv_shift;
+};
+
+__device__ __forceinline__ int lanes_below(uint64_t mask) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+}
+
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+}
+
+// k-th largest of the 64 lane values (k <= 64): the largest T with
+// |{lanes : x >= T}| >= k, built from the top bit down.
+__device__ __forceinline__ uint32_t kth_largest_lane(uint32_t x, int k) {
+  uint32_t t = 0;
+#pragma unroll
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t cand = t | (1u << bit);
+    if (__popcll(__ballot(x >= cand)) >= k) t = cand;
+  }
+  return t;
+}
+
+constexpr int kKeep = kTopK - 1;  // non-local blocks kept per row
+constexpr int kCached = 16;       // candidates per lane held in registers (rows with c <= 1024)
+
+template <bool CACHED>
+__device__ void select_row(const float* __restrict__ row, int c, int32_t* __restrict__ out, uint32_t* surv_key,
+                           int32_t* surv_idx) {
+  const int lane = threadIdx.x & 63;
+  uint32_t keys[CACHED ? kCached : 1];
+  auto key_at = [&](int j) -> uint32_t {
+    if constexpr (CACHED) return keys[j];
+    const int b = j * 64 + lane;
+    return b < c ? order_key(row[b]) : 0u;
+  };
+  const int nj = CACHED ? kCached : (c + 63) / 64;
+
+  // 1. lane maxima and theta.
+  uint32_t lmax = 0;
+  if constexpr (CACHED) {
+#pragma unroll
+    for (int j = 0; j < kCached; ++j) {
+      const int b = j * 64 + lane;
+      keys[j] = b < c ? order_key(row[b]) : 0u;
+      lmax = max(lmax, keys[j]);
+    }
+  } else {
+    for (int j = 0; j < nj; ++j) lmax = max(lmax, key_at(j));
+  }
+  const uint32_t theta = kth_largest_lane(lmax, kKeep);
+
+  // 2. compact survivors (key >= theta) in ascending block order.
+  int count = 0;
+  for (int j = 0; j < nj; ++j) {
+    const uint32_t k = key_at(j);
+    const bool ok = k >= theta && k != 0u;
+    const uint64_t m = __ballot(ok);
+    const int pos = count + lanes_below(m);
+    if (ok && pos < 64) {
+      surv_key[pos] = k;
+      surv_idx[pos] = j * 64 + lane;
+    }
+    count += __popcll(m);
+  }
+  wave_lds_sync();
+
+  if (count <= 64) {
+    // 3. exact threshold among the survivors.
+    const bool have = lane < count;
+    const uint32_t k = have ? surv_key[lane] : 0u;
+    const int idx = have ? surv_idx[lane] : 0;
+    const uint32_t T = kth_largest_lane(k, kKeep);
+    const int need = kKeep - __popcll(__ballot(have && k > T));
+    const uint64_t eq = __ballot(have && k == T);
+    const bool take = have && (k > T || (k == T && lanes_below(eq) < need));
+    const uint64_t tm = __ballot(take);
+    // 4. ascending output, local block last.
+    if (take) out[lanes_below(tm)] = idx;
+  } else {
+    // Massive ties: exact k-th largest over all candidates, bit by bit.
+    uint32_t T = 0;
+    for (int bit = 31; bit >= 0; --bit) {
+      const uint32_t cand = T | (1u << bit);
+      int n = 0;
+      for (int j = 0; j < nj; ++j) n += __popcll(__ballot(key_at(j) >= cand));
+      if (n >= kKeep) T = cand;
+    }
+    int gt = 0;
+    for (int j = 0; j < nj; ++j) gt += __popcll(__ballot(key_at(j) > T));
+    const int need = kKeep - gt;
+    int taken = 0, ties = 0;
+    for (int j = 0; j < nj && taken < kKeep; ++j) {
+      const uint32_t k = key_at(j);
+      const uint64_t eq = __ballot(k == T);
+      const bool take = k > T || (k == T && ties + lanes_below(eq) < need);
+      const uint64_t tm = __ballot(take);
+      if (take) out[taken + lanes_below(tm)] = j * 64 + lane;
+      taken += __popcll(tm);
+      ties += __popcll(eq);
+    }
+  }
+  if (lane == 0) out[kKeep] = c;
+}
+
+__global__ __launch_bounds__(256) void block_topk_kernel(TopkArgs a) {
+  __shared__ uint32_t surv_key[4][64];
+  __shared__ int32_t surv_idx[4][64];
+  const Problem& p = a.p;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int64_t R = (int64_t)blockIdx.x * 4 + wave;
+  if (R >= ((int64_t)p.total_q << a.hkv_shift)) return;
+  const int r = (int)(R >> a.hkv_shift);
+  const int s = seq_of_row(p.cu_q, p.num_seqs, r);
+  const int t = p.seq_lens[s] - (p.cu_q[s + 1] - r);
+  const int c = t >> 7;
+  int32_t* out = a.sel + R * kTopK;
+  if (c + 1 <= kTopK) {
+    if (lane < kTopK) out[lane] = lane <= c ? lane : -1;
+    return;
+  }
+  const float* row = a.scores + R * a.ld;
+  if (c <= kCached * 64)
+    select_row<true>(row, c, out, surv_key[wave], surv_idx[wave]);
+  else
+    select_row<false>(row, c, out, surv_key[wave], surv_idx[wave]);
+}
+
+hipError_t launch_block_topk(const Problem& p, const float* scores, int64_t ld, int32_t* sel, hipStream_t stream) {
+  int hkv_shift = 0;
+  while ((1 << hkv_shift) < p.hkv) ++hkv_shift;
+  const int64_t rows = (int64_t)p.total_q << hkv_shift;
+  if (rows == 0) return hipSuccess;
+  TopkArgs a{p, scores, ld, sel, hkv_shift};
+  hipLaunchKernelGGL(block_topk_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace msa

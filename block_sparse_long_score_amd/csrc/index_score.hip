@@ -1,0 +1,219 @@
+// index_score.hip — Index Branch scoring fused with the 128-token block
+// max-pool.
+//
+// Source: "MiniMax 模型迭代与竞品分析：从 Text-01、M1、M2 到 M3", §2, MSA
+// inference steps 1-2: per GQA group a light Q_idx scores the whole causal
+// context against one K_idx per token shared by all groups; the token scores
+// of each 128-token block are reduced by max so that a single strong token
+// lets its block be recalled.  "MiniMax：Text-01 / M1 → M2.7 → M3", §5: the
+// Index Branch works per GQA group.
+//
+// Mapping onto gfx950.  The scores of one tile form the product
+//     S^T[keys x columns] = K_idx[keys x d_idx] * Q_idx^T[d_idx x columns],
+// where a column is one (query, group) pair: the columns of consecutive query
+// rows are consecutive rows of the flattened Q_idx [total_q*Hkv][d_idx], so a
+// 32-column MFMA tile is 32/Hkv queries times all Hkv groups, and one K_idx
+// tile serves every group.  Keys sit on the MFMA M axis, so the 32x32 output
+// leaves 16 keys of one column in each lane's accumulators: the block max is
+// an in-lane max over the 4 key tiles of a block plus one exchange between the
+// two wave halves.  Token scores never leave registers; only one fp32 value
+// per (query, group, block) is written, staged through LDS so that each
+// (query, group) row is written as one contiguous run.
+//
+// Work split.  A workgroup (4 waves) owns a tile of 32*NCT columns (queries
+// aligned to absolute positions, so the tile lies inside one 128-token block)
+// and a chunk of `kc` key blocks; wave w takes blocks w, w+4, ... of the chunk.
+// Every wave keeps the whole Q_idx tile in registers and streams K_idx from
+// the cache through the block table.  Only the query tile's own block needs a
+// causal mask (key position > query position).
+#include "msa_device.h"
+#include "msa_kernels.h"
+
+namespace msa {
+
+struct IndexArgs {
+  Problem p;
+  const uint16_t* q_idx;
+  float* out;
+  int64_t ld;
+  int tq;         // queries per tile = 32 * NCT / hkv
+  int hkv_shift;  // log2(hkv)
+  int kc;         // key blocks per workgroup
+};
+
+// Pooled scores of one key block for every column tile, returned per lane
+// (lanes l and l^32 hold the two halves of column l%32 before the exchange).
+// DIAG: the block holds the query tile itself; keys after a column's query
+// position are masked.
+template <int DIDX, int NCT, bool DIAG>
+__device__ __forceinline__ void pool_block(const uint16_t* __restrict__ kbase, const bf16x8 (&bq)[NCT][DIDX / 16],
+                                           const int (&lim)[NCT], float (&runmax)[NCT]) {
+  constexpr int KS = DIDX / 16;
+  const int lane = threadIdx.x & 63;
+  const int half = lane >> 5, l32 = lane & 31;
+#pragma unroll
+  for (int ct = 0; ct < NCT; ++ct) runmax[ct] = -__builtin_inff();
+  // One 32-key tile at a time, the next tile's K_idx loaded while this one is
+  // multiplied: KS 16-byte loads per lane per tile.
+  bf16x8 ak[KS], ak_next[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) ak[ks] = as_bf16x8(load16(kbase + l32 * DIDX + ks * 16));
+  // The masked (diagonal) block keeps the key-tile loop rolled so its
+  // per-element masks are formed inside the loop instead of all up front.
+  constexpr int kUnroll = DIAG ? 1 : 4;
+#pragma unroll kUnroll
+  for (int m = 0; m < 4; ++m) {
+    __builtin_amdgcn_sched_barrier(0);
+    if (m < 3) {
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) ak_next[ks] = as_bf16x8(load16(kbase + ((m + 1) * 32 + l32) * DIDX + ks * 16));
+    }
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
+      f32x16 acc = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) acc = mfma32(ak[ks], bq[ct][ks], acc);
+      if constexpr (DIAG) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = m * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+          acc[r] = key > lim[ct] ? -__builtin_inff() : acc[r];
+        }
+      }
+      float mx = acc[0];
+#pragma unroll
+      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, acc[r]);
+      runmax[ct] = fmaxf(runmax[ct], mx);
+    }
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) ak[ks] = ak_next[ks];
+  }
+}
+
+template <int DIDX, int NCT>
+__global__ __launch_bounds__(256, 2) void index_score_kernel(IndexArgs a) {
+  constexpr int KS = DIDX / 16;  // MFMA k-steps over the index dimension
+  constexpr int NC = 32 * NCT;   // columns per workgroup
+  extern __shared__ float pooled_s[];  // [NC][kc + 1]
+  const Problem& p = a.p;
+
+  const int s = blockIdx.z;
+  const int row0 = p.cu_q[s];
+  const int nq = p.cu_q[s + 1] - row0;
+  if (nq <= 0) return;
+  const int seq_len = p.seq_lens[s];
+  const int first_pos = seq_len - nq;
+  const int tq = a.tq;
+  const int tile0 = (first_pos / tq) * tq;
+  const int n_tiles = (seq_len - 1 - tile0) / tq + 1;
+  if ((int)blockIdx.x >= n_tiles) return;
+  const int p0 = tile0 + (n_tiles - 1 - (int)blockIdx.x) * tq;  // late (heavy) tiles first
+  const int c_tile = p0 >> 7;
+  const int kb0 = blockIdx.y * a.kc;
+  if (kb0 > c_tile) return;
+  const int nkb = min(a.kc, c_tile + 1 - kb0);
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int half = lane >> 5;
+  const int l32 = lane & 31;
+  const int ld_s = a.kc + 1;
+  const int hkv_mask = (1 << a.hkv_shift) - 1;
+
+  // This lane's column in every column tile, and its Q_idx operand.
+  bf16x8 bq[NCT][KS];
+  int col_pos[NCT];
+#pragma unroll
+  for (int ct = 0; ct < NCT; ++ct) {
+    const int col = ct * 32 + l32;
+    const int pos = p0 + (col >> a.hkv_shift);
+    const bool valid = pos >= first_pos && pos < seq_len;
+    col_pos[ct] = pos;
+    const int64_t R = ((int64_t)(row0 + pos - first_pos) << a.hkv_shift) + (col & hkv_mask);
+    const uint16_t* src = a.q_idx + R * DIDX + half * 8;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      u32x4 v = valid ? load16(src + ks * 16) : u32x4{0u, 0u, 0u, 0u};
+      bq[ct][ks] = as_bf16x8(v);
+    }
+  }
+
+  const int32_t* table = p.block_table + (int64_t)s * p.max_blocks_per_seq;
+  for (int kb = kb0 + wave; kb < kb0 + nkb; kb += 4) {
+    const int phys = table[kb];
+    float runmax[NCT];
+    if (phys >= 0 && phys < p.num_blocks) {
+      const uint16_t* kbase = p.k_idx + (int64_t)phys * kBlock * DIDX + half * 8;
+      if (kb == c_tile) {
+        int lim[NCT];  // in-block index of each column's query: later keys are masked
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) lim[ct] = col_pos[ct] - kb * kBlock;
+        pool_block<DIDX, NCT, true>(kbase, bq, lim, runmax);
+      } else {
+        const int lim[NCT] = {};
+        pool_block<DIDX, NCT, false>(kbase, bq, lim, runmax);
+      }
+    } else {
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct) runmax[ct] = __builtin_nanf("");  // table precondition violated
+    }
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
+      const float v = fmaxf(runmax[ct], swap_halves(runmax[ct]));
+      if (half == 0) pooled_s[(ct * 32 + l32) * ld_s + (kb - kb0)] = v;
+    }
+  }
+  __syncthreads();
+
+  // Each valid (query, group) row writes its nkb pooled scores contiguously.
+  for (int idx = threadIdx.x; idx < NC * nkb; idx += blockDim.x) {
+    const int col = idx / nkb;
+    const int j = idx - col * nkb;
+    const int pos = p0 + (col >> a.hkv_shift);
+    if (pos < first_pos || pos >= seq_len) continue;
+    const int64_t R = ((int64_t)(row0 + pos - first_pos) << a.hkv_shift) + (col & hkv_mask);
+    float v = pooled_s[col * ld_s + j];
+    v = (v == 0.0f) ? 0.0f : v;  // -0 and +0 are the same score
+    a.out[R * a.ld + kb0 + j] = v;
+  }
+}
+
+template <int DIDX, int NCT>
+static hipError_t launch_index_t(const IndexArgs& a, dim3 grid, hipStream_t stream) {
+  const size_t lds = (size_t)32 * NCT * (a.kc + 1) * sizeof(float);
+  hipLaunchKernelGGL((index_score_kernel<DIDX, NCT>), grid, dim3(256), lds, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_index_score(const Problem& p, const uint16_t* q_idx, float* scores, int64_t ld,
+                              const int32_t* seq_lens_host, const int32_t* cu_q_host, hipStream_t stream) {
+  int hkv_shift = 0;
+  while ((1 << hkv_shift) < p.hkv) ++hkv_shift;
+  // Decode-shaped batches (few queries per sequence) use one 32-column tile;
+  // prefill uses four, which reuses each K_idx tile across 128 columns.
+  int max_q = 0;
+  for (int s = 0; s < p.num_seqs; ++s) max_q = std::max(max_q, cu_q_host[s + 1] - cu_q_host[s]);
+  if (max_q <= 0) return hipSuccess;
+  const int nct = (max_q * p.hkv <= 32) ? 1 : 4;
+  const int tq = 32 * nct / p.hkv;
+  // Grid: tiles x key chunks x sequences; count the block-tile work to size the chunks.
+  int max_tiles = 0, max_blocks = 0;
+  int64_t work = 0;
+  for (int s = 0; s < p.num_seqs; ++s) {
+    const int nq = cu_q_host[s + 1] - cu_q_host[s];
+    if (nq <= 0) continue;
+    const int L = seq_lens_host[s];
+    const int t0 = ((L - nq) / tq) * tq;
+    const int tiles = (L - 1 - t0) / tq + 1;
+    max_tiles = std::max(max_tiles, tiles);
+    max_blocks = std::max(max_blocks, (L - 1) / kBlock + 1);
+    work += (int64_t)tiles * ((t0 / kBlock + (L - 1) / kBlock) / 2 + 1);
+  }
+  int kc = (int)std::min<int64_t>(64, std::max<int64_t>(4, (work / 8192 + 3) / 4 * 4));
+  IndexArgs a{p, q_idx, scores, ld, tq, hkv_shift, kc};
+  dim3 grid((unsigned)max_tiles, (unsigned)((max_blocks + kc - 1) / kc), (unsigned)p.num_seqs);
+  if (p.index_dim == 64) return nct == 4 ? launch_index_t<64, 4>(a, grid, stream) : launch_index_t<64, 1>(a, grid, stream);
+  return nct == 4 ? launch_index_t<32, 4>(a, grid, stream) : launch_index_t<32, 1>(a, grid, stream);
+}
+
+}  // namespace msa

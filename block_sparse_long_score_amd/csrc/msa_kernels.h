@@ -1,0 +1,49 @@
+// msa_kernels.h — internal interface between the C-ABI host layer
+// (msa_api.hip) and the kernel files.  Not part of the C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include <algorithm>
+
+namespace msa {
+
+// Everything a kernel needs about the batch and the cache, by value.
+struct Problem {
+  // geometry
+  int hq, hkv, head_dim, index_dim, group;  // group = hq / hkv
+  float scale_log2e;                         // softmax scale * log2(e)
+  // batch
+  int num_seqs, total_q;
+  const int32_t* seq_lens;  // device
+  const int32_t* cu_q;      // device
+  // cache
+  const uint16_t* k;        // bf16 [num_blocks][128][hkv][head_dim]
+  const uint16_t* v;
+  const uint16_t* k_idx;    // bf16 [num_blocks][128][index_dim]
+  const int32_t* block_table;
+  int num_blocks, max_blocks_per_seq;
+};
+
+hipError_t launch_kv_append(const Problem& p, uint16_t* k_cache, uint16_t* v_cache, uint16_t* k_idx_cache,
+                            const uint16_t* k_new, const uint16_t* v_new, const uint16_t* k_idx_new,
+                            int max_q_per_seq, hipStream_t stream);
+
+hipError_t launch_index_score(const Problem& p, const uint16_t* q_idx, float* scores, int64_t ld,
+                              const int32_t* seq_lens_host, const int32_t* cu_q_host, hipStream_t stream);
+
+hipError_t launch_block_topk(const Problem& p, const float* scores, int64_t ld, int32_t* sel, hipStream_t stream);
+
+// Prefill Main Branch (blocks outer, queries inner) and its workspace.
+size_t prefill_workspace_bytes(const Problem& p);
+hipError_t launch_attn_prefill(const Problem& p, const uint16_t* q, const int32_t* sel, uint16_t* out, void* ws,
+                               const int32_t* seq_lens_host, const int32_t* cu_q_host, hipStream_t stream);
+
+// Decode Main Branch (one query per sequence, split over its selected blocks).
+size_t decode_workspace_bytes(const Problem& p);
+hipError_t launch_attn_decode(const Problem& p, const uint16_t* q, const int32_t* sel, uint16_t* out, void* ws,
+                              hipStream_t stream);
+
+}  // namespace msa

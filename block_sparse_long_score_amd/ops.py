@@ -1,0 +1,171 @@
+"""Python binding of libmsa with the C ABI's entry-point names.
+
+Argument marshalling only: tensors become device pointers, host mirrors
+become host pointers, and the call is enqueued on the current HIP stream (or
+the one given).  Every step of the computation runs in the library's kernels;
+a failing status raises MsaError with the library's own message.
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+
+import numpy as np
+import torch
+
+from . import _lib
+from ._lib import MSA_CALL_SPARSE_ATTN_DECODE, MSA_CALL_SPARSE_ATTN_PREFILL, MsaBatch, MsaCache, MsaDims
+
+__all__ = ["Dims", "Cache", "Batch", "MsaError", "msa_kv_append", "msa_index_score", "msa_block_topk",
+           "msa_sparse_attn_prefill", "msa_sparse_attn_decode", "msa_workspace_size", "msa_abi_version",
+           "MSA_CALL_SPARSE_ATTN_PREFILL", "MSA_CALL_SPARSE_ATTN_DECODE"]
+
+
+class MsaError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{_lib.STATUS_NAMES.get(status, status)}: {message}")
+        self.status = status
+
+
+@dataclasses.dataclass(frozen=True)
+class Dims:
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim: int
+    index_dim: int
+    block_size: int = 128
+    top_k: int = 16
+    softmax_scale: float = 0.0  # <= 0: 1/sqrt(head_dim)
+
+    def c(self) -> MsaDims:
+        return MsaDims(self.num_q_heads, self.num_kv_heads, self.head_dim, self.index_dim, self.block_size,
+                       self.top_k, self.softmax_scale)
+
+
+@dataclasses.dataclass
+class Cache:
+    """Block-major cache: k, v bf16 [num_blocks, 128, Hkv, D]; k_idx bf16
+    [num_blocks, 128, d_idx]; block_table int32 [num_seqs, max_blocks_per_seq]."""
+    k: torch.Tensor
+    v: torch.Tensor
+    k_idx: torch.Tensor
+    block_table: torch.Tensor
+
+    @staticmethod
+    def allocate(dims: Dims, num_blocks: int, block_table: torch.Tensor) -> "Cache":
+        dev = block_table.device
+        shape = (num_blocks, dims.block_size, dims.num_kv_heads, dims.head_dim)
+        return Cache(torch.empty(shape, dtype=torch.bfloat16, device=dev),
+                     torch.empty(shape, dtype=torch.bfloat16, device=dev),
+                     torch.empty((num_blocks, dims.block_size, dims.index_dim), dtype=torch.bfloat16, device=dev),
+                     block_table.to(torch.int32).contiguous())
+
+    def c(self) -> MsaCache:
+        return MsaCache(self.k.data_ptr(), self.v.data_ptr(), self.k_idx.data_ptr(), self.block_table.data_ptr(),
+                        self.k.shape[0], self.block_table.shape[1])
+
+
+@dataclasses.dataclass
+class Batch:
+    """seq_lens: tokens per sequence after this step's append; the queries of
+    sequence s are its last cu_q[s+1]-cu_q[s] positions."""
+    seq_lens: torch.Tensor  # device int32 [num_seqs]
+    cu_q: torch.Tensor      # device int32 [num_seqs + 1]
+    seq_lens_host: np.ndarray
+    cu_q_host: np.ndarray
+
+    @staticmethod
+    def make(seq_lens, q_lens, device) -> "Batch":
+        sl = np.ascontiguousarray(np.asarray(seq_lens, dtype=np.int32))
+        cu = np.ascontiguousarray(np.concatenate([[0], np.cumsum(np.asarray(q_lens, dtype=np.int64))]).astype(np.int32))
+        return Batch(torch.from_numpy(sl).to(device), torch.from_numpy(cu).to(device), sl, cu)
+
+    @property
+    def num_seqs(self) -> int:
+        return int(self.seq_lens_host.shape[0])
+
+    @property
+    def total_q(self) -> int:
+        return int(self.cu_q_host[-1])
+
+    @property
+    def max_blocks(self) -> int:
+        return int(max(((int(n) + 127) // 128 for n in self.seq_lens_host), default=0))
+
+    def c(self) -> MsaBatch:
+        return MsaBatch(self.num_seqs, self.total_q, self.seq_lens.data_ptr(), self.cu_q.data_ptr(),
+                        self.seq_lens_host.ctypes.data, self.cu_q_host.ctypes.data)
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def _ptr(t: torch.Tensor, name: str, dtype) -> int:
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def _check(status: int):
+    if status != _lib.MSA_OK:
+        raise MsaError(status, _lib.load().msa_last_error().decode())
+
+
+def msa_abi_version() -> int:
+    return int(_lib.load().msa_abi_version())
+
+
+def msa_kv_append(dims: Dims, cache: Cache, batch: Batch, k_new, v_new, k_idx_new, stream=None):
+    L = _lib.load()
+    d, c, b = dims.c(), cache.c(), batch.c()
+    _check(L.msa_kv_append(ctypes.byref(d), ctypes.byref(c), ctypes.byref(b), _ptr(k_new, "k_new", torch.bfloat16),
+                           _ptr(v_new, "v_new", torch.bfloat16), _ptr(k_idx_new, "k_idx_new", torch.bfloat16),
+                           _stream(stream)))
+
+
+def msa_index_score(dims: Dims, cache: Cache, batch: Batch, q_idx, block_scores, stream=None):
+    """block_scores: float32 [total_q, Hkv, ld]; entries after each row's block are left untouched."""
+    L = _lib.load()
+    d, c, b = dims.c(), cache.c(), batch.c()
+    _check(L.msa_index_score(ctypes.byref(d), ctypes.byref(c), ctypes.byref(b), _ptr(q_idx, "q_idx", torch.bfloat16),
+                             _ptr(block_scores, "block_scores", torch.float32), block_scores.shape[-1],
+                             _stream(stream)))
+
+
+def msa_block_topk(dims: Dims, batch: Batch, block_scores, sel, stream=None):
+    L = _lib.load()
+    d, b = dims.c(), batch.c()
+    _check(L.msa_block_topk(ctypes.byref(d), ctypes.byref(b), _ptr(block_scores, "block_scores", torch.float32),
+                            block_scores.shape[-1], _ptr(sel, "sel", torch.int32), _stream(stream)))
+
+
+def msa_workspace_size(dims: Dims, cache: Cache, batch: Batch, call: int) -> int:
+    L = _lib.load()
+    d, c, b = dims.c(), cache.c(), batch.c()
+    n = int(L.msa_workspace_size(ctypes.byref(d), ctypes.byref(c), ctypes.byref(b), call))
+    if n == 0:
+        raise MsaError(2, L.msa_last_error().decode())
+    return n
+
+
+def _attn(fn_name, dims, cache, batch, q, sel, out, workspace, stream):
+    L = _lib.load()
+    d, c, b = dims.c(), cache.c(), batch.c()
+    _check(getattr(L, fn_name)(ctypes.byref(d), ctypes.byref(c), ctypes.byref(b), _ptr(q, "q", torch.bfloat16),
+                               _ptr(sel, "sel", torch.int32), _ptr(out, "out", torch.bfloat16),
+                               _ptr(workspace, "workspace", torch.uint8), workspace.numel(), _stream(stream)))
+
+
+def msa_sparse_attn_prefill(dims: Dims, cache: Cache, batch: Batch, q, sel, out, workspace, stream=None):
+    _attn("msa_sparse_attn_prefill", dims, cache, batch, q, sel, out, workspace, stream)
+
+
+def msa_sparse_attn_decode(dims: Dims, cache: Cache, batch: Batch, q, sel, out, workspace, stream=None):
+    _attn("msa_sparse_attn_decode", dims, cache, batch, q, sel, out, workspace, stream)

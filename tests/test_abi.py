@@ -1,0 +1,140 @@
+"""C-ABI checks that need no GPU: the library loads, exports every entry
+point declared in include/msa.h, and rejects invalid arguments on the host
+(before any HIP call) with the documented status codes."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from block_sparse_long_score_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "msa.h")
+
+OK, NULLP, SHAPE, UNSUP, MISAL, CAP, WS, HIP = range(8)
+FAKE = 1 << 20  # a 16-byte aligned non-null address that is never dereferenced
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        from block_sparse_long_score_amd import build
+        build.build()
+    return _lib.load()
+
+
+def _dims(**kw):
+    base = dict(num_q_heads=48, num_kv_heads=8, head_dim=128, index_dim=64, block_size=128, top_k=16,
+                softmax_scale=0.0)
+    base.update(kw)
+    return _lib.MsaDims(**base)
+
+
+class _Batch:
+    def __init__(self, seq_lens, q_lens):
+        self.sl = np.asarray(seq_lens, np.int32)
+        self.cu = np.concatenate([[0], np.cumsum(q_lens)]).astype(np.int32)
+        self.c = _lib.MsaBatch(len(seq_lens), int(self.cu[-1]), FAKE, FAKE, self.sl.ctypes.data, self.cu.ctypes.data)
+
+
+def _cache(num_blocks=64, mbps=16, **kw):
+    base = dict(k=FAKE, v=FAKE, k_idx=FAKE, block_table=FAKE, num_blocks=num_blocks, max_blocks_per_seq=mbps)
+    base.update(kw)
+    return _lib.MsaCache(**base)
+
+
+def test_exports_every_declared_entry_point(lib):
+    decls = set(re.findall(r"^\S.*?\b(msa_\w+)\(", open(HEADER).read(), re.M))
+    assert {"msa_kv_append", "msa_index_score", "msa_block_topk", "msa_sparse_attn_prefill",
+            "msa_sparse_attn_decode"} <= decls
+    for name in decls:
+        assert hasattr(lib, name), f"{name} declared in msa.h but not exported"
+
+
+def test_abi_version_matches_header(lib):
+    m = re.search(r"#define MSA_ABI_VERSION (\d+)", open(HEADER).read())
+    assert lib.msa_abi_version() == int(m.group(1))
+
+
+def test_status_strings(lib):
+    for code, name in _lib.STATUS_NAMES.items():
+        assert lib.msa_status_string(code).decode() == name
+    assert lib.msa_status_string(99).decode() == "MSA_ERR_UNKNOWN"
+
+
+def _index(lib, dims, cache, batch, q_idx=FAKE, out=FAKE, ld=16):
+    return lib.msa_index_score(ctypes.byref(dims), ctypes.byref(cache), ctypes.byref(batch.c), q_idx, out, ld, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(head_dim=96), UNSUP), (dict(index_dim=48), UNSUP), (dict(block_size=64), UNSUP), (dict(top_k=8), UNSUP),
+    (dict(num_kv_heads=6, num_q_heads=48), UNSUP), (dict(num_q_heads=44), SHAPE), (dict(num_q_heads=0), SHAPE),
+    (dict(num_q_heads=8 * 32, num_kv_heads=8), UNSUP), (dict(softmax_scale=float("inf")), SHAPE),
+])
+def test_bad_dims(lib, kw, status):
+    b = _Batch([1024], [1024])
+    assert _index(lib, _dims(**kw), _cache(), b) == status
+    assert lib.msa_last_error().decode() != ""
+
+
+def test_bad_batch(lib):
+    d, c = _dims(), _cache()
+    assert _index(lib, d, c, _Batch([100], [101])) == SHAPE           # more queries than tokens
+    assert _index(lib, d, c, _Batch([16 * 128 + 1], [1])) == CAP       # beyond max_blocks_per_seq
+    b = _Batch([100, 100], [10, 10])
+    b.cu[2] = 5
+    assert _index(lib, d, c, b) == SHAPE                               # cu_q decreasing
+    b = _Batch([100], [10])
+    b.c.total_q = 11
+    assert _index(lib, d, c, b) == SHAPE                               # total_q mismatch
+    assert _index(lib, d, c, _Batch([2048], [2048]), ld=15) == SHAPE   # ld too small
+    b = _Batch([100], [10])
+    b.c.seq_lens_host = None
+    assert _index(lib, d, c, b) == NULLP
+
+
+def test_null_and_misaligned_pointers(lib):
+    d, b = _dims(), _Batch([1024], [1024])
+    assert _index(lib, d, _cache(k=None), b) == NULLP
+    assert _index(lib, d, _cache(k_idx=FAKE + 8), b) == MISAL
+    assert _index(lib, d, _cache(), b, q_idx=None) == NULLP
+    assert _index(lib, d, _cache(), b, out=FAKE + 4) == MISAL
+    assert lib.msa_index_score(None, ctypes.byref(_cache()), ctypes.byref(b.c), FAKE, FAKE, 16, None) == NULLP
+
+
+def test_topk_and_append_validation(lib):
+    d, b = _dims(), _Batch([1024], [1024])
+    assert lib.msa_block_topk(ctypes.byref(d), ctypes.byref(b.c), FAKE, 4, FAKE, None) == SHAPE  # ld < 8 blocks
+    assert lib.msa_block_topk(ctypes.byref(d), ctypes.byref(b.c), FAKE, 8, None, None) == NULLP
+    c = _cache()
+    assert lib.msa_kv_append(ctypes.byref(d), ctypes.byref(c), ctypes.byref(b.c), FAKE, None, FAKE, None) == NULLP
+    assert lib.msa_kv_append(ctypes.byref(d), ctypes.byref(c), ctypes.byref(b.c), FAKE, FAKE, FAKE + 2, None) == MISAL
+
+
+def test_attention_validation(lib):
+    d, c = _dims(), _cache()
+    b = _Batch([1024, 900], [1, 2])
+    need = lib.msa_workspace_size(ctypes.byref(d), ctypes.byref(c), ctypes.byref(b.c), 2)
+    assert need > 0
+    args = (ctypes.byref(d), ctypes.byref(c), ctypes.byref(b.c), FAKE, FAKE, FAKE)
+    assert lib.msa_sparse_attn_decode(*args, FAKE, need, None) == SHAPE  # sequence 1 has two queries
+    b1 = _Batch([1024, 900], [1, 1])
+    need1 = lib.msa_workspace_size(ctypes.byref(d), ctypes.byref(c), ctypes.byref(b1.c), 2)
+    args1 = (ctypes.byref(d), ctypes.byref(c), ctypes.byref(b1.c), FAKE, FAKE, FAKE)
+    assert lib.msa_sparse_attn_decode(*args1, FAKE, need1 - 1, None) == WS
+    assert lib.msa_sparse_attn_decode(*args1, None, need1, None) == WS
+    needp = lib.msa_workspace_size(ctypes.byref(d), ctypes.byref(c), ctypes.byref(b.c), 1)
+    assert lib.msa_sparse_attn_prefill(*args, FAKE, needp - 1, None) == WS
+    assert lib.msa_sparse_attn_prefill(*args, FAKE + 8, needp, None) == MISAL
+    assert lib.msa_workspace_size(ctypes.byref(d), ctypes.byref(c), ctypes.byref(b.c), 7) == 0
+
+
+def test_workspace_grows_with_queries(lib):
+    d, c = _dims(), _cache(num_blocks=4096, mbps=1024)
+    sizes = [lib.msa_workspace_size(ctypes.byref(d), ctypes.byref(c), ctypes.byref(_Batch([n], [n]).c), 1)
+             for n in (128, 4096, 65536)]
+    assert sizes[0] < sizes[1] < sizes[2]
+    # fp16 partials of up to 15 non-local blocks per (row, head) dominate
+    assert sizes[2] >= 65536 * 48 * 15 * 128 * 2

@@ -1,0 +1,220 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle.
+
+Selections and pooled index scores must match bit for bit (the indexer
+inputs are dyadic, so every score is exact in any summation order);
+attention outputs must be within max-abs 2e-2 and mean-abs 2e-3 of the
+oracle's double-precision result.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from block_sparse_long_score_amd import ops
+from block_sparse_long_score_amd.inputs import WORKLOADS, bf16_bits, make_inputs
+from block_sparse_long_score_amd.pipeline import MsaRunner
+from tests.gpu_helpers import check_selection_invariants, compare_rows, oracle_rows, seq_rows
+
+pytestmark = pytest.mark.gpu
+
+M2 = WORKLOADS["c1"]
+
+
+def _announce(msg):
+    print(f"[gpu-case] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def _run(w, seed=None):
+    _announce(f"{w.name}: seq_lens={w.seq_lens[:4]}{'...' if w.num_seqs > 4 else ''} q_lens={w.q_lens[:4]} "
+              f"Hq={w.num_q_heads} Hkv={w.num_kv_heads} D={w.head_dim} d_idx={w.index_dim}")
+    inp = make_inputs(w, "cuda", seed)
+    runner = MsaRunner(inp)
+    runner.step()
+    torch.cuda.synchronize()
+    return runner
+
+
+def _all_rows(runner, check_out=True):
+    w = runner.inputs.workload
+    for s in range(w.num_seqs):
+        if w.q_lens[s]:
+            compare_rows(runner, s, runner.inputs.positions(s), check_out=check_out)
+
+
+@pytest.fixture(autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def test_kv_append_places_every_token():
+    w = M2.with_sizes("append", [300, 1, 4097], [300, 1, 5], permuted_table=True)
+    runner = _run(w)
+    inp = runner.inputs
+    table = inp.block_table.long()
+    for s in range(w.num_seqs):
+        n = w.seq_lens[s]
+        pos = torch.arange(n, device="cuda")
+        phys = table[s, pos // 128]
+        off = int(inp.tok_off[s])
+        assert torch.equal(runner.cache.k[phys, pos % 128], inp.k[off:off + n])
+        assert torch.equal(runner.cache.v[phys, pos % 128], inp.v[off:off + n])
+        assert torch.equal(runner.cache.k_idx[phys, pos % 128], inp.k_idx[off:off + n])
+
+
+def test_c0_tiny_prefill_all_rows():
+    runner = _run(WORKLOADS["c0"])
+    _all_rows(runner)
+    check_selection_invariants(runner)
+
+
+def test_m2_shape_ragged_prefill():
+    runner = _run(M2.with_sizes("ragged", [3001], [3001]))
+    _all_rows(runner)
+
+
+def test_prefill_chunk_starting_mid_block():
+    runner = _run(M2.with_sizes("chunk", [5000], [777]))
+    _all_rows(runner)
+
+
+def test_multi_sequence_prefill_batch():
+    runner = _run(M2.with_sizes("multi", [2500, 129, 1, 4100, 2048], [2500, 60, 1, 900, 17], permuted_table=True))
+    _all_rows(runner)
+    check_selection_invariants(runner)
+
+
+def test_decode_batch_ragged_lengths():
+    runner = _run(M2.with_sizes("decode", [1, 128, 129, 2049, 5000, 9999, 16 * 128, 16 * 128 + 1], [1] * 8,
+                                permuted_table=True))
+    assert runner.decode
+    _all_rows(runner)
+    check_selection_invariants(runner)
+
+
+def test_decode_equals_prefill_last_row():
+    """A decode step over N cached tokens computes the prefill's last row."""
+    import dataclasses
+    w = M2.with_sizes("p9", [4500], [4500])
+    runner_p = _run(w)
+    inp = runner_p.inputs
+    wd = M2.with_sizes("p9d", [4500], [1])
+    inp_d = dataclasses.replace(inp, workload=wd, q=inp.q[-1:].contiguous(), q_idx=inp.q_idx[-1:].contiguous())
+    _announce("decode over the same 4500 tokens")
+    runner_d = MsaRunner(inp_d)
+    runner_d.step()
+    torch.cuda.synchronize()
+    assert runner_d.decode
+    assert torch.equal(runner_d.sel[0], runner_p.sel[-1])
+    assert torch.equal(runner_d.scores[0], runner_p.scores[-1])
+    diff = (runner_d.out[0].float() - runner_p.out[-1].float()).abs()
+    assert float(diff.max()) <= 2e-2
+    compare_rows(runner_d, 0, [4499])
+
+
+def test_topk_on_oracle_scores_with_ties():
+    """The selection kernel alone, fed block scores written by the oracle
+    (real rows) and by hand (massive ties, +/-0, long rows past the register
+    cache)."""
+    w = M2.with_sizes("topk", [9000], [9000])
+    inp = make_inputs(w, "cuda")
+    runner = MsaRunner(inp)
+    pos = np.array([0, 127, 128, 2047, 2048, 2049, 5000, 8999], np.int64)
+    pooled, sel, _ = oracle_rows(inp, 0, pos, attend=False)
+    rows = seq_rows(inp, 0, pos)
+    runner.scores.zero_()
+    runner.scores[torch.from_numpy(rows).cuda()] = torch.from_numpy(np.nan_to_num(pooled, neginf=0.0)).cuda()
+    runner.block_topk()
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(runner.sel[torch.from_numpy(rows).cuda()].cpu().numpy(), sel)
+
+    import oracle
+    rng = np.random.default_rng(3)
+    n_rows, ld = 64, 8300
+    pos = np.sort(rng.integers(2048, ld * 128, size=n_rows)).astype(np.int64)
+    pos[:3] = [ld * 128 - 1, 1024 * 128 + 5, 1024 * 128 - 1]
+    vals = rng.integers(-3, 4, size=(n_rows, 1, ld)).astype(np.float32) / 4
+    vals[0] = 0.0                      # every block ties
+    vals[1, 0, ::2] = -0.0             # signed zeros tie with +0
+    vals[2, 0, :] = 1.5
+    want = oracle.select(pos, vals, 128, 16)
+    wt = M2.with_sizes("topk2", [int(p) + 1 for p in pos], [1] * n_rows)
+    d = ops.Dims(8, 1, 128, 64)
+    b = ops.Batch.make(wt.seq_lens, wt.q_lens, "cuda")
+    scores = torch.from_numpy(vals).cuda()
+    got = torch.empty((n_rows, 1, 16), dtype=torch.int32, device="cuda")
+    _announce("topk on hand-made scores, rows up to 8300 blocks")
+    ops.msa_block_topk(d, b, scores, got)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(got.cpu().numpy(), want)
+
+
+def test_attention_alone_with_oracle_selection():
+    """The Main Branch alone, fed the oracle's selection."""
+    w = M2.with_sizes("attn", [4000], [4000])
+    inp = make_inputs(w, "cuda")
+    runner = MsaRunner(inp)
+    runner.append()
+    pos = inp.positions(0)
+    pooled, sel, _ = oracle_rows(inp, 0, pos, attend=False)
+    _announce("prefill attention with oracle selection, T=4000")
+    runner.attend(sel=torch.from_numpy(sel).cuda())
+    torch.cuda.synchronize()
+    runner.sel.copy_(torch.from_numpy(sel).cuda())
+    runner.scores.copy_(torch.from_numpy(np.nan_to_num(pooled, neginf=0.0)).cuda())
+    compare_rows(runner, 0, pos, check_scores=False)
+
+
+def test_two_runs_are_identical():
+    w = M2.with_sizes("det", [3000, 2000], [3000, 300])
+    runner = _run(w)
+    sel1, out1 = runner.sel.clone(), runner.out.clone()
+    runner.step()
+    torch.cuda.synchronize()
+    assert torch.equal(sel1, runner.sel)
+    assert torch.equal(out1.view(torch.int16), runner.out.view(torch.int16))
+
+
+# ----------------------------------------------------------- full sizes
+
+
+def _sample_positions(n, first, count, seed):
+    rng = np.random.default_rng(seed)
+    fixed = [p for p in (0, 127, 128, 2047, 2048, n - 1) if first <= p < n]
+    extra = rng.integers(first, n, size=count - len(fixed))
+    return np.unique(np.concatenate([fixed, extra]).astype(np.int64))
+
+
+def test_c1_full_size_sampled_rows():
+    runner = _run(WORKLOADS["c1"])
+    check_selection_invariants(runner)
+    compare_rows(runner, 0, _sample_positions(32768, 0, 384, 1))
+
+
+def test_c2_full_size_decode_all_rows():
+    runner = _run(WORKLOADS["c2"])
+    check_selection_invariants(runner)
+    for s in range(32):
+        compare_rows(runner, s, [131071])
+
+
+def test_c3_full_size_sampled_rows():
+    runner = _run(WORKLOADS["c3"])
+    check_selection_invariants(runner)
+    compare_rows(runner, 0, _sample_positions(131072, 0, 256, 3))
+
+
+def test_c4_decode_1m_all_rows():
+    runner = _run(WORKLOADS["c4d"])
+    check_selection_invariants(runner)
+    for s in range(4):
+        compare_rows(runner, s, [(1 << 20) - 1])
+
+
+def test_c4_prefill_chunk_on_1m_cache_sampled_rows():
+    n = (1 << 20) + 8192
+    runner = _run(WORKLOADS["c4p"])
+    check_selection_invariants(runner)
+    compare_rows(runner, 0, _sample_positions(n, 1 << 20, 66, 4))
