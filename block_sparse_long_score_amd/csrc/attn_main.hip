@@ -1,0 +1,600 @@
+// attn_main.hip — Main Branch of MSA: exact softmax attention of every query
+// row over the tokens of its selected blocks, for prefill and decode.
+//
+// Source: "MiniMax 模型迭代与竞品分析：从 Text-01、M1、M2 到 M3", §2: the
+// softmax-attention equation (scores q.k/sqrt(d_k), softmax over the attended
+// keys, probability-weighted sum of values) and MSA step 4 (standard softmax
+// attention restricted to the chosen blocks, at most 16 x 128 = 2048 tokens).
+// "MiniMax：Text-01 / M1 → M2.7 → M3", §5 names a KV-outer kernel design for
+// the block-level irregular access; "前沿架构解码手记（三）" §2.1 motivates the
+// block-major cache: a chosen block is one contiguous piece per head.
+//
+// Schedule (blocks outer).  The up-to-16 blocks a (query, group) row selects
+// are scattered, so queries that share a block are scattered too: gathering
+// the blocks per query would move 1 MB of K/V per (query, group) at head_dim
+// 128.  Instead every (block, group) pair is loaded into LDS once per chunk of
+// the queries that selected it:
+//   prefill  1. invert the selections into one list of (row, slot) entries per
+//               (sequence, group, logical block): an LDS histogram per chunk of
+//               512 query rows, a column scan over the chunks, a scan over the
+//               lists, and a scatter (no global atomics);
+//            2. kvouter: one workgroup per chunk of a list stages the block's K
+//               and V in LDS and runs every listed row's heads against it with
+//               bf16 MFMA; rows whose local block this is mask the keys after
+//               the query.  Output per (row, slot, head): block-local softmax
+//               statistics and the normalised output in fp16 scaled by 2^-e;
+//   decode   kvouter in direct mode: one workgroup per (slot, group, sequence);
+//   both     3. merge: per (row, head) a streaming log-sum-exp over the slots,
+//               rounded to bf16.
+// The softmax works in base 2 with the scale folded into log2(e).
+//
+// MFMA mapping (32x32x16 bf16, wave64), per tile of 32 (row, head) pairs:
+//   S^T[128 keys x 32 rows] = K[keys x D] * Q^T[D x rows]   (K from LDS, Q from HBM)
+//   O^T[D x 32 rows]        = V^T[D x keys] * P^T[keys x rows]
+// With keys on the M axis each lane owns one row, so row max/sum are in-lane
+// plus one exchange between wave halves, and the S^T accumulators rounded to
+// bf16 are directly the B operand of the P.V product; V is stored transposed
+// in LDS so its A operand is two 8-byte reads.
+#include "msa_device.h"
+#include "msa_kernels.h"
+
+namespace msa {
+
+constexpr int kCsrRows = 512;  // query rows per selection-inversion workgroup
+
+static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+static int hkv_shift_of(const Problem& p) {
+  int s = 0;
+  while ((1 << s) < p.hkv) ++s;
+  return s;
+}
+
+// Entries (row, slot) per kvouter workgroup: ~768 (row, head) pairs.
+static int kv_chunk(const Problem& p) { return std::max(16, 768 / p.group); }
+
+// ---------------------------------------------------------------- workspace
+
+struct MainWs {
+  size_t cnt_mat, list_cnt, off, coff, chunk_list, entries, part_o, part_st, total;
+  int64_t n_lists, max_entries, max_kv_chunks;
+  int csr_chunks;  // row chunks per sequence (grid x of the inversion kernels)
+  int chunk;       // entries per kvouter workgroup
+};
+
+static MainWs main_layout(const Problem& p, bool decode) {
+  MainWs w{};
+  const int64_t parts = (int64_t)p.total_q * p.hkv * kTopK * p.group;
+  size_t o = 0;
+  if (!decode) {
+    w.chunk = kv_chunk(p);
+    w.csr_chunks = std::max(1, (p.max_q_per_seq + kCsrRows - 1) / kCsrRows);
+    w.n_lists = (int64_t)p.num_seqs * p.hkv * p.max_blocks_per_seq;
+    w.max_entries = (int64_t)p.total_q * p.hkv * kTopK;
+    w.max_kv_chunks = (w.max_entries + w.chunk - 1) / w.chunk + std::min<int64_t>(w.n_lists, w.max_entries);
+    w.cnt_mat = o;    o = align256(o + sizeof(int32_t) * w.n_lists * w.csr_chunks);
+    w.list_cnt = o;   o = align256(o + sizeof(int32_t) * w.n_lists);
+    w.off = o;        o = align256(o + sizeof(int32_t) * (w.n_lists + 1));
+    w.coff = o;       o = align256(o + sizeof(int32_t) * (w.n_lists + 1));
+    w.chunk_list = o; o = align256(o + sizeof(int32_t) * (w.max_kv_chunks + 1));
+    w.entries = o;    o = align256(o + sizeof(int32_t) * (w.max_entries + 1));
+  }
+  w.part_o = o;  o = align256(o + sizeof(uint16_t) * parts * p.head_dim);
+  w.part_st = o; o = align256(o + sizeof(float) * 4 * parts);
+  w.total = o;
+  return w;
+}
+
+size_t prefill_workspace_bytes(const Problem& p) { return main_layout(p, false).total; }
+size_t decode_workspace_bytes(const Problem& p) { return main_layout(p, true).total; }
+
+// An entry (query at position t of sequence s, selected logical block b) is
+// attended iff b is causal for t and the block table names a cached block.
+__device__ __forceinline__ bool entry_valid(const Problem& p, int s, int b, int t) {
+  if (b < 0 || b > (t >> 7)) return false;
+  const int phys = p.block_table[(int64_t)s * p.max_blocks_per_seq + b];
+  return phys >= 0 && phys < p.num_blocks;
+}
+
+// ------------------------------------------------------- selection inversion
+
+struct CsrArgs {
+  Problem p;
+  const int32_t* sel;
+  int32_t* cnt_mat;   // [num_seqs][hkv][csr_chunks][mbps]
+  int32_t* list_cnt;  // [n_lists], list = (s * hkv + g) * mbps + b
+  int32_t* off;
+  int32_t* coff;
+  int32_t* chunk_list;
+  int32_t* entries;
+  int64_t n_lists;
+  int csr_chunks;
+  int hkv_shift;
+  int chunk;
+};
+
+// Per (row chunk, group, sequence): histogram of the chunk's selected blocks
+// in LDS.  Count pass: write the histogram row of the count matrix.  Fill pass
+// (after the scans): turn it into write positions and scatter the entries.
+template <bool FILL>
+__global__ __launch_bounds__(256) void csr_chunk_kernel(CsrArgs a) {
+  extern __shared__ int32_t hist[];  // [mbps]
+  const Problem& p = a.p;
+  const int k = blockIdx.x, g = blockIdx.y, s = blockIdx.z;
+  const int mbps = p.max_blocks_per_seq;
+  const int row0 = p.cu_q[s];
+  const int nq = p.cu_q[s + 1] - row0;
+  const int seq_len = p.seq_lens[s];
+  const int first_pos = seq_len - nq;
+  const int i0 = k * kCsrRows;
+  const int nrows = max(0, min(nq - i0, kCsrRows));
+  const int64_t list0 = ((int64_t)s * p.hkv + g) * mbps;
+  int32_t* mat = a.cnt_mat + (((int64_t)s * p.hkv + g) * a.csr_chunks + k) * mbps;
+
+  for (int b = threadIdx.x; b < mbps; b += blockDim.x) hist[b] = 0;
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < nrows * kTopK; idx += blockDim.x) {
+    const int i = i0 + (idx >> 4), slot = idx & 15;
+    const int64_t R = ((int64_t)(row0 + i) << a.hkv_shift) + g;
+    const int b = a.sel[R * kTopK + slot];
+    if (entry_valid(p, s, b, first_pos + i)) atomicAdd(&hist[b], 1);
+  }
+  __syncthreads();
+  if (!FILL) {
+    for (int b = threadIdx.x; b < mbps; b += blockDim.x) mat[b] = hist[b];
+    return;
+  }
+  for (int b = threadIdx.x; b < mbps; b += blockDim.x) hist[b] = a.off[list0 + b] + mat[b];
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < nrows * kTopK; idx += blockDim.x) {
+    const int i = i0 + (idx >> 4), slot = idx & 15;
+    const int64_t R = ((int64_t)(row0 + i) << a.hkv_shift) + g;
+    const int b = a.sel[R * kTopK + slot];
+    if (entry_valid(p, s, b, first_pos + i)) a.entries[atomicAdd(&hist[b], 1)] = (int32_t)((R << 4) | slot);
+  }
+}
+
+// Per list: exclusive prefix over the row chunks (in place) and the total.
+__global__ __launch_bounds__(256) void csr_colscan_kernel(CsrArgs a) {
+  const int64_t list = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (list >= a.n_lists) return;
+  const int mbps = a.p.max_blocks_per_seq;
+  const int64_t sg = list / mbps, b = list - sg * mbps;
+  int32_t* col = a.cnt_mat + sg * a.csr_chunks * mbps + b;
+  int run = 0;
+  for (int k = 0; k < a.csr_chunks; ++k) {
+    const int v = col[(int64_t)k * mbps];
+    col[(int64_t)k * mbps] = run;
+    run += v;
+  }
+  a.list_cnt[list] = run;
+}
+
+// One workgroup: exclusive scans of the list sizes (entry offsets) and of the
+// per-list kvouter chunk counts (chunk offsets).
+__global__ __launch_bounds__(1024) void csr_scan_kernel(CsrArgs a) {
+  __shared__ int64_t sums[2][1024];
+  const int tid = threadIdx.x;
+  const int64_t n = a.n_lists;
+  const int64_t per = (n + 1023) / 1024;
+  const int64_t lo = std::min<int64_t>(n, tid * per), hi = std::min<int64_t>(n, lo + per);
+  int64_t se = 0, sc = 0;
+  for (int64_t i = lo; i < hi; ++i) {
+    const int c = a.list_cnt[i];
+    se += c;
+    sc += (c + a.chunk - 1) / a.chunk;
+  }
+  sums[0][tid] = se;
+  sums[1][tid] = sc;
+  __syncthreads();
+  for (int d = 1; d < 1024; d <<= 1) {  // inclusive Hillis-Steele scan
+    int64_t ve = 0, vc = 0;
+    if (tid >= d) { ve = sums[0][tid - d]; vc = sums[1][tid - d]; }
+    __syncthreads();
+    sums[0][tid] += ve;
+    sums[1][tid] += vc;
+    __syncthreads();
+  }
+  int64_t e = sums[0][tid] - se, c = sums[1][tid] - sc;
+  for (int64_t i = lo; i < hi; ++i) {
+    const int k = a.list_cnt[i];
+    a.off[i] = (int32_t)e;
+    a.coff[i] = (int32_t)c;
+    e += k;
+    c += (k + a.chunk - 1) / a.chunk;
+  }
+  if (tid == 1023) {
+    a.off[n] = (int32_t)sums[0][1023];
+    a.coff[n] = (int32_t)sums[1][1023];
+  }
+}
+
+__global__ __launch_bounds__(256) void csr_chunk_map_kernel(CsrArgs a) {
+  const int64_t list = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (list >= a.n_lists) return;
+  for (int j = a.coff[list]; j < a.coff[list + 1]; ++j) a.chunk_list[j] = (int32_t)list;
+}
+
+// ------------------------------------------------------------ MFMA pieces
+
+template <int D>
+struct Lds {
+  static constexpr int KP = D + 8;    // K row pitch (bf16): rows stay 16-byte aligned
+  static constexpr int VP = 128 + 8;  // V^T row pitch (bf16)
+  uint16_t k[128 * KP];
+  uint16_t vt[D * VP];
+};
+
+// Stage one block of one KV head into LDS: K as [key][d], V as [d][key].
+// Keys at or after `valid` are written as zeros (never read from the cache).
+template <int D>
+__device__ __forceinline__ void stage_block(Lds<D>& sm, const uint16_t* __restrict__ kg,
+                                            const uint16_t* __restrict__ vg, int64_t key_stride, int valid) {
+  constexpr int C8 = D / 8;
+  for (int idx = threadIdx.x; idx < 128 * C8; idx += blockDim.x) {
+    const int key = idx / C8, c8 = idx - key * C8;
+    u32x4 v = key < valid ? load16(kg + key * key_stride + c8 * 8) : u32x4{0u, 0u, 0u, 0u};
+    store16(&sm.k[key * Lds<D>::KP + c8 * 8], v);
+  }
+  for (int idx = threadIdx.x; idx < 32 * C8; idx += blockDim.x) {
+    const int k4 = idx / C8, c8 = idx - k4 * C8;
+    u32x4 r[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int key = k4 * 4 + i;
+      r[i] = key < valid ? load16(vg + key * key_stride + c8 * 8) : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int sh = (e & 1) * 16;
+      const uint32_t x0 = (r[0][e >> 1] >> sh) & 0xffffu, x1 = (r[1][e >> 1] >> sh) & 0xffffu;
+      const uint32_t x2 = (r[2][e >> 1] >> sh) & 0xffffu, x3 = (r[3][e >> 1] >> sh) & 0xffffu;
+      *reinterpret_cast<u32x2*>(&sm.vt[(c8 * 8 + e) * Lds<D>::VP + k4 * 4]) = u32x2{x0 | (x1 << 16), x2 | (x3 << 16)};
+    }
+  }
+}
+
+// Scores of 32 rows against the staged block: S^T, 4 key tiles.
+template <int D>
+__device__ __forceinline__ void block_scores(const Lds<D>& sm, const bf16x8 (&bq)[D / 16], f32x16 (&sacc)[4]) {
+  const int lane = threadIdx.x & 63;
+  const int half = lane >> 5, l32 = lane & 31;
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    __builtin_amdgcn_sched_barrier(0);  // one key tile at a time: bounds live operand registers
+    sacc[m] = f32x16{0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+      const bf16x8 ak = as_bf16x8(*reinterpret_cast<const u32x4*>(&sm.k[(m * 32 + l32) * Lds<D>::KP + ks * 16 + half * 8]));
+      sacc[m] = mfma32(ak, bq[ks], sacc[m]);
+    }
+  }
+}
+
+// O^T = V^T P^T for 32 rows; P given by the (exponentiated) S^T accumulators.
+template <int D>
+__device__ __forceinline__ void block_pv(const Lds<D>& sm, const f32x16 (&sacc)[4], f32x16 (&oacc)[D / 32]) {
+  const int lane = threadIdx.x & 63;
+  const int half = lane >> 5, l32 = lane & 31;
+  bf16x8 pb[8];
+#pragma unroll
+  for (int kk = 0; kk < 8; ++kk) {
+    const f32x16& s = sacc[kk >> 1];
+    const int r0 = (kk & 1) * 8;
+    pb[kk] = as_bf16x8(u32x4{pack_bf16x2(s[r0 + 0], s[r0 + 1]), pack_bf16x2(s[r0 + 2], s[r0 + 3]),
+                             pack_bf16x2(s[r0 + 4], s[r0 + 5]), pack_bf16x2(s[r0 + 6], s[r0 + 7])});
+  }
+#pragma unroll
+  for (int n = 0; n < D / 32; ++n) {
+    __builtin_amdgcn_sched_barrier(0);
+    oacc[n] = f32x16{0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    const uint16_t* vrow = &sm.vt[(n * 32 + l32) * Lds<D>::VP + half * 4];
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+      const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow + kk * 16);
+      const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + kk * 16 + 8);
+      oacc[n] = mfma32(as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]}), pb[kk], oacc[n]);
+    }
+  }
+}
+
+// Row max (base-2 scaled scores in place), exponentials and row sum.
+__device__ __forceinline__ void softmax_rows(f32x16 (&sacc)[4], float& m, float& l) {
+  float mx = -__builtin_inff();
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[t][r]);
+  mx = fmaxf(mx, swap_halves(mx));
+  float sum = 0.f;
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float e = fast_exp2(sacc[t][r] - mx);
+      sacc[t][r] = e;
+      sum += e;
+    }
+  sum += swap_halves(sum);
+  m = mx;
+  l = sum;
+}
+
+template <int D>
+__device__ __forceinline__ void load_q(const uint16_t* __restrict__ qrow, bool valid, bf16x8 (&bq)[D / 16]) {
+  const int half = (threadIdx.x & 63) >> 5;
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks)
+    bq[ks] = as_bf16x8(valid ? load16(qrow + ks * 16 + half * 8) : u32x4{0u, 0u, 0u, 0u});
+}
+
+// ------------------------------------------------------------- kvouter pass
+
+struct KvOuterArgs {
+  Problem p;
+  const uint16_t* q;
+  const int32_t* sel;
+  const int32_t* entries;
+  const int32_t* off;
+  const int32_t* coff;
+  const int32_t* chunk_list;
+  uint16_t* part_o;  // fp16 [R][16][G][D], normalised output * 2^-e
+  float* part_st;    // [R][16][G][4]: (max, sum, e, 0), max in base-2 units
+  int64_t n_lists;
+  int hkv_shift;
+  int chunk;
+};
+
+// One (row, head) pair of a tile: where its query lives and how its keys are masked.
+struct TileRow {
+  bool valid;
+  int64_t R;  // row * hkv + group
+  int slot;
+  int hj;     // head within the group
+  int lim;    // keys with in-block index > lim are after the query (local block only)
+  const uint16_t* q;
+};
+
+template <int D, bool DIRECT>
+__global__ __launch_bounds__(256, 2) void kvouter_kernel(KvOuterArgs a) {
+  __shared__ Lds<D> sm;
+  const Problem& p = a.p;
+  const int G = p.group;
+  int s, g, b, e0, n_ent;
+  int64_t direct_code = 0;
+  if constexpr (DIRECT) {
+    // One (slot, group, sequence) per workgroup: the decode row's slot-th block.
+    const int slot = blockIdx.x;
+    g = blockIdx.y;
+    s = blockIdx.z;
+    const int64_t R = ((int64_t)p.cu_q[s] << a.hkv_shift) + g;
+    b = a.sel[R * kTopK + slot];
+    if (!entry_valid(p, s, b, p.seq_lens[s] - 1)) return;
+    direct_code = (R << 4) | slot;
+    e0 = 0;
+    n_ent = 1;
+  } else {
+    if ((int)blockIdx.x >= a.coff[a.n_lists]) return;
+    const int list = a.chunk_list[blockIdx.x];
+    const int mbps = p.max_blocks_per_seq;
+    const int sg = list / mbps;
+    b = list - sg * mbps;
+    g = sg & ((1 << a.hkv_shift) - 1);
+    s = sg >> a.hkv_shift;
+    e0 = a.off[list] + ((int)blockIdx.x - a.coff[list]) * a.chunk;
+    n_ent = min(a.chunk, a.off[list + 1] - e0);
+  }
+  const int seq_len = p.seq_lens[s];
+  const int row_end = p.cu_q[s + 1];
+  const int phys = p.block_table[(int64_t)s * p.max_blocks_per_seq + b];
+  const int64_t base = ((int64_t)phys * kBlock * p.hkv + g) * D;
+  stage_block<D>(sm, p.k + base, p.v + base, (int64_t)p.hkv * D, min(kBlock, seq_len - b * kBlock));
+  __syncthreads();
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int half = lane >> 5, l32 = lane & 31;
+  const int rows = n_ent * G;
+  auto tile_row = [&](int tile) -> TileRow {
+    TileRow tr;
+    const int rr = tile * 32 + l32;
+    tr.valid = rr < rows;
+    const int ei = tr.valid ? rr / G : 0;
+    const int hj = tr.valid ? rr - ei * G : 0;
+    int64_t code = 0;
+    if (tr.valid) code = DIRECT ? direct_code : (int64_t)a.entries[e0 + ei];
+    tr.R = code >> 4;
+    tr.slot = (int)(code & 15);
+    const int64_t r = tr.R >> a.hkv_shift;
+    const int t = seq_len - (row_end - (int)r);
+    tr.lim = (tr.valid && (t >> 7) == b) ? t - b * kBlock : kBlock - 1;
+    tr.q = a.q + (r * p.hq + g * G + hj) * D;
+    tr.hj = hj;
+    return tr;
+  };
+
+  int tile = wave;
+  if (tile * 32 >= rows) return;
+  TileRow cur = tile_row(tile);
+  bf16x8 bq[D / 16];
+  load_q<D>(cur.q, cur.valid, bq);
+  for (; tile * 32 < rows; tile += 4) {
+    // Next tile's row and query loads are issued before this tile's math.
+    const int nxt = tile + 4;
+    TileRow next = cur;
+    bf16x8 bq_next[D / 16];
+    if (nxt * 32 < rows) {
+      next = tile_row(nxt);
+      load_q<D>(next.q, next.valid, bq_next);
+    }
+
+    f32x16 sacc[4];
+    block_scores<D>(sm, bq, sacc);
+    const bool masked = __ballot(cur.lim < kBlock - 1) != 0;
+#pragma unroll
+    for (int t4 = 0; t4 < 4; ++t4)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float z = sacc[t4][i] * p.scale_log2e;
+        if (masked) {
+          const int key = t4 * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
+          sacc[t4][i] = key <= cur.lim ? z : -__builtin_inff();
+        } else {
+          sacc[t4][i] = z;
+        }
+      }
+    float m, l;
+    softmax_rows(sacc, m, l);
+    f32x16 oacc[D / 32];
+    block_pv<D>(sm, sacc, oacc);
+
+    // Normalised output, scaled by 2^-e into [-1, 1] for fp16 storage.
+    const float inv_l = 1.0f / l;
+    float amax = 0.f;
+#pragma unroll
+    for (int n = 0; n < D / 32; ++n)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        oacc[n][i] *= inv_l;
+        amax = fmaxf(amax, fabsf(oacc[n][i]));
+      }
+    amax = fmaxf(amax, swap_halves(amax));
+    const int ex = amax > 0.f ? (int)((__float_as_uint(amax) >> 23) & 0xff) - 126 : 0;
+    const float f = ldexpf(1.0f, -ex);
+    if (cur.valid) {
+      const int64_t pidx = (cur.R * kTopK + cur.slot) * G + cur.hj;
+      uint16_t* dst = a.part_o + pidx * D + half * 4;
+#pragma unroll
+      for (int n = 0; n < D / 32; ++n)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const f32x16& o = oacc[n];
+          *reinterpret_cast<u32x2*>(dst + n * 32 + q4 * 8) =
+              u32x2{pack_f16x2(o[4 * q4] * f, o[4 * q4 + 1] * f), pack_f16x2(o[4 * q4 + 2] * f, o[4 * q4 + 3] * f)};
+        }
+      if (half == 0) *reinterpret_cast<f32x4*>(a.part_st + pidx * 4) = f32x4{m, l, (float)ex, 0.f};
+    }
+    cur = next;
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) bq[ks] = bq_next[ks];
+  }
+}
+
+// ----------------------------------------------------------------- merge
+
+struct MergeArgs {
+  Problem p;
+  const int32_t* sel;
+  const uint16_t* part_o;
+  const float* part_st;
+  uint16_t* out;
+  int hkv_shift;
+};
+
+// One thread per (row, head, 8 output dims): log-sum-exp over the row's
+// attended slots, then the bf16 output.
+template <int D>
+__global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
+  constexpr int C8 = D / 8;
+  const Problem& p = a.p;
+  const int G = p.group;
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t n = ((int64_t)p.total_q << a.hkv_shift) * G * C8;
+  if (idx >= n) return;
+  const int d8 = (int)(idx % C8);
+  const int64_t rest = idx / C8;
+  const int hj = (int)(rest % G);
+  const int64_t R = rest / G;
+  const int r = (int)(R >> a.hkv_shift);
+  const int g = (int)(R & ((1 << a.hkv_shift) - 1));
+  const int s = seq_of_row(p.cu_q, p.num_seqs, r);
+  const int t = p.seq_lens[s] - (p.cu_q[s + 1] - r);
+
+  const int32_t* srow = a.sel + R * kTopK;
+  uint32_t mask = 0;
+#pragma unroll
+  for (int j = 0; j < kTopK; ++j)
+    if (entry_valid(p, s, srow[j], t)) mask |= 1u << j;
+
+  const float* st = a.part_st + (R * kTopK * G + hj) * 4;
+  float M = -__builtin_inff();
+#pragma unroll
+  for (int j = 0; j < kTopK; ++j)
+    if (mask >> j & 1u) M = fmaxf(M, st[(int64_t)j * G * 4]);
+  float L = 0.f;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  const uint16_t* y = a.part_o + (R * kTopK * G + hj) * D + d8 * 8;
+#pragma unroll 4
+  for (int j = 0; j < kTopK; ++j) {
+    if (!(mask >> j & 1u)) continue;
+    const f32x4 sj = *reinterpret_cast<const f32x4*>(st + (int64_t)j * G * 4);
+    const float w = sj[1] * fast_exp2(sj[0] - M);
+    L += w;
+    const float wy = ldexpf(w, (int)sj[2]);
+    const u32x4 v = load16(y + (int64_t)j * G * D);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      acc[2 * i] += wy * f16_lo(v[i]);
+      acc[2 * i + 1] += wy * f16_hi(v[i]);
+    }
+  }
+  const float inv = 1.0f / L;
+  u32x4 o;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) o[i] = pack_bf16x2(acc[2 * i] * inv, acc[2 * i + 1] * inv);
+  store16(a.out + ((int64_t)r * p.hq + g * G + hj) * D + d8 * 8, o);
+}
+
+// ------------------------------------------------------------------ launch
+
+template <int D>
+static hipError_t launch_main_t(const Problem& p, const uint16_t* q, const int32_t* sel, uint16_t* out, void* ws,
+                                bool decode, hipStream_t stream) {
+  const MainWs w = main_layout(p, decode);
+  char* base = static_cast<char*>(ws);
+  const int hs = hkv_shift_of(p);
+  KvOuterArgs k{p, q, sel, nullptr, nullptr, nullptr, nullptr,
+                reinterpret_cast<uint16_t*>(base + w.part_o), reinterpret_cast<float*>(base + w.part_st),
+                w.n_lists, hs, w.chunk};
+  if (decode) {
+    hipLaunchKernelGGL((kvouter_kernel<D, true>), dim3(kTopK, p.hkv, p.num_seqs), dim3(256), 0, stream, k);
+  } else {
+    CsrArgs c{p, sel,
+              reinterpret_cast<int32_t*>(base + w.cnt_mat), reinterpret_cast<int32_t*>(base + w.list_cnt),
+              reinterpret_cast<int32_t*>(base + w.off), reinterpret_cast<int32_t*>(base + w.coff),
+              reinterpret_cast<int32_t*>(base + w.chunk_list), reinterpret_cast<int32_t*>(base + w.entries),
+              w.n_lists, w.csr_chunks, hs, w.chunk};
+    const dim3 cgrid(w.csr_chunks, p.hkv, p.num_seqs);
+    const size_t lds = sizeof(int32_t) * p.max_blocks_per_seq;
+    const unsigned list_blocks = (unsigned)((w.n_lists + 255) / 256);
+    hipLaunchKernelGGL((csr_chunk_kernel<false>), cgrid, dim3(256), lds, stream, c);
+    hipLaunchKernelGGL(csr_colscan_kernel, dim3(list_blocks), dim3(256), 0, stream, c);
+    hipLaunchKernelGGL(csr_scan_kernel, dim3(1), dim3(1024), 0, stream, c);
+    hipLaunchKernelGGL((csr_chunk_kernel<true>), cgrid, dim3(256), lds, stream, c);
+    hipLaunchKernelGGL(csr_chunk_map_kernel, dim3(list_blocks), dim3(256), 0, stream, c);
+    k.entries = c.entries;
+    k.off = c.off;
+    k.coff = c.coff;
+    k.chunk_list = c.chunk_list;
+    hipLaunchKernelGGL((kvouter_kernel<D, false>), dim3((unsigned)w.max_kv_chunks), dim3(256), 0, stream, k);
+  }
+  MergeArgs m{p, sel, k.part_o, k.part_st, out, hs};
+  const int64_t threads = ((int64_t)p.total_q << hs) * p.group * (D / 8);
+  hipLaunchKernelGGL(merge_kernel<D>, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream, m);
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_prefill(const Problem& p, const uint16_t* q, const int32_t* sel, uint16_t* out, void* ws,
+                               hipStream_t stream) {
+  if (p.total_q == 0) return hipSuccess;
+  return p.head_dim == 128 ? launch_main_t<128>(p, q, sel, out, ws, false, stream)
+                           : launch_main_t<64>(p, q, sel, out, ws, false, stream);
+}
+
+hipError_t launch_attn_decode(const Problem& p, const uint16_t* q, const int32_t* sel, uint16_t* out, void* ws,
+                              hipStream_t stream) {
+  if (p.total_q == 0) return hipSuccess;
+  return p.head_dim == 128 ? launch_main_t<128>(p, q, sel, out, ws, true, stream)
+                           : launch_main_t<64>(p, q, sel, out, ws, true, stream);
+}
+
+}  // namespace msa

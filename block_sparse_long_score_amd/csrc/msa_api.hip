@@ -122,6 +122,7 @@ msa::Problem make_problem(const msa_dims* d, const msa_batch* b, const msa_cache
   p.scale_log2e = (float)(scale * 1.4426950408889634);
   p.num_seqs = b->num_seqs;
   p.total_q = b->total_q;
+  p.max_q_per_seq = max_q_per_seq(b);
   p.seq_lens = b->seq_lens;
   p.cu_q = b->cu_q;
   if (c) {
@@ -145,6 +146,15 @@ msa_status hip_status(hipError_t e, const char* what) {
     const msa_status st_ = (expr);  \
     if (st_ != MSA_OK) return st_;  \
   } while (0)
+
+msa_status check_prefill_capacity(const msa_dims* dims, const msa_cache* cache, const msa_batch* batch) {
+  if (cache->max_blocks_per_seq > msa::kMaxPrefillBlocks)
+    return fail(MSA_ERR_CAPACITY, "prefill supports max_blocks_per_seq <= %d (got %d)", msa::kMaxPrefillBlocks,
+                cache->max_blocks_per_seq);
+  if ((int64_t)batch->num_seqs * dims->num_kv_heads * cache->max_blocks_per_seq >= (int64_t)1 << 31)
+    return fail(MSA_ERR_CAPACITY, "num_seqs * Hkv * max_blocks_per_seq overflows 32-bit list ids");
+  return MSA_OK;
+}
 
 msa_status check_attn(const msa_dims* dims, const msa_cache* cache, const msa_batch* batch, const void* q,
                       const int32_t* sel, void* out) {
@@ -231,7 +241,10 @@ size_t msa_workspace_size(const msa_dims* dims, const msa_cache* cache, const ms
     return 0;
   const msa::Problem p = make_problem(dims, batch, cache);
   switch (call) {
-    case MSA_CALL_SPARSE_ATTN_PREFILL: ok(); return msa::prefill_workspace_bytes(p);
+    case MSA_CALL_SPARSE_ATTN_PREFILL:
+      if (check_prefill_capacity(dims, cache, batch) != MSA_OK) return 0;
+      ok();
+      return msa::prefill_workspace_bytes(p);
     case MSA_CALL_SPARSE_ATTN_DECODE: ok(); return msa::decode_workspace_bytes(p);
   }
   fail(MSA_ERR_BAD_SHAPE, "unknown call id %d", call);
@@ -241,16 +254,14 @@ size_t msa_workspace_size(const msa_dims* dims, const msa_cache* cache, const ms
 msa_status msa_sparse_attn_prefill(const msa_dims* dims, const msa_cache* cache, const msa_batch* batch, const void* q,
                                    const int32_t* sel, void* out, void* workspace, size_t ws_bytes, void* stream) {
   MSA_TRY(check_attn(dims, cache, batch, q, sel, out));
+  MSA_TRY(check_prefill_capacity(dims, cache, batch));
   const msa::Problem p = make_problem(dims, batch, cache);
   const size_t need = msa::prefill_workspace_bytes(p);
   if (!workspace || ws_bytes < need)
     return fail(MSA_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace ? ws_bytes : 0, need);
   if (!aligned16(workspace)) return fail(MSA_ERR_MISALIGNED, "workspace is not 16-byte aligned");
-  if ((int64_t)cache->num_blocks * dims->num_kv_heads >= (int64_t)1 << 31)
-    return fail(MSA_ERR_CAPACITY, "num_blocks * Hkv overflows 32-bit list ids");
   return hip_status(msa::launch_attn_prefill(p, static_cast<const uint16_t*>(q), sel, static_cast<uint16_t*>(out),
-                                             workspace, batch->seq_lens_host, batch->cu_q_host,
-                                             static_cast<hipStream_t>(stream)),
+                                             workspace, static_cast<hipStream_t>(stream)),
                     "msa_sparse_attn_prefill launch");
 }
 

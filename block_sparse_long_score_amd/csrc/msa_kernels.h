@@ -17,6 +17,7 @@ struct Problem {
   float scale_log2e;                         // softmax scale * log2(e)
   // batch
   int num_seqs, total_q;
+  int max_q_per_seq;        // max over sequences of their query rows (host mirror)
   const int32_t* seq_lens;  // device
   const int32_t* cu_q;      // device
   // cache
@@ -36,10 +37,14 @@ hipError_t launch_index_score(const Problem& p, const uint16_t* q_idx, float* sc
 
 hipError_t launch_block_topk(const Problem& p, const float* scores, int64_t ld, int32_t* sel, hipStream_t stream);
 
+// Largest max_blocks_per_seq the prefill selection inversion supports (its
+// per-workgroup LDS histogram holds one counter per logical block).
+constexpr int kMaxPrefillBlocks = 16384;
+
 // Prefill Main Branch (blocks outer, queries inner) and its workspace.
 size_t prefill_workspace_bytes(const Problem& p);
 hipError_t launch_attn_prefill(const Problem& p, const uint16_t* q, const int32_t* sel, uint16_t* out, void* ws,
-                               const int32_t* seq_lens_host, const int32_t* cu_q_host, hipStream_t stream);
+                               hipStream_t stream);
 
 // Decode Main Branch (one query per sequence, split over its selected blocks).
 size_t decode_workspace_bytes(const Problem& p);
