@@ -106,11 +106,14 @@ def cpu_baseline(inputs, runner, budget_s: float):
         s = 0
         n_q = w.q_lens[0]
         first = w.seq_lens[0] - n_q
-        probe = np.linspace(first, w.seq_lens[0] - 1, 8).astype(np.int64)
-        per_row = run_rows(s, probe) / len(probe)
-        n = int(np.clip(budget_s / max(per_row, 1e-9), 8, n_q))
-        pos = np.unique(np.linspace(first, w.seq_lens[0] - 1, n).astype(np.int64))
-        spent = run_rows(s, pos)
+        # grow the evenly spaced sample until it holds about `budget_s` of oracle work
+        n = 16
+        while True:
+            pos = np.unique(np.linspace(first, w.seq_lens[0] - 1, n).astype(np.int64))
+            spent = run_rows(s, pos)
+            if spent >= budget_s / 2 or n >= n_q:
+                break
+            n = int(min(n_q, max(2 * n, n * budget_s / max(spent, 1e-3))))
         sample = f"{len(pos)} query rows evenly spaced over positions {first}..{w.seq_lens[0] - 1} (all groups/heads)"
         value = len(pos) / spent
     return {"value": value, "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle", "sample": sample,
@@ -125,6 +128,10 @@ def main():
     ap.add_argument("--workload", default="c3", choices=["c0", "c1", "c2", "c3", "c4d", "c4p"])
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="run one device-to-device copy of this many MiB first (scales PMC byte counters)")
+    ap.add_argument("--chunk-rows", type=int, default=16384,
+                    help="prefill query rows per pipelined chunk (0: one chunk, no overlap)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build measures one GPU only; the MSA hot path is not sharded across GPUs "
@@ -140,37 +147,52 @@ def main():
     w = WORKLOADS[args.workload]
     torch.cuda.set_device(0)
     inputs = make_inputs(w, "cuda")
-    runner = MsaRunner(inputs)
+    runner = MsaRunner(inputs, chunk_rows=args.chunk_rows or None)
     work = algorithmic_work(w)
     stream = torch.cuda.current_stream()
+
+    if args.calib_copy_mib:
+        src = torch.empty(args.calib_copy_mib << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     stages = ("append", "index_score", "block_topk", "attend")
     for _ in range(args.warmup):
         runner.step()
     torch.cuda.synchronize()
 
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)] for _ in range(args.steps)]
+    # Timed region: K whole steps (pipelined over two streams when chunked).
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_host = time.perf_counter()
     start.record(stream)
-    for k in range(args.steps):
-        ev[k][0].record(stream)
-        runner.append()
-        ev[k][1].record(stream)
-        runner.index_score()
-        ev[k][2].record(stream)
-        runner.block_topk()
-        ev[k][3].record(stream)
-        runner.attend()
-        ev[k][4].record(stream)
+    for _ in range(args.steps):
+        runner.step()
     end.record(stream)
     torch.cuda.synchronize()
     t_host = time.perf_counter() - t_host
     total_ms = start.elapsed_time(end)
     ms_per_step = total_ms / args.steps
-    stage_ms = {name: float(np.mean([ev[k][i].elapsed_time(ev[k][i + 1]) for k in range(args.steps)]))
-                for i, name in enumerate(stages)}
+
+    # Stage breakdown: the same step run serially, an event after each stage
+    # (per chunk when chunked); stage time = sum over its launches.
+    stage_ms = {k: 0.0 for k in stages}
+    n_stage_steps = max(2, min(args.steps, 5))
+    for _ in range(n_stage_steps):
+        marks = []
+
+        def mark(name):
+            e = torch.cuda.Event(enable_timing=True)
+            e.record(stream)
+            marks.append((name, e))
+
+        runner.staged_step(mark)
+        torch.cuda.synchronize()
+        for (_, e0), (name, e1) in zip(marks, marks[1:]):
+            stage_ms[name] += e0.elapsed_time(e1) / n_stage_steps
+    serial_ms = sum(stage_ms.values())
 
     tokens = w.total_q
     value = tokens / (ms_per_step / 1e3)
@@ -188,7 +210,7 @@ def main():
         algo = work["index_flops"] if dom == "index_score" else work["main_flops"]
         achieved = algo / (stage_ms[dom] / 1e3) / 1e12
         name = ("msa_index_score (index_score_kernel)" if dom == "index_score"
-                else "msa_sparse_attn_prefill (csr + kvouter + merge_local kernels)")
+                else "msa_sparse_attn_prefill (selection inversion + kvouter + merge kernels)")
         roof = {"bound": "mfma", "kernel": name, "achieved": achieved, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": achieved / BF16_PEAK_TFLOPS, "traffic": None}
         step_flops = work["index_flops"] + work["main_flops"]
@@ -218,6 +240,8 @@ def main():
                    "q_heads": w.num_q_heads, "kv_heads": w.num_kv_heads, "head_dim": w.head_dim,
                    "index_dim": w.index_dim, "block_size": w.block_size, "top_k": w.top_k},
         "stage_ms": stage_ms,
+        "serial_ms_per_step": serial_ms,
+        "pipeline": {"chunks": max(1, len(runner.chunks)), "streams": 2 if runner.chunks else 1},
         "step": step_info,
         "roofline": roof,
         "cpu_baseline": cpu,

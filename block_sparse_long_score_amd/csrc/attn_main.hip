@@ -50,13 +50,14 @@ static int hkv_shift_of(const Problem& p) {
   return s;
 }
 
-// Entries (row, slot) per kvouter workgroup: ~768 (row, head) pairs.
-static int kv_chunk(const Problem& p) { return std::max(16, 768 / p.group); }
+// Entries (row, slot) per kvouter workgroup: ~1536 (row, head) pairs, so
+// each staged block serves ~48 row tiles before it is dropped.
+static int kv_chunk(const Problem& p) { return std::max(16, 1536 / p.group); }
 
 // ---------------------------------------------------------------- workspace
 
 struct MainWs {
-  size_t cnt_mat, list_cnt, off, coff, chunk_list, entries, part_o, part_st, total;
+  size_t cnt_mat, list_cnt, off, coff, chunk_list, entries, entry_of, part_o, part_st, total;
   int64_t n_lists, max_entries, max_kv_chunks;
   int csr_chunks;  // row chunks per sequence (grid x of the inversion kernels)
   int chunk;       // entries per kvouter workgroup
@@ -78,6 +79,7 @@ static MainWs main_layout(const Problem& p, bool decode) {
     w.coff = o;       o = align256(o + sizeof(int32_t) * (w.n_lists + 1));
     w.chunk_list = o; o = align256(o + sizeof(int32_t) * (w.max_kv_chunks + 1));
     w.entries = o;    o = align256(o + sizeof(int32_t) * (w.max_entries + 1));
+    w.entry_of = o;   o = align256(o + sizeof(int32_t) * w.max_entries);
   }
   w.part_o = o;  o = align256(o + sizeof(uint16_t) * parts * p.head_dim);
   w.part_st = o; o = align256(o + sizeof(float) * 4 * parts);
@@ -106,7 +108,8 @@ struct CsrArgs {
   int32_t* off;
   int32_t* coff;
   int32_t* chunk_list;
-  int32_t* entries;
+  int32_t* entries;   // list order: (R << 4) | slot
+  int32_t* entry_of;  // [R * 16 + slot] -> position in entries (valid slots only)
   int64_t n_lists;
   int csr_chunks;
   int hkv_shift;
@@ -150,7 +153,11 @@ __global__ __launch_bounds__(256) void csr_chunk_kernel(CsrArgs a) {
     const int i = i0 + (idx >> 4), slot = idx & 15;
     const int64_t R = ((int64_t)(row0 + i) << a.hkv_shift) + g;
     const int b = a.sel[R * kTopK + slot];
-    if (entry_valid(p, s, b, first_pos + i)) a.entries[atomicAdd(&hist[b], 1)] = (int32_t)((R << 4) | slot);
+    if (entry_valid(p, s, b, first_pos + i)) {
+      const int pos = atomicAdd(&hist[b], 1);
+      a.entries[pos] = (int32_t)((R << 4) | slot);
+      a.entry_of[R * kTopK + slot] = pos;
+    }
   }
 }
 
@@ -298,20 +305,23 @@ __device__ __forceinline__ void block_pv(const Lds<D>& sm, const f32x16 (&sacc)[
   }
 }
 
-// Row max (base-2 scaled scores in place), exponentials and row sum.
-__device__ __forceinline__ void softmax_rows(f32x16 (&sacc)[4], float& m, float& l) {
+// Softmax statistics of 32 rows over the staged block, in base 2: with raw
+// scores s and c = softmax_scale * log2(e) > 0, m = c * max(s) and
+// p = 2^(c*s - m) (one FMA and one exp per score).  p replaces s in place;
+// masked scores are -inf and give p = 0.
+__device__ __forceinline__ void softmax_rows(f32x16 (&sacc)[4], float c, float& m, float& l) {
   float mx = -__builtin_inff();
 #pragma unroll
   for (int t = 0; t < 4; ++t)
 #pragma unroll
     for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[t][r]);
-  mx = fmaxf(mx, swap_halves(mx));
+  mx = fmaxf(mx, swap_halves(mx)) * c;
   float sum = 0.f;
 #pragma unroll
   for (int t = 0; t < 4; ++t)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const float e = fast_exp2(sacc[t][r] - mx);
+      const float e = fast_exp2(fmaf(sacc[t][r], c, -mx));
       sacc[t][r] = e;
       sum += e;
     }
@@ -338,8 +348,11 @@ struct KvOuterArgs {
   const int32_t* off;
   const int32_t* coff;
   const int32_t* chunk_list;
-  uint16_t* part_o;  // fp16 [R][16][G][D], normalised output * 2^-e
-  float* part_st;    // [R][16][G][4]: (max, sum, e, 0), max in base-2 units
+  // Partials, one row per (entry, head): prefill stores entry e's heads at
+  // rows e*G .. e*G+G-1 (entry = position in the list order, so a workgroup
+  // writes one contiguous range); decode stores (R, slot) at (R*16+slot)*G.
+  uint16_t* part_o;  // fp16 [entries][G][D] in lane order (see kvouter), normalised output * 2^-e
+  float* part_st;    // [entries][G][4]: (max, sum, e, 0), max in base-2 units
   int64_t n_lists;
   int hkv_shift;
   int chunk;
@@ -348,9 +361,9 @@ struct KvOuterArgs {
 // One (row, head) pair of a tile: where its query lives and how its keys are masked.
 struct TileRow {
   bool valid;
-  int64_t R;  // row * hkv + group
-  int slot;
-  int hj;     // head within the group
+  int64_t R;     // row * hkv + group
+  int64_t prow;  // partial row: entry * G + head
+  int hj;        // head within the group
   int lim;    // keys with in-block index > lim are after the query (local block only)
   const uint16_t* q;
 };
@@ -403,7 +416,7 @@ __global__ __launch_bounds__(256, 2) void kvouter_kernel(KvOuterArgs a) {
     int64_t code = 0;
     if (tr.valid) code = DIRECT ? direct_code : (int64_t)a.entries[e0 + ei];
     tr.R = code >> 4;
-    tr.slot = (int)(code & 15);
+    tr.prow = (DIRECT ? code : (int64_t)(e0 + ei)) * G + hj;
     const int64_t r = tr.R >> a.hkv_shift;
     const int t = seq_len - (row_end - (int)r);
     tr.lim = (tr.valid && (t >> 7) == b) ? t - b * kBlock : kBlock - 1;
@@ -429,48 +442,49 @@ __global__ __launch_bounds__(256, 2) void kvouter_kernel(KvOuterArgs a) {
 
     f32x16 sacc[4];
     block_scores<D>(sm, bq, sacc);
-    const bool masked = __ballot(cur.lim < kBlock - 1) != 0;
+    if (__ballot(cur.lim < kBlock - 1) != 0) {  // local-block rows in this tile: mask keys after the query
 #pragma unroll
-    for (int t4 = 0; t4 < 4; ++t4)
+      for (int t4 = 0; t4 < 4; ++t4)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float z = sacc[t4][i] * p.scale_log2e;
-        if (masked) {
+        for (int i = 0; i < 16; ++i) {
           const int key = t4 * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
-          sacc[t4][i] = key <= cur.lim ? z : -__builtin_inff();
-        } else {
-          sacc[t4][i] = z;
+          sacc[t4][i] = key <= cur.lim ? sacc[t4][i] : -__builtin_inff();
         }
-      }
+    }
     float m, l;
-    softmax_rows(sacc, m, l);
+    softmax_rows(sacc, p.scale_log2e, m, l);
     f32x16 oacc[D / 32];
     block_pv<D>(sm, sacc, oacc);
 
-    // Normalised output, scaled by 2^-e into [-1, 1] for fp16 storage.
-    const float inv_l = 1.0f / l;
+    // Normalised output, scaled by 2^-e into [-1, 1] for fp16 storage; the
+    // normalisation 1/l and the 2^-e scale are one multiply.
     float amax = 0.f;
 #pragma unroll
     for (int n = 0; n < D / 32; ++n)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        oacc[n][i] *= inv_l;
-        amax = fmaxf(amax, fabsf(oacc[n][i]));
-      }
-    amax = fmaxf(amax, swap_halves(amax));
+      for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(oacc[n][i]));
+    const float inv_l = 1.0f / l;
+    amax = fmaxf(amax, swap_halves(amax)) * inv_l;
     const int ex = amax > 0.f ? (int)((__float_as_uint(amax) >> 23) & 0xff) - 126 : 0;
-    const float f = ldexpf(1.0f, -ex);
+    const float f = ldexpf(inv_l, -ex);
     if (cur.valid) {
-      const int64_t pidx = (cur.R * kTopK + cur.slot) * G + cur.hj;
-      uint16_t* dst = a.part_o + pidx * D + half * 4;
+      // Partial row in lane order: position half*(D/2) + n*16 + 4*q4 + i holds
+      // output dim 32*n + 8*q4 + 4*half + i, so each lane writes D bytes
+      // contiguously and the merge reads 8 consecutive dims as two 8-byte pieces.
+      const int64_t pidx = cur.prow;
+      uint16_t* dst = a.part_o + pidx * D + half * (D / 2);
 #pragma unroll
-      for (int n = 0; n < D / 32; ++n)
+      for (int n = 0; n < D / 32; ++n) {
+        const f32x16& o = oacc[n];
+        u32x4 w0, w1;
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          const f32x16& o = oacc[n];
-          *reinterpret_cast<u32x2*>(dst + n * 32 + q4 * 8) =
-              u32x2{pack_f16x2(o[4 * q4] * f, o[4 * q4 + 1] * f), pack_f16x2(o[4 * q4 + 2] * f, o[4 * q4 + 3] * f)};
+        for (int i = 0; i < 4; ++i) {
+          w0[i] = pack_f16x2(o[2 * i] * f, o[2 * i + 1] * f);
+          w1[i] = pack_f16x2(o[8 + 2 * i] * f, o[8 + 2 * i + 1] * f);
         }
+        store16(dst + n * 16, w0);
+        store16(dst + n * 16 + 8, w1);
+      }
       if (half == 0) *reinterpret_cast<f32x4*>(a.part_st + pidx * 4) = f32x4{m, l, (float)ex, 0.f};
     }
     cur = next;
@@ -484,14 +498,17 @@ __global__ __launch_bounds__(256, 2) void kvouter_kernel(KvOuterArgs a) {
 struct MergeArgs {
   Problem p;
   const int32_t* sel;
+  const int32_t* entry_of;  // prefill: partial entry of (R, slot); decode: NULL (entry = R*16 + slot)
   const uint16_t* part_o;
   const float* part_st;
   uint16_t* out;
   int hkv_shift;
 };
 
-// One thread per (row, head, 8 output dims): log-sum-exp over the row's
-// attended slots, then the bf16 output.
+// One thread per (row, head, 8 consecutive output dims): log-sum-exp over
+// the row's attended slots, then the bf16 output.  A slot is attended iff its
+// block id is causal (0 <= b <= c); the kvouter pass wrote exactly those.  All
+// loads of the 16 slots are issued before any arithmetic.
 template <int D>
 __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
   constexpr int C8 = D / 8;
@@ -507,34 +524,63 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
   const int r = (int)(R >> a.hkv_shift);
   const int g = (int)(R & ((1 << a.hkv_shift) - 1));
   const int s = seq_of_row(p.cu_q, p.num_seqs, r);
-  const int t = p.seq_lens[s] - (p.cu_q[s + 1] - r);
+  const int c = (p.seq_lens[s] - (p.cu_q[s + 1] - r)) >> 7;
 
-  const int32_t* srow = a.sel + R * kTopK;
-  uint32_t mask = 0;
+  // Partial rows of the attended slots (0 for slots that are not attended).
+  uint32_t ok_mask = 0;
+  int64_t prow[kTopK];
 #pragma unroll
-  for (int j = 0; j < kTopK; ++j)
-    if (entry_valid(p, s, srow[j], t)) mask |= 1u << j;
-
-  const float* st = a.part_st + (R * kTopK * G + hj) * 4;
-  float M = -__builtin_inff();
-#pragma unroll
-  for (int j = 0; j < kTopK; ++j)
-    if (mask >> j & 1u) M = fmaxf(M, st[(int64_t)j * G * 4]);
-  float L = 0.f;
-  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  const uint16_t* y = a.part_o + (R * kTopK * G + hj) * D + d8 * 8;
-#pragma unroll 4
-  for (int j = 0; j < kTopK; ++j) {
-    if (!(mask >> j & 1u)) continue;
-    const f32x4 sj = *reinterpret_cast<const f32x4*>(st + (int64_t)j * G * 4);
-    const float w = sj[1] * fast_exp2(sj[0] - M);
-    L += w;
-    const float wy = ldexpf(w, (int)sj[2]);
-    const u32x4 v = load16(y + (int64_t)j * G * D);
+  for (int j4 = 0; j4 < kTopK / 4; ++j4) {
+    const u32x4 bv = load16(a.sel + R * kTopK + j4 * 4);
+    const u32x4 ev = a.entry_of ? load16(a.entry_of + R * kTopK + j4 * 4) : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      acc[2 * i] += wy * f16_lo(v[i]);
-      acc[2 * i + 1] += wy * f16_hi(v[i]);
+      const int j = j4 * 4 + i;
+      const int bj = (int)bv[i];
+      const bool ok = bj >= 0 && bj <= c;
+      ok_mask |= (ok ? 1u : 0u) << j;
+      const int64_t ent = a.entry_of ? (int64_t)(int32_t)ev[i] : R * kTopK + j;
+      prow[j] = (ok ? ent : 0) * G + hj;
+    }
+  }
+  float M = -__builtin_inff();
+  f32x4 sj[kTopK];
+#pragma unroll
+  for (int j = 0; j < kTopK; ++j) {
+    sj[j] = (ok_mask >> j & 1u) ? *reinterpret_cast<const f32x4*>(a.part_st + prow[j] * 4)
+                                : f32x4{-__builtin_inff(), 0.f, 0.f, 0.f};
+    M = fmaxf(M, sj[j][0]);
+  }
+  // Lane-order positions of dims 8*d8 .. 8*d8+7 (see kvouter): two 4-value runs.
+  const int pos0 = (d8 >> 2) * 16 + (d8 & 3) * 4;
+  float L = 0.f;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int h8 = 0; h8 < kTopK; h8 += 8) {
+    __builtin_amdgcn_sched_barrier(0);  // eight slots' loads in flight at a time
+    u32x2 ylo[8], yhi[8];
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) {
+      const int j = h8 + jj;
+      const uint16_t* y = a.part_o + prow[j] * D + pos0;
+      const bool ok = ok_mask >> j & 1u;
+      ylo[jj] = ok ? *reinterpret_cast<const u32x2*>(y) : u32x2{0u, 0u};
+      yhi[jj] = ok ? *reinterpret_cast<const u32x2*>(y + D / 2) : u32x2{0u, 0u};
+    }
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) {
+      const int j = h8 + jj;
+      const float w = sj[j][1] > 0.f ? sj[j][1] * fast_exp2(sj[j][0] - M) : 0.f;
+      L += w;
+      const float wy = ldexpf(w, (int)sj[j][2]);
+      acc[0] += wy * f16_lo(ylo[jj][0]);
+      acc[1] += wy * f16_hi(ylo[jj][0]);
+      acc[2] += wy * f16_lo(ylo[jj][1]);
+      acc[3] += wy * f16_hi(ylo[jj][1]);
+      acc[4] += wy * f16_lo(yhi[jj][0]);
+      acc[5] += wy * f16_hi(yhi[jj][0]);
+      acc[6] += wy * f16_lo(yhi[jj][1]);
+      acc[7] += wy * f16_hi(yhi[jj][1]);
     }
   }
   const float inv = 1.0f / L;
@@ -562,7 +608,7 @@ static hipError_t launch_main_t(const Problem& p, const uint16_t* q, const int32
               reinterpret_cast<int32_t*>(base + w.cnt_mat), reinterpret_cast<int32_t*>(base + w.list_cnt),
               reinterpret_cast<int32_t*>(base + w.off), reinterpret_cast<int32_t*>(base + w.coff),
               reinterpret_cast<int32_t*>(base + w.chunk_list), reinterpret_cast<int32_t*>(base + w.entries),
-              w.n_lists, w.csr_chunks, hs, w.chunk};
+              reinterpret_cast<int32_t*>(base + w.entry_of), w.n_lists, w.csr_chunks, hs, w.chunk};
     const dim3 cgrid(w.csr_chunks, p.hkv, p.num_seqs);
     const size_t lds = sizeof(int32_t) * p.max_blocks_per_seq;
     const unsigned list_blocks = (unsigned)((w.n_lists + 255) / 256);
@@ -577,7 +623,8 @@ static hipError_t launch_main_t(const Problem& p, const uint16_t* q, const int32
     k.chunk_list = c.chunk_list;
     hipLaunchKernelGGL((kvouter_kernel<D, false>), dim3((unsigned)w.max_kv_chunks), dim3(256), 0, stream, k);
   }
-  MergeArgs m{p, sel, k.part_o, k.part_st, out, hs};
+  MergeArgs m{p, sel, decode ? nullptr : reinterpret_cast<const int32_t*>(base + w.entry_of), k.part_o, k.part_st,
+              out, hs};
   const int64_t threads = ((int64_t)p.total_q << hs) * p.group * (D / 8);
   hipLaunchKernelGGL(merge_kernel<D>, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream, m);
   return hipGetLastError();

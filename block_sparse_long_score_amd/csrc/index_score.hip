@@ -178,6 +178,164 @@ __global__ __launch_bounds__(256, 2) void index_score_kernel(IndexArgs a) {
   }
 }
 
+// Prefill variant: the four waves of a workgroup share each K_idx block
+// through LDS (double-buffered) and each owns its own 32*NCTW columns, so a
+// block fetched from L2 once feeds 4*32*NCTW columns (512 at NCTW=4: 64
+// queries x 8 groups).  Blocks at or after the tile's first query block are
+// masked per column (key position > query position).  Pooled scores are
+// staged in LDS and written as one contiguous run per (query, group) row.
+constexpr int kSharedKc = 16;  // key blocks per workgroup
+
+// Pooled scores of one LDS-staged key block for a wave's NCTW column tiles.
+// MASKED keeps the key-tile loop rolled so its per-element masks are formed
+// inside the loop rather than all up front.
+template <int DIDX, int NCTW, int KP, bool MASKED>
+__device__ __forceinline__ void shared_pool(const uint16_t* __restrict__ kt, const bf16x8 (&bq)[NCTW][DIDX / 16],
+                                            const int (&lim)[NCTW], float (&runmax)[NCTW]) {
+  constexpr int KS = DIDX / 16;
+  const int lane = threadIdx.x & 63;
+  const int half = lane >> 5, l32 = lane & 31;
+#pragma unroll
+  for (int ct = 0; ct < NCTW; ++ct) runmax[ct] = -__builtin_inff();
+  constexpr int kUnroll = MASKED ? 1 : 4;
+#pragma unroll kUnroll
+  for (int m = 0; m < 4; ++m) {
+    __builtin_amdgcn_sched_barrier(0);
+    bf16x8 ak[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      ak[ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(&kt[(m * 32 + l32) * KP + ks * 16 + half * 8]));
+#pragma unroll
+    for (int ct = 0; ct < NCTW; ++ct) {
+      f32x16 acc = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) acc = mfma32(ak[ks], bq[ct][ks], acc);
+      if constexpr (MASKED) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = m * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+          acc[r] = key > lim[ct] ? -__builtin_inff() : acc[r];
+        }
+      }
+      float mx = acc[0];
+#pragma unroll
+      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, acc[r]);
+      runmax[ct] = fmaxf(runmax[ct], mx);
+    }
+  }
+}
+
+template <int DIDX, int NCTW>
+__global__ __launch_bounds__(256, 2) void index_score_shared_kernel(IndexArgs a) {
+  constexpr int KS = DIDX / 16;
+  constexpr int NCW = 32 * NCTW;          // columns per wave
+  constexpr int NC = 4 * NCW;             // columns per workgroup
+  constexpr int BLK = kBlock * DIDX;      // bf16 elements of one K_idx block
+  constexpr int KP = DIDX + 8;            // LDS row pitch (bf16)
+  __shared__ uint16_t kbuf[2][kBlock * KP];
+  __shared__ float pooled_s[NC][kSharedKc + 1];
+  const Problem& p = a.p;
+
+  const int s = blockIdx.z;
+  const int row0 = p.cu_q[s];
+  const int nq = p.cu_q[s + 1] - row0;
+  if (nq <= 0) return;
+  const int seq_len = p.seq_lens[s];
+  const int first_pos = seq_len - nq;
+  const int tq = a.tq;  // = NC / hkv
+  const int tile0 = (first_pos / tq) * tq;
+  const int n_tiles = (seq_len - 1 - tile0) / tq + 1;
+  if ((int)blockIdx.x >= n_tiles) return;
+  const int p0 = tile0 + (n_tiles - 1 - (int)blockIdx.x) * tq;  // late (heavy) tiles first
+  const int plo = max(p0, first_pos);
+  const int phi = min(p0 + tq, seq_len) - 1;
+  const int c_hi = phi >> 7;   // last block any column needs
+  const int kb0 = blockIdx.y * kSharedKc;
+  if (kb0 > c_hi) return;
+  const int nkb = min(kSharedKc, c_hi + 1 - kb0);
+  const int unmasked_end = (plo + 1) >> 7;  // blocks below this are fully causal for every column
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int half = lane >> 5, l32 = lane & 31;
+  const int hkv_mask = (1 << a.hkv_shift) - 1;
+
+  bf16x8 bq[NCTW][KS];
+  int col_pos[NCTW];
+#pragma unroll
+  for (int ct = 0; ct < NCTW; ++ct) {
+    const int col = wave * NCW + ct * 32 + l32;
+    const int pos = p0 + (col >> a.hkv_shift);
+    const bool valid = pos >= first_pos && pos < seq_len;
+    col_pos[ct] = pos;
+    const int64_t R = ((int64_t)(row0 + pos - first_pos) << a.hkv_shift) + (col & hkv_mask);
+    const uint16_t* src = a.q_idx + R * DIDX + half * 8;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) bq[ct][ks] = as_bf16x8(valid ? load16(src + ks * 16) : u32x4{0u, 0u, 0u, 0u});
+  }
+
+  // Staging: each thread moves BLK/8/256 16-byte pieces of a block.
+  constexpr int PIECES = BLK / 8 / 256;
+  const int32_t* table = p.block_table + (int64_t)s * p.max_blocks_per_seq;
+  auto fetch = [&](int kb, u32x4 (&r)[PIECES]) {
+    const int phys = table[kb];
+    const bool ok = phys >= 0 && phys < p.num_blocks;
+    const uint16_t* src = p.k_idx + (int64_t)(ok ? phys : 0) * BLK;
+#pragma unroll
+    for (int i = 0; i < PIECES; ++i) r[i] = ok ? load16(src + (threadIdx.x + i * 256) * 8) : u32x4{0u, 0u, 0u, 0u};
+  };
+  auto put = [&](int buf, const u32x4 (&r)[PIECES]) {
+#pragma unroll
+    for (int i = 0; i < PIECES; ++i) {
+      const int e = (threadIdx.x + i * 256) * 8;  // element index in the block
+      store16(&kbuf[buf][(e / DIDX) * KP + (e % DIDX)], r[i]);
+    }
+  };
+  {
+    u32x4 r[PIECES];
+    fetch(kb0, r);
+    put(0, r);
+  }
+  __syncthreads();
+
+  for (int i = 0; i < nkb; ++i) {
+    const int kb = kb0 + i;
+    u32x4 nxt[PIECES];
+    if (i + 1 < nkb) fetch(kb + 1, nxt);
+    const uint16_t* kt = kbuf[i & 1];
+    float runmax[NCTW];
+    if (kb >= unmasked_end) {
+      int lim[NCTW];
+#pragma unroll
+      for (int ct = 0; ct < NCTW; ++ct) lim[ct] = col_pos[ct] - kb * kBlock;
+      shared_pool<DIDX, NCTW, KP, true>(kt, bq, lim, runmax);
+    } else {
+      const int lim[NCTW] = {};
+      shared_pool<DIDX, NCTW, KP, false>(kt, bq, lim, runmax);
+    }
+#pragma unroll
+    for (int ct = 0; ct < NCTW; ++ct) {
+      const float v = fmaxf(runmax[ct], swap_halves(runmax[ct]));
+      if (half == 0) pooled_s[wave * NCW + ct * 32 + l32][i] = v;
+    }
+    if (i + 1 < nkb) put((i + 1) & 1, nxt);
+    __syncthreads();
+  }
+
+  // Each valid (query, group) row writes its pooled scores for the blocks it
+  // can see (b <= its own block) contiguously.
+  for (int idx = threadIdx.x; idx < NC * nkb; idx += blockDim.x) {
+    const int col = idx / nkb;
+    const int j = idx - col * nkb;
+    const int pos = p0 + (col >> a.hkv_shift);
+    if (pos < first_pos || pos >= seq_len || kb0 + j > (pos >> 7)) continue;
+    const int64_t R = ((int64_t)(row0 + pos - first_pos) << a.hkv_shift) + (col & hkv_mask);
+    float v = pooled_s[col][j];
+    v = (v == 0.0f) ? 0.0f : v;  // -0 and +0 are the same score
+    a.out[R * a.ld + kb0 + j] = v;
+  }
+}
+
 template <int DIDX, int NCT>
 static hipError_t launch_index_t(const IndexArgs& a, dim3 grid, hipStream_t stream) {
   const size_t lds = (size_t)32 * NCT * (a.kc + 1) * sizeof(float);
@@ -189,14 +347,33 @@ hipError_t launch_index_score(const Problem& p, const uint16_t* q_idx, float* sc
                               const int32_t* seq_lens_host, const int32_t* cu_q_host, hipStream_t stream) {
   int hkv_shift = 0;
   while ((1 << hkv_shift) < p.hkv) ++hkv_shift;
-  // Decode-shaped batches (few queries per sequence) use one 32-column tile;
-  // prefill uses four, which reuses each K_idx tile across 128 columns.
   int max_q = 0;
   for (int s = 0; s < p.num_seqs; ++s) max_q = std::max(max_q, cu_q_host[s + 1] - cu_q_host[s]);
   if (max_q <= 0) return hipSuccess;
+  // Prefill-shaped batches: 512 columns per workgroup sharing each K_idx block.
+  constexpr int kSharedCols = 4 * 32 * 4;
+  if (max_q * p.hkv > 4 * kSharedCols) {
+    const int tq = kSharedCols / p.hkv;
+    int max_tiles = 0, max_blocks = 0;
+    for (int s = 0; s < p.num_seqs; ++s) {
+      const int nq = cu_q_host[s + 1] - cu_q_host[s];
+      if (nq <= 0) continue;
+      const int L = seq_lens_host[s];
+      const int t0 = ((L - nq) / tq) * tq;
+      max_tiles = std::max(max_tiles, (L - 1 - t0) / tq + 1);
+      max_blocks = std::max(max_blocks, (L - 1) / kBlock + 1);
+    }
+    IndexArgs a{p, q_idx, scores, ld, tq, hkv_shift, kSharedKc};
+    dim3 grid((unsigned)max_tiles, (unsigned)((max_blocks + kSharedKc - 1) / kSharedKc), (unsigned)p.num_seqs);
+    if (p.index_dim == 64)
+      hipLaunchKernelGGL((index_score_shared_kernel<64, 4>), grid, dim3(256), 0, stream, a);
+    else
+      hipLaunchKernelGGL((index_score_shared_kernel<32, 4>), grid, dim3(256), 0, stream, a);
+    return hipGetLastError();
+  }
+  // Decode-shaped and small batches: each wave streams its own key blocks.
   const int nct = (max_q * p.hkv <= 32) ? 1 : 4;
   const int tq = 32 * nct / p.hkv;
-  // Grid: tiles x key chunks x sequences; count the block-tile work to size the chunks.
   int max_tiles = 0, max_blocks = 0;
   int64_t work = 0;
   for (int s = 0; s < p.num_seqs; ++s) {

@@ -4,6 +4,14 @@ A step is the whole hot path for one batch: append the new tokens' K, V and
 K_idx to the block-major cache, score and max-pool the index branch, select
 the blocks, and run the Main Branch (prefill or decode).  The runner holds the
 device buffers; it does no arithmetic of its own.
+
+Pipelined prefill.  The index branch is bound by the matrix cores and the
+Main Branch by HBM bandwidth, so a long prefill is cut into chunks of query
+rows (each chunk is an ordinary prefill chunk: its queries are the last rows
+of a sequence truncated after the chunk).  Scoring and selection of chunk i+1
+run on the caller's stream while the Main Branch of chunk i runs on a second
+stream of the same (default) priority; events order each chunk's attention
+after its own selection, and the caller's stream waits for the last one.
 """
 from __future__ import annotations
 
@@ -15,7 +23,7 @@ from .inputs import Inputs
 
 
 class MsaRunner:
-    def __init__(self, inputs: Inputs):
+    def __init__(self, inputs: Inputs, chunk_rows: int | None = None):
         w = inputs.workload
         dev = inputs.q.device
         self.inputs = inputs
@@ -32,8 +40,17 @@ class MsaRunner:
         self.scores = torch.empty((w.total_q, w.num_kv_heads, self.ld), dtype=torch.float32, device=dev)
         self.sel = torch.empty((w.total_q, w.num_kv_heads, w.top_k), dtype=torch.int32, device=dev)
         self.out = torch.empty((w.total_q, w.num_q_heads, w.head_dim), dtype=torch.bfloat16, device=dev)
+        self.chunks = []
+        if chunk_rows and not self.decode and w.num_seqs == 1 and w.q_lens[0] > chunk_rows:
+            first = w.seq_lens[0] - w.q_lens[0]
+            for r0 in range(0, w.q_lens[0], chunk_rows):
+                r1 = min(r0 + chunk_rows, w.q_lens[0])
+                self.chunks.append((r0, r1, ops.Batch.make([first + r1], [r1 - r0], dev)))
+            self.stream_b = torch.cuda.Stream(device=dev)  # default priority
+            self.events = [torch.cuda.Event() for _ in range(len(self.chunks) + 1)]
         call = ops.MSA_CALL_SPARSE_ATTN_DECODE if self.decode else ops.MSA_CALL_SPARSE_ATTN_PREFILL
-        self.workspace = torch.empty(ops.msa_workspace_size(self.dims, self.cache, self.batch, call),
+        ws_batch = self.chunks[0][2] if self.chunks else self.batch
+        self.workspace = torch.empty(ops.msa_workspace_size(self.dims, self.cache, ws_batch, call),
                                      dtype=torch.uint8, device=dev)
 
     def _fill_prefix(self):
@@ -66,7 +83,47 @@ class MsaRunner:
         fn(self.dims, self.cache, self.batch, self.inputs.q, sel, self.out, self.workspace, stream)
 
     def step(self, stream=None):
+        if self.chunks:
+            return self.pipelined_step()
         self.append(stream)
         self.index_score(stream)
         self.block_topk(stream)
         self.attend(stream=stream)
+
+    def staged_step(self, mark):
+        """The step run serially on the current stream, calling mark(name)
+        after each stage (chunk by chunk when chunked) so a caller can record
+        an event there.  Used to time the stages one by one."""
+        a = torch.cuda.current_stream()
+        inp = self.inputs
+        mark("start")
+        self.append(a)
+        mark("append")
+        parts = self.chunks or [(0, self.inputs.workload.total_q, self.batch)]
+        for r0, r1, cb in parts:
+            scores, sel = self.scores[r0:r1], self.sel[r0:r1]
+            ops.msa_index_score(self.dims, self.cache, cb, inp.q_idx[r0:r1], scores, a)
+            mark("index_score")
+            ops.msa_block_topk(self.dims, cb, scores, sel, a)
+            mark("block_topk")
+            fn = ops.msa_sparse_attn_decode if self.decode else ops.msa_sparse_attn_prefill
+            fn(self.dims, self.cache, cb, inp.q[r0:r1], sel, self.out[r0:r1], self.workspace, a)
+            mark("attend")
+
+    def pipelined_step(self):
+        """The same step, chunked over query rows with scoring/selection and
+        attention of consecutive chunks overlapped on two streams."""
+        a = torch.cuda.current_stream()
+        b = self.stream_b
+        inp = self.inputs
+        self.append(a)
+        for i, (r0, r1, cb) in enumerate(self.chunks):
+            scores, sel = self.scores[r0:r1], self.sel[r0:r1]
+            ops.msa_index_score(self.dims, self.cache, cb, inp.q_idx[r0:r1], scores, a)
+            ops.msa_block_topk(self.dims, cb, scores, sel, a)
+            self.events[i].record(a)
+            b.wait_event(self.events[i])
+            ops.msa_sparse_attn_prefill(self.dims, self.cache, cb, inp.q[r0:r1], sel, self.out[r0:r1],
+                                        self.workspace, b)
+        self.events[-1].record(b)
+        a.wait_event(self.events[-1])

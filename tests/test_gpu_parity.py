@@ -26,11 +26,14 @@ def _announce(msg):
     sys.stdout.flush()
 
 
-def _run(w, seed=None):
+BENCH_CHUNK_ROWS = 16384  # bench.py's default prefill chunk
+
+
+def _run(w, seed=None, chunk_rows=None):
     _announce(f"{w.name}: seq_lens={w.seq_lens[:4]}{'...' if w.num_seqs > 4 else ''} q_lens={w.q_lens[:4]} "
-              f"Hq={w.num_q_heads} Hkv={w.num_kv_heads} D={w.head_dim} d_idx={w.index_dim}")
+              f"Hq={w.num_q_heads} Hkv={w.num_kv_heads} D={w.head_dim} d_idx={w.index_dim} chunk_rows={chunk_rows}")
     inp = make_inputs(w, "cuda", seed)
-    runner = MsaRunner(inp)
+    runner = MsaRunner(inp, chunk_rows=chunk_rows)
     runner.step()
     torch.cuda.synchronize()
     return runner
@@ -167,6 +170,21 @@ def test_attention_alone_with_oracle_selection():
     compare_rows(runner, 0, pos, check_scores=False)
 
 
+def test_pipelined_prefill_equals_serial():
+    """Chunked prefill overlapped on two streams gives bit-identical results."""
+    w = M2.with_sizes("pipe", [5000], [5000])
+    runner_p = _run(w, chunk_rows=1024)
+    assert len(runner_p.chunks) == 5
+    runner_p.step()  # a second step reuses every buffer
+    torch.cuda.synchronize()
+    runner_s = MsaRunner(runner_p.inputs)
+    runner_s.step()
+    torch.cuda.synchronize()
+    assert torch.equal(runner_p.sel, runner_s.sel)
+    assert torch.equal(runner_p.out.view(torch.int16), runner_s.out.view(torch.int16))
+    compare_rows(runner_p, 0, _sample_positions(5000, 0, 64, 5))
+
+
 def test_two_runs_are_identical():
     w = M2.with_sizes("det", [3000, 2000], [3000, 300])
     runner = _run(w)
@@ -188,7 +206,7 @@ def _sample_positions(n, first, count, seed):
 
 
 def test_c1_full_size_sampled_rows():
-    runner = _run(WORKLOADS["c1"])
+    runner = _run(WORKLOADS["c1"], chunk_rows=BENCH_CHUNK_ROWS)
     check_selection_invariants(runner)
     compare_rows(runner, 0, _sample_positions(32768, 0, 384, 1))
 
@@ -201,7 +219,8 @@ def test_c2_full_size_decode_all_rows():
 
 
 def test_c3_full_size_sampled_rows():
-    runner = _run(WORKLOADS["c3"])
+    runner = _run(WORKLOADS["c3"], chunk_rows=BENCH_CHUNK_ROWS)
+    assert len(runner.chunks) == 8
     check_selection_invariants(runner)
     compare_rows(runner, 0, _sample_positions(131072, 0, 256, 3))
 
