@@ -23,7 +23,7 @@
 //               bf16 MFMA; rows whose local block this is mask the keys after
 //               the query.  Output per (row, slot, head): block-local softmax
 //               statistics and the normalised output in fp16 scaled by 2^-e;
-//   decode   kvouter in direct mode: one workgroup per (slot, group, sequence);
+//   decode   decode_block: one workgroup per (slot, group, sequence), no staging;
 //   both     3. merge: per (row, head) a streaming log-sum-exp over the slots,
 //               rounded to bf16.
 // The softmax works in base 2 with the scale folded into log2(e).
@@ -368,35 +368,20 @@ struct TileRow {
   const uint16_t* q;
 };
 
-template <int D, bool DIRECT>
+template <int D>
 __global__ __launch_bounds__(256, 2) void kvouter_kernel(KvOuterArgs a) {
   __shared__ Lds<D> sm;
   const Problem& p = a.p;
   const int G = p.group;
-  int s, g, b, e0, n_ent;
-  int64_t direct_code = 0;
-  if constexpr (DIRECT) {
-    // One (slot, group, sequence) per workgroup: the decode row's slot-th block.
-    const int slot = blockIdx.x;
-    g = blockIdx.y;
-    s = blockIdx.z;
-    const int64_t R = ((int64_t)p.cu_q[s] << a.hkv_shift) + g;
-    b = a.sel[R * kTopK + slot];
-    if (!entry_valid(p, s, b, p.seq_lens[s] - 1)) return;
-    direct_code = (R << 4) | slot;
-    e0 = 0;
-    n_ent = 1;
-  } else {
-    if ((int)blockIdx.x >= a.coff[a.n_lists]) return;
-    const int list = a.chunk_list[blockIdx.x];
-    const int mbps = p.max_blocks_per_seq;
-    const int sg = list / mbps;
-    b = list - sg * mbps;
-    g = sg & ((1 << a.hkv_shift) - 1);
-    s = sg >> a.hkv_shift;
-    e0 = a.off[list] + ((int)blockIdx.x - a.coff[list]) * a.chunk;
-    n_ent = min(a.chunk, a.off[list + 1] - e0);
-  }
+  if ((int)blockIdx.x >= a.coff[a.n_lists]) return;
+  const int list = a.chunk_list[blockIdx.x];
+  const int mbps = p.max_blocks_per_seq;
+  const int sg = list / mbps;
+  const int b = list - sg * mbps;
+  const int g = sg & ((1 << a.hkv_shift) - 1);
+  const int s = sg >> a.hkv_shift;
+  const int e0 = a.off[list] + ((int)blockIdx.x - a.coff[list]) * a.chunk;
+  const int n_ent = min(a.chunk, a.off[list + 1] - e0);
   const int seq_len = p.seq_lens[s];
   const int row_end = p.cu_q[s + 1];
   const int phys = p.block_table[(int64_t)s * p.max_blocks_per_seq + b];
@@ -413,10 +398,9 @@ __global__ __launch_bounds__(256, 2) void kvouter_kernel(KvOuterArgs a) {
     tr.valid = rr < rows;
     const int ei = tr.valid ? rr / G : 0;
     const int hj = tr.valid ? rr - ei * G : 0;
-    int64_t code = 0;
-    if (tr.valid) code = DIRECT ? direct_code : (int64_t)a.entries[e0 + ei];
+    const int64_t code = tr.valid ? (int64_t)a.entries[e0 + ei] : 0;
     tr.R = code >> 4;
-    tr.prow = (DIRECT ? code : (int64_t)(e0 + ei)) * G + hj;
+    tr.prow = (int64_t)(e0 + ei) * G + hj;
     const int64_t r = tr.R >> a.hkv_shift;
     const int t = seq_len - (row_end - (int)r);
     tr.lim = (tr.valid && (t >> 7) == b) ? t - b * kBlock : kBlock - 1;
@@ -490,6 +474,166 @@ __global__ __launch_bounds__(256, 2) void kvouter_kernel(KvOuterArgs a) {
     cur = next;
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) bq[ks] = bq_next[ks];
+  }
+}
+
+// --------------------------------------------------------- decode blocks
+
+// Decode: one workgroup per (slot, group, sequence) attends the sequence's
+// single query (the group's G heads) to one selected block.  At one query
+// row per block this is a streaming read of 2 x 128 x D bf16 (HBM-bound), so
+// nothing is staged in LDS: wave w owns keys [32w, 32w+32).  Scores use the
+// 16x16x32 bf16 MFMA with the wave's keys on M (K rows read straight from the
+// cache) and the group's heads on N (padded to 16); P.V uses vector ALU math
+// with each lane owning D/64 output dims.  Output: the same partial rows as
+// the prefill pass (row (R*16 + slot)*G + head, lane order, fp16 * 2^-e).
+// 16x16x32 bf16 MFMA lane layout: A lane l holds A[l%16][8*(l/16) .. +7],
+// B lane l holds B[8*(l/16) .. +7][l%16], D lane l register i holds
+// D[4*(l/16) + i][l%16].
+template <int D, int GM>
+__global__ __launch_bounds__(256) void decode_block_kernel(KvOuterArgs a) {
+  constexpr int VPL = D / 64;  // output dims per lane in P.V
+  constexpr int KS = D / 32;   // MFMA k-steps
+  __shared__ float s_s[GM][kBlock];
+  __shared__ float red_s[4][GM][D];
+  __shared__ float stat_s[GM][4];
+  const Problem& p = a.p;
+  const int G = p.group;
+  const int slot = blockIdx.x, g = blockIdx.y, s = blockIdx.z;
+  const int64_t R = ((int64_t)p.cu_q[s] << a.hkv_shift) + g;
+  const int b = a.sel[R * kTopK + slot];
+  const int t = p.seq_lens[s] - 1;
+  if (!entry_valid(p, s, b, t)) return;
+  const int phys = p.block_table[(int64_t)s * p.max_blocks_per_seq + b];
+  const int nvalid = min(kBlock, t - b * kBlock + 1);
+  const int64_t key_stride = (int64_t)p.hkv * D;
+  const uint16_t* kb = p.k + ((int64_t)phys * kBlock * p.hkv + g) * D;
+  const uint16_t* vb = p.v + ((int64_t)phys * kBlock * p.hkv + g) * D;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l16 = lane & 15, q16 = lane >> 4;
+
+  // V rows of this wave's keys (lane: dims lane*VPL ..), issued first.
+  uint32_t vreg[32];
+#pragma unroll
+  for (int k = 0; k < 32; ++k) {
+    const int kk = wave * 32 + k;
+    if constexpr (VPL == 2)
+      vreg[k] = kk < nvalid ? *reinterpret_cast<const uint32_t*>(vb + kk * key_stride + lane * 2) : 0u;
+    else
+      vreg[k] = kk < nvalid ? (uint32_t)vb[kk * key_stride + lane] : 0u;
+  }
+  // K rows (A operand) for the wave's two 16-key tiles, and the heads' Q (B operand).
+  bf16x8 ak[2][KS], bq[KS];
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt) {
+    const int key = wave * 32 + mt * 16 + l16;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      ak[mt][ks] = as_bf16x8(key < nvalid ? load16(kb + key * key_stride + ks * 32 + q16 * 8) : u32x4{0u, 0u, 0u, 0u});
+  }
+  const uint16_t* qh = a.q + ((int64_t)p.cu_q[s] * p.hq + g * G + l16) * D;
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks)
+    bq[ks] = as_bf16x8(l16 < G ? load16(qh + ks * 32 + q16 * 8) : u32x4{0u, 0u, 0u, 0u});
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak[mt][ks], bq[ks], acc, 0, 0, 0);
+    if (l16 < GM) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int key = wave * 32 + mt * 16 + q16 * 4 + i;
+        if (l16 < G) s_s[l16][key] = key < nvalid ? acc[i] : -__builtin_inff();
+      }
+    }
+  }
+  __syncthreads();
+
+  // Softmax statistics per head (wave w: heads w, w+4, ...), base 2.
+  const float c = p.scale_log2e;
+  for (int j = wave; j < G; j += 4) {
+    const float z0 = s_s[j][lane], z1 = s_s[j][lane + 64];
+    float mx = fmaxf(z0, z1);
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+    mx *= c;
+    const float e0 = fast_exp2(fmaf(z0, c, -mx)), e1 = fast_exp2(fmaf(z1, c, -mx));
+    s_s[j][lane] = e0;
+    s_s[j][lane + 64] = e1;
+    float l = e0 + e1;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) l += __shfl_xor(l, o);
+    if (lane == 0) {
+      stat_s[j][0] = mx;
+      stat_s[j][1] = l;
+    }
+  }
+  __syncthreads();
+
+  // P.V over this wave's keys, then the sum over the four waves.
+  float o[GM][VPL];
+#pragma unroll
+  for (int j = 0; j < GM; ++j)
+#pragma unroll
+    for (int v = 0; v < VPL; ++v) o[j][v] = 0.f;
+#pragma unroll
+  for (int k = 0; k < 32; ++k) {
+    float vv[VPL];
+    if constexpr (VPL == 2) {
+      vv[0] = bf16_to_f32(vreg[k] & 0xffffu);
+      vv[1] = bf16_to_f32(vreg[k] >> 16);
+    } else {
+      vv[0] = bf16_to_f32(vreg[k] & 0xffffu);
+    }
+#pragma unroll
+    for (int j = 0; j < GM; ++j) {
+      const float pj = s_s[j][wave * 32 + k];
+#pragma unroll
+      for (int v = 0; v < VPL; ++v) o[j][v] = fmaf(pj, vv[v], o[j][v]);
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < GM; ++j)
+#pragma unroll
+    for (int v = 0; v < VPL; ++v) red_s[wave][j][lane * VPL + v] = o[j][v];
+  __syncthreads();
+  for (int idx = tid; idx < G * D; idx += 256) {
+    const int j = idx / D, d = idx - j * D;
+    red_s[0][j][d] = (red_s[0][j][d] + red_s[1][j][d] + red_s[2][j][d] + red_s[3][j][d]) / stat_s[j][1];
+  }
+  __syncthreads();
+  for (int j = wave; j < G; j += 4) {
+    float amax = 0.f;
+    for (int d = lane; d < D; d += 64) amax = fmaxf(amax, fabsf(red_s[0][j][d]));
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+    if (lane == 0) stat_s[j][2] = amax > 0.f ? (float)((int)((__float_as_uint(amax) >> 23) & 0xff) - 126) : 0.f;
+  }
+  __syncthreads();
+  // Partial rows in lane order: position half*(D/2) + n*16 + 4*q4 + i holds dim 32n + 8q4 + 4*half + i.
+  for (int idx = tid; idx < G * (D / 8); idx += 256) {
+    const int j = idx / (D / 8), p8 = idx - j * (D / 8);
+    const float f = ldexpf(1.0f, -(int)stat_s[j][2]);
+    u32x4 w;
+#pragma unroll
+    for (int i2 = 0; i2 < 4; ++i2) {
+      float x[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int pos = p8 * 8 + i2 * 2 + u;
+        const int hh = pos / (D / 2), rem = pos - hh * (D / 2);
+        const int d = 32 * (rem / 16) + 8 * ((rem % 16) / 4) + 4 * hh + (rem % 4);
+        x[u] = red_s[0][j][d] * f;
+      }
+      w[i2] = pack_f16x2(x[0], x[1]);
+    }
+    const int64_t prow = (R * kTopK + slot) * G + j;
+    store16(a.part_o + prow * D + p8 * 8, w);
+  }
+  if (tid < G) {
+    const int64_t prow = (R * kTopK + slot) * G + tid;
+    *reinterpret_cast<f32x4*>(a.part_st + prow * 4) = f32x4{stat_s[tid][0], stat_s[tid][1], stat_s[tid][2], 0.f};
   }
 }
 
@@ -602,7 +746,13 @@ static hipError_t launch_main_t(const Problem& p, const uint16_t* q, const int32
                 reinterpret_cast<uint16_t*>(base + w.part_o), reinterpret_cast<float*>(base + w.part_st),
                 w.n_lists, hs, w.chunk};
   if (decode) {
-    hipLaunchKernelGGL((kvouter_kernel<D, true>), dim3(kTopK, p.hkv, p.num_seqs), dim3(256), 0, stream, k);
+    const dim3 dgrid(kTopK, p.hkv, p.num_seqs);
+    if (p.group <= 4)
+      hipLaunchKernelGGL((decode_block_kernel<D, 4>), dgrid, dim3(256), 0, stream, k);
+    else if (p.group <= 8)
+      hipLaunchKernelGGL((decode_block_kernel<D, 8>), dgrid, dim3(256), 0, stream, k);
+    else
+      hipLaunchKernelGGL((decode_block_kernel<D, 16>), dgrid, dim3(256), 0, stream, k);
   } else {
     CsrArgs c{p, sel,
               reinterpret_cast<int32_t*>(base + w.cnt_mat), reinterpret_cast<int32_t*>(base + w.list_cnt),
@@ -621,7 +771,7 @@ static hipError_t launch_main_t(const Problem& p, const uint16_t* q, const int32
     k.off = c.off;
     k.coff = c.coff;
     k.chunk_list = c.chunk_list;
-    hipLaunchKernelGGL((kvouter_kernel<D, false>), dim3((unsigned)w.max_kv_chunks), dim3(256), 0, stream, k);
+    hipLaunchKernelGGL(kvouter_kernel<D>, dim3((unsigned)w.max_kv_chunks), dim3(256), 0, stream, k);
   }
   MergeArgs m{p, sel, decode ? nullptr : reinterpret_cast<const int32_t*>(base + w.entry_of), k.part_o, k.part_st,
               out, hs};

@@ -60,44 +60,54 @@ __device__ __forceinline__ uint32_t kth_largest_lane(uint32_t x, int k) {
 constexpr int kKeep = kTopK - 1;  // non-local blocks kept per row
 constexpr int kCached = 16;       // candidates per lane held in registers (rows with c <= 1024)
 
+// Keys of candidates j*64 + lane for j in [j0, j0 + kCached): one batch of
+// independent loads (0 beyond the last candidate).
+__device__ __forceinline__ void load_batch(const float* __restrict__ row, int c, int j0, uint32_t (&keys)[kCached]) {
+  const int lane = threadIdx.x & 63;
+  float v[kCached];
+#pragma unroll
+  for (int j = 0; j < kCached; ++j) {
+    const int b = (j0 + j) * 64 + lane;
+    v[j] = b < c ? row[b] : 0.f;
+  }
+#pragma unroll
+  for (int j = 0; j < kCached; ++j) keys[j] = (j0 + j) * 64 + lane < c ? order_key(v[j]) : 0u;
+}
+
+// Selection for one row.  Rows with c <= 1024 candidates keep their keys in
+// registers; longer rows are streamed in batches of 1024 (16 per lane).
 template <bool CACHED>
 __device__ void select_row(const float* __restrict__ row, int c, int32_t* __restrict__ out, uint32_t* surv_key,
                            int32_t* surv_idx) {
   const int lane = threadIdx.x & 63;
-  uint32_t keys[CACHED ? kCached : 1];
-  auto key_at = [&](int j) -> uint32_t {
-    if constexpr (CACHED) return keys[j];
-    const int b = j * 64 + lane;
-    return b < c ? order_key(row[b]) : 0u;
-  };
-  const int nj = CACHED ? kCached : (c + 63) / 64;
+  const int nj = (c + 63) / 64;
+  uint32_t keys[kCached];
+  if constexpr (CACHED) load_batch(row, c, 0, keys);
 
   // 1. lane maxima and theta.
   uint32_t lmax = 0;
-  if constexpr (CACHED) {
+  for (int j0 = 0; j0 < nj; j0 += kCached) {
+    if constexpr (!CACHED) load_batch(row, c, j0, keys);
 #pragma unroll
-    for (int j = 0; j < kCached; ++j) {
-      const int b = j * 64 + lane;
-      keys[j] = b < c ? order_key(row[b]) : 0u;
-      lmax = max(lmax, keys[j]);
-    }
-  } else {
-    for (int j = 0; j < nj; ++j) lmax = max(lmax, key_at(j));
+    for (int j = 0; j < kCached; ++j) lmax = max(lmax, keys[j]);
   }
   const uint32_t theta = kth_largest_lane(lmax, kKeep);
 
   // 2. compact survivors (key >= theta) in ascending block order.
   int count = 0;
-  for (int j = 0; j < nj; ++j) {
-    const uint32_t k = key_at(j);
-    const bool ok = k >= theta && k != 0u;
-    const uint64_t m = __ballot(ok);
-    const int pos = count + lanes_below(m);
-    if (ok && pos < 64) {
-      surv_key[pos] = k;
-      surv_idx[pos] = j * 64 + lane;
+  for (int j0 = 0; j0 < nj; j0 += kCached) {
+    if constexpr (!CACHED) load_batch(row, c, j0, keys);
+#pragma unroll
+    for (int j = 0; j < kCached; ++j) {
+      const bool ok = keys[j] >= theta && keys[j] != 0u;
+      const uint64_t m = __ballot(ok);
+      const int pos = count + lanes_below(m);
+      if (ok && pos < 64) {
+        surv_key[pos] = keys[j];
+        surv_idx[pos] = (j0 + j) * 64 + lane;
+      }
+      count += __popcll(m);
     }
-    count += __popcll(m);
   }
   wave_lds_sync();
 
@@ -115,6 +125,10 @@ __device__ void select_row(const float* __restrict__ row, int c, int32_t* __rest
     if (take) out[lanes_below(tm)] = idx;
   } else {
     // Massive ties: exact k-th largest over all candidates, bit by bit.
+    auto key_at = [&](int j) -> uint32_t {
+      const int b = j * 64 + lane;
+      return b < c ? order_key(row[b]) : 0u;
+    };
     uint32_t T = 0;
     for (int bit = 31; bit >= 0; --bit) {
       const uint32_t cand = T | (1u << bit);

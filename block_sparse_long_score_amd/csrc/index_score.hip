@@ -184,7 +184,7 @@ __global__ __launch_bounds__(256, 2) void index_score_kernel(IndexArgs a) {
 // queries x 8 groups).  Blocks at or after the tile's first query block are
 // masked per column (key position > query position).  Pooled scores are
 // staged in LDS and written as one contiguous run per (query, group) row.
-constexpr int kSharedKc = 16;  // key blocks per workgroup
+constexpr int kSharedFlush = 16;  // pooled scores staged in LDS per flush
 
 // Pooled scores of one LDS-staged key block for a wave's NCTW column tiles.
 // MASKED keeps the key-tile loop rolled so its per-element masks are formed
@@ -233,7 +233,7 @@ __global__ __launch_bounds__(256, 2) void index_score_shared_kernel(IndexArgs a)
   constexpr int BLK = kBlock * DIDX;      // bf16 elements of one K_idx block
   constexpr int KP = DIDX + 8;            // LDS row pitch (bf16)
   __shared__ uint16_t kbuf[2][kBlock * KP];
-  __shared__ float pooled_s[NC][kSharedKc + 1];
+  __shared__ float pooled_s[NC][kSharedFlush + 1];
   const Problem& p = a.p;
 
   const int s = blockIdx.z;
@@ -250,9 +250,9 @@ __global__ __launch_bounds__(256, 2) void index_score_shared_kernel(IndexArgs a)
   const int plo = max(p0, first_pos);
   const int phi = min(p0 + tq, seq_len) - 1;
   const int c_hi = phi >> 7;   // last block any column needs
-  const int kb0 = blockIdx.y * kSharedKc;
+  const int kb0 = blockIdx.y * a.kc;
   if (kb0 > c_hi) return;
-  const int nkb = min(kSharedKc, c_hi + 1 - kb0);
+  const int nkb = min(a.kc, c_hi + 1 - kb0);
   const int unmasked_end = (plo + 1) >> 7;  // blocks below this are fully causal for every column
 
   const int lane = threadIdx.x & 63;
@@ -298,6 +298,21 @@ __global__ __launch_bounds__(256, 2) void index_score_shared_kernel(IndexArgs a)
   }
   __syncthreads();
 
+  // Each valid (query, group) row writes the staged pooled scores of blocks
+  // [kf, kf + n) it can see (b <= its own block) as one contiguous run.
+  auto flush = [&](int kf, int n) {
+    for (int idx = threadIdx.x; idx < NC * n; idx += blockDim.x) {
+      const int col = idx / n;
+      const int j = idx - col * n;
+      const int pos = p0 + (col >> a.hkv_shift);
+      if (pos < first_pos || pos >= seq_len || kf + j > (pos >> 7)) continue;
+      const int64_t R = ((int64_t)(row0 + pos - first_pos) << a.hkv_shift) + (col & hkv_mask);
+      float v = pooled_s[col][j];
+      v = (v == 0.0f) ? 0.0f : v;  // -0 and +0 are the same score
+      a.out[R * a.ld + kf + j] = v;
+    }
+  };
+
   for (int i = 0; i < nkb; ++i) {
     const int kb = kb0 + i;
     u32x4 nxt[PIECES];
@@ -313,26 +328,18 @@ __global__ __launch_bounds__(256, 2) void index_score_shared_kernel(IndexArgs a)
       const int lim[NCTW] = {};
       shared_pool<DIDX, NCTW, KP, false>(kt, bq, lim, runmax);
     }
+    const int slot = i % kSharedFlush;
 #pragma unroll
     for (int ct = 0; ct < NCTW; ++ct) {
       const float v = fmaxf(runmax[ct], swap_halves(runmax[ct]));
-      if (half == 0) pooled_s[wave * NCW + ct * 32 + l32][i] = v;
+      if (half == 0) pooled_s[wave * NCW + ct * 32 + l32][slot] = v;
     }
     if (i + 1 < nkb) put((i + 1) & 1, nxt);
     __syncthreads();
-  }
-
-  // Each valid (query, group) row writes its pooled scores for the blocks it
-  // can see (b <= its own block) contiguously.
-  for (int idx = threadIdx.x; idx < NC * nkb; idx += blockDim.x) {
-    const int col = idx / nkb;
-    const int j = idx - col * nkb;
-    const int pos = p0 + (col >> a.hkv_shift);
-    if (pos < first_pos || pos >= seq_len || kb0 + j > (pos >> 7)) continue;
-    const int64_t R = ((int64_t)(row0 + pos - first_pos) << a.hkv_shift) + (col & hkv_mask);
-    float v = pooled_s[col][j];
-    v = (v == 0.0f) ? 0.0f : v;  // -0 and +0 are the same score
-    a.out[R * a.ld + kb0 + j] = v;
+    if (slot == kSharedFlush - 1 || i + 1 == nkb) {
+      flush(kb - slot, slot + 1);
+      __syncthreads();
+    }
   }
 }
 
@@ -363,8 +370,11 @@ hipError_t launch_index_score(const Problem& p, const uint16_t* q_idx, float* sc
       max_tiles = std::max(max_tiles, (L - 1 - t0) / tq + 1);
       max_blocks = std::max(max_blocks, (L - 1) / kBlock + 1);
     }
-    IndexArgs a{p, q_idx, scores, ld, tq, hkv_shift, kSharedKc};
-    dim3 grid((unsigned)max_tiles, (unsigned)((max_blocks + kSharedKc - 1) / kSharedKc), (unsigned)p.num_seqs);
+    // Long contexts: 64 key blocks per workgroup amortise loading the Q_idx
+    // tile; shorter ones keep 16 so the grid still fills the chip.
+    const int kc = max_blocks >= 2048 ? 64 : 16;
+    IndexArgs a{p, q_idx, scores, ld, tq, hkv_shift, kc};
+    dim3 grid((unsigned)max_tiles, (unsigned)((max_blocks + kc - 1) / kc), (unsigned)p.num_seqs);
     if (p.index_dim == 64)
       hipLaunchKernelGGL((index_score_shared_kernel<64, 4>), grid, dim3(256), 0, stream, a);
     else
