@@ -351,7 +351,7 @@ struct KvOuterArgs {
   // Partials, one row per (entry, head): prefill stores entry e's heads at
   // rows e*G .. e*G+G-1 (entry = position in the list order, so a workgroup
   // writes one contiguous range); decode stores (R, slot) at (R*16+slot)*G.
-  uint16_t* part_o;  // fp16 [entries][G][D] in lane order (see kvouter), normalised output * 2^-e
+  uint16_t* part_o;  // fp16 [entries][G][D], natural dim order: normalised output * 2^-e
   float* part_st;    // [entries][G][4]: (max, sum, e, 0), max in base-2 units
   int64_t n_lists;
   int hkv_shift;
@@ -451,26 +451,38 @@ __global__ __launch_bounds__(256, 2) void kvouter_kernel(KvOuterArgs a) {
     amax = fmaxf(amax, swap_halves(amax)) * inv_l;
     const int ex = amax > 0.f ? (int)((__float_as_uint(amax) >> 23) & 0xff) - 126 : 0;
     const float f = ldexpf(inv_l, -ex);
-    if (cur.valid) {
-      // Partial row in lane order: position half*(D/2) + n*16 + 4*q4 + i holds
-      // output dim 32*n + 8*q4 + 4*half + i, so each lane writes D bytes
-      // contiguously and the merge reads 8 consecutive dims as two 8-byte pieces.
-      const int64_t pidx = cur.prow;
-      uint16_t* dst = a.part_o + pidx * D + half * (D / 2);
+    // Partial rows in natural dim order, stored as 64-byte row segments.
+    // Lane (row rho, half h) holds dims 32n + 8*(i/4) + 4h + (i%4) of oacc[n];
+    // a swap across the wave halves gives it dims 32n + 8h .. +7 (c1) and
+    // 32n + 16 + 8h .. +7 (c2), and a swap of c2 with the lane 16 away lets
+    // four lanes cover 32 consecutive dims of one row in each store: the
+    // first store writes tile rows 0..15, the second rows 16..31.
+    const int a16 = l32 >> 4, b16 = l32 & 15;
+    const int64_t prow0 = (int64_t)e0 * G + (int64_t)tile * 32;
+    const bool okA = tile * 32 + b16 < rows, okB = tile * 32 + 16 + b16 < rows;
+    uint16_t* dstA = a.part_o + (prow0 + b16) * D + 8 * half + 16 * a16;
+    uint16_t* dstB = a.part_o + (prow0 + 16 + b16) * D + 8 * half + 16 * (1 - a16);
 #pragma unroll
-      for (int n = 0; n < D / 32; ++n) {
-        const f32x16& o = oacc[n];
-        u32x4 w0, w1;
+    for (int n = 0; n < D / 32; ++n) {
+      const f32x16& o = oacc[n];
+      uint32_t w[8];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          w0[i] = pack_f16x2(o[2 * i] * f, o[2 * i + 1] * f);
-          w1[i] = pack_f16x2(o[8 + 2 * i] * f, o[8 + 2 * i + 1] * f);
-        }
-        store16(dst + n * 16, w0);
-        store16(dst + n * 16 + 8, w1);
+      for (int i = 0; i < 8; ++i) w[i] = pack_f16x2(o[2 * i] * f, o[2 * i + 1] * f);
+      const auto s0 = __builtin_amdgcn_permlane32_swap(w[0], w[2], false, false);
+      const auto s1 = __builtin_amdgcn_permlane32_swap(w[1], w[3], false, false);
+      const auto s2 = __builtin_amdgcn_permlane32_swap(w[4], w[6], false, false);
+      const auto s3 = __builtin_amdgcn_permlane32_swap(w[5], w[7], false, false);
+      const u32x4 c1{s0[0], s1[0], s0[1], s1[1]};
+      u32x4 c2{s2[0], s3[0], s2[1], s3[1]};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const auto t = __builtin_amdgcn_permlane16_swap(c2[i], c2[i], false, false);
+        c2[i] = a16 ? t[0] : t[1];
       }
-      if (half == 0) *reinterpret_cast<f32x4*>(a.part_st + pidx * 4) = f32x4{m, l, (float)ex, 0.f};
+      if (okA) store16(dstA + 32 * n, a16 ? c2 : c1);
+      if (okB) store16(dstB + 32 * n, a16 ? c1 : c2);
     }
+    if (cur.valid && half == 0) *reinterpret_cast<f32x4*>(a.part_st + cur.prow * 4) = f32x4{m, l, (float)ex, 0.f};
     cur = next;
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) bq[ks] = bq_next[ks];
@@ -486,7 +498,7 @@ __global__ __launch_bounds__(256, 2) void kvouter_kernel(KvOuterArgs a) {
 // 16x16x32 bf16 MFMA with the wave's keys on M (K rows read straight from the
 // cache) and the group's heads on N (padded to 16); P.V uses vector ALU math
 // with each lane owning D/64 output dims.  Output: the same partial rows as
-// the prefill pass (row (R*16 + slot)*G + head, lane order, fp16 * 2^-e).
+// the prefill pass (row (R*16 + slot)*G + head, natural dim order, fp16 * 2^-e).
 // 16x16x32 bf16 MFMA lane layout: A lane l holds A[l%16][8*(l/16) .. +7],
 // B lane l holds B[8*(l/16) .. +7][l%16], D lane l register i holds
 // D[4*(l/16) + i][l%16].
@@ -611,23 +623,13 @@ __global__ __launch_bounds__(256) void decode_block_kernel(KvOuterArgs a) {
     if (lane == 0) stat_s[j][2] = amax > 0.f ? (float)((int)((__float_as_uint(amax) >> 23) & 0xff) - 126) : 0.f;
   }
   __syncthreads();
-  // Partial rows in lane order: position half*(D/2) + n*16 + 4*q4 + i holds dim 32n + 8q4 + 4*half + i.
+  // Partial rows in natural dim order, 8 dims per store.
   for (int idx = tid; idx < G * (D / 8); idx += 256) {
     const int j = idx / (D / 8), p8 = idx - j * (D / 8);
     const float f = ldexpf(1.0f, -(int)stat_s[j][2]);
-    u32x4 w;
-#pragma unroll
-    for (int i2 = 0; i2 < 4; ++i2) {
-      float x[2];
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int pos = p8 * 8 + i2 * 2 + u;
-        const int hh = pos / (D / 2), rem = pos - hh * (D / 2);
-        const int d = 32 * (rem / 16) + 8 * ((rem % 16) / 4) + 4 * hh + (rem % 4);
-        x[u] = red_s[0][j][d] * f;
-      }
-      w[i2] = pack_f16x2(x[0], x[1]);
-    }
+    const float* x = &red_s[0][j][p8 * 8];
+    const u32x4 w{pack_f16x2(x[0] * f, x[1] * f), pack_f16x2(x[2] * f, x[3] * f), pack_f16x2(x[4] * f, x[5] * f),
+                  pack_f16x2(x[6] * f, x[7] * f)};
     const int64_t prow = (R * kTopK + slot) * G + j;
     store16(a.part_o + prow * D + p8 * 8, w);
   }
@@ -695,21 +697,16 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
                                 : f32x4{-__builtin_inff(), 0.f, 0.f, 0.f};
     M = fmaxf(M, sj[j][0]);
   }
-  // Lane-order positions of dims 8*d8 .. 8*d8+7 (see kvouter): two 4-value runs.
-  const int pos0 = (d8 >> 2) * 16 + (d8 & 3) * 4;
   float L = 0.f;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int h8 = 0; h8 < kTopK; h8 += 8) {
     __builtin_amdgcn_sched_barrier(0);  // eight slots' loads in flight at a time
-    u32x2 ylo[8], yhi[8];
+    u32x4 y[8];
 #pragma unroll
     for (int jj = 0; jj < 8; ++jj) {
       const int j = h8 + jj;
-      const uint16_t* y = a.part_o + prow[j] * D + pos0;
-      const bool ok = ok_mask >> j & 1u;
-      ylo[jj] = ok ? *reinterpret_cast<const u32x2*>(y) : u32x2{0u, 0u};
-      yhi[jj] = ok ? *reinterpret_cast<const u32x2*>(y + D / 2) : u32x2{0u, 0u};
+      y[jj] = (ok_mask >> j & 1u) ? load16(a.part_o + prow[j] * D + d8 * 8) : u32x4{0u, 0u, 0u, 0u};
     }
 #pragma unroll
     for (int jj = 0; jj < 8; ++jj) {
@@ -717,14 +714,11 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
       const float w = sj[j][1] > 0.f ? sj[j][1] * fast_exp2(sj[j][0] - M) : 0.f;
       L += w;
       const float wy = ldexpf(w, (int)sj[j][2]);
-      acc[0] += wy * f16_lo(ylo[jj][0]);
-      acc[1] += wy * f16_hi(ylo[jj][0]);
-      acc[2] += wy * f16_lo(ylo[jj][1]);
-      acc[3] += wy * f16_hi(ylo[jj][1]);
-      acc[4] += wy * f16_lo(yhi[jj][0]);
-      acc[5] += wy * f16_hi(yhi[jj][0]);
-      acc[6] += wy * f16_lo(yhi[jj][1]);
-      acc[7] += wy * f16_hi(yhi[jj][1]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        acc[2 * i] += wy * f16_lo(y[jj][i]);
+        acc[2 * i + 1] += wy * f16_hi(y[jj][i]);
+      }
     }
   }
   const float inv = 1.0f / L;
