@@ -132,6 +132,8 @@ def main():
                     help="run one device-to-device copy of this many MiB first (scales PMC byte counters)")
     ap.add_argument("--chunk-rows", type=int, default=16384,
                     help="prefill query rows per pipelined chunk (0: one chunk, no overlap)")
+    ap.add_argument("--graph", choices=["auto", "on", "off"], default="auto",
+                    help="replay unchunked steps from a captured HIP graph (auto: when the step is unchunked)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build measures one GPU only; the MSA hot path is not sharded across GPUs "
@@ -159,17 +161,23 @@ def main():
         del src, dst
 
     stages = ("append", "index_score", "block_topk", "attend")
+    use_graph = args.graph == "on" or (args.graph == "auto" and not runner.chunks)
+    step = runner.step
+    if use_graph:
+        runner.capture()
+        step = runner.replay
     for _ in range(args.warmup):
-        runner.step()
+        step()
     torch.cuda.synchronize()
 
-    # Timed region: K whole steps (pipelined over two streams when chunked).
+    # Timed region: K whole steps (pipelined over two streams when chunked,
+    # replayed from a captured HIP graph when not).
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_host = time.perf_counter()
     start.record(stream)
     for _ in range(args.steps):
-        runner.step()
+        step()
     end.record(stream)
     torch.cuda.synchronize()
     t_host = time.perf_counter() - t_host
@@ -241,7 +249,8 @@ def main():
                    "index_dim": w.index_dim, "block_size": w.block_size, "top_k": w.top_k},
         "stage_ms": stage_ms,
         "serial_ms_per_step": serial_ms,
-        "pipeline": {"chunks": max(1, len(runner.chunks)), "streams": 2 if runner.chunks else 1},
+        "pipeline": {"chunks": max(1, len(runner.chunks)), "streams": 2 if runner.chunks else 1,
+                     "hip_graph": use_graph},
         "step": step_info,
         "roofline": roof,
         "cpu_baseline": cpu,

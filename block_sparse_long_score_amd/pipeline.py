@@ -90,6 +90,25 @@ class MsaRunner:
         self.block_topk(stream)
         self.attend(stream=stream)
 
+    def capture(self):
+        """Record one unchunked step as a HIP graph, so that replay() issues
+        the whole step with a single launch from the host.  The step's kernels
+        allocate nothing and clear nothing with memset nodes; every buffer is
+        the runner's own, so replays are the same work on the same memory."""
+        if self.chunks:
+            raise ValueError("a chunked (two-stream) prefill step is not captured")
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            self.step()
+        torch.cuda.current_stream().wait_stream(side)
+        self.graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(self.graph):
+            self.step()
+
+    def replay(self):
+        self.graph.replay()
+
     def staged_step(self, mark):
         """The step run serially on the current stream, calling mark(name)
         after each stage (chunk by chunk when chunked) so a caller can record

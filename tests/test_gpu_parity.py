@@ -97,6 +97,60 @@ def test_decode_batch_ragged_lengths():
     check_selection_invariants(runner)
 
 
+_RAGGED = [1, 128, 129, 2047, 2049, 5000, 16 * 128, 16 * 128 + 1, 300, 4097, 7777, 12000, 64, 1500, 2176, 9000]
+
+
+@pytest.mark.parametrize("shape", ["g6_d128", "g4_d128", "g8_d64"])
+def test_decode_large_batch_one_workgroup_per_group(shape):
+    """Batches with >= 128 (sequence, group) pairs take the one-workgroup-per-pair decode kernel."""
+    import dataclasses
+    if shape == "g6_d128":
+        w = M2.with_sizes("decode16", _RAGGED, [1] * 16, permuted_table=True)
+    elif shape == "g4_d128":
+        w = dataclasses.replace(M2, num_q_heads=32).with_sizes("decode16g4", _RAGGED, [1] * 16, permuted_table=True)
+    else:
+        lens = [_RAGGED[i % 16] + 7 * (i // 16) for i in range(128)]
+        w = WORKLOADS["c0"].with_sizes("decode128", lens, [1] * 128, permuted_table=True)
+    assert w.num_seqs * w.num_kv_heads >= 128
+    runner = _run(w)
+    assert runner.decode
+    _all_rows(runner)
+    check_selection_invariants(runner)
+
+
+@pytest.mark.parametrize("case", ["decode_fused", "decode_split", "prefill"])
+def test_graph_replays_equal_eager_step(case):
+    """A captured step replays to the eager step's results, replay after replay,
+    with eager work and synchronisation in between."""
+    if case == "decode_fused":
+        w = M2.with_sizes("g_fused", _RAGGED, [1] * 16, permuted_table=True)
+    elif case == "decode_split":
+        w = M2.with_sizes("g_split", _RAGGED[:8], [1] * 8, permuted_table=True)
+    else:
+        w = M2.with_sizes("g_prefill", [3000], [3000])
+    runner = _run(w)
+    ref = [t.clone() for t in (runner.scores, runner.sel, runner.out)]
+    runner.capture()
+    torch.cuda.synchronize()
+    for i in range(3):
+        for t in (runner.scores, runner.sel, runner.out):
+            t.zero_()
+        torch.cuda.synchronize()
+        runner.replay()
+        torch.cuda.synchronize()
+        _announce(f"{case}: replay {i}")
+        assert torch.equal(runner.sel, ref[1]), f"replay {i}: selections differ"
+        assert torch.equal(runner.out, ref[2]), f"replay {i}: outputs differ"
+        # block scores of the blocks before each row's local block (the ones the kernel writes)
+        wl = runner.inputs.workload
+        for s_ in range(wl.num_seqs):
+            pos = runner.inputs.positions(s_)
+            for r, t in zip(seq_rows(runner.inputs, s_, pos), pos):
+                c = int(t) >> 7
+                assert torch.equal(runner.scores[r, :, :c], ref[0][r, :, :c]), f"replay {i}: scores of row {r} differ"
+    compare_rows(runner, 0, runner.inputs.positions(0)[-1:])
+
+
 def test_decode_equals_prefill_last_row():
     """A decode step over N cached tokens computes the prefill's last row."""
     import dataclasses
