@@ -76,7 +76,7 @@ __device__ __forceinline__ void load_batch(const float* __restrict__ row, int c,
 
 // Selection for one row.  Rows with c <= 1024 candidates keep their keys in
 // registers; longer rows are streamed in batches of 1024 (16 per lane).
-template <bool CACHED>
+template <bool CACHED, bool WRITE_LOCAL = true>
 __device__ void select_row(const float* __restrict__ row, int c, int32_t* __restrict__ out, uint32_t* surv_key,
                            int32_t* surv_idx) {
   const int lane = threadIdx.x & 63;
@@ -150,7 +150,7 @@ __device__ void select_row(const float* __restrict__ row, int c, int32_t* __rest
       ties += __popcll(eq);
     }
   }
-  if (lane == 0) out[kKeep] = c;
+  if (WRITE_LOCAL && lane == 0) out[kKeep] = c;
 }
 
 __global__ __launch_bounds__(256) void block_topk_kernel(TopkArgs a) {
@@ -177,12 +177,94 @@ __global__ __launch_bounds__(256) void block_topk_kernel(TopkArgs a) {
     select_row<false>(row, c, out, surv_key[wave], surv_idx[wave]);
 }
 
-hipError_t launch_block_topk(const Problem& p, const float* scores, int64_t ld, int32_t* sel, hipStream_t stream) {
+// Long rows when there are few of them (decode over very long contexts): one
+// workgroup of kSplitWaves waves per row.  Wave w finds the exact top 15 of
+// its contiguous share of the candidates (ties to the lower index, as above);
+// the overall top 15 lies in the union of these, which wave 0 then searches
+// in ascending block order with the same exact threshold and tie rule.
+constexpr int kSplitWaves = 16;
+constexpr int64_t kSplitMaxRows = 1024;    // split only while one wave per row leaves the chip idle
+constexpr int64_t kSplitMinBlocks = 2048;  // and rows are long enough to be worth splitting
+
+__global__ __launch_bounds__(kSplitWaves * 64) void block_topk_split_kernel(TopkArgs a) {
+  __shared__ uint32_t surv_key[kSplitWaves][64];
+  __shared__ int32_t surv_idx[kSplitWaves][64];
+  __shared__ int32_t cand[kSplitWaves][kKeep];
+  const Problem& p = a.p;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t R = blockIdx.x;
+  const int r = (int)(R >> a.hkv_shift);
+  const int s = seq_of_row(p.cu_q, p.num_seqs, r);
+  const int t = p.seq_lens[s] - (p.cu_q[s + 1] - r);
+  const int c = t >> 7;
+  int32_t* out = a.sel + R * kTopK;
+  if (c + 1 <= kTopK) {  // every causal block is kept
+    if (wave == 0 && lane < kTopK) out[lane] = lane <= c ? lane : -1;
+    return;
+  }
+  const float* row = a.scores + R * a.ld;
+  // Shares are multiples of 64 candidates; a share of n <= 15 keeps all n.
+  const int share = ((c + kSplitWaves * 64 - 1) / (kSplitWaves * 64)) * 64;
+  const int lo = min(c, wave * share), n = min(share, c - lo);
+  if (n > 0) {
+    if (n <= kCached * 64)
+      select_row<true, false>(row + lo, n, cand[wave], surv_key[wave], surv_idx[wave]);
+    else
+      select_row<false, false>(row + lo, n, cand[wave], surv_key[wave], surv_idx[wave]);
+  }
+  __syncthreads();
+  if (wave != 0) return;
+  // Candidates of all shares in ascending block order: up to kSplitWaves * 15.
+  constexpr int kRounds = (kSplitWaves * kKeep + 63) / 64;
+  uint32_t key[kRounds];
+  int32_t idx[kRounds];
+#pragma unroll
+  for (int j = 0; j < kRounds; ++j) {
+    const int e = j * 64 + lane;          // position in the concatenated list
+    const int w = e / kKeep, k = e - w * kKeep;
+    const int lo_w = min(c, w * share), n_w = min(share, c - lo_w);
+    const bool have = w < kSplitWaves && k < min(n_w, kKeep);
+    idx[j] = have ? lo_w + cand[w][k] : -1;
+    key[j] = have ? order_key(row[idx[j]]) : 0u;
+  }
+  // Exact 15th-largest key over the candidates, bit by bit.
+  uint32_t T = 0;
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t cnd = T | (1u << bit);
+    int nge = 0;
+#pragma unroll
+    for (int j = 0; j < kRounds; ++j) nge += __popcll(__ballot(key[j] >= cnd));
+    if (nge >= kKeep) T = cnd;
+  }
+  int gt = 0;
+#pragma unroll
+  for (int j = 0; j < kRounds; ++j) gt += __popcll(__ballot(key[j] > T));
+  const int need = kKeep - gt;
+  int taken = 0, ties = 0;
+#pragma unroll
+  for (int j = 0; j < kRounds; ++j) {
+    const uint64_t eq = __ballot(key[j] == T && idx[j] >= 0);
+    const bool take = idx[j] >= 0 && (key[j] > T || (key[j] == T && ties + lanes_below(eq) < need));
+    const uint64_t tm = __ballot(take);
+    if (take) out[taken + lanes_below(tm)] = idx[j];
+    taken += __popcll(tm);
+    ties += __popcll(eq);
+  }
+  if (lane == 0) out[kKeep] = c;
+}
+
+hipError_t launch_block_topk(const Problem& p, const float* scores, int64_t ld, int32_t* sel, int64_t max_blocks,
+                             hipStream_t stream) {
   int hkv_shift = 0;
   while ((1 << hkv_shift) < p.hkv) ++hkv_shift;
   const int64_t rows = (int64_t)p.total_q << hkv_shift;
   if (rows == 0) return hipSuccess;
   TopkArgs a{p, scores, ld, sel, hkv_shift};
+  if (rows <= kSplitMaxRows && max_blocks > kSplitMinBlocks) {
+    hipLaunchKernelGGL(block_topk_split_kernel, dim3((unsigned)rows), dim3(kSplitWaves * 64), 0, stream, a);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(block_topk_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, stream, a);
   return hipGetLastError();
 }

@@ -232,7 +232,7 @@ msa_status msa_block_topk(const msa_dims* dims, const msa_batch* batch, const fl
   if (ld < need) return fail(MSA_ERR_BAD_SHAPE, "ld=%lld is less than the %lld blocks of the longest sequence",
                              (long long)ld, (long long)need);
   const msa::Problem p = make_problem(dims, batch, nullptr);
-  return hip_status(msa::launch_block_topk(p, block_scores, ld, sel, static_cast<hipStream_t>(stream)),
+  return hip_status(msa::launch_block_topk(p, block_scores, ld, sel, need, static_cast<hipStream_t>(stream)),
                     "msa_block_topk launch");
 }
 

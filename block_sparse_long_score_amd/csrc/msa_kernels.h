@@ -35,7 +35,9 @@ hipError_t launch_kv_append(const Problem& p, uint16_t* k_cache, uint16_t* v_cac
 hipError_t launch_index_score(const Problem& p, const uint16_t* q_idx, float* scores, int64_t ld,
                               const int32_t* seq_lens_host, const int32_t* cu_q_host, hipStream_t stream);
 
-hipError_t launch_block_topk(const Problem& p, const float* scores, int64_t ld, int32_t* sel, hipStream_t stream);
+// max_blocks: blocks of the longest sequence (host-side), picks the kernel.
+hipError_t launch_block_topk(const Problem& p, const float* scores, int64_t ld, int32_t* sel, int64_t max_blocks,
+                             hipStream_t stream);
 
 // Largest max_blocks_per_seq the prefill selection inversion supports (its
 // per-workgroup LDS histogram holds one counter per logical block).

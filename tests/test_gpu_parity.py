@@ -171,10 +171,12 @@ def test_decode_equals_prefill_last_row():
     compare_rows(runner_d, 0, [4499])
 
 
-def test_topk_on_oracle_scores_with_ties():
+@pytest.mark.parametrize("n_rows", [64, 1100])
+def test_topk_on_oracle_scores_with_ties(n_rows):
     """The selection kernel alone, fed block scores written by the oracle
     (real rows) and by hand (massive ties, +/-0, long rows past the register
-    cache)."""
+    cache).  64 long rows take the split (16 waves per row) kernel, 1100 the
+    one-wave-per-row kernel."""
     w = M2.with_sizes("topk", [9000], [9000])
     inp = make_inputs(w, "cuda")
     runner = MsaRunner(inp)
@@ -189,7 +191,7 @@ def test_topk_on_oracle_scores_with_ties():
 
     import oracle
     rng = np.random.default_rng(3)
-    n_rows, ld = 64, 8300
+    ld = 8300
     pos = np.sort(rng.integers(2048, ld * 128, size=n_rows)).astype(np.int64)
     pos[:3] = [ld * 128 - 1, 1024 * 128 + 5, 1024 * 128 - 1]
     vals = rng.integers(-3, 4, size=(n_rows, 1, ld)).astype(np.float32) / 4
@@ -202,7 +204,7 @@ def test_topk_on_oracle_scores_with_ties():
     b = ops.Batch.make(wt.seq_lens, wt.q_lens, "cuda")
     scores = torch.from_numpy(vals).cuda()
     got = torch.empty((n_rows, 1, 16), dtype=torch.int32, device="cuda")
-    _announce("topk on hand-made scores, rows up to 8300 blocks")
+    _announce(f"topk on hand-made scores, {n_rows} rows up to 8300 blocks")
     ops.msa_block_topk(d, b, scores, got)
     torch.cuda.synchronize()
     np.testing.assert_array_equal(got.cpu().numpy(), want)
