@@ -57,6 +57,36 @@ def algorithmic_work(w):
                 io_bytes=float(io_bytes), pooled_bytes=float(pooled_bytes), nblk=nblk)
 
 
+def kernel_source_hash() -> str:
+    """Hash of the HIP sources and headers the library is built from."""
+    import hashlib
+    h = hashlib.sha256()
+    for d in (os.path.join(ROOT, "block_sparse_long_score_amd", "csrc"), os.path.join(ROOT, "include")):
+        for f in sorted(os.listdir(d)):
+            if f.endswith((".hip", ".h")):
+                h.update(f.encode())
+                with open(os.path.join(d, f), "rb") as fh:
+                    h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(workload: str, stage: str, launches_per_step: float):
+    """HBM bytes per launch of a stage, from the rocprofv3 FETCH_SIZE / WRITE_SIZE
+    runs recorded under profiles/ (scaled by the copy-kernel calibration
+    recorded with them); None if none was recorded for this workload or the
+    kernels changed since."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f).get(workload, {}).get(stage)
+    if not rec or rec.get("source_hash") != kernel_source_hash():
+        return None
+    return {"bytes_per_launch": rec["read_bytes_per_launch"] + rec["write_bytes_per_launch"],
+            "read_bytes_per_launch": rec["read_bytes_per_launch"], "write_bytes_per_launch": rec["write_bytes_per_launch"],
+            "source": rec["profile"]}
+
+
 def cpu_baseline(inputs, runner, budget_s: float):
     """The oracle as it stands, on a bounded sample of the same workload's
     rows, timed on this host's cores.  Host copies are outside the timing."""
@@ -132,8 +162,8 @@ def main():
                     help="run one device-to-device copy of this many MiB first (scales PMC byte counters)")
     ap.add_argument("--chunk-rows", type=int, default=16384,
                     help="prefill query rows per pipelined chunk (0: one chunk, no overlap)")
-    ap.add_argument("--graph", choices=["auto", "on", "off"], default="auto",
-                    help="replay unchunked steps from a captured HIP graph (auto: when the step is unchunked)")
+    ap.add_argument("--graph", choices=["on", "off"], default="off",
+                    help="replay an unchunked step from a captured HIP graph (stage events then come from a serial pass)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build measures one GPU only; the MSA hot path is not sharded across GPUs "
@@ -161,7 +191,9 @@ def main():
         del src, dst
 
     stages = ("append", "index_score", "block_topk", "attend")
-    use_graph = args.graph == "on" or (args.graph == "auto" and not runner.chunks)
+    use_graph = args.graph == "on"
+    if use_graph and runner.chunks:
+        sys.exit("bench.py: --graph on needs an unchunked step (--chunk-rows 0)")
     step = runner.step
     if use_graph:
         runner.capture()
@@ -170,25 +202,10 @@ def main():
         step()
     torch.cuda.synchronize()
 
-    # Timed region: K whole steps (pipelined over two streams when chunked,
-    # replayed from a captured HIP graph when not).
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t_host = time.perf_counter()
-    start.record(stream)
-    for _ in range(args.steps):
-        step()
-    end.record(stream)
-    torch.cuda.synchronize()
-    t_host = time.perf_counter() - t_host
-    total_ms = start.elapsed_time(end)
-    ms_per_step = total_ms / args.steps
-
-    # Stage breakdown: the same step run serially, an event after each stage
-    # (per chunk when chunked); stage time = sum over its launches.
-    stage_ms = {k: 0.0 for k in stages}
-    n_stage_steps = max(2, min(args.steps, 5))
-    for _ in range(n_stage_steps):
+    def staged_ms():
+        """Stage times of the step run serially on one stream, an event after
+        each stage (per chunk when chunked); stage time = sum over its launches."""
+        out = {k: 0.0 for k in stages}
         marks = []
 
         def mark(name):
@@ -199,32 +216,83 @@ def main():
         runner.staged_step(mark)
         torch.cuda.synchronize()
         for (_, e0), (name, e1) in zip(marks, marks[1:]):
-            stage_ms[name] += e0.elapsed_time(e1) / n_stage_steps
+            out[name] += e0.elapsed_time(e1)
+        return out
+
+    # The dominant stage: decode is bound by the K_idx scan; prefill by
+    # whichever of scoring and attention takes longer on this workload.
+    pre = staged_ms()
+    dom = "index_score" if runner.decode else max(("index_score", "attend"), key=lambda k: pre[k])
+
+    # Timed region: K whole steps (pipelined over two streams when chunked).
+    # Each launch of the dominant stage is bracketed by events on the stream
+    # it runs on.
+    pairs = []
+
+    def hook(name, st, phase):
+        if name != dom:
+            return
+        e = torch.cuda.Event(enable_timing=True)
+        e.record(st)
+        if phase == 0:
+            pairs.append([e, None])
+        else:
+            pairs[-1][1] = e
+
+    if not use_graph:
+        runner.hook = hook
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_host = time.perf_counter()
+    start.record(stream)
+    for _ in range(args.steps):
+        step()
+    end.record(stream)
+    torch.cuda.synchronize()
+    t_host = time.perf_counter() - t_host
+    runner.hook = None
+    total_ms = start.elapsed_time(end)
+    ms_per_step = total_ms / args.steps
+    if pairs:
+        launch_ms = [e0.elapsed_time(e1) for e0, e1 in pairs]
+        launches_per_step = len(pairs) / args.steps
+    else:  # graph replay: no events inside the graph; serial stage time instead
+        launch_ms, launches_per_step = [pre[dom]], 1.0
+    avg_launch_ms = sum(launch_ms) / len(launch_ms)
+
+    # Stage breakdown (serial pass), averaged over a few steps.
+    n_stage_steps = max(2, min(args.steps, 5))
+    stage_ms = {k: 0.0 for k in stages}
+    for _ in range(n_stage_steps):
+        for k, v in staged_ms().items():
+            stage_ms[k] += v / n_stage_steps
     serial_ms = sum(stage_ms.values())
 
     tokens = w.total_q
     value = tokens / (ms_per_step / 1e3)
+    traffic = recorded_traffic(w.name, dom, launches_per_step)
     if runner.decode:
-        dom = "index_score"
-        algo = work["kidx_bytes"] + work["pooled_bytes"] / 2
-        achieved = algo / (stage_ms[dom] / 1e3) / 1e9
-        roof = {"bound": "hbm", "kernel": "msa_index_score (index_score_kernel, K_idx scan)", "achieved": achieved,
-                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": None}
+        algo = (work["kidx_bytes"] + work["pooled_bytes"] / 2) / launches_per_step
+        achieved = algo / (avg_launch_ms / 1e3) / 1e9
+        roof = {"bound": "hbm", "kernel": "msa_index_score (index_score_kernel: K_idx scan + block max-pool)",
+                "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                "traffic": traffic, "algorithmic_bytes_per_launch": algo}
         step_bytes = work["kidx_bytes"] + work["kv_bytes"] + work["io_bytes"] + work["pooled_bytes"]
         step_frac = step_bytes / (ms_per_step / 1e3) / 1e9 / HBM_PEAK_GBS
         step_info = {"algorithmic_bytes": step_bytes, "hbm_frac_whole_step": step_frac}
     else:
-        dom = max(("index_score", "attend"), key=lambda k: stage_ms[k])
-        algo = work["index_flops"] if dom == "index_score" else work["main_flops"]
-        achieved = algo / (stage_ms[dom] / 1e3) / 1e12
-        name = ("msa_index_score (index_score_kernel)" if dom == "index_score"
-                else "msa_sparse_attn_prefill (selection inversion + kvouter + merge kernels)")
+        algo = (work["index_flops"] if dom == "index_score" else work["main_flops"]) / launches_per_step
+        achieved = algo / (avg_launch_ms / 1e3) / 1e12
+        name = ("msa_index_score (index_score_shared_kernel: scoring + block max-pool)" if dom == "index_score"
+                else "msa_sparse_attn_prefill (selection inversion, kvouter_kernel, merge_kernel)")
         roof = {"bound": "mfma", "kernel": name, "achieved": achieved, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": achieved / BF16_PEAK_TFLOPS, "traffic": None}
+                "frac": achieved / BF16_PEAK_TFLOPS, "traffic": traffic, "algorithmic_flops_per_launch": algo}
         step_flops = work["index_flops"] + work["main_flops"]
         step_info = {"algorithmic_flops": step_flops,
                      "mfma_frac_whole_step": step_flops / (ms_per_step / 1e3) / 1e12 / BF16_PEAK_TFLOPS,
                      "prefill_tokens_per_s_without_append": tokens / ((ms_per_step - stage_ms["append"]) / 1e3)}
+    roof["launches_per_step"] = launches_per_step
+    roof["avg_launch_ms"] = avg_launch_ms
 
     cpu = None
     if not args.no_cpu_baseline:

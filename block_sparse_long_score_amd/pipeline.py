@@ -52,6 +52,10 @@ class MsaRunner:
         ws_batch = self.chunks[0][2] if self.chunks else self.batch
         self.workspace = torch.empty(ops.msa_workspace_size(self.dims, self.cache, ws_batch, call),
                                      dtype=torch.uint8, device=dev)
+        # Optional observer: hook(stage, stream, phase) is called right before
+        # (phase 0) and after (phase 1) each stage is enqueued in step(), with
+        # the stream it is enqueued on (used to time a stage with events).
+        self.hook = None
 
     def _fill_prefix(self):
         """Cache every token before the step's queries, one sequence at a time."""
@@ -82,13 +86,21 @@ class MsaRunner:
         fn = ops.msa_sparse_attn_decode if self.decode else ops.msa_sparse_attn_prefill
         fn(self.dims, self.cache, self.batch, self.inputs.q, sel, self.out, self.workspace, stream)
 
+    def _stage(self, name, stream, fn):
+        if self.hook is None:
+            return fn()
+        self.hook(name, stream, 0)
+        fn()
+        self.hook(name, stream, 1)
+
     def step(self, stream=None):
         if self.chunks:
             return self.pipelined_step()
-        self.append(stream)
-        self.index_score(stream)
-        self.block_topk(stream)
-        self.attend(stream=stream)
+        st = stream if stream is not None else torch.cuda.current_stream()
+        self._stage("append", st, lambda: self.append(st))
+        self._stage("index_score", st, lambda: self.index_score(st))
+        self._stage("block_topk", st, lambda: self.block_topk(st))
+        self._stage("attend", st, lambda: self.attend(stream=st))
 
     def capture(self):
         """Record one unchunked step as a HIP graph, so that replay() issues
@@ -135,14 +147,15 @@ class MsaRunner:
         a = torch.cuda.current_stream()
         b = self.stream_b
         inp = self.inputs
-        self.append(a)
+        self._stage("append", a, lambda: self.append(a))
         for i, (r0, r1, cb) in enumerate(self.chunks):
             scores, sel = self.scores[r0:r1], self.sel[r0:r1]
-            ops.msa_index_score(self.dims, self.cache, cb, inp.q_idx[r0:r1], scores, a)
-            ops.msa_block_topk(self.dims, cb, scores, sel, a)
+            self._stage("index_score", a,
+                        lambda: ops.msa_index_score(self.dims, self.cache, cb, inp.q_idx[r0:r1], scores, a))
+            self._stage("block_topk", a, lambda: ops.msa_block_topk(self.dims, cb, scores, sel, a))
             self.events[i].record(a)
             b.wait_event(self.events[i])
-            ops.msa_sparse_attn_prefill(self.dims, self.cache, cb, inp.q[r0:r1], sel, self.out[r0:r1],
-                                        self.workspace, b)
+            self._stage("attend", b, lambda: ops.msa_sparse_attn_prefill(
+                self.dims, self.cache, cb, inp.q[r0:r1], sel, self.out[r0:r1], self.workspace, b))
         self.events[-1].record(b)
         a.wait_event(self.events[-1])
