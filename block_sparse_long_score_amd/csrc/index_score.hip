@@ -178,61 +178,96 @@ __global__ __launch_bounds__(256, 2) void index_score_kernel(IndexArgs a) {
   }
 }
 
-// Prefill variant: the four waves of a workgroup share each K_idx block
-// through LDS (double-buffered) and each owns its own 32*NCTW columns, so a
-// block fetched from L2 once feeds 4*32*NCTW columns (512 at NCTW=4: 64
-// queries x 8 groups).  Blocks at or after the tile's first query block are
-// masked per column (key position > query position).  Pooled scores are
-// staged in LDS and written as one contiguous run per (query, group) row.
+// Prefill variant: the WAVES waves of a workgroup share each K_idx block
+// through LDS (double-buffered, filled by direct global-to-LDS loads) and
+// each owns its own 32*NCTW columns, so a block fetched once feeds
+// WAVES*32*NCTW columns (512 at 8 waves x 64 columns: 64 queries x 8 groups).
+// Eight waves of <= 128 VGPRs give four waves per SIMD to interleave the
+// MFMA stream with the max reductions.  Blocks at or after the tile's first
+// query block are masked per column (key position > query position).  Pooled
+// scores are staged in LDS and written as one contiguous run per (query,
+// group) row.
 constexpr int kSharedFlush = 16;  // pooled scores staged in LDS per flush
 
-// Pooled scores of one LDS-staged key block for a wave's NCTW column tiles.
-// MASKED keeps the key-tile loop rolled so its per-element masks are formed
-// inside the loop rather than all up front.
-template <int DIDX, int NCTW, int KP, bool MASKED>
-__device__ __forceinline__ void shared_pool(const uint16_t* __restrict__ kt, const bf16x8 (&bq)[NCTW][DIDX / 16],
-                                            const int (&lim)[NCTW], float (&runmax)[NCTW]) {
-  constexpr int KS = DIDX / 16;
-  const int lane = threadIdx.x & 63;
-  const int half = lane >> 5, l32 = lane & 31;
-#pragma unroll
-  for (int ct = 0; ct < NCTW; ++ct) runmax[ct] = -__builtin_inff();
-  constexpr int kUnroll = MASKED ? 1 : 4;
-#pragma unroll kUnroll
-  for (int m = 0; m < 4; ++m) {
-    __builtin_amdgcn_sched_barrier(0);
-    bf16x8 ak[KS];
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-      ak[ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(&kt[(m * 32 + l32) * KP + ks * 16 + half * 8]));
-#pragma unroll
-    for (int ct = 0; ct < NCTW; ++ct) {
-      f32x16 acc = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) acc = mfma32(ak[ks], bq[ct][ks], acc);
-      if constexpr (MASKED) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = m * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-          acc[r] = key > lim[ct] ? -__builtin_inff() : acc[r];
-        }
-      }
-      float mx = acc[0];
-#pragma unroll
-      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, acc[r]);
-      runmax[ct] = fmaxf(runmax[ct], mx);
-    }
-  }
+// LDS layout of a staged K_idx block: rows of DIDX bf16 without padding, the
+// 16-byte chunk c of row r stored at chunk position c ^ swz(r), where swz
+// spreads the 16 rows one MFMA operand read touches over distinct banks
+// (rows per 256 bytes: 2 at DIDX=64, 4 at DIDX=32).
+template <int DIDX>
+__device__ __forceinline__ int kidx_swizzle(int r, int c) {
+  constexpr int CPR = DIDX / 8;          // 16-byte chunks per row
+  constexpr int RPB = 256 / (DIDX * 2);  // rows per 256 bytes of banks
+  return c ^ ((r / RPB) & (CPR - 1));
 }
 
-template <int DIDX, int NCTW>
-__global__ __launch_bounds__(256, 2) void index_score_shared_kernel(IndexArgs a) {
-  constexpr int KS = DIDX / 16;
+// Pooled scores of one LDS-staged key block for a wave's 16-column tiles,
+// on the 16x16x32 bf16 MFMA with keys on M: A lane l holds K_idx[key l%16]
+// [8*(l/16) .. +7] of a 32-wide k-step, B lane l holds Q_idx[column l%16]
+// likewise, and D lane l register i holds the score of key 4*(l/16)+i for
+// column l%16.  The 8 key tiles of the block are software-pipelined over two
+// accumulator sets, so each tile's running max overlaps the next tile's
+// MFMAs.  Each lane keeps a running max over its 4-key subsets; the four
+// lanes of a column are combined by the caller.  MASKED: keys after a
+// column's query position are -inf.
+template <int DIDX, int NCT, bool MASKED>
+__device__ __forceinline__ void shared_pool(const uint16_t* __restrict__ kt, const bf16x8 (&bq)[NCT][DIDX / 32],
+                                            const int (&lim)[NCT], float (&runmax)[NCT]) {
+  constexpr int KS = DIDX / 32;
+  const int lane = threadIdx.x & 63;
+  const int l16 = lane & 15, q4 = lane >> 4;
+#pragma unroll
+  for (int ct = 0; ct < NCT; ++ct) runmax[ct] = -__builtin_inff();
+  f32x4 acc[2][NCT];
+  auto issue = [&](int t, f32x4 (&a)[NCT]) {
+    bf16x8 ak[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const int r = t * 16 + l16;
+      ak[ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(&kt[r * DIDX + kidx_swizzle<DIDX>(r, ks * 4 + q4) * 8]));
+    }
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
+      a[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) a[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak[ks], bq[ct][ks], a[ct], 0, 0, 0);
+    }
+  };
+  auto reduce = [&](int t, f32x4 (&a)[NCT]) {
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
+      f32x4 v = a[ct];
+      if constexpr (MASKED) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] = t * 16 + 4 * q4 + i > lim[ct] ? -__builtin_inff() : v[i];
+      }
+      runmax[ct] = fmaxf(fmaxf(fmaxf(fmaxf(runmax[ct], v[0]), v[1]), v[2]), v[3]);  // two v_max3
+    }
+  };
+  issue(0, acc[0]);
+#pragma unroll
+  for (int t = 1; t < kBlock / 16; ++t) {
+    issue(t, acc[t & 1]);
+    reduce(t - 1, acc[(t - 1) & 1]);
+  }
+  reduce(kBlock / 16 - 1, acc[1]);
+}
+
+// The running maxima of the four lanes that share a column (lanes l%16 + 16j).
+__device__ __forceinline__ float column_max16(float v) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(v, __uint_as_float((threadIdx.x & 32) ? a[0] : a[1]));
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(v, __uint_as_float((threadIdx.x & 16) ? b[0] : b[1]));
+}
+
+template <int DIDX, int NCTW, int WAVES>
+__global__ __launch_bounds__(64 * WAVES, WAVES / 2) void index_score_shared_kernel(IndexArgs a) {
+  constexpr int KS = DIDX / 32;           // 16x16x32 MFMA k-steps
+  constexpr int NCT = 2 * NCTW;           // 16-column tiles per wave
   constexpr int NCW = 32 * NCTW;          // columns per wave
-  constexpr int NC = 4 * NCW;             // columns per workgroup
+  constexpr int NC = WAVES * NCW;         // columns per workgroup
   constexpr int BLK = kBlock * DIDX;      // bf16 elements of one K_idx block
-  constexpr int KP = DIDX + 8;            // LDS row pitch (bf16)
-  __shared__ uint16_t kbuf[2][kBlock * KP];
+  __shared__ __attribute__((aligned(1024))) uint16_t kbuf[2][BLK];
   __shared__ float pooled_s[NC][kSharedFlush + 1];
   const Problem& p = a.p;
 
@@ -257,45 +292,49 @@ __global__ __launch_bounds__(256, 2) void index_score_shared_kernel(IndexArgs a)
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int half = lane >> 5, l32 = lane & 31;
+  const int l16 = lane & 15, q4 = lane >> 4;
   const int hkv_mask = (1 << a.hkv_shift) - 1;
 
-  bf16x8 bq[NCTW][KS];
-  int col_pos[NCTW];
+  // This lane's column in every 16-column tile and its Q_idx operand
+  // (dims 32*ks + 8*q4 .. +7).
+  bf16x8 bq[NCT][KS];
+  int col_pos[NCT];
 #pragma unroll
-  for (int ct = 0; ct < NCTW; ++ct) {
-    const int col = wave * NCW + ct * 32 + l32;
+  for (int ct = 0; ct < NCT; ++ct) {
+    const int col = wave * NCW + ct * 16 + l16;
     const int pos = p0 + (col >> a.hkv_shift);
     const bool valid = pos >= first_pos && pos < seq_len;
     col_pos[ct] = pos;
     const int64_t R = ((int64_t)(row0 + pos - first_pos) << a.hkv_shift) + (col & hkv_mask);
-    const uint16_t* src = a.q_idx + R * DIDX + half * 8;
+    const uint16_t* src = a.q_idx + R * DIDX + q4 * 8;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) bq[ct][ks] = as_bf16x8(valid ? load16(src + ks * 16) : u32x4{0u, 0u, 0u, 0u});
+    for (int ks = 0; ks < KS; ++ks) bq[ct][ks] = as_bf16x8(valid ? load16(src + ks * 32) : u32x4{0u, 0u, 0u, 0u});
   }
 
-  // Staging: each thread moves BLK/8/256 16-byte pieces of a block.
-  constexpr int PIECES = BLK / 8 / 256;
+  // Staging: direct global-to-LDS loads (16 bytes per lane, one contiguous
+  // 1 KB LDS run per wave instruction).  Lane L of the instruction that fills
+  // rows [8j, 8j+8) (DIDX=64) lands at chunk position L % CPR of row
+  // 8j + L / CPR, so it loads the global chunk that the swizzle puts there.
+  constexpr int CPR = DIDX / 8;                // 16-byte chunks per row
+  constexpr int RUNS = BLK * 2 / 1024;         // 1 KB runs per block
+  static_assert(RUNS % WAVES == 0, "runs per wave");
   const int32_t* table = p.block_table + (int64_t)s * p.max_blocks_per_seq;
-  auto fetch = [&](int kb, u32x4 (&r)[PIECES]) {
+  auto dma = [&](int kb, int buf) {
     const int phys = table[kb];
-    const bool ok = phys >= 0 && phys < p.num_blocks;
-    const uint16_t* src = p.k_idx + (int64_t)(ok ? phys : 0) * BLK;
+    const uint16_t* src = p.k_idx + (int64_t)((phys >= 0 && phys < p.num_blocks) ? phys : 0) * BLK;
 #pragma unroll
-    for (int i = 0; i < PIECES; ++i) r[i] = ok ? load16(src + (threadIdx.x + i * 256) * 8) : u32x4{0u, 0u, 0u, 0u};
-  };
-  auto put = [&](int buf, const u32x4 (&r)[PIECES]) {
-#pragma unroll
-    for (int i = 0; i < PIECES; ++i) {
-      const int e = (threadIdx.x + i * 256) * 8;  // element index in the block
-      store16(&kbuf[buf][(e / DIDX) * KP + (e % DIDX)], r[i]);
+    for (int k = 0; k < RUNS / WAVES; ++k) {
+      const int run = wave + WAVES * k;
+      const int row = run * (1024 / (DIDX * 2)) + lane / CPR;
+      const int chunk = kidx_swizzle<DIDX>(row, lane % CPR);
+      __builtin_amdgcn_global_load_lds(static_cast<const void*>(src + row * DIDX + chunk * 8),
+                                       reinterpret_cast<__attribute__((address_space(3))) void*>(
+                                           reinterpret_cast<uintptr_t>(&kbuf[buf][run * 512])),
+                                       16, 0, 0);
     }
   };
-  {
-    u32x4 r[PIECES];
-    fetch(kb0, r);
-    put(0, r);
-  }
+  dma(kb0, 0);
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
   // Each valid (query, group) row writes the staged pooled scores of blocks
@@ -315,26 +354,25 @@ __global__ __launch_bounds__(256, 2) void index_score_shared_kernel(IndexArgs a)
 
   for (int i = 0; i < nkb; ++i) {
     const int kb = kb0 + i;
-    u32x4 nxt[PIECES];
-    if (i + 1 < nkb) fetch(kb + 1, nxt);
+    if (i + 1 < nkb) dma(kb + 1, (i + 1) & 1);  // that buffer was released by the last barrier
     const uint16_t* kt = kbuf[i & 1];
-    float runmax[NCTW];
+    float runmax[NCT];
     if (kb >= unmasked_end) {
-      int lim[NCTW];
+      int lim[NCT];
 #pragma unroll
-      for (int ct = 0; ct < NCTW; ++ct) lim[ct] = col_pos[ct] - kb * kBlock;
-      shared_pool<DIDX, NCTW, KP, true>(kt, bq, lim, runmax);
+      for (int ct = 0; ct < NCT; ++ct) lim[ct] = col_pos[ct] - kb * kBlock;
+      shared_pool<DIDX, NCT, true>(kt, bq, lim, runmax);
     } else {
-      const int lim[NCTW] = {};
-      shared_pool<DIDX, NCTW, KP, false>(kt, bq, lim, runmax);
+      const int lim[NCT] = {};
+      shared_pool<DIDX, NCT, false>(kt, bq, lim, runmax);
     }
     const int slot = i % kSharedFlush;
 #pragma unroll
-    for (int ct = 0; ct < NCTW; ++ct) {
-      const float v = fmaxf(runmax[ct], swap_halves(runmax[ct]));
-      if (half == 0) pooled_s[wave * NCW + ct * 32 + l32][slot] = v;
+    for (int ct = 0; ct < NCT; ++ct) {
+      const float v = column_max16(runmax[ct]);
+      if (q4 == 0) pooled_s[wave * NCW + ct * 16 + l16][slot] = v;
     }
-    if (i + 1 < nkb) put((i + 1) & 1, nxt);
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of the next block have landed
     __syncthreads();
     if (slot == kSharedFlush - 1 || i + 1 == nkb) {
       flush(kb - slot, slot + 1);
@@ -358,7 +396,7 @@ hipError_t launch_index_score(const Problem& p, const uint16_t* q_idx, float* sc
   for (int s = 0; s < p.num_seqs; ++s) max_q = std::max(max_q, cu_q_host[s + 1] - cu_q_host[s]);
   if (max_q <= 0) return hipSuccess;
   // Prefill-shaped batches: 512 columns per workgroup sharing each K_idx block.
-  constexpr int kSharedCols = 4 * 32 * 4;
+  constexpr int kSharedCols = 8 * 32 * 2;  // 8 waves x 64 columns
   if (max_q * p.hkv > 4 * kSharedCols) {
     const int tq = kSharedCols / p.hkv;
     int max_tiles = 0, max_blocks = 0;
@@ -376,9 +414,9 @@ hipError_t launch_index_score(const Problem& p, const uint16_t* q_idx, float* sc
     IndexArgs a{p, q_idx, scores, ld, tq, hkv_shift, kc};
     dim3 grid((unsigned)max_tiles, (unsigned)((max_blocks + kc - 1) / kc), (unsigned)p.num_seqs);
     if (p.index_dim == 64)
-      hipLaunchKernelGGL((index_score_shared_kernel<64, 4>), grid, dim3(256), 0, stream, a);
+      hipLaunchKernelGGL((index_score_shared_kernel<64, 2, 8>), grid, dim3(512), 0, stream, a);
     else
-      hipLaunchKernelGGL((index_score_shared_kernel<32, 4>), grid, dim3(256), 0, stream, a);
+      hipLaunchKernelGGL((index_score_shared_kernel<32, 2, 8>), grid, dim3(512), 0, stream, a);
     return hipGetLastError();
   }
   // Decode-shaped and small batches: each wave streams its own key blocks.
