@@ -232,7 +232,7 @@ __global__ __launch_bounds__(256) void csr_chunk_map_kernel(CsrArgs a) {
 template <int D>
 struct Lds {
   static constexpr int KP = D + 8;    // K row pitch (bf16): rows stay 16-byte aligned
-  static constexpr int VP = 128 + 8;  // V^T row pitch (bf16)
+  static constexpr int VP = 128 + 4;  // V^T row pitch (bf16): 66 words, so the 32 rows one PV operand read touches fill all 64 banks once
   uint16_t k[128 * KP];
   uint16_t vt[D * VP];
 };
@@ -335,12 +335,54 @@ __device__ __forceinline__ void softmax_rows(f32x16 (&sacc)[4], float c, float& 
   l = sum;
 }
 
+// Query rows of a 32-row tile as the B operand of block_scores: lane (row
+// rho, half h) needs dims 16*ks + 8h .. +7 of row rho for every k-step ks.
+// They are loaded as 64-byte row segments: in load pair j, lane (h, a, b)
+// (a = bit 4 of the lane, b its low 4 bits) reads 16 bytes of tile row b
+// (first load) and of tile row 16 + b (second load), so four lanes cover 32
+// consecutive dims of one row per load.  q_operand() then swaps with the
+// lane 16 away to give every lane its own row.  Loads are issued early
+// (load_q_raw) and the swaps done when the operand is needed.
 template <int D>
-__device__ __forceinline__ void load_q(const uint16_t* __restrict__ qrow, bool valid, bf16x8 (&bq)[D / 16]) {
-  const int half = (threadIdx.x & 63) >> 5;
+struct QRaw {
+  u32x4 a[D / 32], b[D / 32];
+};
+
+__device__ __forceinline__ uint32_t partner16(uint32_t x) {
+  const auto t = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+  return (threadIdx.x & 16) ? t[0] : t[1];
+}
+
+template <int D>
+__device__ __forceinline__ void load_q_raw(const uint16_t* __restrict__ qrow, QRaw<D>& raw) {
+  const int lane = threadIdx.x & 63;
+  const int h = lane >> 5, a16 = (lane >> 4) & 1;
+  const uint64_t own = reinterpret_cast<uint64_t>(qrow);
+  const uint64_t other = ((uint64_t)partner16((uint32_t)(own >> 32)) << 32) | partner16((uint32_t)own);
+  const uint16_t* rowA = reinterpret_cast<const uint16_t*>(a16 ? other : own);  // tile row b
+  const uint16_t* rowB = reinterpret_cast<const uint16_t*>(a16 ? own : other);  // tile row 16 + b
 #pragma unroll
-  for (int ks = 0; ks < D / 16; ++ks)
-    bq[ks] = as_bf16x8(valid ? load16(qrow + ks * 16 + half * 8) : u32x4{0u, 0u, 0u, 0u});
+  for (int j = 0; j < D / 32; ++j) {
+    raw.a[j] = load16(rowA + (4 * j + 2 * a16 + h) * 8);
+    raw.b[j] = load16(rowB + (4 * j + 2 * (1 - a16) + h) * 8);
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void q_operand(const QRaw<D>& raw, bf16x8 (&bq)[D / 16]) {
+  const bool a16 = (threadIdx.x & 16) != 0;
+#pragma unroll
+  for (int j = 0; j < D / 32; ++j) {
+    u32x4 x, y;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const auto t = __builtin_amdgcn_permlane16_swap(raw.a[j][i], raw.b[j][i], false, false);
+      x[i] = a16 ? t[1] : t[0];  // dims 32j + 8h .. +7 of this lane's row
+      y[i] = a16 ? t[0] : t[1];  // dims 32j + 16 + 8h .. +7
+    }
+    bq[2 * j] = as_bf16x8(x);
+    bq[2 * j + 1] = as_bf16x8(y);
+  }
 }
 
 // ------------------------------------------------------------- kvouter pass
@@ -418,16 +460,17 @@ __global__ __launch_bounds__(256, 2) void kvouter_kernel(KvOuterArgs a) {
   int tile = wave;
   if (tile * 32 >= rows) return;
   TileRow cur = tile_row(tile);
-  bf16x8 bq[D / 16];
-  load_q<D>(cur.q, cur.valid, bq);
+  QRaw<D> raw;
+  load_q_raw<D>(cur.q, raw);  // rows past the list end read a valid row's query; nothing of theirs is stored
   for (; tile * 32 < rows; tile += 4) {
+    bf16x8 bq[D / 16];
+    q_operand<D>(raw, bq);
     // Next tile's row and query loads are issued before this tile's math.
     const int nxt = tile + 4;
     TileRow next = cur;
-    bf16x8 bq_next[D / 16];
     if (nxt * 32 < rows) {
       next = tile_row(nxt);
-      load_q<D>(next.q, next.valid, bq_next);
+      load_q_raw<D>(next.q, raw);
     }
 
     f32x16 sacc[4];
@@ -490,8 +533,6 @@ __global__ __launch_bounds__(256, 2) void kvouter_kernel(KvOuterArgs a) {
     }
     if (cur.valid && half == 0) *reinterpret_cast<f32x4*>(a.part_st + cur.prow * 4) = f32x4{m, l, (float)ex, 0.f};
     cur = next;
-#pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) bq[ks] = bq_next[ks];
   }
 }
 
