@@ -87,7 +87,7 @@ static MainWs main_layout(const Problem& p, bool decode) {
     w.entry_of = o;   o = align256(o + sizeof(int32_t) * w.max_entries);
   }
   w.part_o = o;  o = align256(o + sizeof(uint16_t) * parts * p.head_dim);
-  w.part_st = o; o = align256(o + sizeof(float) * 4 * parts);
+  w.part_st = o; o = align256(o + sizeof(float) * 2 * parts);
   w.total = o;
   return w;
 }
@@ -400,7 +400,7 @@ struct KvOuterArgs {
   // writes one contiguous range); decode stores (R, slot) at (R*16+slot)*G.
   uint16_t* part_o;  // fp16 [entries][G][D], natural dim order: normalised output * 2^-e
   uint16_t* out_direct;  // decode_fused_kernel: the bf16 output [total_q][hq][D]
-  float* part_st;    // [entries][G][4]: (max, sum, e, 0), max in base-2 units
+  float* part_st;    // [entries][G][2]: (log2 of the slot's softmax mass, e)
   int64_t n_lists;
   int hkv_shift;
   int chunk;
@@ -531,7 +531,7 @@ __global__ __launch_bounds__(256, 2) void kvouter_kernel(KvOuterArgs a) {
       if (okA) store16(dstA + 32 * n, a16 ? c2 : c1);
       if (okB) store16(dstB + 32 * n, a16 ? c1 : c2);
     }
-    if (cur.valid && half == 0) *reinterpret_cast<f32x4*>(a.part_st + cur.prow * 4) = f32x4{m, l, (float)ex, 0.f};
+    if (cur.valid && half == 0) *reinterpret_cast<f32x2*>(a.part_st + cur.prow * 2) = f32x2{m + __log2f(l), (float)ex};
     cur = next;
   }
 }
@@ -682,7 +682,7 @@ __global__ __launch_bounds__(256) void decode_block_kernel(KvOuterArgs a) {
   }
   if (tid < G) {
     const int64_t prow = (R * kTopK + slot) * G + tid;
-    *reinterpret_cast<f32x4*>(a.part_st + prow * 4) = f32x4{stat_s[tid][0], stat_s[tid][1], stat_s[tid][2], 0.f};
+    *reinterpret_cast<f32x2*>(a.part_st + prow * 2) = f32x2{stat_s[tid][0] + __log2f(stat_s[tid][1]), stat_s[tid][2]};
   }
 }
 
@@ -899,12 +899,13 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
       prow[j] = (ok ? ent : 0) * G + hj;
     }
   }
+  // Slot j's weight is its softmax mass 2^lse_j relative to the largest.
   float M = -__builtin_inff();
-  f32x4 sj[kTopK];
+  f32x2 sj[kTopK];
 #pragma unroll
   for (int j = 0; j < kTopK; ++j) {
-    sj[j] = (ok_mask >> j & 1u) ? *reinterpret_cast<const f32x4*>(a.part_st + prow[j] * 4)
-                                : f32x4{-__builtin_inff(), 0.f, 0.f, 0.f};
+    sj[j] = (ok_mask >> j & 1u) ? *reinterpret_cast<const f32x2*>(a.part_st + prow[j] * 2)
+                                : f32x2{-__builtin_inff(), 0.f};
     M = fmaxf(M, sj[j][0]);
   }
   float L = 0.f;
@@ -921,9 +922,9 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
 #pragma unroll
     for (int jj = 0; jj < 8; ++jj) {
       const int j = h8 + jj;
-      const float w = sj[j][1] > 0.f ? sj[j][1] * fast_exp2(sj[j][0] - M) : 0.f;
+      const float w = (ok_mask >> j & 1u) ? fast_exp2(sj[j][0] - M) : 0.f;
       L += w;
-      const float wy = ldexpf(w, (int)sj[j][2]);
+      const float wy = ldexpf(w, (int)sj[j][1]);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         acc[2 * i] += wy * f16_lo(y[jj][i]);
