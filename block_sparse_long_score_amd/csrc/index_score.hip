@@ -381,6 +381,122 @@ __global__ __launch_bounds__(64 * WAVES, WAVES / 2) void index_score_shared_kern
   }
 }
 
+// Decode-shaped batches (one 32-column tile per sequence): each wave streams
+// its own key blocks.  A block arrives by direct global-to-LDS loads into the
+// wave's own 16 KB LDS region (coalesced 1 KB runs, swizzled as in the
+// prefill kernel), is read into registers, and the wave's next block is
+// requested into the same region before this one is multiplied, so one block
+// per wave is always in flight without a workgroup barrier.
+template <int DIDX>
+__global__ __launch_bounds__(256, 2) void index_score_stream_kernel(IndexArgs a) {
+  constexpr int KS = DIDX / 16;          // 32x32x16 MFMA k-steps
+  constexpr int BLK = kBlock * DIDX;     // bf16 elements of one K_idx block
+  constexpr int CPR = DIDX / 8;          // 16-byte chunks per row
+  constexpr int RUNS = BLK * 2 / 1024;   // 1 KB runs per block
+  __shared__ __attribute__((aligned(1024))) uint16_t kbuf[4][BLK];
+  extern __shared__ float pooled_s[];  // [32][kc + 1]
+  const Problem& p = a.p;
+
+  const int s = blockIdx.z;
+  const int row0 = p.cu_q[s];
+  const int nq = p.cu_q[s + 1] - row0;
+  if (nq <= 0) return;
+  const int seq_len = p.seq_lens[s];
+  const int first_pos = seq_len - nq;
+  const int tq = a.tq;
+  const int tile0 = (first_pos / tq) * tq;
+  const int n_tiles = (seq_len - 1 - tile0) / tq + 1;
+  if ((int)blockIdx.x >= n_tiles) return;
+  const int p0 = tile0 + (n_tiles - 1 - (int)blockIdx.x) * tq;
+  const int c_tile = p0 >> 7;
+  const int kb0 = blockIdx.y * a.kc;
+  if (kb0 > c_tile) return;
+  const int nkb = min(a.kc, c_tile + 1 - kb0);
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int half = lane >> 5, l32 = lane & 31;
+  const int ld_s = a.kc + 1;
+  const int hkv_mask = (1 << a.hkv_shift) - 1;
+
+  bf16x8 bq[KS];
+  const int col_pos = p0 + (l32 >> a.hkv_shift);
+  {
+    const bool valid = col_pos >= first_pos && col_pos < seq_len;
+    const int64_t R = ((int64_t)(row0 + col_pos - first_pos) << a.hkv_shift) + (l32 & hkv_mask);
+    const uint16_t* src = a.q_idx + R * DIDX + half * 8;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) bq[ks] = as_bf16x8(valid ? load16(src + ks * 16) : u32x4{0u, 0u, 0u, 0u});
+  }
+
+  const int32_t* table = p.block_table + (int64_t)s * p.max_blocks_per_seq;
+  uint16_t* region = kbuf[wave];
+  auto dma = [&](int kb) {
+    const int phys = table[kb];
+    const uint16_t* src = p.k_idx + (int64_t)((phys >= 0 && phys < p.num_blocks) ? phys : 0) * BLK;
+#pragma unroll
+    for (int run = 0; run < RUNS; ++run) {
+      const int row = run * (1024 / (DIDX * 2)) + lane / CPR;
+      const int chunk = kidx_swizzle<DIDX>(row, lane % CPR);
+      __builtin_amdgcn_global_load_lds(static_cast<const void*>(src + row * DIDX + chunk * 8),
+                                       reinterpret_cast<__attribute__((address_space(3))) void*>(
+                                           reinterpret_cast<uintptr_t>(region + run * 512)),
+                                       16, 0, 0);
+    }
+  };
+  int kb = kb0 + wave;
+  if (kb < kb0 + nkb) dma(kb);
+  for (; kb < kb0 + nkb; kb += 4) {
+    __builtin_amdgcn_s_waitcnt(0);  // this block has landed in the region
+    // Whole block into registers: key tile m, k-step ks -> 16 bytes per lane.
+    bf16x8 ak[4][KS];
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const int r = m * 32 + l32;
+        ak[m][ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(&region[r * DIDX + kidx_swizzle<DIDX>(r, 2 * ks + half) * 8]));
+      }
+    __builtin_amdgcn_s_waitcnt(0);  // reads done before the region is refilled
+    if (kb + 4 < kb0 + nkb) dma(kb + 4);
+    const bool diag = kb == c_tile;  // the query's own block: keys after it are masked
+    const int lim = col_pos - kb * kBlock;
+    float runmax = -__builtin_inff();
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      f32x16 acc = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) acc = mfma32(ak[m][ks], bq[ks], acc);
+      if (diag) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = m * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+          acc[r] = key > lim ? -__builtin_inff() : acc[r];
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) runmax = fmaxf(runmax, acc[r]);
+    }
+    const int phys = table[kb];
+    if (!(phys >= 0 && phys < p.num_blocks)) runmax = __builtin_nanf("");  // table precondition violated
+    const float v = fmaxf(runmax, swap_halves(runmax));
+    if (half == 0) pooled_s[l32 * ld_s + (kb - kb0)] = v;
+  }
+  __syncthreads();
+
+  // Each valid (query, group) row writes its nkb pooled scores contiguously.
+  for (int idx = threadIdx.x; idx < 32 * nkb; idx += blockDim.x) {
+    const int col = idx / nkb;
+    const int j = idx - col * nkb;
+    const int pos = p0 + (col >> a.hkv_shift);
+    if (pos < first_pos || pos >= seq_len) continue;
+    const int64_t R = ((int64_t)(row0 + pos - first_pos) << a.hkv_shift) + (col & hkv_mask);
+    float v = pooled_s[col * ld_s + j];
+    v = (v == 0.0f) ? 0.0f : v;  // -0 and +0 are the same score
+    a.out[R * a.ld + kb0 + j] = v;
+  }
+}
+
 template <int DIDX, int NCT>
 static hipError_t launch_index_t(const IndexArgs& a, dim3 grid, hipStream_t stream) {
   const size_t lds = (size_t)32 * NCT * (a.kc + 1) * sizeof(float);
@@ -434,11 +550,19 @@ hipError_t launch_index_score(const Problem& p, const uint16_t* q_idx, float* sc
     max_blocks = std::max(max_blocks, (L - 1) / kBlock + 1);
     work += (int64_t)tiles * ((t0 / kBlock + (L - 1) / kBlock) / 2 + 1);
   }
-  int kc = (int)std::min<int64_t>(64, std::max<int64_t>(4, (work / 8192 + 3) / 4 * 4));
+  // Decode tiles stream at least 2 blocks per wave so each wave's next block is in flight while it multiplies.
+  int kc = (int)std::min<int64_t>(64, std::max<int64_t>(nct == 1 ? 8 : 4, (work / 8192 + 3) / 4 * 4));
   IndexArgs a{p, q_idx, scores, ld, tq, hkv_shift, kc};
   dim3 grid((unsigned)max_tiles, (unsigned)((max_blocks + kc - 1) / kc), (unsigned)p.num_seqs);
-  if (p.index_dim == 64) return nct == 4 ? launch_index_t<64, 4>(a, grid, stream) : launch_index_t<64, 1>(a, grid, stream);
-  return nct == 4 ? launch_index_t<32, 4>(a, grid, stream) : launch_index_t<32, 1>(a, grid, stream);
+  if (nct == 1) {
+    const size_t lds = (size_t)32 * (a.kc + 1) * sizeof(float);
+    if (p.index_dim == 64)
+      hipLaunchKernelGGL((index_score_stream_kernel<64>), grid, dim3(256), lds, stream, a);
+    else
+      hipLaunchKernelGGL((index_score_stream_kernel<32>), grid, dim3(256), lds, stream, a);
+    return hipGetLastError();
+  }
+  return p.index_dim == 64 ? launch_index_t<64, 4>(a, grid, stream) : launch_index_t<32, 4>(a, grid, stream);
 }
 
 }  // namespace msa
