@@ -151,6 +151,28 @@ def test_graph_replays_equal_eager_step(case):
     compare_rows(runner, 0, runner.inputs.positions(0)[-1:])
 
 
+M3 = WORKLOADS["m3p"]
+
+
+def test_m3_shape_prefill_and_decode():
+    """M3's 64 query / 4 KV heads (G = 16): a ragged prefill and a decode batch."""
+    runner = _run(M3.with_sizes("m3_prefill", [3001, 2300], [3001, 700], permuted_table=True))
+    _all_rows(runner)
+    check_selection_invariants(runner)
+    runner = _run(M3.with_sizes("m3_decode", _RAGGED, [1] * 16, permuted_table=True))
+    assert runner.decode
+    _all_rows(runner)
+    check_selection_invariants(runner)
+
+
+def test_m3_decode_large_batch():
+    """32 sequences x 4 groups: 128 (sequence, group) pairs at G = 16."""
+    lens = [_RAGGED[i % 16] + 11 * (i // 16) for i in range(32)]
+    runner = _run(M3.with_sizes("m3_decode32", lens, [1] * 32, permuted_table=True))
+    _all_rows(runner)
+    check_selection_invariants(runner)
+
+
 def test_decode_equals_prefill_last_row():
     """A decode step over N cached tokens computes the prefill's last row."""
     import dataclasses
@@ -279,6 +301,17 @@ def test_c3_full_size_sampled_rows():
     assert len(runner.chunks) == 8
     check_selection_invariants(runner)
     compare_rows(runner, 0, _sample_positions(131072, 0, 256, 3))
+
+
+def test_m3p_full_size_sampled_rows():
+    runner = _run(WORKLOADS["m3p"], chunk_rows=BENCH_CHUNK_ROWS)
+    check_selection_invariants(runner)
+    compare_rows(runner, 0, _sample_positions(131072, 0, 64, 5))
+
+
+def test_m3d_full_size_decode_all_rows():
+    runner = _run(WORKLOADS["m3d"])
+    _all_rows(runner)
 
 
 def test_c4_decode_1m_all_rows():
