@@ -9,7 +9,11 @@ per step of the method); this module only compiles it, loads it with ctypes
 and marshals numpy arrays.  The steps follow "MiniMax 模型迭代与竞品分析：从
 Text-01、M1、M2 到 M3", §2: index scoring against a shared K_idx, max-pooling
 into 128-token blocks, top-16 selection with the local block forced in, and
-exact softmax attention over the selected tokens.
+exact softmax attention over the selected tokens.  The same section's
+training and evaluation quantities are here too: the dense attention mass per
+block (the group-averaged importance P) and a selection's coverage of it,
+recall of its largest blocks and D_KL(P || Q) against the indexer's
+softmax Q over the pooled scores.
 
 All tensors are numpy arrays in plain logical order for ONE sequence:
 bf16 inputs are passed as ``uint16`` bit patterns, keys are indexed by token
@@ -55,7 +59,10 @@ def _load():
         lib.msa_oracle_block_scores.argtypes = [i64, p, p, i32, i32, p, i64, i32, p, i64]
         lib.msa_oracle_select.argtypes = [i64, p, p, i32, i64, i32, i32, p]
         lib.msa_oracle_attend.argtypes = [i64, p, p, i32, i32, i32, p, p, i64, p, i32, i32, dbl, p]
-        for f in (lib.msa_oracle_block_scores, lib.msa_oracle_select, lib.msa_oracle_attend):
+        lib.msa_oracle_block_mass.argtypes = [i64, p, p, i32, i32, i32, p, i64, i32, dbl, p, i64]
+        lib.msa_oracle_selection_quality.argtypes = [i64, p, p, p, p, i32, i64, i32, i32, p, p, p]
+        for f in (lib.msa_oracle_block_scores, lib.msa_oracle_select, lib.msa_oracle_attend,
+                  lib.msa_oracle_block_mass, lib.msa_oracle_selection_quality):
             f.restype = ctypes.c_int
         lib.msa_oracle_num_threads.restype = ctypes.c_int
         _lib = lib
@@ -142,3 +149,45 @@ def msa(pos, q_idx, k_idx, q, k, v, block_size: int = 128, top_k: int = 16, scal
     sel = select(pos, pooled, block_size, top_k)
     out = attend(pos, q, k, v, sel, block_size, scale)
     return pooled, sel, out
+
+
+def block_mass(pos, q, k, block_size: int = 128, scale: float | None = None, ld: int | None = None) -> np.ndarray:
+    """Step 5: float64 [n, G, ld] dense attention mass per block, averaged over
+    each group's heads (0 for blocks after the row's own block).
+
+    q : uint16 [n, Hq, D]; k : uint16 [L, G, D].  scale defaults to 1/sqrt(D).
+    """
+    pos = np.ascontiguousarray(pos, dtype=np.int64)
+    q, k = _u16(q), _u16(k)
+    n, hq, d = q.shape
+    groups = k.shape[1]
+    if scale is None:
+        scale = 1.0 / float(np.sqrt(d))
+    if ld is None:
+        ld = int(pos.max()) // block_size + 1 if n else 1
+    out = np.empty((n, groups, ld), dtype=np.float64)
+    rc = _load().msa_oracle_block_mass(n, _ptr(pos), _ptr(q), hq, groups, d, _ptr(k), k.shape[0], block_size,
+                                       float(scale), _ptr(out), ld)
+    _check(rc, "block_mass")
+    return out
+
+
+def selection_quality(pos, mass, pooled, sel, block_size: int = 128):
+    """Step 6: (coverage, recall, kl), each float64 [n, G].
+
+    mass : float64 [n, G, ld] (converted if given as float32); pooled : float32
+    [n, G, ld] index scores; sel : int32 [n, G, top_k].
+    """
+    pos = np.ascontiguousarray(pos, dtype=np.int64)
+    mass = np.ascontiguousarray(mass, dtype=np.float64)
+    pooled = np.ascontiguousarray(pooled, dtype=np.float32)
+    sel = np.ascontiguousarray(sel, dtype=np.int32)
+    n, groups, ld = mass.shape
+    if pooled.shape != mass.shape:
+        raise ValueError("mass and pooled scores must have the same shape")
+    top_k = sel.shape[2]
+    cov, rec, kl = (np.empty((n, groups), dtype=np.float64) for _ in range(3))
+    rc = _load().msa_oracle_selection_quality(n, _ptr(pos), _ptr(mass), _ptr(pooled), _ptr(sel), groups, ld,
+                                              block_size, top_k, _ptr(cov), _ptr(rec), _ptr(kl))
+    _check(rc, "selection_quality")
+    return cov, rec, kl

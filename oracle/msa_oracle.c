@@ -38,6 +38,20 @@
  * Every function processes a list of query rows of ONE sequence whose keys
  * are given in plain logical order (token i at index i), independently of any
  * cache layout.  Rows are independent; OpenMP spreads them over host cores.
+ *
+ * Selection quality (same page, §2: the indexer is trained by aligning its
+ * distribution Q with the Main Branch's group-averaged importance P by
+ * D_KL(P||Q), and MSA is judged by selection recall and by how much of the
+ * attention mass the chosen blocks cover):
+ *     5. mass       P_b = (1/G) sum over the group's heads of the DENSE causal
+ *                   softmax probabilities of the tokens of block b;
+ *     6. quality    coverage = sum of P over the selected blocks; recall = the
+ *                   share of the min(top_k, c+1) largest-P blocks (ties to the
+ *                   lower index) that were selected; D_KL(P||Q) with Q the
+ *                   softmax over the pooled index scores of blocks 0..c.
+ * Readings (listed in the design notes): P and Q range over every causal
+ * block including the local one; Q uses the raw pooled scores (no
+ * temperature); natural logarithms.
  */
 #include <math.h>
 #include <stdint.h>
@@ -253,6 +267,135 @@ int msa_oracle_attend(int64_t n_rows, const int64_t* pos, const uint16_t* q, int
     free(z);
     free(idx);
     free(acc);
+  }
+  return status;
+}
+
+/*
+ * Step 5: dense attention mass per block.  For each row (position t) and
+ * group g, every head h of the group gets the softmax of z_i = scale * q_h.k_i
+ * over ALL causal tokens i <= t (not only the selected ones); the mass of
+ * block b is the sum of those probabilities over the tokens of b, averaged
+ * over the G heads of the group.  out: double [n_rows][n_groups][ld], blocks
+ * after the row's own block are 0.
+ */
+int msa_oracle_block_mass(int64_t n_rows, const int64_t* pos, const uint16_t* q, int n_q_heads, int n_groups,
+                          int head_dim, const uint16_t* k, int64_t n_keys, int block_size, double scale,
+                          double* out, int64_t ld) {
+  if (n_rows < 0 || n_groups <= 0 || n_q_heads <= 0 || n_q_heads % n_groups != 0 || head_dim <= 0 ||
+      block_size <= 0 || ld <= 0 || !pos || !out)
+    return ORACLE_BAD_ARG;
+  if (n_rows > 0 && (!q || !k)) return ORACLE_BAD_ARG;
+  for (int64_t r = 0; r < n_rows; ++r)
+    if (pos[r] < 0 || pos[r] >= n_keys || pos[r] / block_size >= ld) return ORACLE_BAD_ARG;
+  const int group_size = n_q_heads / n_groups;
+  int status = ORACLE_OK;
+#pragma omp parallel
+  {
+    double* z = (double*)malloc(sizeof(double) * (size_t)n_keys);
+    if (!z) {
+#pragma omp atomic write
+      status = ORACLE_NO_MEMORY;
+    }
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t r = 0; r < n_rows; ++r) {
+      if (!z) continue;
+      const int64_t t = pos[r];
+      for (int g = 0; g < n_groups; ++g) {
+        double* mass = out + (r * n_groups + g) * ld;
+        for (int64_t b = 0; b < ld; ++b) mass[b] = 0.0;
+        for (int j = 0; j < group_size; ++j) {
+          const int h = g * group_size + j;
+          const uint16_t* qh = q + (r * n_q_heads + h) * (int64_t)head_dim;
+          double zmax = -INFINITY;
+          for (int64_t i = 0; i < t + 1; ++i) { /* every causal token */
+            const uint16_t* key = k + (i * n_groups + g) * (int64_t)head_dim;
+            double dot = 0.0;
+            for (int d = 0; d < head_dim; ++d) dot += bf16_to_double(qh[d]) * bf16_to_double(key[d]);
+            z[i] = scale * dot;
+            if (z[i] > zmax) zmax = z[i];
+          }
+          double denom = 0.0;
+          for (int64_t i = 0; i < t + 1; ++i) { /* softmax denominator */
+            z[i] = exp(z[i] - zmax);
+            denom += z[i];
+          }
+          for (int64_t i = 0; i < t + 1; ++i) mass[i / block_size] += z[i] / denom / group_size;
+        }
+      }
+    }
+    free(z);
+  }
+  return status;
+}
+
+/*
+ * Step 6: quality of one selection against the dense mass P.
+ *   coverage = sum of P_b over the selected blocks (ids >= 0);
+ *   recall   = |selected AND top| / |top|, top = the K = min(top_k, c+1)
+ *              blocks of largest P (repeated argmax, strictly greater wins, so
+ *              equal masses go to the lower index);
+ *   kl       = sum over b <= c with P_b > 0 of P_b * (ln P_b - ln Q_b), where
+ *              Q = softmax over b <= c of the pooled index scores.
+ * mass is double [n_rows][n_groups][ld]; pooled float [n_rows][n_groups][ld];
+ * sel int32 [n_rows][n_groups][top_k].  Outputs double [n_rows][n_groups].
+ */
+int msa_oracle_selection_quality(int64_t n_rows, const int64_t* pos, const double* mass, const float* pooled,
+                                 const int32_t* sel, int n_groups, int64_t ld, int block_size, int top_k,
+                                 double* coverage, double* recall, double* kl) {
+  if (n_rows < 0 || n_groups <= 0 || ld <= 0 || block_size <= 0 || top_k <= 0 || !pos || !coverage || !recall || !kl)
+    return ORACLE_BAD_ARG;
+  if (n_rows > 0 && (!mass || !pooled || !sel)) return ORACLE_BAD_ARG;
+  for (int64_t r = 0; r < n_rows; ++r)
+    if (pos[r] < 0 || pos[r] / block_size >= ld) return ORACLE_BAD_ARG;
+  int status = ORACLE_OK;
+#pragma omp parallel
+  {
+    char* taken = (char*)malloc((size_t)ld);
+    if (!taken) {
+#pragma omp atomic write
+      status = ORACLE_NO_MEMORY;
+    }
+#pragma omp for schedule(dynamic, 4)
+    for (int64_t r = 0; r < n_rows; ++r) {
+      if (!taken) continue;
+      const int64_t c = pos[r] / block_size;
+      for (int g = 0; g < n_groups; ++g) {
+        const int64_t row = r * n_groups + g;
+        const double* P = mass + row * ld;
+        const float* S = pooled + row * ld;
+        const int32_t* s = sel + row * (int64_t)top_k;
+        double cov = 0.0;
+        for (int j = 0; j < top_k; ++j)
+          if (s[j] >= 0) cov += P[s[j]];
+        /* The K blocks of largest mass. */
+        const int64_t K = c + 1 < top_k ? c + 1 : top_k;
+        for (int64_t b = 0; b <= c; ++b) taken[b] = 0;
+        for (int64_t round = 0; round < K; ++round) {
+          int64_t best = -1;
+          for (int64_t b = 0; b <= c; ++b)
+            if (!taken[b] && (best < 0 || P[b] > P[best])) best = b;
+          taken[best] = 1;
+        }
+        int64_t hits = 0;
+        for (int j = 0; j < top_k; ++j)
+          if (s[j] >= 0 && s[j] <= c && taken[s[j]]) ++hits;
+        /* ln Q_b = S_b - log sum_b' exp(S_b'). */
+        double smax = -INFINITY;
+        for (int64_t b = 0; b <= c; ++b)
+          if (S[b] > smax) smax = S[b];
+        double sum = 0.0;
+        for (int64_t b = 0; b <= c; ++b) sum += exp((double)S[b] - smax);
+        const double lse = smax + log(sum);
+        double d = 0.0;
+        for (int64_t b = 0; b <= c; ++b)
+          if (P[b] > 0.0) d += P[b] * (log(P[b]) - ((double)S[b] - lse));
+        coverage[row] = cov;
+        recall[row] = (double)hits / (double)K;
+        kl[row] = d;
+      }
+    }
+    free(taken);
   }
   return status;
 }

@@ -8,6 +8,7 @@ import subprocess
 import pytest
 
 from tests import test_oracle_pins as pins
+from tests import test_oracle_quality as quality
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SRC = os.path.join(ROOT, "oracle", "msa_oracle.c")
@@ -32,6 +33,18 @@ MUTANTS = [
      "const uint16_t* vi = v + ((idx[m] > 0 ? idx[m] - 1 : 0) * n_groups + g) * (int64_t)head_dim;"),
     ("key dimension transposed", "const uint16_t* ki = k + (i * n_groups + g) * (int64_t)head_dim;",
      "const uint16_t* ki = k + (g * n_keys + i) * (int64_t)head_dim;"),
+    ("mass scores skip token t", "for (int64_t i = 0; i < t + 1; ++i) { /* every causal token */",
+     "for (int64_t i = 0; i < t; ++i) { /* every causal token */"),
+    ("mass not averaged over the group", "mass[i / block_size] += z[i] / denom / group_size;",
+     "mass[i / block_size] += z[i] / denom;"),
+    ("mass credited to the previous block", "mass[i / block_size] += z[i] / denom / group_size;",
+     "mass[i / block_size > 0 ? i / block_size - 1 : 0] += z[i] / denom / group_size;"),
+    ("recall ties go to the higher index", "if (!taken[b] && (best < 0 || P[b] > P[best])) best = b;",
+     "if (!taken[b] && (best < 0 || P[b] >= P[best])) best = b;"),
+    ("KL with the logarithm ratio flipped", "if (P[b] > 0.0) d += P[b] * (log(P[b]) - ((double)S[b] - lse));",
+     "if (P[b] > 0.0) d += P[b] * (((double)S[b] - lse) - log(P[b]));"),
+    ("coverage misses the last selected block", "for (int j = 0; j < top_k; ++j)\n          if (s[j] >= 0) cov += P[s[j]];",
+     "for (int j = 0; j + 1 < top_k; ++j)\n          if (s[j] >= 0) cov += P[s[j]];"),
 ]
 
 PINS = [
@@ -44,6 +57,12 @@ PINS = [
     lambda o: pins.test_short_context_is_dense_attention(o, 4, 3, 12, 4, 1, 8),
     lambda o: pins.test_short_context_is_dense_attention(o, 128, 16, 300, 4, 2, 16),
     pins.test_sparse_rows_equal_dense_attention_over_selected_tokens,
+    lambda o: quality.test_block_mass_is_attention_with_block_indicator_values(o, 0, 300, 16, 4, 2, 32),
+    quality.test_block_mass_sums_to_one_and_stops_at_the_local_block,
+    quality.test_coverage_and_recall_against_sorting,
+    quality.test_all_blocks_selected_covers_everything,
+    quality.test_kl_hand_example,
+    quality.test_kl_vanishes_when_the_indexer_matches_and_is_nonnegative,
 ]
 
 
