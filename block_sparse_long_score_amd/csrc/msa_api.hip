@@ -236,6 +236,48 @@ msa_status msa_block_topk(const msa_dims* dims, const msa_batch* batch, const fl
                     "msa_block_topk launch");
 }
 
+msa_status msa_block_attn_mass(const msa_dims* dims, const msa_cache* cache, const msa_batch* batch, const void* q,
+                               const int32_t* rows, int32_t n_rows, float* mass, int64_t ld, void* stream) {
+  MSA_TRY(check_dims(dims));
+  MSA_TRY(check_cache(cache));
+  MSA_TRY(check_batch(dims, batch, cache));
+  MSA_TRY(check_ptr(q, "q"));
+  MSA_TRY(check_ptr(rows, "rows"));
+  MSA_TRY(check_ptr(mass, "mass"));
+  if (n_rows < 0) return fail(MSA_ERR_BAD_SHAPE, "n_rows=%d is negative", n_rows);
+  if ((int64_t)n_rows * dims->num_kv_heads > INT32_MAX)
+    return fail(MSA_ERR_BAD_SHAPE, "n_rows * num_kv_heads exceeds 2^31 - 1");
+  const int64_t need = max_query_blocks(batch);
+  if (ld < need) return fail(MSA_ERR_BAD_SHAPE, "ld=%lld is less than the %lld blocks of the longest sequence",
+                             (long long)ld, (long long)need);
+  const msa::Problem p = make_problem(dims, batch, cache);
+  return hip_status(msa::launch_block_attn_mass(p, static_cast<const uint16_t*>(q), rows, n_rows, mass, ld,
+                                                static_cast<hipStream_t>(stream)),
+                    "msa_block_attn_mass launch");
+}
+
+msa_status msa_selection_quality(const msa_dims* dims, const msa_batch* batch, const int32_t* rows, int32_t n_rows,
+                                 const float* mass, const float* block_scores, const int32_t* sel, int64_t ld,
+                                 float* quality, void* stream) {
+  MSA_TRY(check_dims(dims));
+  MSA_TRY(check_batch(dims, batch, nullptr));
+  MSA_TRY(check_ptr(rows, "rows"));
+  MSA_TRY(check_ptr(mass, "mass"));
+  MSA_TRY(check_ptr(block_scores, "block_scores"));
+  MSA_TRY(check_ptr(sel, "sel"));
+  MSA_TRY(check_ptr(quality, "quality"));
+  if (n_rows < 0) return fail(MSA_ERR_BAD_SHAPE, "n_rows=%d is negative", n_rows);
+  if ((int64_t)n_rows * dims->num_kv_heads > INT32_MAX)
+    return fail(MSA_ERR_BAD_SHAPE, "n_rows * num_kv_heads exceeds 2^31 - 1");
+  const int64_t need = max_query_blocks(batch);
+  if (ld < need) return fail(MSA_ERR_BAD_SHAPE, "ld=%lld is less than the %lld blocks of the longest sequence",
+                             (long long)ld, (long long)need);
+  const msa::Problem p = make_problem(dims, batch, nullptr);
+  return hip_status(msa::launch_selection_quality(p, rows, n_rows, mass, block_scores, sel, ld, quality,
+                                                  static_cast<hipStream_t>(stream)),
+                    "msa_selection_quality launch");
+}
+
 size_t msa_workspace_size(const msa_dims* dims, const msa_cache* cache, const msa_batch* batch, int32_t call) {
   if (check_dims(dims) != MSA_OK || check_cache(cache) != MSA_OK || check_batch(dims, batch, cache) != MSA_OK)
     return 0;

@@ -36,6 +36,12 @@ hipError_t launch_index_score(const Problem& p, const uint16_t* q_idx, float* sc
                               const int32_t* seq_lens_host, const int32_t* cu_q_host, hipStream_t stream);
 
 // max_blocks: blocks of the longest sequence (host-side), picks the kernel.
+// Selection quality against dense attention (sampled rows).
+hipError_t launch_block_attn_mass(const Problem& p, const uint16_t* q, const int32_t* rows, int32_t n_rows,
+                                  float* mass, int64_t ld, hipStream_t stream);
+hipError_t launch_selection_quality(const Problem& p, const int32_t* rows, int32_t n_rows, const float* mass,
+                                    const float* scores, const int32_t* sel, int64_t ld, float* quality,
+                                    hipStream_t stream);
 hipError_t launch_block_topk(const Problem& p, const float* scores, int64_t ld, int32_t* sel, int64_t max_blocks,
                              hipStream_t stream);
 

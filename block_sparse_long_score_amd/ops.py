@@ -169,3 +169,24 @@ def msa_sparse_attn_prefill(dims: Dims, cache: Cache, batch: Batch, q, sel, out,
 
 def msa_sparse_attn_decode(dims: Dims, cache: Cache, batch: Batch, q, sel, out, workspace, stream=None):
     _attn("msa_sparse_attn_decode", dims, cache, batch, q, sel, out, workspace, stream)
+
+
+def msa_block_attn_mass(dims: Dims, cache: Cache, batch: Batch, q, rows, mass, stream=None):
+    """mass: float32 [n_rows, Hkv, ld]; rows: int32 [n_rows] query-row indices of the batch."""
+    L = _lib.load()
+    d, c, b = dims.c(), cache.c(), batch.c()
+    _check(L.msa_block_attn_mass(ctypes.byref(d), ctypes.byref(c), ctypes.byref(b), _ptr(q, "q", torch.bfloat16),
+                                 _ptr(rows, "rows", torch.int32), rows.numel(), _ptr(mass, "mass", torch.float32),
+                                 mass.shape[-1], _stream(stream)))
+
+
+def msa_selection_quality(dims: Dims, batch: Batch, rows, mass, block_scores, sel, quality, stream=None):
+    """quality: float32 [n_rows, Hkv, 3] = (coverage, recall, kl)."""
+    L = _lib.load()
+    d, b = dims.c(), batch.c()
+    if block_scores.shape[-1] != mass.shape[-1]:
+        raise ValueError("mass and block_scores must share the row pitch ld")
+    _check(L.msa_selection_quality(ctypes.byref(d), ctypes.byref(b), _ptr(rows, "rows", torch.int32), rows.numel(),
+                                   _ptr(mass, "mass", torch.float32),
+                                   _ptr(block_scores, "block_scores", torch.float32), _ptr(sel, "sel", torch.int32),
+                                   mass.shape[-1], _ptr(quality, "quality", torch.float32), _stream(stream)))

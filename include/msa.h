@@ -210,6 +210,51 @@ msa_status msa_sparse_attn_decode(const msa_dims* dims, const msa_cache* cache,
                                   const msa_batch* batch, const void* q, const int32_t* sel,
                                   void* out, void* workspace, size_t ws_bytes, void* stream);
 
+/* ------------------------------------------------------------------------- *
+ * msa_block_attn_mass — dense attention mass per block for a sample of query
+ * rows ([M3-evo] §2, the paragraph on training the indexer: the Main Branch's
+ * group-averaged importance distribution P over the candidate blocks).  For
+ * sampled row k (query row r = rows[k] at position t, local block c = t/128)
+ * and group g:
+ *     P[k][g][b] = (1/G) * sum over the group's heads h of
+ *                  sum over tokens i of block b, i <= t, of softmax_i(z_h),
+ *     z_h,i = softmax_scale * (q[r][h] . k[i][g]) over ALL causal tokens i,
+ * for b = 0..c (entries b > c are not written).  fp32 arithmetic.
+ *   q    : bf16 [total_q][Hq][D] (the Main Branch queries)
+ *   rows : int32 [n_rows], query-row indices into the batch; a row outside
+ *          [0, total_q) is skipped (its outputs are not written).
+ *   mass : fp32 [n_rows][Hkv][ld], ld >= the blocks of the longest sequence.
+ * Reads K of every causal block through the block table (twice: once for
+ * the softmax statistics, once for the masses).  Meant for sampled rows: the
+ * work is that of dense attention without the values.
+ * Errors: NULL_POINTER, BAD_SHAPE, UNSUPPORTED, MISALIGNED, CAPACITY, HIP.
+ * ------------------------------------------------------------------------- */
+msa_status msa_block_attn_mass(const msa_dims* dims, const msa_cache* cache, const msa_batch* batch,
+                               const void* q, const int32_t* rows, int32_t n_rows, float* mass, int64_t ld,
+                               void* stream);
+
+/* ------------------------------------------------------------------------- *
+ * msa_selection_quality — how well the selections of the sampled rows match
+ * the dense attention ([M3-evo] §2: MSA is judged by selection recall and by
+ * the share of attention score the chosen blocks cover; the indexer is
+ * trained with D_KL(P || Q)).  For sampled row k and group g, with P the
+ * mass from msa_block_attn_mass and c = t/128:
+ *   coverage = sum of P[b] over the selected blocks;
+ *   recall   = |selected AND top| / |top|, top = the min(top_k, c+1) blocks
+ *              of largest P (equal masses go to the lower block index);
+ *   kl       = sum over b <= c with P[b] > 0 of P[b] (ln P[b] - ln Q[b]),
+ *              Q = softmax over b <= c of the pooled index scores.
+ *   rows         : int32 [n_rows] as for msa_block_attn_mass
+ *   mass         : fp32 [n_rows][Hkv][ld]
+ *   block_scores : fp32 [total_q][Hkv][ld] from msa_index_score
+ *   sel          : int32 [total_q][Hkv][top_k] from msa_block_topk
+ *   quality      : fp32 [n_rows][Hkv][3] = (coverage, recall, kl)
+ * Errors: NULL_POINTER, BAD_SHAPE, UNSUPPORTED, MISALIGNED, HIP.
+ * ------------------------------------------------------------------------- */
+msa_status msa_selection_quality(const msa_dims* dims, const msa_batch* batch, const int32_t* rows,
+                                 int32_t n_rows, const float* mass, const float* block_scores,
+                                 const int32_t* sel, int64_t ld, float* quality, void* stream);
+
 /* Bytes of workspace `call` needs for this problem; 0 if the arguments are
  * invalid (the failing check is reported by msa_last_error()). */
 size_t msa_workspace_size(const msa_dims* dims, const msa_cache* cache, const msa_batch* batch,

@@ -138,3 +138,20 @@ def test_workspace_grows_with_queries(lib):
     assert sizes[0] < sizes[1] < sizes[2]
     # fp16 partials of up to 15 non-local blocks per (row, head) dominate
     assert sizes[2] >= 65536 * 48 * 15 * 128 * 2
+
+
+def test_quality_entry_points_validate_on_the_host(lib):
+    d, c = _dims(), _cache()
+    b = _Batch([1024, 900], [1, 1])
+    dp, cp, bp = ctypes.byref(d), ctypes.byref(c), ctypes.byref(b.c)
+    # block mass: null / misaligned pointers, negative counts, short rows
+    assert lib.msa_block_attn_mass(dp, cp, bp, None, FAKE, 4, FAKE, 16, None) == NULLP
+    assert lib.msa_block_attn_mass(dp, cp, bp, FAKE, FAKE + 4, 4, FAKE, 16, None) == MISAL
+    assert lib.msa_block_attn_mass(dp, cp, bp, FAKE, FAKE, -1, FAKE, 16, None) == SHAPE
+    assert lib.msa_block_attn_mass(dp, cp, bp, FAKE, FAKE, 4, FAKE, 7, None) == SHAPE  # 8 blocks needed
+    assert lib.msa_block_attn_mass(dp, cp, bp, FAKE, FAKE, 0, FAKE, 16, None) == OK  # nothing to do
+    # selection quality
+    assert lib.msa_selection_quality(dp, bp, FAKE, 4, FAKE, FAKE, None, 16, FAKE, None) == NULLP
+    assert lib.msa_selection_quality(dp, bp, FAKE, -2, FAKE, FAKE, FAKE, 16, FAKE, None) == SHAPE
+    assert lib.msa_selection_quality(dp, bp, FAKE, 4, FAKE, FAKE, FAKE, 3, FAKE, None) == SHAPE
+    assert lib.msa_selection_quality(dp, bp, FAKE, 0, FAKE, FAKE, FAKE, 16, FAKE, None) == OK

@@ -1,0 +1,154 @@
+"""Parity of the selection-quality calls (msa_block_attn_mass,
+msa_selection_quality) with the CPU oracle.
+
+- Block mass: fp32 on the GPU against the oracle's double-precision dense
+  softmax (max |diff| <= 1e-6 + 1e-4 |P|).
+- Quality: fed the oracle's own mass (rounded to float), pooled scores and
+  selections, the GPU must give the oracle's recall exactly (both decide from
+  the same float values) and its coverage and KL within float rounding.
+- End to end on the GPU's own mass, scores and selections: coverage and KL
+  close to the oracle's; recall equal except where two masses sit within
+  float rounding of each other.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from block_sparse_long_score_amd import ops
+from block_sparse_long_score_amd.inputs import WORKLOADS, bf16_bits, make_inputs
+from block_sparse_long_score_amd.pipeline import MsaRunner
+from tests.gpu_helpers import oracle_rows, seq_rows
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def _announce(msg):
+    print(f"[gpu-case] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+CASES = {
+    "m2_prefill": (WORKLOADS["c1"].with_sizes("q_m2", [3000], [3000]), [0, 1, 127, 128, 500, 2047, 2048, 2999]),
+    "c0_shape": (WORKLOADS["c0"], [0, 64, 2047, 2048, 3000, 4095]),
+    "decode_batch": (WORKLOADS["c1"].with_sizes("q_dec", [1, 129, 2049, 5000, 9999], [1] * 5, permuted_table=True),
+                     None),
+    "m3_shape": (WORKLOADS["m3p"].with_sizes("q_m3", [2600], [2600]), [5, 1000, 2047, 2048, 2599]),
+}
+
+
+def _sample(runner, positions):
+    """(sequence, positions, batch rows) of the rows to evaluate."""
+    w = runner.inputs.workload
+    out = []
+    for s in range(w.num_seqs):
+        pos = runner.inputs.positions(s) if positions is None else np.asarray(positions, np.int64)
+        out.append((s, pos, seq_rows(runner.inputs, s, pos)))
+    return out
+
+
+def _oracle_mass(inp, s, pos, ld):
+    w = inp.workload
+    off = int(inp.tok_off[s])
+    length = int(pos.max()) + 1
+    rows = torch.from_numpy(seq_rows(inp, s, pos)).to(inp.q.device)
+    q = bf16_bits(inp.q.index_select(0, rows))
+    k = bf16_bits(inp.k[off:off + length])
+    return oracle.block_mass(pos, q, k, w.block_size, ld=ld)
+
+
+def _run(name):
+    w, positions = CASES[name]
+    _announce(f"{name}: seq_lens={w.seq_lens} Hq={w.num_q_heads} Hkv={w.num_kv_heads} D={w.head_dim}")
+    runner = MsaRunner(make_inputs(w, "cuda"))
+    runner.step()
+    torch.cuda.synchronize()
+    return runner, _sample(runner, positions)
+
+
+def _pad(pooled, ld):
+    """Oracle pooled scores (-inf after each row's block) as float32 rows of pitch ld, zeros past the end."""
+    out = np.zeros(pooled.shape[:-1] + (ld,), np.float32)
+    out[..., : pooled.shape[-1]] = np.nan_to_num(pooled, neginf=0.0)
+    return out
+
+
+def _gpu_mass(runner, rows):
+    dev = runner.inputs.q.device
+    rows_t = torch.from_numpy(np.asarray(rows, np.int32)).to(dev)
+    mass = torch.full((len(rows), runner.dims.num_kv_heads, runner.ld), float("nan"), dtype=torch.float32, device=dev)
+    ops.msa_block_attn_mass(runner.dims, runner.cache, runner.batch, runner.inputs.q, rows_t, mass)
+    torch.cuda.synchronize()
+    return rows_t, mass
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_block_mass_matches_oracle(name):
+    runner, sample = _run(name)
+    for s, pos, rows in sample:
+        _, mass = _gpu_mass(runner, rows)
+        want = _oracle_mass(runner.inputs, s, pos, runner.ld)
+        got = mass.cpu().numpy().astype(np.float64)
+        for i, t in enumerate(pos):
+            c = int(t) // 128
+            err = np.abs(got[i, :, : c + 1] - want[i, :, : c + 1])
+            assert np.all(err <= 1e-6 + 1e-4 * want[i, :, : c + 1]), \
+                f"{name}: mass of position {t} off by {err.max():.3g}"
+            assert np.all(np.isnan(got[i, :, c + 1:])), "blocks after the local block must not be written"
+            np.testing.assert_allclose(got[i, :, : c + 1].sum(axis=-1), 1.0, atol=1e-4)
+
+
+@pytest.mark.parametrize("name", ["m2_prefill", "decode_batch", "m3_shape"])
+def test_selection_quality_on_oracle_inputs(name):
+    """Same float inputs on both sides: recall bit-exact, coverage and KL close."""
+    runner, sample = _run(name)
+    inp, dev = runner.inputs, runner.inputs.q.device
+    hkv = runner.dims.num_kv_heads
+    for s, pos, rows in sample:
+        pooled, sel, _ = oracle_rows(inp, s, pos, attend=False)
+        pooled = _pad(pooled, runner.ld)
+        mass = _oracle_mass(inp, s, pos, runner.ld).astype(np.float32)
+        scores_full = torch.zeros_like(runner.scores)
+        sel_full = torch.full_like(runner.sel, -1)
+        rows_t = torch.from_numpy(np.asarray(rows, np.int64)).to(dev)
+        scores_full[rows_t] = torch.from_numpy(pooled).to(dev)
+        sel_full[rows_t] = torch.from_numpy(sel).to(dev)
+        quality = torch.empty((len(rows), hkv, 3), dtype=torch.float32, device=dev)
+        ops.msa_selection_quality(runner.dims, runner.batch, rows_t.int(), torch.from_numpy(mass).to(dev),
+                                  scores_full, sel_full, quality)
+        torch.cuda.synchronize()
+        q = quality.cpu().numpy().astype(np.float64)
+        cov, rec, kl = oracle.selection_quality(pos, mass.astype(np.float64), pooled, sel)
+        np.testing.assert_array_equal(q[..., 1], rec, err_msg=f"{name}: recall")
+        np.testing.assert_allclose(q[..., 0], cov, rtol=0, atol=2e-6, err_msg=f"{name}: coverage")
+        np.testing.assert_allclose(q[..., 2], kl, rtol=1e-4, atol=1e-4, err_msg=f"{name}: KL")
+
+
+@pytest.mark.parametrize("name", ["m2_prefill", "decode_batch"])
+def test_selection_quality_end_to_end(name):
+    """The GPU's own mass, pooled scores and selections."""
+    runner, sample = _run(name)
+    inp, dev = runner.inputs, runner.inputs.q.device
+    hkv = runner.dims.num_kv_heads
+    for s, pos, rows in sample:
+        rows_t, mass = _gpu_mass(runner, rows)
+        quality = torch.empty((len(rows), hkv, 3), dtype=torch.float32, device=dev)
+        ops.msa_selection_quality(runner.dims, runner.batch, rows_t, mass, runner.scores, runner.sel, quality)
+        torch.cuda.synchronize()
+        q = quality.cpu().numpy().astype(np.float64)
+        pooled, sel, _ = oracle_rows(inp, s, pos, attend=False)
+        omass = _oracle_mass(inp, s, pos, runner.ld)
+        cov, rec, kl = oracle.selection_quality(pos, omass, _pad(pooled, runner.ld), sel)
+        np.testing.assert_allclose(q[..., 0], cov, rtol=0, atol=1e-4, err_msg=f"{name}: coverage")
+        np.testing.assert_allclose(q[..., 2], kl, rtol=1e-3, atol=1e-3, err_msg=f"{name}: KL")
+        assert np.all(np.abs(q[..., 1] - rec) <= 1.0 / 16 + 1e-6)
+        assert np.mean(q[..., 1] == rec) >= 0.95
+        assert np.all((q[..., 0] >= -1e-6) & (q[..., 0] <= 1 + 1e-5))
