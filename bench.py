@@ -88,6 +88,40 @@ def recorded_traffic(workload: str, stage: str, launches_per_step: float):
             "source": rec["profile"]}
 
 
+def selection_quality(runner, n_rows: int):
+    """Coverage, recall and D_KL(P||Q) of the step's selections on evenly spaced
+    query rows, against the dense attention mass P (msa_block_attn_mass), with
+    the mass kernel timed by events.  After the timed region; not part of a step."""
+    import torch
+    from block_sparse_long_score_amd import ops
+    w, dev = runner.inputs.workload, runner.inputs.q.device
+    n = min(n_rows, w.total_q)
+    rows = torch.from_numpy(np.unique(np.linspace(0, w.total_q - 1, n).astype(np.int32))).to(dev)
+    mass = torch.empty((rows.numel(), w.num_kv_heads, runner.ld), dtype=torch.float32, device=dev)
+    qual = torch.empty((rows.numel(), w.num_kv_heads, 3), dtype=torch.float32, device=dev)
+    runner.step()  # the selections and scores of one step
+    ops.msa_block_attn_mass(runner.dims, runner.cache, runner.batch, runner.inputs.q, rows, mass)  # warm-up
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    ops.msa_block_attn_mass(runner.dims, runner.cache, runner.batch, runner.inputs.q, rows, mass)
+    e1.record()
+    ops.msa_selection_quality(runner.dims, runner.batch, rows, mass, runner.scores, runner.sel, qual)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1)
+    # positions of the sampled rows -> keys each (row, group) scans: t + 1 (read twice by the two passes)
+    cu = np.asarray(runner.inputs.cu_q)
+    r = rows.cpu().numpy()
+    seq = np.searchsorted(cu, r, side="right") - 1
+    pos = np.asarray(w.seq_lens)[seq] - (cu[seq + 1] - r)
+    k_bytes = float(np.sum(pos + 1)) * w.num_kv_heads * w.head_dim * 2
+    q = qual.cpu().numpy().astype(np.float64)
+    blocks = pos // w.block_size + 1
+    return {"rows": int(rows.numel()), "coverage_mean": float(q[..., 0].mean()), "recall_mean": float(q[..., 1].mean()),
+            "kl_mean": float(q[..., 2].mean()),
+            "uniform_coverage_mean": float(np.mean(np.minimum(w.top_k, blocks) / blocks)),
+            "mass_kernel_ms": ms, "mass_kernel_gbs": 2 * k_bytes / (ms / 1e3) / 1e9}
+
+
 def cpu_baseline(inputs, runner, budget_s: float):
     """The oracle as it stands, on a bounded sample of the same workload's
     rows, timed on this host's cores.  Host copies are outside the timing."""
@@ -163,6 +197,8 @@ def main():
                     help="run one device-to-device copy of this many MiB first (scales PMC byte counters)")
     ap.add_argument("--chunk-rows", type=int, default=16384,
                     help="prefill query rows per pipelined chunk (0: one chunk, no overlap)")
+    ap.add_argument("--quality-rows", type=int, default=64,
+                    help="query rows (evenly spaced) on which to measure selection quality against dense attention; 0: skip")
     ap.add_argument("--graph", choices=["on", "off"], default="off",
                     help="replay an unchunked step from a captured HIP graph (stage events then come from a serial pass)")
     args = ap.parse_args()
@@ -295,6 +331,8 @@ def main():
     roof["launches_per_step"] = launches_per_step
     roof["avg_launch_ms"] = avg_launch_ms
 
+    quality = selection_quality(runner, args.quality_rows) if args.quality_rows > 0 else None
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(inputs, runner, args.cpu_budget)
@@ -323,6 +361,7 @@ def main():
         "step": step_info,
         "roofline": roof,
         "cpu_baseline": cpu,
+        "selection_quality": quality,
         "host_wall_s_timed_region": t_host,
     }
     print(json.dumps(line))

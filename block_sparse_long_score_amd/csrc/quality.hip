@@ -7,7 +7,8 @@
 // recall and by how much of the attention score the chosen blocks cover.
 //
 // block_mass_kernel: P for sampled query rows.  One workgroup per (sampled
-// row, group); its four waves take the causal blocks round-robin.  Scores of
+// row, group); its waves (4, or 16 for small samples) take the causal blocks
+// round-robin.  Scores of
 // the group's heads use the 16x16x32 bf16 MFMA with 16 keys on M (K rows read
 // straight from the block-major cache) and the heads on N (padded to 16), so
 // lane (head l%16, quarter l/16) holds 4 keys of one head per key tile.  Pass
@@ -44,10 +45,10 @@ __device__ __forceinline__ float max_quarters(float v) {
   return fmaxf(v, __shfl_xor(v, 32));
 }
 
-template <int D>
-__global__ __launch_bounds__(256) void block_mass_kernel(MassArgs a) {
+template <int D, int WAVES>
+__global__ __launch_bounds__(64 * WAVES) void block_mass_kernel(MassArgs a) {
   constexpr int KS = D / 32;
-  __shared__ float st_s[4][16][2];
+  __shared__ float st_s[WAVES][16][2];
   const Problem& p = a.p;
   const int G = p.group;
   const int k = blockIdx.x >> a.hkv_shift;
@@ -92,7 +93,7 @@ __global__ __launch_bounds__(256) void block_mass_kernel(MassArgs a) {
 
   // Pass 1: per head, max and sum of 2^z over every causal token.
   float m = -__builtin_inff(), l = 0.f;
-  for (int b = wave; b <= c; b += 4) {
+  for (int b = wave; b <= c; b += WAVES) {
     const int phys = table[b];
     if (phys < 0 || phys >= p.num_blocks) continue;
     const uint16_t* kb = p.k + ((int64_t)phys * kBlock * p.hkv + g) * D;
@@ -119,10 +120,10 @@ __global__ __launch_bounds__(256) void block_mass_kernel(MassArgs a) {
   __syncthreads();
   float M = -__builtin_inff();
 #pragma unroll
-  for (int w = 0; w < 4; ++w) M = fmaxf(M, st_s[w][l16][0]);
+  for (int w = 0; w < WAVES; ++w) M = fmaxf(M, st_s[w][l16][0]);
   float L = 0.f;
 #pragma unroll
-  for (int w = 0; w < 4; ++w) {
+  for (int w = 0; w < WAVES; ++w) {
     const float mw = st_s[w][l16][0];
     L += mw > -__builtin_inff() ? st_s[w][l16][1] * fast_exp2(mw - M) : 0.f;
   }
@@ -130,7 +131,7 @@ __global__ __launch_bounds__(256) void block_mass_kernel(MassArgs a) {
 
   // Pass 2: mass of each block, summed over the group's heads.
   float* out = a.mass + ((int64_t)k * p.hkv + g) * a.ld;
-  for (int b = wave; b <= c; b += 4) {
+  for (int b = wave; b <= c; b += WAVES) {
     const int phys = table[b];
     if (phys < 0 || phys >= p.num_blocks) continue;
     const uint16_t* kb = p.k + ((int64_t)phys * kBlock * p.hkv + g) * D;
@@ -255,11 +256,19 @@ hipError_t launch_block_attn_mass(const Problem& p, const uint16_t* q, const int
   while ((1 << hkv_shift) < p.hkv) ++hkv_shift;
   if (n_rows == 0) return hipSuccess;
   MassArgs a{p, q, rows, n_rows, mass, ld, hkv_shift};
-  const dim3 grid((unsigned)((int64_t)n_rows << hkv_shift));
-  if (p.head_dim == 128)
-    hipLaunchKernelGGL(block_mass_kernel<128>, grid, dim3(256), 0, stream, a);
-  else
-    hipLaunchKernelGGL(block_mass_kernel<64>, grid, dim3(256), 0, stream, a);
+  const int64_t pairs = (int64_t)n_rows << hkv_shift;
+  const dim3 grid((unsigned)pairs);
+  // Few (row, group) pairs (decode-sized samples): 16 waves each to keep enough loads in flight.
+  if (pairs < 512) {
+    if (p.head_dim == 128)
+      hipLaunchKernelGGL((block_mass_kernel<128, 16>), grid, dim3(1024), 0, stream, a);
+    else
+      hipLaunchKernelGGL((block_mass_kernel<64, 16>), grid, dim3(1024), 0, stream, a);
+  } else if (p.head_dim == 128) {
+    hipLaunchKernelGGL((block_mass_kernel<128, 4>), grid, dim3(256), 0, stream, a);
+  } else {
+    hipLaunchKernelGGL((block_mass_kernel<64, 4>), grid, dim3(256), 0, stream, a);
+  }
   return hipGetLastError();
 }
 

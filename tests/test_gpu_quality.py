@@ -42,6 +42,8 @@ CASES = {
     "decode_batch": (WORKLOADS["c1"].with_sizes("q_dec", [1, 129, 2049, 5000, 9999], [1] * 5, permuted_table=True),
                      None),
     "m3_shape": (WORKLOADS["m3p"].with_sizes("q_m3", [2600], [2600]), [5, 1000, 2047, 2048, 2599]),
+    # 64 rows x 8 groups = 512 (row, group) pairs: the 4-wave mass kernel (smaller samples use 16 waves)
+    "m2_many_rows": (WORKLOADS["c1"].with_sizes("q_m2b", [3000], [3000]), list(range(0, 3000, 47))[:64]),
 }
 
 
