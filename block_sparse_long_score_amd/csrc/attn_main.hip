@@ -55,7 +55,7 @@ static int hkv_shift_of(const Problem& p) {
 static int kv_chunk(const Problem& p) { return std::max(16, 1536 / p.group); }
 
 // Decode batches with at least this many (sequence, group) pairs use one
-// 16-wave workgroup per pair (decode_fused_kernel); smaller ones split each
+// 16-wave workgroup per pair (decode_fused_kernel, any G <= 16); smaller ones split each
 // pair over 16 workgroups (one per selected block) and merge.
 constexpr int64_t kFusedDecodeMinGroups = 128;
 
@@ -696,9 +696,11 @@ __global__ __launch_bounds__(256) void decode_block_kernel(KvOuterArgs a) {
 // Layout of the 16x16x32 operands as in decode_block_kernel.
 template <int D, int GM>
 __global__ __launch_bounds__(1024) void decode_fused_kernel(KvOuterArgs a) {
-  constexpr int VPL = D / 64;  // output dims per lane in P.V
-  constexpr int KS = D / 32;   // MFMA k-steps
-  __shared__ float p_s[kTopK][GM][32];
+  constexpr int VPL = D / 64;            // output dims per lane in P.V
+  constexpr int KS = D / 32;             // MFMA k-steps
+  constexpr int SUB = GM > 8 ? 16 : 32;  // keys per online-softmax step (registers bound it at G = 16)
+  constexpr int MT = SUB / 16;           // 16-key MFMA tiles per step
+  __shared__ float p_s[kTopK][GM][SUB];
   __shared__ float alpha_s[kTopK][GM];
   __shared__ float m_s[kTopK][GM], l_s[kTopK][GM];
   __shared__ float o_s[kTopK][GM][D];
@@ -741,10 +743,10 @@ __global__ __launch_bounds__(1024) void decode_fused_kernel(KvOuterArgs a) {
       bq[ks] = as_bf16x8(head_ok ? x : u32x4{0u, 0u, 0u, 0u});
     }
 
-    for (int c0 = 0; c0 < nvalid; c0 += 32) {
-      uint32_t vreg[32];
+    for (int c0 = 0; c0 < nvalid; c0 += SUB) {
+      uint32_t vreg[SUB];
 #pragma unroll
-      for (int k = 0; k < 32; ++k) {
+      for (int k = 0; k < SUB; ++k) {
         const int key = min(c0 + k, nvalid - 1);
         if constexpr (VPL == 2)
           vreg[k] = *reinterpret_cast<const uint32_t*>(vb + key * key_stride + lane * 2);
@@ -752,10 +754,10 @@ __global__ __launch_bounds__(1024) void decode_fused_kernel(KvOuterArgs a) {
           vreg[k] = (uint32_t)vb[key * key_stride + lane];
       }
 #pragma unroll
-      for (int k = 0; k < 32; ++k) vreg[k] = c0 + k < nvalid ? vreg[k] : 0u;
-      float sc[8];
+      for (int k = 0; k < SUB; ++k) vreg[k] = c0 + k < nvalid ? vreg[k] : 0u;
+      float sc[4 * MT];
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
+      for (int mt = 0; mt < MT; ++mt) {
         const int key = c0 + mt * 16 + l16;
         const uint16_t* krow = kb + min(key, nvalid - 1) * key_stride + q16 * 8;
         bf16x8 ak[KS];
@@ -773,14 +775,14 @@ __global__ __launch_bounds__(1024) void decode_fused_kernel(KvOuterArgs a) {
       }
       float mx = sc[0];
 #pragma unroll
-      for (int e = 1; e < 8; ++e) mx = fmaxf(mx, sc[e]);
+      for (int e = 1; e < 4 * MT; ++e) mx = fmaxf(mx, sc[e]);
       mx = fmaxf(mx, __shfl_xor(mx, 16));
       mx = fmaxf(mx, __shfl_xor(mx, 32));
       const float m_new = fmaxf(m_run, mx * c);  // finite: key c0 is valid
       const float alpha = fast_exp2(m_run - m_new);
       float psum = 0.f;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
+      for (int e = 0; e < 4 * MT; ++e) {
         const float pe = fast_exp2(fmaf(sc[e], c, -m_new));
         psum += pe;
         if (l16 < GM) p_s[w][l16][(e >> 2) * 16 + 4 * q16 + (e & 3)] = pe;
@@ -800,7 +802,7 @@ __global__ __launch_bounds__(1024) void decode_fused_kernel(KvOuterArgs a) {
         for (int v = 0; v < VPL; ++v) acc[j][v] *= al;
       }
 #pragma unroll
-      for (int k4 = 0; k4 < 8; ++k4) {
+      for (int k4 = 0; k4 < SUB / 4; ++k4) {
         __builtin_amdgcn_sched_barrier(0);  // four keys at a time: bounds live P and V registers
         float vv[4][VPL];
 #pragma unroll
@@ -950,13 +952,15 @@ static hipError_t launch_main_t(const Problem& p, const uint16_t* q, const int32
   KvOuterArgs k{p, q, sel, nullptr, nullptr, nullptr, nullptr,
                 reinterpret_cast<uint16_t*>(base + w.part_o), out, reinterpret_cast<float*>(base + w.part_st),
                 w.n_lists, hs, w.chunk};
-  if (decode && p.group <= 8 && (int64_t)p.num_seqs * p.hkv >= kFusedDecodeMinGroups) {
+  if (decode && (int64_t)p.num_seqs * p.hkv >= kFusedDecodeMinGroups) {
     // Enough (sequence, group) pairs to fill the chip: one workgroup each, no merge pass.
     const unsigned n = (unsigned)(p.num_seqs * p.hkv);
     if (p.group <= 4)
       hipLaunchKernelGGL((decode_fused_kernel<D, 4>), dim3(n), dim3(1024), 0, stream, k);
-    else
+    else if (p.group <= 8)
       hipLaunchKernelGGL((decode_fused_kernel<D, 8>), dim3(n), dim3(1024), 0, stream, k);
+    else
+      hipLaunchKernelGGL((decode_fused_kernel<D, 16>), dim3(n), dim3(1024), 0, stream, k);
     return hipGetLastError();
   }
   if (decode) {
