@@ -56,6 +56,7 @@ def load() -> ctypes.CDLL:
         "msa_sparse_attn_decode": ([dims, cache, batch, vp, vp, vp, vp, sz, vp], ctypes.c_int),
         "msa_block_attn_mass": ([dims, cache, batch, vp, vp, i32, vp, i64, vp], ctypes.c_int),
         "msa_selection_quality": ([dims, batch, vp, i32, vp, vp, vp, i64, vp, vp], ctypes.c_int),
+        "msa_dense_attn_prefill": ([dims, cache, batch, vp, vp, vp], ctypes.c_int),
         "msa_workspace_size": ([dims, cache, batch, i32], sz),
         "msa_status_string": ([ctypes.c_int], ctypes.c_char_p),
         "msa_last_error": ([], ctypes.c_char_p),

@@ -278,6 +278,19 @@ msa_status msa_selection_quality(const msa_dims* dims, const msa_batch* batch, c
                     "msa_selection_quality launch");
 }
 
+msa_status msa_dense_attn_prefill(const msa_dims* dims, const msa_cache* cache, const msa_batch* batch,
+                                  const void* q, void* out, void* stream) {
+  MSA_TRY(check_dims(dims));
+  MSA_TRY(check_cache(cache));
+  MSA_TRY(check_batch(dims, batch, cache));
+  MSA_TRY(check_ptr(q, "q"));
+  MSA_TRY(check_ptr(out, "out"));
+  const msa::Problem p = make_problem(dims, batch, cache);
+  return hip_status(msa::launch_dense_prefill(p, static_cast<const uint16_t*>(q), static_cast<uint16_t*>(out),
+                                              static_cast<hipStream_t>(stream)),
+                    "msa_dense_attn_prefill launch");
+}
+
 size_t msa_workspace_size(const msa_dims* dims, const msa_cache* cache, const msa_batch* batch, int32_t call) {
   if (check_dims(dims) != MSA_OK || check_cache(cache) != MSA_OK || check_batch(dims, batch, cache) != MSA_OK)
     return 0;

@@ -59,4 +59,7 @@ size_t decode_workspace_bytes(const Problem& p);
 hipError_t launch_attn_decode(const Problem& p, const uint16_t* q, const int32_t* sel, uint16_t* out, void* ws,
                               hipStream_t stream);
 
+// Dense causal attention over the same cache (queries outer, no workspace).
+hipError_t launch_dense_prefill(const Problem& p, const uint16_t* q, uint16_t* out, hipStream_t stream);
+
 }  // namespace msa

@@ -171,6 +171,14 @@ def msa_sparse_attn_decode(dims: Dims, cache: Cache, batch: Batch, q, sel, out, 
     _attn("msa_sparse_attn_decode", dims, cache, batch, q, sel, out, workspace, stream)
 
 
+def msa_dense_attn_prefill(dims: Dims, cache: Cache, batch: Batch, q, out, stream=None):
+    """Dense causal attention of every query row over all its causal keys; out: bf16 [total_q, Hq, D]."""
+    L = _lib.load()
+    d, c, b = dims.c(), cache.c(), batch.c()
+    _check(L.msa_dense_attn_prefill(ctypes.byref(d), ctypes.byref(c), ctypes.byref(b), _ptr(q, "q", torch.bfloat16),
+                                    _ptr(out, "out", torch.bfloat16), _stream(stream)))
+
+
 def msa_block_attn_mass(dims: Dims, cache: Cache, batch: Batch, q, rows, mass, stream=None):
     """mass: float32 [n_rows, Hkv, ld]; rows: int32 [n_rows] query-row indices of the batch."""
     L = _lib.load()

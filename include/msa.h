@@ -255,6 +255,26 @@ msa_status msa_selection_quality(const msa_dims* dims, const msa_batch* batch, c
                                  int32_t n_rows, const float* mass, const float* block_scores,
                                  const int32_t* sel, int64_t ld, float* quality, void* stream);
 
+/* ------------------------------------------------------------------------- *
+ * msa_dense_attn_prefill — dense causal attention over the same cache
+ * ([M3-evo] §2, the softmax-attention equation; §2–§3: the layers and the
+ * training warmup that keep full attention).  For query row r at position t
+ * and head h of group g = h / (Hq/Hkv):
+ *     z_i = softmax_scale * (q[r][h] . k[i][g])  for every i <= t,
+ *     out[r][h] = sum_{i <= t} softmax(z)_i v[i][g]
+ * i.e. msa_sparse_attn_prefill with every causal block selected.  bf16 x bf16
+ * -> fp32 arithmetic, output rounded to bf16.  Blocks whose block-table
+ * entry lies outside [0, num_blocks) hold no keys (skipped, as in the sparse
+ * calls).  Designed for many query rows per sequence (query tiles of 128
+ * rows); correct for any batch.
+ *   q    : bf16 [total_q][Hq][D]
+ *   out  : bf16 [total_q][Hq][D]
+ * No workspace.
+ * Errors: NULL_POINTER, BAD_SHAPE, UNSUPPORTED, MISALIGNED, CAPACITY, HIP.
+ * ------------------------------------------------------------------------- */
+msa_status msa_dense_attn_prefill(const msa_dims* dims, const msa_cache* cache, const msa_batch* batch,
+                                  const void* q, void* out, void* stream);
+
 /* Bytes of workspace `call` needs for this problem; 0 if the arguments are
  * invalid (the failing check is reported by msa_last_error()). */
 size_t msa_workspace_size(const msa_dims* dims, const msa_cache* cache, const msa_batch* batch,

@@ -142,6 +142,23 @@ def attend(pos, q, k, v, sel, block_size: int = 128, scale: float | None = None)
     return out
 
 
+def dense_attend(pos, q, k, v, block_size: int = 128, scale: float | None = None) -> np.ndarray:
+    """Dense causal attention: float64 [n, Hq, D], every key i <= t attended.
+
+    It is step 4 with every causal block selected (the full-attention layers
+    beside MSA in "MiniMax 模型迭代与竞品分析" §2-§3).
+    """
+    pos = np.ascontiguousarray(pos, dtype=np.int64)
+    n = pos.shape[0]
+    groups = np.asarray(k).shape[1]
+    nblk = int(pos.max()) // block_size + 1 if n else 1
+    sel = np.full((n, groups, nblk), -1, dtype=np.int32)
+    for r in range(n):
+        c = int(pos[r]) // block_size
+        sel[r, :, : c + 1] = np.arange(c + 1, dtype=np.int32)
+    return attend(pos, q, k, v, sel, block_size, scale)
+
+
 def msa(pos, q_idx, k_idx, q, k, v, block_size: int = 128, top_k: int = 16, scale: float | None = None,
         ld: int | None = None):
     """All four steps for query rows of one sequence: (pooled, sel, out)."""

@@ -155,3 +155,18 @@ def test_quality_entry_points_validate_on_the_host(lib):
     assert lib.msa_selection_quality(dp, bp, FAKE, -2, FAKE, FAKE, FAKE, 16, FAKE, None) == SHAPE
     assert lib.msa_selection_quality(dp, bp, FAKE, 4, FAKE, FAKE, FAKE, 3, FAKE, None) == SHAPE
     assert lib.msa_selection_quality(dp, bp, FAKE, 0, FAKE, FAKE, FAKE, 16, FAKE, None) == OK
+
+
+def test_dense_attention_validates_on_the_host(lib):
+    d, c = _dims(), _cache()
+    b = _Batch([1024, 900], [512, 3])
+    dp, cp, bp = ctypes.byref(d), ctypes.byref(c), ctypes.byref(b.c)
+    assert lib.msa_dense_attn_prefill(dp, cp, bp, None, FAKE, None) == NULLP
+    assert lib.msa_dense_attn_prefill(dp, cp, bp, FAKE, FAKE + 2, None) == MISAL
+    assert lib.msa_dense_attn_prefill(ctypes.byref(_dims(head_dim=96)), cp, bp, FAKE, FAKE, None) == UNSUP
+    short = _cache(mbps=4)  # 1024 tokens need 8 blocks
+    assert lib.msa_dense_attn_prefill(dp, ctypes.byref(short), bp, FAKE, FAKE, None) == CAP
+    bad = _Batch([100], [101])  # more queries than tokens
+    assert lib.msa_dense_attn_prefill(dp, cp, ctypes.byref(bad.c), FAKE, FAKE, None) == SHAPE
+    empty = _Batch([100, 5], [0, 0])
+    assert lib.msa_dense_attn_prefill(dp, cp, ctypes.byref(empty.c), FAKE, FAKE, None) == OK  # nothing to do

@@ -1,0 +1,133 @@
+"""Parity of the dense causal attention call (msa_dense_attn_prefill) with the
+oracle's dense path (every causal block attended), through the C ABI.
+
+Outputs must be within max-abs 2e-2 and mean-abs 2e-3 of the oracle's
+double-precision result, the tolerance of the Main Branch.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from block_sparse_long_score_amd import ops
+from block_sparse_long_score_amd.inputs import WORKLOADS, bf16_bits, make_inputs
+from block_sparse_long_score_amd.pipeline import MsaRunner
+from tests.gpu_helpers import MAX_ABS, MEAN_ABS, seq_rows
+
+pytestmark = pytest.mark.gpu
+
+M2 = WORKLOADS["c1"]
+
+
+@pytest.fixture(autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def _announce(msg):
+    print(f"[gpu-case] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def _dense(w):
+    _announce(f"dense {w.name}: seq_lens={w.seq_lens[:4]}{'...' if w.num_seqs > 4 else ''} q_lens={w.q_lens[:4]} "
+              f"Hq={w.num_q_heads} Hkv={w.num_kv_heads} D={w.head_dim}")
+    runner = MsaRunner(make_inputs(w, "cuda"))
+    runner.append()
+    out = torch.full_like(runner.inputs.q, float("nan"))
+    ops.msa_dense_attn_prefill(runner.dims, runner.cache, runner.batch, runner.inputs.q, out)
+    torch.cuda.synchronize()
+    return runner, out
+
+
+def _oracle_dense(inp, s, positions):
+    positions = np.asarray(positions, dtype=np.int64)
+    rows = torch.from_numpy(seq_rows(inp, s, positions)).to(inp.q.device)
+    off = int(inp.tok_off[s])
+    length = int(positions.max()) + 1
+    k = bf16_bits(inp.k[off:off + length])
+    v = bf16_bits(inp.v[off:off + length])
+    q = bf16_bits(inp.q.index_select(0, rows))
+    return rows, oracle.dense_attend(positions, q, k, v, inp.workload.block_size)
+
+
+def _compare(runner, out, s, positions):
+    inp = runner.inputs
+    rows, want = _oracle_dense(inp, s, positions)
+    got = out.index_select(0, rows).float().cpu().numpy().astype(np.float64)
+    err = np.abs(got - want)
+    assert np.all(np.isfinite(got)), "rows left unwritten"
+    max_abs, mean_abs = float(err.max()), float(err.mean())
+    assert max_abs <= MAX_ABS and mean_abs <= MEAN_ABS, (s, max_abs, mean_abs)
+
+
+def _all_rows(runner, out):
+    w = runner.inputs.workload
+    for s in range(w.num_seqs):
+        if w.q_lens[s]:
+            _compare(runner, out, s, runner.inputs.positions(s))
+
+
+def test_dense_c0_all_rows():
+    """One KV group (8 heads, D = 64): every XCD deals tiles of the same group."""
+    runner, out = _dense(WORKLOADS["c0"])
+    _all_rows(runner, out)
+
+
+def test_dense_ragged_prefill_beyond_the_cap():
+    """3001 rows: a partial first tile and rows past 16 x 128, where dense differs from MSA."""
+    runner, out = _dense(M2.with_sizes("dense_ragged", [3001], [3001]))
+    _all_rows(runner, out)
+
+
+def test_dense_chunk_starting_mid_block():
+    runner, out = _dense(M2.with_sizes("dense_chunk", [5000], [777]))
+    _all_rows(runner, out)
+
+
+def test_dense_multi_sequence_batch_permuted_table():
+    runner, out = _dense(M2.with_sizes("dense_multi", [2500, 129, 1, 4100, 2048], [2500, 60, 1, 900, 17],
+                                       permuted_table=True))
+    _all_rows(runner, out)
+    assert torch.isfinite(out.float()).all()
+
+
+def test_dense_one_query_per_sequence():
+    runner, out = _dense(M2.with_sizes("dense_decode", [1, 128, 129, 2049, 5000, 9999], [1] * 6,
+                                       permuted_table=True))
+    _all_rows(runner, out)
+
+
+def test_dense_m3_shape():
+    """64 query heads over 4 KV heads (two XCDs per group)."""
+    runner, out = _dense(WORKLOADS["m3p"].with_sizes("dense_m3", [2600], [2600]))
+    _all_rows(runner, out)
+
+
+def test_dense_matches_msa_below_the_cap():
+    """Rows before position 2048 attend to every causal block under MSA too."""
+    w = M2.with_sizes("dense_vs_msa", [2048], [2048])
+    runner, out = _dense(w)
+    runner.step()
+    torch.cuda.synchronize()
+    diff = (runner.out.float() - out.float()).abs()
+    assert float(diff.max()) <= 2 * MAX_ABS and float(diff.mean()) <= MEAN_ABS
+
+
+def test_dense_c1_full_size_sampled_rows():
+    runner, out = _dense(WORKLOADS["c1"])
+    rng = np.random.default_rng(11)
+    pos = np.unique(np.concatenate([[0, 127, 128, 2047, 2048, 32767], rng.integers(0, 32768, 90)]))
+    _compare(runner, out, 0, pos)
+    assert torch.isfinite(out.float()).all()
+
+
+def test_dense_c3_full_size_sampled_rows():
+    runner, out = _dense(WORKLOADS["c3"])
+    rng = np.random.default_rng(12)
+    pos = np.unique(np.concatenate([[0, 128, 65535, 131071], rng.integers(0, 131072, 20)]))
+    _compare(runner, out, 0, pos)
+    assert torch.isfinite(out.float()).all()

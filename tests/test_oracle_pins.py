@@ -237,6 +237,21 @@ def test_top_k_covering_everything_is_dense(oracle_lib):
     np.testing.assert_allclose(out, ref, rtol=1e-11, atol=1e-12)
 
 
+def test_dense_path_equals_textbook_attention_beyond_the_cap(oracle_lib):
+    """The dense path (every causal block attended) on a context longer than
+    16 x 128: textbook dense causal GQA attention, and unlike MSA there."""
+    length = 2600
+    p = _problem(25, length, 6, 2, 16, 16)
+    pos = np.array([0, 5, 127, 128, 2047, 2048, 2300, 2599], np.int64)
+    q = p["q"][pos]
+    out = oracle_lib.dense_attend(pos, q, p["k"], p["v"])
+    ref = dense_causal_gqa(bits_to_f64(q), bits_to_f64(p["k"]), bits_to_f64(p["v"]), pos, 0.25)
+    np.testing.assert_allclose(out, ref, rtol=1e-12, atol=1e-13)
+    _, _, sparse = oracle_lib.msa(pos, p["q_idx"][pos], p["k_idx"], q, p["k"], p["v"])
+    np.testing.assert_array_equal(sparse[:5], out[:5])  # t < 2048: identical
+    assert np.abs(sparse[5:] - out[5:]).max() > 1e-3
+
+
 def test_sparse_rows_equal_dense_attention_over_selected_tokens(oracle_lib):
     """Beyond 2048 tokens: each row equals textbook softmax attention over
     exactly the tokens of its selected blocks (keys and values gathered by
