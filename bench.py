@@ -122,6 +122,33 @@ def selection_quality(runner, n_rows: int):
             "mass_kernel_ms": ms, "mass_kernel_gbs": 2 * k_bytes / (ms / 1e3) / 1e9}
 
 
+def dense_attention(runner, n_calls: int):
+    """The dense path on the same batch and cache (msa_dense_attn_prefill:
+    every causal key attended), timed by events over n_calls calls after the
+    timed region; not part of a step.  Gives an in-repo dense attention time
+    to set beside the sparse Main Branch and the whole MSA step."""
+    import torch
+    from block_sparse_long_score_amd import ops
+    w = runner.inputs.workload
+    out = torch.empty_like(runner.inputs.q)
+    call = lambda: ops.msa_dense_attn_prefill(runner.dims, runner.cache, runner.batch, runner.inputs.q, out)
+    call()  # warm-up
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(n_calls):
+        call()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / n_calls
+    flops = 0.0
+    for n, nq in zip(w.seq_lens, w.q_lens):
+        t = np.arange(n - nq, n, dtype=np.float64)
+        flops += 4.0 * w.head_dim * w.num_q_heads * float(np.sum(t + 1))
+    tflops = flops / (ms / 1e3) / 1e12
+    return {"kernel": "msa_dense_attn_prefill (dense_prefill_kernel)", "calls": n_calls, "ms": ms,
+            "algorithmic_flops": flops, "achieved_tflops": tflops, "mfma_frac": tflops / BF16_PEAK_TFLOPS}
+
+
 def cpu_baseline(inputs, runner, budget_s: float):
     """The oracle as it stands, on a bounded sample of the same workload's
     rows, timed on this host's cores.  Host copies are outside the timing."""
@@ -199,6 +226,8 @@ def main():
                     help="prefill query rows per pipelined chunk (0: one chunk, no overlap)")
     ap.add_argument("--quality-rows", type=int, default=64,
                     help="query rows (evenly spaced) on which to measure selection quality against dense attention; 0: skip")
+    ap.add_argument("--dense-calls", type=int, default=3,
+                    help="prefill workloads: time the dense attention path over this many calls after the timed region (0: skip)")
     ap.add_argument("--graph", choices=["on", "off"], default="off",
                     help="replay an unchunked step from a captured HIP graph (stage events then come from a serial pass)")
     args = ap.parse_args()
@@ -332,6 +361,11 @@ def main():
     roof["avg_launch_ms"] = avg_launch_ms
 
     quality = selection_quality(runner, args.quality_rows) if args.quality_rows > 0 else None
+    dense = None
+    if not runner.decode and args.dense_calls > 0:
+        dense = dense_attention(runner, args.dense_calls)
+        dense["msa_attend_speedup"] = dense["ms"] / stage_ms["attend"]
+        dense["msa_step_speedup"] = dense["ms"] / ms_per_step
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -362,6 +396,7 @@ def main():
         "roofline": roof,
         "cpu_baseline": cpu,
         "selection_quality": quality,
+        "dense_attention": dense,
         "host_wall_s_timed_region": t_host,
     }
     print(json.dumps(line))

@@ -7,16 +7,23 @@
 // layers and the training warmup that run full attention beside the sparse
 // ones.  It is MSA with every causal block selected, on the cache MSA uses.
 //
-// Schedule (queries outer).  One workgroup of 4 waves per (sequence, tile of
-// 128 query rows, query head); wave w owns 32 consecutive rows.  The
-// workgroup walks the causal blocks in order, stages each block's K and V^T
-// in LDS (shared by the 4 waves) and every wave runs its rows against it on
-// the 32x32x16 bf16 MFMA (the tile pieces of attn_tiles.h), with an online
-// softmax in base 2.  Only the one or two blocks that hold the tile's own
-// positions are masked.  The running maximum is raised only when a block's
-// maximum exceeds it by more than 2^8, so the accumulators are rescaled
-// rarely; numerator and denominator share the reference value, so the
-// result is unchanged.
+// Schedule (queries outer).  One workgroup of 8 waves per (sequence, tile of
+// 256 query rows, query head); wave w owns 32 consecutive rows, two waves
+// share each SIMD.  The workgroup walks the causal blocks in order.  K and V
+// of a block are copied from the cache straight into LDS with the
+// asynchronous global->LDS loads (row-major, 16-byte chunks XOR-swizzled per
+// row), double-buffered so the copies of the next block overlap the math of
+// this one.  Every wave runs its rows against the staged block on the
+// 32x32x16 bf16 MFMA: S^T = K Q^T with K rows as the A operand, then
+// O^T += V^T P^T with the V^T operand read by the LDS transpose load
+// (ds_read_b64_tr_b16), so nothing is transposed by the vector ALU.  The
+// softmax is online, in base 2; only the one or two blocks that hold the
+// tile's own positions are masked.  The running maximum is raised only when
+// a block's maximum exceeds it by more than 2^8, so the accumulators are
+// rescaled rarely; numerator and denominator share the reference value, so
+// the result is unchanged.  Per wave and block the operand reads move 64 KB
+// out of LDS for 64 MFMAs (32 query rows per wave), which bounds the kernel
+// at roughly half of the MFMA peak on this LDS.
 //
 // Work order.  Workgroups are dispatched round-robin over the 8 XCDs
 // (workgroup i runs on XCD i % 8), each with its own L2.  The mapping from
@@ -26,6 +33,8 @@
 // (the longest rows first) for load balance.
 #include "attn_tiles.h"
 #include "msa_kernels.h"
+
+#include <type_traits>
 
 namespace msa {
 
@@ -79,12 +88,6 @@ __device__ __forceinline__ bool dense_item(const DenseArgs& a, int& tf, int& s, 
 // a lane reads, both XOR terms depend on the lane only, so every operand
 // address is a per-lane base plus a compile-time offset.
 template <int D>
-struct DenseBuf {
-  uint16_t k[kBlock * D];
-  uint16_t v[kBlock * D];
-};
-
-template <int D>
 __device__ __forceinline__ int dense_kslot(int r, int c) {
   constexpr int CPR = D / 8, RPB = 128 / D;
   return c ^ ((r / RPB) & (CPR - 1));
@@ -121,33 +124,25 @@ __device__ __forceinline__ DmaLane<D> dma_lane(int wave, int lane, int64_t key_s
   return d;
 }
 
-// Asynchronous copy of one block of group g into LDS with the global->LDS
-// loads (each wave instruction fills 64 consecutive 16-byte slots).  In a
-// block cut short by the end of the sequence, keys at or after `valid` read
-// the last valid key instead: finite data, and always masked since they lie
+// Asynchronous copy of the K rows (V = false) or V rows (V = true) of one
+// block of group g into a 128 x D LDS matrix with the global->LDS loads
+// (each wave instruction fills 64 consecutive 16-byte slots).  In a block
+// cut short by the end of the sequence, keys at or after `valid` read the
+// last valid key instead: finite data, and always masked since they lie
 // after every query position.
-template <int D>
-__device__ __forceinline__ void dense_dma(DenseBuf<D>& B, const DmaLane<D>& dl, int wave, const uint16_t* kg,
-                                          const uint16_t* vg, int64_t key_stride, int valid) {
-  const char* kb = reinterpret_cast<const char*>(kg);
-  const char* vb = reinterpret_cast<const char*>(vg);
+template <int D, bool V>
+__device__ __forceinline__ void dense_dma(uint16_t* dst, const DmaLane<D>& dl, int wave, const uint16_t* src,
+                                          int64_t key_stride, int valid) {
+  const char* sb = reinterpret_cast<const char*>(src);
   const bool full = valid == kBlock;
 #pragma unroll
   for (int i = 0; i < DmaLane<D>::ROUNDS; ++i) {
     const int run = i * kDenseWaves + wave;
-    uint32_t ko = dl.koff[i], vo = dl.voff[i];
-    if (!full && dl.row[i] >= valid) {
-      const uint32_t shift = (uint32_t)((dl.row[i] - (valid - 1)) * key_stride * 2);
-      ko -= shift;
-      vo -= shift;
-    }
-    __builtin_amdgcn_global_load_lds(static_cast<const void*>(kb + ko),
+    uint32_t off = V ? dl.voff[i] : dl.koff[i];
+    if (!full && dl.row[i] >= valid) off -= (uint32_t)((dl.row[i] - (valid - 1)) * key_stride * 2);
+    __builtin_amdgcn_global_load_lds(static_cast<const void*>(sb + off),
                                      reinterpret_cast<__attribute__((address_space(3))) void*>(
-                                         reinterpret_cast<uintptr_t>(&B.k[run * 512])),
-                                     16, 0, 0);
-    __builtin_amdgcn_global_load_lds(static_cast<const void*>(vb + vo),
-                                     reinterpret_cast<__attribute__((address_space(3))) void*>(
-                                         reinterpret_cast<uintptr_t>(&B.v[run * 512])),
+                                         reinterpret_cast<uintptr_t>(dst + run * 512)),
                                      16, 0, 0);
   }
 }
@@ -158,6 +153,16 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 // lanes, lane 4a+b receives element b of the 4-element row addressed by
 // lane 4j+a, for j = 0..3.
 typedef __attribute__((address_space(3))) const char lds_byte;
+
+// An LDS buffer's address as a run-time value: the operand reads then add
+// one per-lane base to it and fold their constant offsets (a buffer placed
+// at 64 KB or above would otherwise need an extra add per read, its address
+// exceeding the 16-bit offset field).
+__device__ __forceinline__ lds_byte* opaque_lds(const uint16_t* p) {
+  uint32_t a = (uint32_t)reinterpret_cast<uintptr_t>((lds_byte*)p);
+  asm volatile("" : "+s"(a));
+  return (lds_byte*)(uintptr_t)a;
+}
 
 __device__ __forceinline__ i16x4 lds_read_tr16(lds_byte* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(p));
@@ -192,27 +197,43 @@ __device__ __forceinline__ OpLane<D> op_lane(int lane) {
   return o;
 }
 
-// One block for this wave's 32 rows: S^T = K Q^T, mask, online softmax, O^T += V^T P^T.
+// S^T = K Q^T of one staged block for this wave's 32 rows (4 key tiles).
+// The K operands of k-step ks+1 are read while the products of step ks run.
 template <int D>
-__device__ __forceinline__ void dense_block(const DenseBuf<D>& B, const OpLane<D>& ol, const bf16x8 (&bq)[D / 16],
-                                           f32x16 (&oacc)[D / 32], float& m, float& l, float c, bool masked,
-                                           int lim) {
-  const int lane = threadIdx.x & 63;
-  const int half = lane >> 5;
-  const char* kb = reinterpret_cast<const char*>(B.k);
-  lds_byte* vb = (lds_byte*)(B.v);
-  f32x16 sacc[4];
+__device__ __forceinline__ void dense_scores(lds_byte* kb, const OpLane<D>& ol, const bf16x8 (&bq)[D / 16],
+                                            f32x16 (&sacc)[4]) {
+  __builtin_amdgcn_sched_barrier(0);  // phases are scheduled apart: bounds live operand registers
 #pragma unroll
   for (int t4 = 0; t4 < 4; ++t4)
     sacc[t4] = f32x16{0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  auto rd = [&](int ks, int t4) {
+    return *reinterpret_cast<__attribute__((address_space(3))) const u32x4*>(kb + ol.k[ks] + t4 * 32 * D * 2);
+  };
+  u32x4 cur[4], nxt[4];
 #pragma unroll
-  for (int ks = 0; ks < D / 16; ++ks)
+  for (int t4 = 0; t4 < 4; ++t4) cur[t4] = rd(0, t4);
 #pragma unroll
-    for (int t4 = 0; t4 < 4; ++t4) {
-      const bf16x8 ak = as_bf16x8(*reinterpret_cast<const u32x4*>(kb + ol.k[ks] + t4 * 32 * D * 2));
-      sacc[t4] = mfma32(ak, bq[ks], sacc[t4]);
-    }
+  for (int ks = 0; ks < D / 16; ++ks) {
+    if (ks + 1 < D / 16)
+#pragma unroll
+      for (int t4 = 0; t4 < 4; ++t4) nxt[t4] = rd(ks + 1, t4);
+#pragma unroll
+    for (int t4 = 0; t4 < 4; ++t4) sacc[t4] = mfma32(as_bf16x8(cur[t4]), bq[ks], sacc[t4]);
+#pragma unroll
+    for (int t4 = 0; t4 < 4; ++t4) cur[t4] = nxt[t4];
+  }
+}
+
+// Mask (keys after the row's position, in the blocks that hold the tile's
+// own positions), online softmax update and P rounded to bf16 in the key
+// order of the P^T operand.  The running maximum is raised only when the
+// block's maximum exceeds it by more than 8 (log2 units), so the O
+// accumulators are rescaled rarely.
+template <int D>
+__device__ __forceinline__ void dense_softmax(f32x16 (&sacc)[4], bool masked, int lim, float c, float& m, float& l,
+                                             f32x16 (&oacc)[D / 32], bf16x8 (&pb)[8]) {
   __builtin_amdgcn_sched_barrier(0);
+  const int half = (threadIdx.x >> 5) & 1;
   if (masked) {
 #pragma unroll
     for (int t4 = 0; t4 < 4; ++t4)
@@ -240,7 +261,6 @@ __device__ __forceinline__ void dense_block(const DenseBuf<D>& B, const OpLane<D
     m = mn;
   }
   float sum = 0.f;
-  bf16x8 pb[8];
 #pragma unroll
   for (int kk = 0; kk < 8; ++kk) {
     float e[8];
@@ -253,21 +273,39 @@ __device__ __forceinline__ void dense_block(const DenseBuf<D>& B, const OpLane<D
                              pack_bf16x2(e[6], e[7])});
   }
   l += sum + swap_halves(sum);
+}
+
+// O^T += V^T P^T for one staged block.  The V^T operands of k-step kk+1
+// are read while the products of step kk run.
+template <int D>
+__device__ __forceinline__ void dense_pv(lds_byte* vb, const OpLane<D>& ol, const bf16x8 (&pb)[8],
+                                        f32x16 (&oacc)[D / 32]) {
   __builtin_amdgcn_sched_barrier(0);
+  constexpr int NT = D / 32;
+  auto rd = [&](int kk, int n) {
+    const i16x4 lo = lds_read_tr16(vb + ol.v[n] + (16 * kk) * D * 2);
+    const i16x4 hi = lds_read_tr16(vb + ol.v[n] + (16 * kk + 8) * D * 2);
+    const u32x2 lw = __builtin_bit_cast(u32x2, lo), hw = __builtin_bit_cast(u32x2, hi);
+    return u32x4{lw[0], lw[1], hw[0], hw[1]};
+  };
+  u32x4 cur[NT], nxt[NT];
 #pragma unroll
-  for (int kk = 0; kk < 8; ++kk)
+  for (int n = 0; n < NT; ++n) cur[n] = rd(0, n);
 #pragma unroll
-    for (int n = 0; n < D / 32; ++n) {
-      const i16x4 lo = lds_read_tr16(vb + ol.v[n] + (16 * kk) * D * 2);
-      const i16x4 hi = lds_read_tr16(vb + ol.v[n] + (16 * kk + 8) * D * 2);
-      const u32x2 lw = __builtin_bit_cast(u32x2, lo), hw = __builtin_bit_cast(u32x2, hi);
-      oacc[n] = mfma32(as_bf16x8(u32x4{lw[0], lw[1], hw[0], hw[1]}), pb[kk], oacc[n]);
-    }
+  for (int kk = 0; kk < 8; ++kk) {
+    if (kk + 1 < 8)
+#pragma unroll
+      for (int n = 0; n < NT; ++n) nxt[n] = rd(kk + 1, n);
+#pragma unroll
+    for (int n = 0; n < NT; ++n) oacc[n] = mfma32(as_bf16x8(cur[n]), pb[kk], oacc[n]);
+#pragma unroll
+    for (int n = 0; n < NT; ++n) cur[n] = nxt[n];
+  }
 }
 
 template <int D>
 __global__ __launch_bounds__(64 * kDenseWaves, 2) void dense_prefill_kernel(DenseArgs a) {
-  __shared__ DenseBuf<D> buf0, buf1;
+  __shared__ uint16_t k0[kBlock * D], k1[kBlock * D], v0[kBlock * D], v1[kBlock * D];
   const Problem& p = a.p;
   int tf, s, h;
   if (!dense_item(a, tf, s, h)) return;
@@ -291,6 +329,7 @@ __global__ __launch_bounds__(64 * kDenseWaves, 2) void dense_prefill_kernel(Dens
   const bool active = row0 + 31 >= q_beg;          // wave has rows of its own
   const int last_b = active ? t_last >> 7 : -1;
   const int first_masked = t_first >> 7;
+  const bool lead = wave < kDenseWaves / 2;        // waves 0-3 lead, 4-7 trail (one of each per SIMD)
 
   bf16x8 bq[D / 16];
   {
@@ -304,43 +343,66 @@ __global__ __launch_bounds__(64 * kDenseWaves, 2) void dense_prefill_kernel(Dens
 #pragma unroll
   for (int n = 0; n < D / 32; ++n)
     oacc[n] = f32x16{0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  f32x16 sacc[4];
+  bf16x8 pb[8];
   const DmaLane<D> dl = dma_lane<D>(wave, lane, key_stride);
   const OpLane<D> ol = op_lane<D>(lane);
 
-  // Block b is staged in buf0 (b even) or buf1 (b odd), one block ahead:
-  // the copy of b+1 runs while block b is computed.  Blocks whose table
-  // entry is out of range hold no keys: neither copied nor computed.  The
-  // table entries of blocks b+2 and b+3 are loaded by alternate lanes while
-  // block b is computed and read out of lanes 0 and 1 after the next
-  // barrier, so no wait for them ever waits for a copy in flight.
-  auto phys_ok = [&](int b, int ph) { return (b < nb && ph >= 0 && ph < p.num_blocks) ? ph : -1; };
-  auto stage = [&](DenseBuf<D>& B, int b, int phys) {
-    if (phys < 0) return;
-    const int64_t base = ((int64_t)phys * kBlock * p.hkv + g) * D;
-    dense_dma<D>(B, dl, wave, p.k + base, p.v + base, key_stride, min(kBlock, seq_len - b * kBlock));
-  };
-  auto run = [&](const DenseBuf<D>& B, int b, int phys) {
-    if (b > last_b || phys < 0) return;
-    dense_block<D>(B, ol, bq, oacc, m, l, c, b >= first_masked, t - b * kBlock);
-  };
+  // Ping-pong schedule.  Barrier interval i computes, per wave, the matrix
+  // products P.V of block i-1 and S = K.Q of block i, and one softmax:
+  // leading waves run the products first and then the softmax of block i,
+  // trailing waves run the softmax of block i-1 first and then the
+  // products.  The two waves that share a SIMD thus alternate between the
+  // matrix cores and the vector ALU.  Interval i reads K_i and V_{i-1};
+  // meanwhile K_{i+1} and V_i are copied into the other K and V buffers.
+  // Blocks whose table entry is out of range hold no keys: neither copied
+  // nor computed.  Table entries are loaded two intervals ahead by alternate
+  // lanes and read out of lane 0 after the next barrier.
+  auto phys_ok = [&](int b, int ph) { return (b >= 0 && b < nb && ph >= 0 && ph < p.num_blocks) ? ph : -1; };
+  auto computes = [&](int b, int ph) { return b >= 0 && b <= last_b && ph >= 0; };
+  auto block_src = [&](int ph) { return ((int64_t)ph * kBlock * p.hkv + g) * D; };
+  auto valid_of = [&](int b) { return min(kBlock, seq_len - b * kBlock); };
+
   int pair = bt[min(lane & 1, nb - 1)];
+  int ph_prev = -1;
   int ph_cur = phys_ok(0, __builtin_amdgcn_readlane(pair, 0));
-  int ph_nxt = phys_ok(1, __builtin_amdgcn_readlane(pair, 1));
-  stage(buf0, 0, ph_cur);
-  for (int b = 0; b < nb; b += 2) {
-    __builtin_amdgcn_s_waitcnt(0);  // this wave's copies of block b have landed
-    __syncthreads();                // everyone's have, and block b-1 (buf1) is no longer read
-    pair = bt[min(b + 2 + (lane & 1), nb - 1)];
-    stage(buf1, b + 1, ph_nxt);
-    run(buf0, b, ph_cur);
-    if (b + 1 >= nb) break;
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    const int ph_odd = ph_nxt;
-    ph_cur = phys_ok(b + 2, __builtin_amdgcn_readlane(pair, 0));
-    ph_nxt = phys_ok(b + 3, __builtin_amdgcn_readlane(pair, 1));
-    stage(buf0, b + 2, ph_cur);
-    run(buf1, b + 1, ph_odd);
+  int ph_next = phys_ok(1, __builtin_amdgcn_readlane(pair, 1));
+  if (ph_cur >= 0) dense_dma<D, false>(k0, dl, wave, p.k + block_src(ph_cur), key_stride, valid_of(0));
+
+  auto interval = [&](auto parity, int i) {
+    constexpr int P = decltype(parity)::value;
+    uint16_t* knext = P ? k0 : k1;
+    uint16_t* vcur = P ? v1 : v0;
+    lds_byte* kcur = opaque_lds(P ? k1 : k0);
+    lds_byte* vprev = opaque_lds(P ? v0 : v1);
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's copies for this interval have landed
+    __syncthreads();                // everyone's have, and the previous interval's buffers are free
+    if (i >= 1) ph_next = phys_ok(i + 1, __builtin_amdgcn_readlane(pair, 0));
+    pair = bt[min(i + 2 + (lane & 1), nb - 1)];
+    if (ph_next >= 0)
+      dense_dma<D, false>(knext, dl, wave, p.k + block_src(ph_next), key_stride, valid_of(i + 1));
+    if (i < nb && ph_cur >= 0)
+      dense_dma<D, true>(vcur, dl, wave, p.v + block_src(ph_cur), key_stride, valid_of(i));
+    const bool pv = computes(i - 1, ph_prev), sc = i < nb && computes(i, ph_cur);
+    // leading: P.V(i-1), S(i), softmax(i); trailing: softmax(i-1), P.V(i-1), S(i)
+    if (!lead && pv) dense_softmax<D>(sacc, i - 1 >= first_masked, t - (i - 1) * kBlock, c, m, l, oacc, pb);
+    if (pv) dense_pv<D>(vprev, ol, pb, oacc);
+    if (sc) {
+      dense_scores<D>(kcur, ol, bq, sacc);
+    } else {  // defined on every path: no S value is live across the P.V products
+#pragma unroll
+      for (int t4 = 0; t4 < 4; ++t4)
+        sacc[t4] = f32x16{0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    }
+    if (lead && sc) dense_softmax<D>(sacc, i >= first_masked, t - i * kBlock, c, m, l, oacc, pb);
+    ph_prev = ph_cur;
+    ph_cur = ph_next;
+    ph_next = -1;
+  };
+  for (int i = 0; i <= nb; i += 2) {
+    interval(std::integral_constant<int, 0>(), i);
+    if (i + 1 > nb) break;
+    interval(std::integral_constant<int, 1>(), i + 1);
   }
   if (!active) return;
 
