@@ -260,7 +260,7 @@ struct TileRow {
 
 template <int D>
 __global__ __launch_bounds__(256, 2) void kvouter_kernel(KvOuterArgs a) {
-  __shared__ Lds<D> sm;
+  __shared__ uint16_t k_s[kBlock * D], v_s[kBlock * D];
   const Problem& p = a.p;
   const int G = p.group;
   if ((int)blockIdx.x >= a.coff[a.n_lists]) return;
@@ -276,11 +276,16 @@ __global__ __launch_bounds__(256, 2) void kvouter_kernel(KvOuterArgs a) {
   const int row_end = p.cu_q[s + 1];
   const int phys = p.block_table[(int64_t)s * p.max_blocks_per_seq + b];
   const int64_t base = ((int64_t)phys * kBlock * p.hkv + g) * D;
-  stage_block<D>(sm, p.k + base, p.v + base, (int64_t)p.hkv * D, min(kBlock, seq_len - b * kBlock));
-  __syncthreads();
-
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int half = lane >> 5, l32 = lane & 31;
+  {  // the block's K and V into LDS, asynchronously (keys past the sequence end are never attended)
+    const int64_t key_stride = (int64_t)p.hkv * D;
+    const DmaLane<D, 4> dl = dma_lane<D, 4>(wave, lane, key_stride);
+    const int valid = min(kBlock, seq_len - b * kBlock);
+    block_dma<D, 4, false>(k_s, dl, wave, p.k + base, key_stride, valid);
+    block_dma<D, 4, true>(v_s, dl, wave, p.v + base, key_stride, valid);
+  }
   const int rows = n_ent * G;
   auto tile_row = [&](int tile) -> TileRow {
     TileRow tr;
@@ -299,11 +304,21 @@ __global__ __launch_bounds__(256, 2) void kvouter_kernel(KvOuterArgs a) {
     return tr;
   };
 
+  // The first tile's rows and queries load while the block is in flight.
   int tile = wave;
-  if (tile * 32 >= rows) return;
-  TileRow cur = tile_row(tile);
+  const bool has_tiles = tile * 32 < rows;
+  TileRow cur{};
   QRaw<D> raw;
-  load_q_raw<D>(cur.q, raw);  // rows past the list end read a valid row's query; nothing of theirs is stored
+  if (has_tiles) {
+    cur = tile_row(tile);
+    load_q_raw<D>(cur.q, raw);  // rows past the list end read a valid row's query; nothing of theirs is stored
+  }
+  __builtin_amdgcn_s_waitcnt(0);  // this wave's copies have landed
+  __syncthreads();                // and everyone's
+  if (!has_tiles) return;
+  lds_byte* kb = opaque_lds(k_s);
+  lds_byte* vb = opaque_lds(v_s);
+  const OpLane<D> ol = op_lane<D>(lane);
   for (; tile * 32 < rows; tile += 4) {
     bf16x8 bq[D / 16];
     q_operand<D>(raw, bq);
@@ -316,7 +331,7 @@ __global__ __launch_bounds__(256, 2) void kvouter_kernel(KvOuterArgs a) {
     }
 
     f32x16 sacc[4];
-    block_scores<D>(sm, bq, sacc);
+    tile_scores<D>(kb, ol, bq, sacc);
     if (__ballot(cur.lim < kBlock - 1) != 0) {  // local-block rows in this tile: mask keys after the query
 #pragma unroll
       for (int t4 = 0; t4 < 4; ++t4)
@@ -329,7 +344,11 @@ __global__ __launch_bounds__(256, 2) void kvouter_kernel(KvOuterArgs a) {
     float m, l;
     softmax_rows(sacc, p.scale_log2e, m, l);
     f32x16 oacc[D / 32];
-    block_pv<D>(sm, sacc, oacc);
+    {
+      bf16x8 pb[8];
+      p_operand(sacc, pb);
+      tile_pv<D, false>(vb, ol, pb, oacc);
+    }
 
     // Normalised output, scaled by 2^-e into [-1, 1] for fp16 storage; the
     // normalisation 1/l and the 2^-e scale are one multiply.

@@ -8,93 +8,202 @@
 //   O^T[D x 32 rows]        = V^T[D x keys] * P^T[keys x rows]
 // With keys on the M axis each lane owns one row, so row max/sum are in-lane
 // plus one exchange between wave halves, and the S^T accumulators rounded to
-// bf16 are directly the B operand of the P.V product; V is stored transposed
-// in LDS so its A operand is two 8-byte reads.
+// bf16 are directly the B operand of the P.V product.  K and V are staged
+// row-major, copied from the cache by the asynchronous global->LDS loads;
+// the V^T operand comes from the LDS transpose load.
 #pragma once
 
 #include "msa_device.h"
 
 namespace msa {
 
+// One staged block: K and V of 128 keys, row-major [key][D], in 16-byte
+// chunks placed at a per-row XOR of their index so that the operand reads
+// touch every bank once per pass:
+//   K (read as 16-byte rows of 16 keys x one chunk): slot = c ^ ((r/RPB) & (CPR-1));
+//   V (read transposed, 4 keys x 4 chunks per 32 lanes): slot = c ^ (((r/RPB) & (CPR/4-1)) << 2),
+// with CPR chunks per row and RPB rows per 256 bytes of banks.  For the rows
+// a lane reads, both XOR terms depend on the lane only, so every operand
+// address is a per-lane base plus a compile-time offset.
 template <int D>
-struct Lds {
-  static constexpr int KP = D + 8;    // K row pitch (bf16): rows stay 16-byte aligned
-  static constexpr int VP = 128 + 4;  // V^T row pitch (bf16): 66 words, so the 32 rows one PV operand read touches fill all 64 banks once
-  uint16_t k[128 * KP];
-  uint16_t vt[D * VP];
+__device__ __forceinline__ int kv_kslot(int r, int c) {
+  constexpr int CPR = D / 8, RPB = 128 / D;
+  return c ^ ((r / RPB) & (CPR - 1));
+}
+
+template <int D>
+__device__ __forceinline__ int kv_vslot(int r, int c) {
+  constexpr int CPR = D / 8, RPB = 128 / D;
+  return c ^ (((r / RPB) & (CPR / 4 - 1)) << 2);
+}
+
+// Per-lane byte offsets of the block copy by a workgroup of WAVES waves:
+// round i moves slots (WAVES*i + wave) * 64 + lane of K and of V (row
+// r = slot / CPR), reading the global chunk that belongs in that slot.
+template <int D, int WAVES>
+struct DmaLane {
+  static constexpr int CPR = D / 8;
+  static constexpr int ROUNDS = kBlock * CPR / (64 * WAVES);
+  uint32_t koff[ROUNDS], voff[ROUNDS];  // bytes from the block's first key row
+  int row[ROUNDS];
 };
 
-// Stage one block of one KV head into LDS: K as [key][d], V as [d][key].
-// Keys at or after `valid` are written as zeros (never read from the cache).
-template <int D>
-__device__ __forceinline__ void stage_block(Lds<D>& sm, const uint16_t* __restrict__ kg,
-                                            const uint16_t* __restrict__ vg, int64_t key_stride, int valid) {
-  constexpr int C8 = D / 8;
-  for (int idx = threadIdx.x; idx < 128 * C8; idx += blockDim.x) {
-    const int key = idx / C8, c8 = idx - key * C8;
-    u32x4 v = key < valid ? load16(kg + key * key_stride + c8 * 8) : u32x4{0u, 0u, 0u, 0u};
-    store16(&sm.k[key * Lds<D>::KP + c8 * 8], v);
+template <int D, int WAVES>
+__device__ __forceinline__ DmaLane<D, WAVES> dma_lane(int wave, int lane, int64_t key_stride) {
+  DmaLane<D, WAVES> d;
+#pragma unroll
+  for (int i = 0; i < DmaLane<D, WAVES>::ROUNDS; ++i) {
+    const int slot_idx = (i * WAVES + wave) * 64 + lane;
+    const int r = slot_idx / DmaLane<D, WAVES>::CPR, sl = slot_idx % DmaLane<D, WAVES>::CPR;
+    d.row[i] = r;
+    d.koff[i] = (uint32_t)((r * key_stride + kv_kslot<D>(r, sl) * 8) * 2);
+    d.voff[i] = (uint32_t)((r * key_stride + kv_vslot<D>(r, sl) * 8) * 2);
   }
-  for (int idx = threadIdx.x; idx < 32 * C8; idx += blockDim.x) {
-    const int k4 = idx / C8, c8 = idx - k4 * C8;
-    u32x4 r[4];
+  return d;
+}
+
+// Asynchronous copy of the K rows (V = false) or V rows (V = true) of one
+// block of group g into a 128 x D LDS matrix with the global->LDS loads
+// (each wave instruction fills 64 consecutive 16-byte slots).  In a block
+// cut short by the end of the sequence, keys at or after `valid` read the
+// last valid key instead: finite data, and always masked since they lie
+// after every query position that reads them.
+template <int D, int WAVES, bool V>
+__device__ __forceinline__ void block_dma(uint16_t* dst, const DmaLane<D, WAVES>& dl, int wave, const uint16_t* src,
+                                          int64_t key_stride, int valid) {
+  const char* sb = reinterpret_cast<const char*>(src);
+  const bool full = valid == kBlock;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int key = k4 * 4 + i;
-      r[i] = key < valid ? load16(vg + key * key_stride + c8 * 8) : u32x4{0u, 0u, 0u, 0u};
-    }
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int sh = (e & 1) * 16;
-      const uint32_t x0 = (r[0][e >> 1] >> sh) & 0xffffu, x1 = (r[1][e >> 1] >> sh) & 0xffffu;
-      const uint32_t x2 = (r[2][e >> 1] >> sh) & 0xffffu, x3 = (r[3][e >> 1] >> sh) & 0xffffu;
-      *reinterpret_cast<u32x2*>(&sm.vt[(c8 * 8 + e) * Lds<D>::VP + k4 * 4]) = u32x2{x0 | (x1 << 16), x2 | (x3 << 16)};
-    }
+  for (int i = 0; i < DmaLane<D, WAVES>::ROUNDS; ++i) {
+    const int run = i * WAVES + wave;
+    uint32_t off = V ? dl.voff[i] : dl.koff[i];
+    if (!full && dl.row[i] >= valid) off -= (uint32_t)((dl.row[i] - (valid - 1)) * key_stride * 2);
+    __builtin_amdgcn_global_load_lds(static_cast<const void*>(sb + off),
+                                     reinterpret_cast<__attribute__((address_space(3))) void*>(
+                                         reinterpret_cast<uintptr_t>(dst + run * 512)),
+                                     16, 0, 0);
   }
 }
 
-// Scores of 32 rows against the staged block: S^T, 4 key tiles.
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+// Transposed LDS read (gfx950 ds_read_b64_tr_b16): within each group of 16
+// lanes, lane 4a+b receives element b of the 4-element row addressed by
+// lane 4j+a, for j = 0..3.
+typedef __attribute__((address_space(3))) const char lds_byte;
+
+// An LDS buffer's address as a run-time value: the operand reads then add
+// one per-lane base to it and fold their constant offsets (a buffer placed
+// at 64 KB or above would otherwise need an extra add per read, its address
+// exceeding the 16-bit offset field).
+__device__ __forceinline__ lds_byte* opaque_lds(const uint16_t* p) {
+  uint32_t a = (uint32_t)reinterpret_cast<uintptr_t>((lds_byte*)p);
+  asm volatile("" : "+s"(a));
+  return (lds_byte*)(uintptr_t)a;
+}
+
+__device__ __forceinline__ i16x4 lds_read_tr16(lds_byte* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(p));
+}
+
+// Per-lane byte offsets of the operand reads within a staged block.
+//   K, k-step ks: row l32 (+ 32 t4), chunk 2ks + half.
+//   V^T, dim tile n: lane (group gi = lane/16, s = lane%16 = 4j + a) addresses
+//   row 4(gi/2) + j (+ 16kk + 8q), dims 32n + 16(gi%2) + 4a .. +3, so the
+//   transposed read hands lane (d = 32n + lane%32, half) keys
+//   16kk + 4half + 8q + {0..3}: the key order of the P^T operand.
 template <int D>
-__device__ __forceinline__ void block_scores(const Lds<D>& sm, const bf16x8 (&bq)[D / 16], f32x16 (&sacc)[4]) {
-  const int lane = threadIdx.x & 63;
+struct OpLane {
+  uint32_t k[D / 16];
+  uint32_t v[D / 32];
+};
+
+template <int D>
+__device__ __forceinline__ OpLane<D> op_lane(int lane) {
+  OpLane<D> o;
   const int half = lane >> 5, l32 = lane & 31;
 #pragma unroll
-  for (int m = 0; m < 4; ++m) {
-    __builtin_amdgcn_sched_barrier(0);  // one key tile at a time: bounds live operand registers
-    sacc[m] = f32x16{0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int ks = 0; ks < D / 16; ++ks) o.k[ks] = (uint32_t)((l32 * D + kv_kslot<D>(l32, 2 * ks + half) * 8) * 2);
+  const int gi = lane >> 4, s16 = lane & 15;
+  const int jr = s16 >> 2, a4 = s16 & 3;
+  const int r = 4 * (gi >> 1) + jr;
 #pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) {
-      const bf16x8 ak = as_bf16x8(*reinterpret_cast<const u32x4*>(&sm.k[(m * 32 + l32) * Lds<D>::KP + ks * 16 + half * 8]));
-      sacc[m] = mfma32(ak, bq[ks], sacc[m]);
-    }
+  for (int n = 0; n < D / 32; ++n) {
+    const int c = 4 * n + 2 * (gi & 1) + (a4 >> 1);
+    o.v[n] = (uint32_t)((r * D + kv_vslot<D>(r, c) * 8 + (a4 & 1) * 4) * 2);
+  }
+  return o;
+}
+
+// S^T = K Q^T of one staged block for this wave's 32 rows (4 key tiles).
+// The K operands of k-step ks+1 are read while the products of step ks run.
+template <int D>
+__device__ __forceinline__ void tile_scores(lds_byte* kb, const OpLane<D>& ol, const bf16x8 (&bq)[D / 16],
+                                            f32x16 (&sacc)[4]) {
+  __builtin_amdgcn_sched_barrier(0);  // phases are scheduled apart: bounds live operand registers
+#pragma unroll
+  for (int t4 = 0; t4 < 4; ++t4)
+    sacc[t4] = f32x16{0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  auto rd = [&](int ks, int t4) {
+    return *reinterpret_cast<__attribute__((address_space(3))) const u32x4*>(kb + ol.k[ks] + t4 * 32 * D * 2);
+  };
+  u32x4 cur[4], nxt[4];
+#pragma unroll
+  for (int t4 = 0; t4 < 4; ++t4) cur[t4] = rd(0, t4);
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) {
+    if (ks + 1 < D / 16)
+#pragma unroll
+      for (int t4 = 0; t4 < 4; ++t4) nxt[t4] = rd(ks + 1, t4);
+#pragma unroll
+    for (int t4 = 0; t4 < 4; ++t4) sacc[t4] = mfma32(as_bf16x8(cur[t4]), bq[ks], sacc[t4]);
+#pragma unroll
+    for (int t4 = 0; t4 < 4; ++t4) cur[t4] = nxt[t4];
   }
 }
 
-// O^T = V^T P^T for 32 rows (ACC: O^T += V^T P^T); P given by the
-// (exponentiated) S^T accumulators.
-template <int D, bool ACC = false>
-__device__ __forceinline__ void block_pv(const Lds<D>& sm, const f32x16 (&sacc)[4], f32x16 (&oacc)[D / 32]) {
-  const int lane = threadIdx.x & 63;
-  const int half = lane >> 5, l32 = lane & 31;
-  bf16x8 pb[8];
+// O^T = V^T P^T (ACC: O^T += V^T P^T) for one staged block.  The V^T
+// operands of k-step kk+1 are read while the products of step kk run.
+template <int D, bool ACC>
+__device__ __forceinline__ void tile_pv(lds_byte* vb, const OpLane<D>& ol, const bf16x8 (&pb)[8],
+                                        f32x16 (&oacc)[D / 32]) {
+  __builtin_amdgcn_sched_barrier(0);
+  if (!ACC)
+#pragma unroll
+    for (int n = 0; n < D / 32; ++n)
+      oacc[n] = f32x16{0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  constexpr int NT = D / 32;
+  auto rd = [&](int kk, int n) {
+    const i16x4 lo = lds_read_tr16(vb + ol.v[n] + (16 * kk) * D * 2);
+    const i16x4 hi = lds_read_tr16(vb + ol.v[n] + (16 * kk + 8) * D * 2);
+    const u32x2 lw = __builtin_bit_cast(u32x2, lo), hw = __builtin_bit_cast(u32x2, hi);
+    return u32x4{lw[0], lw[1], hw[0], hw[1]};
+  };
+  u32x4 cur[NT], nxt[NT];
+#pragma unroll
+  for (int n = 0; n < NT; ++n) cur[n] = rd(0, n);
+#pragma unroll
+  for (int kk = 0; kk < 8; ++kk) {
+    if (kk + 1 < 8)
+#pragma unroll
+      for (int n = 0; n < NT; ++n) nxt[n] = rd(kk + 1, n);
+#pragma unroll
+    for (int n = 0; n < NT; ++n) oacc[n] = mfma32(as_bf16x8(cur[n]), pb[kk], oacc[n]);
+#pragma unroll
+    for (int n = 0; n < NT; ++n) cur[n] = nxt[n];
+  }
+}
+
+// P (the exponentiated S^T accumulators) rounded to bf16 in the key order
+// of the P^T operand: k-step kk holds accumulator registers 8(kk%2)..+7 of
+// key tile kk/2.
+__device__ __forceinline__ void p_operand(const f32x16 (&sacc)[4], bf16x8 (&pb)[8]) {
 #pragma unroll
   for (int kk = 0; kk < 8; ++kk) {
     const f32x16& s = sacc[kk >> 1];
     const int r0 = (kk & 1) * 8;
     pb[kk] = as_bf16x8(u32x4{pack_bf16x2(s[r0 + 0], s[r0 + 1]), pack_bf16x2(s[r0 + 2], s[r0 + 3]),
                              pack_bf16x2(s[r0 + 4], s[r0 + 5]), pack_bf16x2(s[r0 + 6], s[r0 + 7])});
-  }
-#pragma unroll
-  for (int n = 0; n < D / 32; ++n) {
-    __builtin_amdgcn_sched_barrier(0);
-    if (!ACC) oacc[n] = f32x16{0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    const uint16_t* vrow = &sm.vt[(n * 32 + l32) * Lds<D>::VP + half * 4];
-#pragma unroll
-    for (int kk = 0; kk < 8; ++kk) {
-      const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow + kk * 16);
-      const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + kk * 16 + 8);
-      oacc[n] = mfma32(as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]}), pb[kk], oacc[n]);
-    }
   }
 }
 

@@ -79,151 +79,6 @@ __device__ __forceinline__ bool dense_item(const DenseArgs& a, int& tf, int& s, 
   return tf < a.n_tf;
 }
 
-// One staged block: K and V of 128 keys, row-major [key][D], in 16-byte
-// chunks placed at a per-row XOR of their index so that the operand reads
-// touch every bank once per pass:
-//   K (read as 16-byte rows of 16 keys x one chunk): slot = c ^ ((r/RPB) & (CPR-1));
-//   V (read transposed, 4 keys x 4 chunks per 32 lanes): slot = c ^ (((r/RPB) & (CPR/4-1)) << 2),
-// with CPR chunks per row and RPB rows per 256 bytes of banks.  For the rows
-// a lane reads, both XOR terms depend on the lane only, so every operand
-// address is a per-lane base plus a compile-time offset.
-template <int D>
-__device__ __forceinline__ int dense_kslot(int r, int c) {
-  constexpr int CPR = D / 8, RPB = 128 / D;
-  return c ^ ((r / RPB) & (CPR - 1));
-}
-
-template <int D>
-__device__ __forceinline__ int dense_vslot(int r, int c) {
-  constexpr int CPR = D / 8, RPB = 128 / D;
-  return c ^ (((r / RPB) & (CPR / 4 - 1)) << 2);
-}
-
-// Per-lane byte offsets of the block copy: round i moves slots
-// (8i + wave) * 64 + lane of K and of V (row r = slot / CPR), reading the
-// global chunk that belongs in that slot.
-template <int D>
-struct DmaLane {
-  static constexpr int CPR = D / 8;
-  static constexpr int ROUNDS = kBlock * CPR / (64 * kDenseWaves);
-  uint32_t koff[ROUNDS], voff[ROUNDS];  // bytes from the block's first key row
-  int row[ROUNDS];
-};
-
-template <int D>
-__device__ __forceinline__ DmaLane<D> dma_lane(int wave, int lane, int64_t key_stride) {
-  DmaLane<D> d;
-#pragma unroll
-  for (int i = 0; i < DmaLane<D>::ROUNDS; ++i) {
-    const int slot_idx = (i * kDenseWaves + wave) * 64 + lane;
-    const int r = slot_idx / DmaLane<D>::CPR, sl = slot_idx % DmaLane<D>::CPR;
-    d.row[i] = r;
-    d.koff[i] = (uint32_t)((r * key_stride + dense_kslot<D>(r, sl) * 8) * 2);
-    d.voff[i] = (uint32_t)((r * key_stride + dense_vslot<D>(r, sl) * 8) * 2);
-  }
-  return d;
-}
-
-// Asynchronous copy of the K rows (V = false) or V rows (V = true) of one
-// block of group g into a 128 x D LDS matrix with the global->LDS loads
-// (each wave instruction fills 64 consecutive 16-byte slots).  In a block
-// cut short by the end of the sequence, keys at or after `valid` read the
-// last valid key instead: finite data, and always masked since they lie
-// after every query position.
-template <int D, bool V>
-__device__ __forceinline__ void dense_dma(uint16_t* dst, const DmaLane<D>& dl, int wave, const uint16_t* src,
-                                          int64_t key_stride, int valid) {
-  const char* sb = reinterpret_cast<const char*>(src);
-  const bool full = valid == kBlock;
-#pragma unroll
-  for (int i = 0; i < DmaLane<D>::ROUNDS; ++i) {
-    const int run = i * kDenseWaves + wave;
-    uint32_t off = V ? dl.voff[i] : dl.koff[i];
-    if (!full && dl.row[i] >= valid) off -= (uint32_t)((dl.row[i] - (valid - 1)) * key_stride * 2);
-    __builtin_amdgcn_global_load_lds(static_cast<const void*>(sb + off),
-                                     reinterpret_cast<__attribute__((address_space(3))) void*>(
-                                         reinterpret_cast<uintptr_t>(dst + run * 512)),
-                                     16, 0, 0);
-  }
-}
-
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-
-// Transposed LDS read (gfx950 ds_read_b64_tr_b16): within each group of 16
-// lanes, lane 4a+b receives element b of the 4-element row addressed by
-// lane 4j+a, for j = 0..3.
-typedef __attribute__((address_space(3))) const char lds_byte;
-
-// An LDS buffer's address as a run-time value: the operand reads then add
-// one per-lane base to it and fold their constant offsets (a buffer placed
-// at 64 KB or above would otherwise need an extra add per read, its address
-// exceeding the 16-bit offset field).
-__device__ __forceinline__ lds_byte* opaque_lds(const uint16_t* p) {
-  uint32_t a = (uint32_t)reinterpret_cast<uintptr_t>((lds_byte*)p);
-  asm volatile("" : "+s"(a));
-  return (lds_byte*)(uintptr_t)a;
-}
-
-__device__ __forceinline__ i16x4 lds_read_tr16(lds_byte* p) {
-  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(p));
-}
-
-// Per-lane byte offsets of the operand reads within a staged block.
-//   K, k-step ks: row l32 (+ 32 t4), chunk 2ks + half.
-//   V^T, dim tile n: lane (group gi = lane/16, s = lane%16 = 4j + a) addresses
-//   row 4(gi/2) + j (+ 16kk + 8q), dims 32n + 16(gi%2) + 4a .. +3, so the
-//   transposed read hands lane (d = 32n + lane%32, half) keys
-//   16kk + 4half + 8q + {0..3}: the key order of the P^T operand.
-template <int D>
-struct OpLane {
-  uint32_t k[D / 16];
-  uint32_t v[D / 32];
-};
-
-template <int D>
-__device__ __forceinline__ OpLane<D> op_lane(int lane) {
-  OpLane<D> o;
-  const int half = lane >> 5, l32 = lane & 31;
-#pragma unroll
-  for (int ks = 0; ks < D / 16; ++ks) o.k[ks] = (uint32_t)((l32 * D + dense_kslot<D>(l32, 2 * ks + half) * 8) * 2);
-  const int gi = lane >> 4, s16 = lane & 15;
-  const int jr = s16 >> 2, a4 = s16 & 3;
-  const int r = 4 * (gi >> 1) + jr;
-#pragma unroll
-  for (int n = 0; n < D / 32; ++n) {
-    const int c = 4 * n + 2 * (gi & 1) + (a4 >> 1);
-    o.v[n] = (uint32_t)((r * D + dense_vslot<D>(r, c) * 8 + (a4 & 1) * 4) * 2);
-  }
-  return o;
-}
-
-// S^T = K Q^T of one staged block for this wave's 32 rows (4 key tiles).
-// The K operands of k-step ks+1 are read while the products of step ks run.
-template <int D>
-__device__ __forceinline__ void dense_scores(lds_byte* kb, const OpLane<D>& ol, const bf16x8 (&bq)[D / 16],
-                                            f32x16 (&sacc)[4]) {
-  __builtin_amdgcn_sched_barrier(0);  // phases are scheduled apart: bounds live operand registers
-#pragma unroll
-  for (int t4 = 0; t4 < 4; ++t4)
-    sacc[t4] = f32x16{0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  auto rd = [&](int ks, int t4) {
-    return *reinterpret_cast<__attribute__((address_space(3))) const u32x4*>(kb + ol.k[ks] + t4 * 32 * D * 2);
-  };
-  u32x4 cur[4], nxt[4];
-#pragma unroll
-  for (int t4 = 0; t4 < 4; ++t4) cur[t4] = rd(0, t4);
-#pragma unroll
-  for (int ks = 0; ks < D / 16; ++ks) {
-    if (ks + 1 < D / 16)
-#pragma unroll
-      for (int t4 = 0; t4 < 4; ++t4) nxt[t4] = rd(ks + 1, t4);
-#pragma unroll
-    for (int t4 = 0; t4 < 4; ++t4) sacc[t4] = mfma32(as_bf16x8(cur[t4]), bq[ks], sacc[t4]);
-#pragma unroll
-    for (int t4 = 0; t4 < 4; ++t4) cur[t4] = nxt[t4];
-  }
-}
-
 // Mask (keys after the row's position, in the blocks that hold the tile's
 // own positions), online softmax update and P rounded to bf16 in the key
 // order of the P^T operand.  The running maximum is raised only when the
@@ -275,34 +130,6 @@ __device__ __forceinline__ void dense_softmax(f32x16 (&sacc)[4], bool masked, in
   l += sum + swap_halves(sum);
 }
 
-// O^T += V^T P^T for one staged block.  The V^T operands of k-step kk+1
-// are read while the products of step kk run.
-template <int D>
-__device__ __forceinline__ void dense_pv(lds_byte* vb, const OpLane<D>& ol, const bf16x8 (&pb)[8],
-                                        f32x16 (&oacc)[D / 32]) {
-  __builtin_amdgcn_sched_barrier(0);
-  constexpr int NT = D / 32;
-  auto rd = [&](int kk, int n) {
-    const i16x4 lo = lds_read_tr16(vb + ol.v[n] + (16 * kk) * D * 2);
-    const i16x4 hi = lds_read_tr16(vb + ol.v[n] + (16 * kk + 8) * D * 2);
-    const u32x2 lw = __builtin_bit_cast(u32x2, lo), hw = __builtin_bit_cast(u32x2, hi);
-    return u32x4{lw[0], lw[1], hw[0], hw[1]};
-  };
-  u32x4 cur[NT], nxt[NT];
-#pragma unroll
-  for (int n = 0; n < NT; ++n) cur[n] = rd(0, n);
-#pragma unroll
-  for (int kk = 0; kk < 8; ++kk) {
-    if (kk + 1 < 8)
-#pragma unroll
-      for (int n = 0; n < NT; ++n) nxt[n] = rd(kk + 1, n);
-#pragma unroll
-    for (int n = 0; n < NT; ++n) oacc[n] = mfma32(as_bf16x8(cur[n]), pb[kk], oacc[n]);
-#pragma unroll
-    for (int n = 0; n < NT; ++n) cur[n] = nxt[n];
-  }
-}
-
 template <int D>
 __global__ __launch_bounds__(64 * kDenseWaves, 2) void dense_prefill_kernel(DenseArgs a) {
   __shared__ uint16_t k0[kBlock * D], k1[kBlock * D], v0[kBlock * D], v1[kBlock * D];
@@ -345,7 +172,7 @@ __global__ __launch_bounds__(64 * kDenseWaves, 2) void dense_prefill_kernel(Dens
     oacc[n] = f32x16{0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   f32x16 sacc[4];
   bf16x8 pb[8];
-  const DmaLane<D> dl = dma_lane<D>(wave, lane, key_stride);
+  const DmaLane<D, kDenseWaves> dl = dma_lane<D, kDenseWaves>(wave, lane, key_stride);
   const OpLane<D> ol = op_lane<D>(lane);
 
   // Ping-pong schedule.  Barrier interval i computes, per wave, the matrix
@@ -367,7 +194,7 @@ __global__ __launch_bounds__(64 * kDenseWaves, 2) void dense_prefill_kernel(Dens
   int ph_prev = -1;
   int ph_cur = phys_ok(0, __builtin_amdgcn_readlane(pair, 0));
   int ph_next = phys_ok(1, __builtin_amdgcn_readlane(pair, 1));
-  if (ph_cur >= 0) dense_dma<D, false>(k0, dl, wave, p.k + block_src(ph_cur), key_stride, valid_of(0));
+  if (ph_cur >= 0) block_dma<D, kDenseWaves, false>(k0, dl, wave, p.k + block_src(ph_cur), key_stride, valid_of(0));
 
   auto interval = [&](auto parity, int i) {
     constexpr int P = decltype(parity)::value;
@@ -380,15 +207,15 @@ __global__ __launch_bounds__(64 * kDenseWaves, 2) void dense_prefill_kernel(Dens
     if (i >= 1) ph_next = phys_ok(i + 1, __builtin_amdgcn_readlane(pair, 0));
     pair = bt[min(i + 2 + (lane & 1), nb - 1)];
     if (ph_next >= 0)
-      dense_dma<D, false>(knext, dl, wave, p.k + block_src(ph_next), key_stride, valid_of(i + 1));
+      block_dma<D, kDenseWaves, false>(knext, dl, wave, p.k + block_src(ph_next), key_stride, valid_of(i + 1));
     if (i < nb && ph_cur >= 0)
-      dense_dma<D, true>(vcur, dl, wave, p.v + block_src(ph_cur), key_stride, valid_of(i));
+      block_dma<D, kDenseWaves, true>(vcur, dl, wave, p.v + block_src(ph_cur), key_stride, valid_of(i));
     const bool pv = computes(i - 1, ph_prev), sc = i < nb && computes(i, ph_cur);
     // leading: P.V(i-1), S(i), softmax(i); trailing: softmax(i-1), P.V(i-1), S(i)
     if (!lead && pv) dense_softmax<D>(sacc, i - 1 >= first_masked, t - (i - 1) * kBlock, c, m, l, oacc, pb);
-    if (pv) dense_pv<D>(vprev, ol, pb, oacc);
+    if (pv) tile_pv<D, true>(vprev, ol, pb, oacc);
     if (sc) {
-      dense_scores<D>(kcur, ol, bq, sacc);
+      tile_scores<D>(kcur, ol, bq, sacc);
     } else {  // defined on every path: no S value is live across the P.V products
 #pragma unroll
       for (int t4 = 0; t4 < 4; ++t4)
