@@ -123,15 +123,21 @@ def selection_quality(runner, n_rows: int):
 
 
 def dense_attention(runner, n_calls: int):
-    """The dense path on the same batch and cache (msa_dense_attn_prefill:
-    every causal key attended), timed by events over n_calls calls after the
-    timed region; not part of a step.  Gives an in-repo dense attention time
-    to set beside the sparse Main Branch and the whole MSA step."""
+    """The dense path on the same batch and cache (msa_dense_attn_prefill or,
+    for decode, msa_dense_attn_decode: every causal key attended), timed by
+    events over n_calls calls after the timed region; not part of a step.
+    Gives an in-repo dense attention time to set beside the sparse Main
+    Branch and the whole MSA step."""
     import torch
     from block_sparse_long_score_amd import ops
     w = runner.inputs.workload
     out = torch.empty_like(runner.inputs.q)
-    call = lambda: ops.msa_dense_attn_prefill(runner.dims, runner.cache, runner.batch, runner.inputs.q, out)
+    if runner.decode:
+        need = ops.msa_workspace_size(runner.dims, runner.cache, runner.batch, ops.MSA_CALL_DENSE_ATTN_DECODE)
+        ws = torch.empty(need, dtype=torch.uint8, device=out.device)
+        call = lambda: ops.msa_dense_attn_decode(runner.dims, runner.cache, runner.batch, runner.inputs.q, out, ws)
+    else:
+        call = lambda: ops.msa_dense_attn_prefill(runner.dims, runner.cache, runner.batch, runner.inputs.q, out)
     call()  # warm-up
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
@@ -144,6 +150,11 @@ def dense_attention(runner, n_calls: int):
     for n, nq in zip(w.seq_lens, w.q_lens):
         t = np.arange(n - nq, n, dtype=np.float64)
         flops += 4.0 * w.head_dim * w.num_q_heads * float(np.sum(t + 1))
+    if runner.decode:  # HBM-bound: every cached K and V row read once per (sequence, group)
+        kv = sum(2.0 * 2 * w.head_dim * w.num_kv_heads * n for n in w.seq_lens)
+        gbs = kv / (ms / 1e3) / 1e9
+        return {"kernel": "msa_dense_attn_decode (dense_decode_kernel + dense_decode_merge_kernel)", "calls": n_calls,
+                "ms": ms, "algorithmic_bytes": kv, "achieved_gbs": gbs, "hbm_frac": gbs / HBM_PEAK_GBS}
     tflops = flops / (ms / 1e3) / 1e12
     return {"kernel": "msa_dense_attn_prefill (dense_prefill_kernel)", "calls": n_calls, "ms": ms,
             "algorithmic_flops": flops, "achieved_tflops": tflops, "mfma_frac": tflops / BF16_PEAK_TFLOPS}
@@ -227,7 +238,7 @@ def main():
     ap.add_argument("--quality-rows", type=int, default=64,
                     help="query rows (evenly spaced) on which to measure selection quality against dense attention; 0: skip")
     ap.add_argument("--dense-calls", type=int, default=3,
-                    help="prefill workloads: time the dense attention path over this many calls after the timed region (0: skip)")
+                    help="time the dense attention path on the same batch over this many calls after the timed region (0: skip)")
     ap.add_argument("--graph", choices=["on", "off"], default="off",
                     help="replay an unchunked step from a captured HIP graph (stage events then come from a serial pass)")
     args = ap.parse_args()
@@ -362,7 +373,7 @@ def main():
 
     quality = selection_quality(runner, args.quality_rows) if args.quality_rows > 0 else None
     dense = None
-    if not runner.decode and args.dense_calls > 0:
+    if args.dense_calls > 0:
         dense = dense_attention(runner, args.dense_calls)
         dense["msa_attend_speedup"] = dense["ms"] / stage_ms["attend"]
         dense["msa_step_speedup"] = dense["ms"] / ms_per_step

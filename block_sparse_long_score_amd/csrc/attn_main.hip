@@ -557,11 +557,8 @@ __global__ __launch_bounds__(256) void decode_block_kernel(KvOuterArgs a) {
 // Layout of the 16x16x32 operands as in decode_block_kernel.
 template <int D, int GM>
 __global__ __launch_bounds__(1024) void decode_fused_kernel(KvOuterArgs a) {
-  constexpr int VPL = D / 64;            // output dims per lane in P.V
-  constexpr int KS = D / 32;             // MFMA k-steps
-  constexpr int SUB = GM > 8 ? 16 : 32;  // keys per online-softmax step (registers bound it at G = 16)
-  constexpr int MT = SUB / 16;           // 16-key MFMA tiles per step
-  __shared__ float p_s[kTopK][GM][SUB];
+  using W = DecodeWave<D, GM>;
+  __shared__ float p_s[kTopK][GM][W::SUB];
   __shared__ float alpha_s[kTopK][GM];
   __shared__ float m_s[kTopK][GM], l_s[kTopK][GM];
   __shared__ float o_s[kTopK][GM][D];
@@ -572,141 +569,22 @@ __global__ __launch_bounds__(1024) void decode_fused_kernel(KvOuterArgs a) {
   const int r = p.cu_q[s];
   const int64_t R = ((int64_t)r << a.hkv_shift) + g;
   const int t = p.seq_lens[s] - 1;
-  const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int l16 = lane & 15, q16 = lane >> 4;
-  const float c = p.scale_log2e;
   const int b = a.sel[R * kTopK + w];
-  const bool valid = entry_valid(p, s, b, t);
-
-  float m_run = -__builtin_inff(), l_run = 0.f;  // head l16's running max (base 2) and sum
-  float acc[GM][VPL];
-#pragma unroll
-  for (int j = 0; j < GM; ++j)
-#pragma unroll
-    for (int v = 0; v < VPL; ++v) acc[j][v] = 0.f;
-
-  if (valid) {
+  W st;
+  if (entry_valid(p, s, b, t)) {
     const int phys = p.block_table[(int64_t)s * p.max_blocks_per_seq + b];
-    const int nvalid = min(kBlock, t - b * kBlock + 1);
-    const int64_t key_stride = (int64_t)p.hkv * D;
-    const uint16_t* kb = p.k + ((int64_t)phys * kBlock * p.hkv + g) * D;
-    const uint16_t* vb = p.v + ((int64_t)phys * kBlock * p.hkv + g) * D;
-    const uint16_t* qh = a.q + ((int64_t)r * p.hq + g * G + l16) * D;
-    // Loads below read from in-range addresses unconditionally and zero what
-    // is out of range afterwards, so they issue as one batch without branches.
-    const bool head_ok = l16 < G;
-    const uint16_t* qh_c = head_ok ? qh : qh - (int64_t)(l16 - G + 1) * D;  // head G-1
-    bf16x8 bq[KS];
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const u32x4 x = load16(qh_c + ks * 32 + q16 * 8);
-      bq[ks] = as_bf16x8(head_ok ? x : u32x4{0u, 0u, 0u, 0u});
-    }
-
-    for (int c0 = 0; c0 < nvalid; c0 += SUB) {
-      uint32_t vreg[SUB];
-#pragma unroll
-      for (int k = 0; k < SUB; ++k) {
-        const int key = min(c0 + k, nvalid - 1);
-        if constexpr (VPL == 2)
-          vreg[k] = *reinterpret_cast<const uint32_t*>(vb + key * key_stride + lane * 2);
-        else
-          vreg[k] = (uint32_t)vb[key * key_stride + lane];
-      }
-#pragma unroll
-      for (int k = 0; k < SUB; ++k) vreg[k] = c0 + k < nvalid ? vreg[k] : 0u;
-      float sc[4 * MT];
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        const int key = c0 + mt * 16 + l16;
-        const uint16_t* krow = kb + min(key, nvalid - 1) * key_stride + q16 * 8;
-        bf16x8 ak[KS];
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          const u32x4 x = load16(krow + ks * 32);
-          ak[ks] = as_bf16x8(key < nvalid ? x : u32x4{0u, 0u, 0u, 0u});
-        }
-        f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak[ks], bq[ks], sacc, 0, 0, 0);
-        // lane (head l16, q16) holds keys c0 + mt*16 + 4*q16 + i
-#pragma unroll
-        for (int i = 0; i < 4; ++i) sc[mt * 4 + i] = c0 + mt * 16 + 4 * q16 + i < nvalid ? sacc[i] : -__builtin_inff();
-      }
-      float mx = sc[0];
-#pragma unroll
-      for (int e = 1; e < 4 * MT; ++e) mx = fmaxf(mx, sc[e]);
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m_run, mx * c);  // finite: key c0 is valid
-      const float alpha = fast_exp2(m_run - m_new);
-      float psum = 0.f;
-#pragma unroll
-      for (int e = 0; e < 4 * MT; ++e) {
-        const float pe = fast_exp2(fmaf(sc[e], c, -m_new));
-        psum += pe;
-        if (l16 < GM) p_s[w][l16][(e >> 2) * 16 + 4 * q16 + (e & 3)] = pe;
-      }
-      psum += __shfl_xor(psum, 16);
-      psum += __shfl_xor(psum, 32);
-      l_run = fmaf(l_run, alpha, psum);
-      m_run = m_new;
-      if (q16 == 0 && l16 < GM) alpha_s[w][l16] = alpha;
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-#pragma unroll
-      for (int j = 0; j < GM; ++j) {
-        const float al = alpha_s[w][j];
-#pragma unroll
-        for (int v = 0; v < VPL; ++v) acc[j][v] *= al;
-      }
-#pragma unroll
-      for (int k4 = 0; k4 < SUB / 4; ++k4) {
-        __builtin_amdgcn_sched_barrier(0);  // four keys at a time: bounds live P and V registers
-        float vv[4][VPL];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          vv[i][0] = bf16_to_f32(vreg[k4 * 4 + i] & 0xffffu);
-          if constexpr (VPL == 2) vv[i][1] = bf16_to_f32(vreg[k4 * 4 + i] >> 16);
-        }
-#pragma unroll
-        for (int j = 0; j < GM; ++j) {
-          const f32x4 pj = *reinterpret_cast<const f32x4*>(&p_s[w][j][k4 * 4]);
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int v = 0; v < VPL; ++v) acc[j][v] = fmaf(pj[i], vv[i][v], acc[j][v]);
-        }
-      }
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-    }
+    bf16x8 bq[W::KS];
+    st.load_q(a.q + ((int64_t)r * p.hq + g * G) * D, G, bq);
+    st.attend_block(p.k, p.v, ((int64_t)phys * kBlock * p.hkv + g) * D, (int64_t)p.hkv * D,
+                    min(kBlock, t - b * kBlock + 1), bq, p.scale_log2e, p_s[w], alpha_s[w]);
   }
-#pragma unroll
-  for (int j = 0; j < GM; ++j)
-#pragma unroll
-    for (int v = 0; v < VPL; ++v) o_s[w][j][lane * VPL + v] = acc[j][v];
-  if (q16 == 0 && l16 < GM) {
-    m_s[w][l16] = m_run;  // -inf and 0 for a slot that is not attended
-    l_s[w][l16] = l_run;
-  }
+  st.store(o_s[w], m_s[w], l_s[w]);
   __syncthreads();
   for (int idx = threadIdx.x; idx < G * (D / 2); idx += blockDim.x) {
     const int j = idx / (D / 2), d = (idx - j * (D / 2)) * 2;
-    float M = -__builtin_inff();
-#pragma unroll
-    for (int ww = 0; ww < kTopK; ++ww) M = fmaxf(M, m_s[ww][j]);
-    float L = 0.f, o0 = 0.f, o1 = 0.f;
-#pragma unroll
-    for (int ww = 0; ww < kTopK; ++ww) {
-      const float f = l_s[ww][j] > 0.f ? fast_exp2(m_s[ww][j] - M) : 0.f;
-      L = fmaf(l_s[ww][j], f, L);
-      o0 = fmaf(o_s[ww][j][d], f, o0);
-      o1 = fmaf(o_s[ww][j][d + 1], f, o1);
-    }
+    float o0, o1, L, M;
+    combine_waves<D, GM, kTopK>(o_s, m_s, l_s, j, d, o0, o1, L, M);
     const float inv = L > 0.f ? 1.0f / L : 0.f;
     *reinterpret_cast<uint32_t*>(a.out_direct + ((int64_t)r * p.hq + g * G + j) * D + d) = pack_bf16x2(o0 * inv, o1 * inv);
   }

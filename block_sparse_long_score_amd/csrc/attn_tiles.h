@@ -282,4 +282,172 @@ __device__ __forceinline__ void q_operand(const QRaw<D>& raw, bf16x8 (&bq)[D / 1
   }
 }
 
+// ------------------------------------------------------ decode, one wave
+
+// One wave attends a decode query's G heads (G <= GM <= 16) to the keys of
+// one block after another, keeping a running softmax state.  Scores use the
+// 16x16x32 bf16 MFMA with 16 keys on M (K rows read straight from the cache)
+// and the heads on N (padded to 16); P.V uses vector ALU math with each lane
+// owning D/64 output dims.  16x16x32 lane layout: A lane l holds
+// A[l%16][8*(l/16) .. +7], B lane l holds B[8*(l/16) .. +7][l%16], D lane l
+// register i holds D[4*(l/16) + i][l%16].
+template <int D, int GM>
+struct DecodeWave {
+  static constexpr int VPL = D / 64;            // output dims per lane in P.V
+  static constexpr int KS = D / 32;             // MFMA k-steps
+  static constexpr int SUB = GM > 8 ? 16 : 32;  // keys per online-softmax step (registers bound it at G = 16)
+  static constexpr int MT = SUB / 16;           // 16-key MFMA tiles per step
+  float m_run = -__builtin_inff(), l_run = 0.f;  // head l16's running max (base 2) and sum
+  float acc[GM][VPL];
+
+  __device__ DecodeWave() {
+#pragma unroll
+    for (int j = 0; j < GM; ++j)
+#pragma unroll
+      for (int v = 0; v < VPL; ++v) acc[j][v] = 0.f;
+  }
+
+  // The B operand: head l16 of the group (heads G.. are zero), dims of k-step ks.
+  // Loads read from in-range addresses unconditionally and zero what is out
+  // of range afterwards, so they issue as one batch without branches.
+  __device__ __forceinline__ void load_q(const uint16_t* q_group, int G, bf16x8 (&bq)[KS]) const {
+    const int lane = threadIdx.x & 63;
+    const int l16 = lane & 15, q16 = lane >> 4;
+    const bool head_ok = l16 < G;
+    const uint16_t* qh = q_group + (int64_t)min(l16, G - 1) * D;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const u32x4 x = load16(qh + ks * 32 + q16 * 8);
+      bq[ks] = as_bf16x8(head_ok ? x : u32x4{0u, 0u, 0u, 0u});
+    }
+  }
+
+  // Keys [0, nvalid) of the block whose head-g rows start at k + base / v + base.
+  // p_w, alpha_w: this wave's LDS scratch for the P rows and the rescale factors.
+  __device__ __forceinline__ void attend_block(const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+                                               int64_t base, int64_t key_stride, int nvalid, const bf16x8 (&bq)[KS],
+                                               float c, float (&p_w)[GM][SUB], float (&alpha_w)[GM]) {
+    const int lane = threadIdx.x & 63;
+    const int l16 = lane & 15, q16 = lane >> 4;
+    const uint16_t* kb = k + base;
+    const uint16_t* vb = v + base;
+    for (int c0 = 0; c0 < nvalid; c0 += SUB) {
+      uint32_t vreg[SUB];
+#pragma unroll
+      for (int kk = 0; kk < SUB; ++kk) {
+        const int key = min(c0 + kk, nvalid - 1);
+        if constexpr (VPL == 2)
+          vreg[kk] = *reinterpret_cast<const uint32_t*>(vb + key * key_stride + lane * 2);
+        else
+          vreg[kk] = (uint32_t)vb[key * key_stride + lane];
+      }
+#pragma unroll
+      for (int kk = 0; kk < SUB; ++kk) vreg[kk] = c0 + kk < nvalid ? vreg[kk] : 0u;
+      float sc[4 * MT];
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const int key = c0 + mt * 16 + l16;
+        const uint16_t* krow = kb + min(key, nvalid - 1) * key_stride + q16 * 8;
+        bf16x8 ak[KS];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          const u32x4 x = load16(krow + ks * 32);
+          ak[ks] = as_bf16x8(key < nvalid ? x : u32x4{0u, 0u, 0u, 0u});
+        }
+        f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak[ks], bq[ks], sacc, 0, 0, 0);
+        // lane (head l16, q16) holds keys c0 + mt*16 + 4*q16 + i
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sc[mt * 4 + i] = c0 + mt * 16 + 4 * q16 + i < nvalid ? sacc[i] : -__builtin_inff();
+      }
+      float mx = sc[0];
+#pragma unroll
+      for (int e = 1; e < 4 * MT; ++e) mx = fmaxf(mx, sc[e]);
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float m_new = fmaxf(m_run, mx * c);  // finite: key c0 is valid
+      const float alpha = fast_exp2(m_run - m_new);
+      float psum = 0.f;
+#pragma unroll
+      for (int e = 0; e < 4 * MT; ++e) {
+        const float pe = fast_exp2(fmaf(sc[e], c, -m_new));
+        psum += pe;
+        if (l16 < GM) p_w[l16][(e >> 2) * 16 + 4 * q16 + (e & 3)] = pe;
+      }
+      psum += __shfl_xor(psum, 16);
+      psum += __shfl_xor(psum, 32);
+      l_run = fmaf(l_run, alpha, psum);
+      m_run = m_new;
+      if (q16 == 0 && l16 < GM) alpha_w[l16] = alpha;
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+#pragma unroll
+      for (int j = 0; j < GM; ++j) {
+        const float al = alpha_w[j];
+#pragma unroll
+        for (int vv = 0; vv < VPL; ++vv) acc[j][vv] *= al;
+      }
+#pragma unroll
+      for (int k4 = 0; k4 < SUB / 4; ++k4) {
+        __builtin_amdgcn_sched_barrier(0);  // four keys at a time: bounds live P and V registers
+        float vf[4][VPL];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          vf[i][0] = bf16_to_f32(vreg[k4 * 4 + i] & 0xffffu);
+          if constexpr (VPL == 2) vf[i][1] = bf16_to_f32(vreg[k4 * 4 + i] >> 16);
+        }
+#pragma unroll
+        for (int j = 0; j < GM; ++j) {
+          const f32x4 pj = *reinterpret_cast<const f32x4*>(&p_w[j][k4 * 4]);
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int vv = 0; vv < VPL; ++vv) acc[j][vv] = fmaf(pj[i], vf[i][vv], acc[j][vv]);
+        }
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    }
+  }
+
+  // This wave's unnormalised output rows and softmax state into LDS for the
+  // combine (-inf and 0 for a wave that attended nothing).
+  __device__ __forceinline__ void store(float (&o_w)[GM][D], float (&m_w)[GM], float (&l_w)[GM]) const {
+    const int lane = threadIdx.x & 63;
+    const int l16 = lane & 15, q16 = lane >> 4;
+#pragma unroll
+    for (int j = 0; j < GM; ++j)
+#pragma unroll
+      for (int v = 0; v < VPL; ++v) o_w[j][lane * VPL + v] = acc[j][v];
+    if (q16 == 0 && l16 < GM) {
+      m_w[l16] = m_run;
+      l_w[l16] = l_run;
+    }
+  }
+};
+
+// Log-sum-exp combine of NW waves' states for head j, dims d and d+1: the
+// unnormalised sums (o0, o1) and the mass L, both relative to 2^M.
+template <int D, int GM, int NW>
+__device__ __forceinline__ void combine_waves(const float (&o_s)[NW][GM][D], const float (&m_s)[NW][GM],
+                                              const float (&l_s)[NW][GM], int j, int d, float& o0, float& o1,
+                                              float& L, float& M) {
+  M = -__builtin_inff();
+#pragma unroll
+  for (int ww = 0; ww < NW; ++ww) M = fmaxf(M, m_s[ww][j]);
+  L = 0.f;
+  o0 = 0.f;
+  o1 = 0.f;
+#pragma unroll
+  for (int ww = 0; ww < NW; ++ww) {
+    const float f = l_s[ww][j] > 0.f ? fast_exp2(m_s[ww][j] - M) : 0.f;
+    L = fmaf(l_s[ww][j], f, L);
+    o0 = fmaf(o_s[ww][j][d], f, o0);
+    o1 = fmaf(o_s[ww][j][d + 1], f, o1);
+  }
+}
+
 }  // namespace msa

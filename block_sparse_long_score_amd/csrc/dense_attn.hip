@@ -264,6 +264,139 @@ __global__ __launch_bounds__(64 * kDenseWaves, 2) void dense_prefill_kernel(Dens
   }
 }
 
+// ------------------------------------------------------------------ decode
+
+// Dense decode: one query row per sequence attends to its whole context.
+// Schedule: one 16-wave workgroup per (sequence, group, split of 64 blocks);
+// the waves take the split's blocks in turn (wave w: blocks w, w+16, ...),
+// each keeping a running softmax over its blocks (DecodeWave: scores on the
+// 16x16x32 MFMA with the group's heads on N, P.V on the vector ALU), and
+// combine in LDS into the split's normalised output and log2 mass.  A merge
+// pass combines the splits.  HBM-bound: every K and V row of the context is
+// read once per (sequence, group).
+constexpr int kDecodeWaves = 16;
+constexpr int kDecodeSplit = 64;  // blocks per workgroup
+
+struct DenseDecodeArgs {
+  Problem p;
+  const uint16_t* q;
+  float* part_o;    // [num_seqs][hkv][n_split][G][D]: the split's normalised output
+  float* part_lse;  // [num_seqs][hkv][n_split][G]: log2 of the split's softmax mass, in the units of the scores
+  uint16_t* out;
+  int n_split;
+};
+
+template <int D, int GM>
+__global__ __launch_bounds__(64 * kDecodeWaves) void dense_decode_kernel(DenseDecodeArgs a) {
+  using W = DecodeWave<D, GM>;
+  __shared__ float p_s[kDecodeWaves][GM][W::SUB];
+  __shared__ float alpha_s[kDecodeWaves][GM];
+  __shared__ float m_s[kDecodeWaves][GM], l_s[kDecodeWaves][GM];
+  __shared__ float o_s[kDecodeWaves][GM][D];
+  const Problem& p = a.p;
+  const int G = p.group;
+  const int split = blockIdx.x, g = blockIdx.y, s = blockIdx.z;
+  const int t = p.seq_lens[s] - 1;
+  const int nb = (t >> 7) + 1;
+  const int b0 = split * kDecodeSplit;
+  if (b0 >= nb) return;
+  const int r = p.cu_q[s];
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int32_t* bt = p.block_table + (int64_t)s * p.max_blocks_per_seq;
+  W st;
+  {
+    bf16x8 bq[W::KS];
+    st.load_q(a.q + ((int64_t)r * p.hq + g * G) * D, G, bq);
+    const int b_end = min(b0 + kDecodeSplit, nb);
+    for (int b = b0 + w; b < b_end; b += kDecodeWaves) {
+      const int phys = bt[b];
+      if (phys < 0 || phys >= p.num_blocks) continue;  // absent blocks hold no keys
+      st.attend_block(p.k, p.v, ((int64_t)phys * kBlock * p.hkv + g) * D, (int64_t)p.hkv * D,
+                      min(kBlock, t - b * kBlock + 1), bq, p.scale_log2e, p_s[w], alpha_s[w]);
+    }
+  }
+  st.store(o_s[w], m_s[w], l_s[w]);
+  __syncthreads();
+  const int64_t part = (((int64_t)s * p.hkv + g) * a.n_split + split) * G;
+  for (int idx = threadIdx.x; idx < G * (D / 2); idx += blockDim.x) {
+    const int j = idx / (D / 2), d = (idx - j * (D / 2)) * 2;
+    float o0, o1, L, M;
+    combine_waves<D, GM, kDecodeWaves>(o_s, m_s, l_s, j, d, o0, o1, L, M);
+    const float inv = L > 0.f ? 1.0f / L : 0.f;
+    *reinterpret_cast<f32x2*>(a.part_o + (part + j) * D + d) = f32x2{o0 * inv, o1 * inv};
+    if (d == 0) a.part_lse[part + j] = L > 0.f ? M + __log2f(L) : -__builtin_inff();
+  }
+}
+
+// Merge of the splits: per (sequence, head, dim pair) a log-sum-exp over the
+// sequence's splits, rounded to bf16.
+template <int D>
+__global__ __launch_bounds__(256) void dense_decode_merge_kernel(DenseDecodeArgs a) {
+  const Problem& p = a.p;
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t per_seq = (int64_t)p.hq * (D / 2);
+  if (idx >= per_seq * p.num_seqs) return;
+  const int s = (int)(idx / per_seq);
+  const int rem = (int)(idx - s * per_seq);
+  const int h = rem / (D / 2), d = (rem - h * (D / 2)) * 2;
+  const int G = p.group;
+  const int g = h / G, j = h - g * G;
+  const int nb = ((p.seq_lens[s] - 1) >> 7) + 1;
+  const int nsp = (nb + kDecodeSplit - 1) / kDecodeSplit;
+  const int64_t part0 = ((int64_t)s * p.hkv + g) * a.n_split * G + j;
+  float M = -__builtin_inff();
+  for (int sp = 0; sp < nsp; ++sp) M = fmaxf(M, a.part_lse[part0 + (int64_t)sp * G]);
+  float L = 0.f, o0 = 0.f, o1 = 0.f;
+  for (int sp = 0; sp < nsp; ++sp) {
+    const float lse = a.part_lse[part0 + (int64_t)sp * G];
+    const float f = lse > -__builtin_inff() ? fast_exp2(lse - M) : 0.f;
+    const f32x2 o = *reinterpret_cast<const f32x2*>(a.part_o + (part0 + (int64_t)sp * G) * D + d);
+    L += f;
+    o0 = fmaf(f, o[0], o0);
+    o1 = fmaf(f, o[1], o1);
+  }
+  const float inv = L > 0.f ? 1.0f / L : 0.f;
+  *reinterpret_cast<uint32_t*>(a.out + ((int64_t)p.cu_q[s] * p.hq + h) * D + d) = pack_bf16x2(o0 * inv, o1 * inv);
+}
+
+static int decode_splits(const Problem& p, int max_ctx_blocks) {
+  return std::max(1, (max_ctx_blocks + kDecodeSplit - 1) / kDecodeSplit);
+}
+
+size_t dense_decode_workspace_bytes(const Problem& p, int max_ctx_blocks) {
+  const int64_t parts = (int64_t)p.num_seqs * p.hkv * decode_splits(p, max_ctx_blocks) * p.group;
+  const size_t o = ((sizeof(float) * parts * p.head_dim) + 255) & ~(size_t)255;
+  return o + sizeof(float) * parts;
+}
+
+template <int D>
+static void launch_dense_decode_t(const DenseDecodeArgs& a, hipStream_t stream) {
+  const dim3 grid(a.n_split, a.p.hkv, a.p.num_seqs);
+  if (a.p.group <= 4)
+    hipLaunchKernelGGL((dense_decode_kernel<D, 4>), grid, dim3(64 * kDecodeWaves), 0, stream, a);
+  else if (a.p.group <= 8)
+    hipLaunchKernelGGL((dense_decode_kernel<D, 8>), grid, dim3(64 * kDecodeWaves), 0, stream, a);
+  else
+    hipLaunchKernelGGL((dense_decode_kernel<D, 16>), grid, dim3(64 * kDecodeWaves), 0, stream, a);
+  const int64_t threads = (int64_t)a.p.num_seqs * a.p.hq * (D / 2);
+  hipLaunchKernelGGL(dense_decode_merge_kernel<D>, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream, a);
+}
+
+hipError_t launch_dense_decode(const Problem& p, const uint16_t* q, uint16_t* out, void* ws, int max_ctx_blocks,
+                               hipStream_t stream) {
+  if (p.total_q == 0) return hipSuccess;
+  const int n_split = decode_splits(p, max_ctx_blocks);
+  const int64_t parts = (int64_t)p.num_seqs * p.hkv * n_split * p.group;
+  char* base = static_cast<char*>(ws);
+  const size_t o_bytes = ((sizeof(float) * parts * p.head_dim) + 255) & ~(size_t)255;
+  const DenseDecodeArgs a{p, q, reinterpret_cast<float*>(base), reinterpret_cast<float*>(base + o_bytes), out, n_split};
+  if (p.head_dim == 128)
+    launch_dense_decode_t<128>(a, stream);
+  else
+    launch_dense_decode_t<64>(a, stream);
+  return hipGetLastError();
+}
+
 int64_t dense_prefill_grid(const Problem& p) {
   const int64_t n_tf = (p.max_q_per_seq + kDenseRows - 1) / kDenseRows;
   if (p.hkv >= 8) return n_tf * p.num_seqs * p.hq;

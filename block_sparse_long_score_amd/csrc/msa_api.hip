@@ -156,6 +156,14 @@ msa_status check_prefill_capacity(const msa_dims* dims, const msa_cache* cache, 
   return MSA_OK;
 }
 
+msa_status check_one_query_per_sequence(const msa_batch* batch) {
+  for (int s = 0; s < batch->num_seqs; ++s)
+    if (batch->cu_q_host[s + 1] - batch->cu_q_host[s] != 1)
+      return fail(MSA_ERR_BAD_SHAPE, "decode needs exactly one query per sequence (sequence %d has %d)", s,
+                  batch->cu_q_host[s + 1] - batch->cu_q_host[s]);
+  return MSA_OK;
+}
+
 msa_status check_attn(const msa_dims* dims, const msa_cache* cache, const msa_batch* batch, const void* q,
                       const int32_t* sel, void* out) {
   MSA_TRY(check_dims(dims));
@@ -291,6 +299,25 @@ msa_status msa_dense_attn_prefill(const msa_dims* dims, const msa_cache* cache, 
                     "msa_dense_attn_prefill launch");
 }
 
+msa_status msa_dense_attn_decode(const msa_dims* dims, const msa_cache* cache, const msa_batch* batch,
+                                 const void* q, void* out, void* workspace, size_t ws_bytes, void* stream) {
+  MSA_TRY(check_dims(dims));
+  MSA_TRY(check_cache(cache));
+  MSA_TRY(check_batch(dims, batch, cache));
+  MSA_TRY(check_ptr(q, "q"));
+  MSA_TRY(check_ptr(out, "out"));
+  MSA_TRY(check_one_query_per_sequence(batch));
+  const msa::Problem p = make_problem(dims, batch, cache);
+  const int max_blocks = (int)max_query_blocks(batch);
+  const size_t need = msa::dense_decode_workspace_bytes(p, max_blocks);
+  if (!workspace || ws_bytes < need)
+    return fail(MSA_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace ? ws_bytes : 0, need);
+  if (!aligned16(workspace)) return fail(MSA_ERR_MISALIGNED, "workspace is not 16-byte aligned");
+  return hip_status(msa::launch_dense_decode(p, static_cast<const uint16_t*>(q), static_cast<uint16_t*>(out),
+                                             workspace, max_blocks, static_cast<hipStream_t>(stream)),
+                    "msa_dense_attn_decode launch");
+}
+
 size_t msa_workspace_size(const msa_dims* dims, const msa_cache* cache, const msa_batch* batch, int32_t call) {
   if (check_dims(dims) != MSA_OK || check_cache(cache) != MSA_OK || check_batch(dims, batch, cache) != MSA_OK)
     return 0;
@@ -301,6 +328,7 @@ size_t msa_workspace_size(const msa_dims* dims, const msa_cache* cache, const ms
       ok();
       return msa::prefill_workspace_bytes(p);
     case MSA_CALL_SPARSE_ATTN_DECODE: ok(); return msa::decode_workspace_bytes(p);
+    case MSA_CALL_DENSE_ATTN_DECODE: ok(); return msa::dense_decode_workspace_bytes(p, (int)max_query_blocks(batch));
   }
   fail(MSA_ERR_BAD_SHAPE, "unknown call id %d", call);
   return 0;
@@ -323,10 +351,7 @@ msa_status msa_sparse_attn_prefill(const msa_dims* dims, const msa_cache* cache,
 msa_status msa_sparse_attn_decode(const msa_dims* dims, const msa_cache* cache, const msa_batch* batch, const void* q,
                                   const int32_t* sel, void* out, void* workspace, size_t ws_bytes, void* stream) {
   MSA_TRY(check_attn(dims, cache, batch, q, sel, out));
-  for (int s = 0; s < batch->num_seqs; ++s)
-    if (batch->cu_q_host[s + 1] - batch->cu_q_host[s] != 1)
-      return fail(MSA_ERR_BAD_SHAPE, "decode needs exactly one query per sequence (sequence %d has %d)", s,
-                  batch->cu_q_host[s + 1] - batch->cu_q_host[s]);
+  MSA_TRY(check_one_query_per_sequence(batch));
   const msa::Problem p = make_problem(dims, batch, cache);
   const size_t need = msa::decode_workspace_bytes(p);
   if (!workspace || ws_bytes < need)

@@ -62,4 +62,10 @@ hipError_t launch_attn_decode(const Problem& p, const uint16_t* q, const int32_t
 // Dense causal attention over the same cache (queries outer, no workspace).
 hipError_t launch_dense_prefill(const Problem& p, const uint16_t* q, uint16_t* out, hipStream_t stream);
 
+// Dense decode (one query per sequence, context split over workgroups and
+// merged); max_ctx_blocks: blocks of the longest context (host-side).
+size_t dense_decode_workspace_bytes(const Problem& p, int max_ctx_blocks);
+hipError_t launch_dense_decode(const Problem& p, const uint16_t* q, uint16_t* out, void* ws, int max_ctx_blocks,
+                               hipStream_t stream);
+
 }  // namespace msa

@@ -14,11 +14,13 @@ import numpy as np
 import torch
 
 from . import _lib
-from ._lib import MSA_CALL_SPARSE_ATTN_DECODE, MSA_CALL_SPARSE_ATTN_PREFILL, MsaBatch, MsaCache, MsaDims
+from ._lib import (MSA_CALL_DENSE_ATTN_DECODE, MSA_CALL_SPARSE_ATTN_DECODE, MSA_CALL_SPARSE_ATTN_PREFILL, MsaBatch,
+                   MsaCache, MsaDims)
 
 __all__ = ["Dims", "Cache", "Batch", "MsaError", "msa_kv_append", "msa_index_score", "msa_block_topk",
-           "msa_sparse_attn_prefill", "msa_sparse_attn_decode", "msa_workspace_size", "msa_abi_version",
-           "MSA_CALL_SPARSE_ATTN_PREFILL", "MSA_CALL_SPARSE_ATTN_DECODE"]
+           "msa_sparse_attn_prefill", "msa_sparse_attn_decode", "msa_dense_attn_prefill", "msa_dense_attn_decode",
+           "msa_block_attn_mass", "msa_selection_quality", "msa_workspace_size", "msa_abi_version",
+           "MSA_CALL_SPARSE_ATTN_PREFILL", "MSA_CALL_SPARSE_ATTN_DECODE", "MSA_CALL_DENSE_ATTN_DECODE"]
 
 
 class MsaError(RuntimeError):
@@ -177,6 +179,16 @@ def msa_dense_attn_prefill(dims: Dims, cache: Cache, batch: Batch, q, out, strea
     d, c, b = dims.c(), cache.c(), batch.c()
     _check(L.msa_dense_attn_prefill(ctypes.byref(d), ctypes.byref(c), ctypes.byref(b), _ptr(q, "q", torch.bfloat16),
                                     _ptr(out, "out", torch.bfloat16), _stream(stream)))
+
+
+def msa_dense_attn_decode(dims: Dims, cache: Cache, batch: Batch, q, out, workspace, stream=None):
+    """Dense attention of one query row per sequence over its whole context; out: bf16 [num_seqs, Hq, D].
+    workspace: uint8, at least msa_workspace_size(..., MSA_CALL_DENSE_ATTN_DECODE) bytes."""
+    L = _lib.load()
+    d, c, b = dims.c(), cache.c(), batch.c()
+    _check(L.msa_dense_attn_decode(ctypes.byref(d), ctypes.byref(c), ctypes.byref(b), _ptr(q, "q", torch.bfloat16),
+                                   _ptr(out, "out", torch.bfloat16), _ptr(workspace, "workspace", torch.uint8),
+                                   workspace.numel(), _stream(stream)))
 
 
 def msa_block_attn_mass(dims: Dims, cache: Cache, batch: Batch, q, rows, mass, stream=None):

@@ -124,7 +124,8 @@ typedef struct msa_batch {
 /* Which call msa_workspace_size() sizes. */
 typedef enum msa_call {
   MSA_CALL_SPARSE_ATTN_PREFILL = 1,
-  MSA_CALL_SPARSE_ATTN_DECODE = 2
+  MSA_CALL_SPARSE_ATTN_DECODE = 2,
+  MSA_CALL_DENSE_ATTN_DECODE = 3
 } msa_call;
 
 /* ------------------------------------------------------------------------- *
@@ -274,6 +275,21 @@ msa_status msa_selection_quality(const msa_dims* dims, const msa_batch* batch, c
  * ------------------------------------------------------------------------- */
 msa_status msa_dense_attn_prefill(const msa_dims* dims, const msa_cache* cache, const msa_batch* batch,
                                   const void* q, void* out, void* stream);
+
+/* ------------------------------------------------------------------------- *
+ * msa_dense_attn_decode — msa_dense_attn_prefill for one query row per
+ * sequence (cu_q[s+1] - cu_q[s] == 1 for every s; BAD_SHAPE otherwise):
+ * the context is split over workgroups of 64 blocks and the splits merged
+ * by log-sum-exp.
+ *   q, out    : as msa_dense_attn_prefill
+ *   workspace : device scratch of at least
+ *               msa_workspace_size(dims, cache, batch, MSA_CALL_DENSE_ATTN_DECODE)
+ *               bytes; its contents on entry are ignored.
+ * Errors: NULL_POINTER, BAD_SHAPE, UNSUPPORTED, MISALIGNED, CAPACITY,
+ *         WORKSPACE, HIP.
+ * ------------------------------------------------------------------------- */
+msa_status msa_dense_attn_decode(const msa_dims* dims, const msa_cache* cache, const msa_batch* batch,
+                                 const void* q, void* out, void* workspace, size_t ws_bytes, void* stream);
 
 /* Bytes of workspace `call` needs for this problem; 0 if the arguments are
  * invalid (the failing check is reported by msa_last_error()). */

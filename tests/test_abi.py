@@ -170,3 +170,23 @@ def test_dense_attention_validates_on_the_host(lib):
     assert lib.msa_dense_attn_prefill(dp, cp, ctypes.byref(bad.c), FAKE, FAKE, None) == SHAPE
     empty = _Batch([100, 5], [0, 0])
     assert lib.msa_dense_attn_prefill(dp, cp, ctypes.byref(empty.c), FAKE, FAKE, None) == OK  # nothing to do
+
+
+def test_dense_decode_validates_on_the_host(lib):
+    d, c = _dims(), _cache()
+    b = _Batch([1024, 900], [1, 1])
+    dp, cp, bp = ctypes.byref(d), ctypes.byref(c), ctypes.byref(b.c)
+    need = lib.msa_workspace_size(dp, cp, bp, 3)
+    # 2 sequences x 8 groups x 1 split x 6 heads: fp32 rows of 128 dims plus one log-mass each
+    assert need >= 2 * 8 * 6 * (128 + 1) * 4
+    assert lib.msa_dense_attn_decode(dp, cp, bp, None, FAKE, FAKE, need, None) == NULLP
+    assert lib.msa_dense_attn_decode(dp, cp, bp, FAKE, FAKE, FAKE, need - 1, None) == WS
+    assert lib.msa_dense_attn_decode(dp, cp, bp, FAKE, FAKE, None, need, None) == WS
+    assert lib.msa_dense_attn_decode(dp, cp, bp, FAKE, FAKE, FAKE + 8, need, None) == MISAL
+    two = _Batch([1024, 900], [2, 1])  # decode takes one query per sequence
+    assert lib.msa_dense_attn_decode(dp, cp, ctypes.byref(two.c), FAKE, FAKE, FAKE, need, None) == SHAPE
+    # one partial per 64-block split of the context
+    big = _cache(mbps=192)
+    one = lib.msa_workspace_size(dp, ctypes.byref(big), ctypes.byref(_Batch([1024], [1]).c), 3)
+    three = lib.msa_workspace_size(dp, ctypes.byref(big), ctypes.byref(_Batch([128 * 64 * 3], [1]).c), 3)
+    assert 2.9 * one < three < 3.1 * one

@@ -131,3 +131,54 @@ def test_dense_c3_full_size_sampled_rows():
     pos = np.unique(np.concatenate([[0, 128, 65535, 131071], rng.integers(0, 131072, 20)]))
     _compare(runner, out, 0, pos)
     assert torch.isfinite(out.float()).all()
+
+
+def _dense_decode(w):
+    _announce(f"dense decode {w.name}: seq_lens={w.seq_lens[:4]}{'...' if w.num_seqs > 4 else ''} "
+              f"Hq={w.num_q_heads} Hkv={w.num_kv_heads} D={w.head_dim}")
+    runner = MsaRunner(make_inputs(w, "cuda"))
+    runner.append()
+    out = torch.full_like(runner.inputs.q, float("nan"))
+    need = ops.msa_workspace_size(runner.dims, runner.cache, runner.batch, ops.MSA_CALL_DENSE_ATTN_DECODE)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    ops.msa_dense_attn_decode(runner.dims, runner.cache, runner.batch, runner.inputs.q, out, ws)
+    torch.cuda.synchronize()
+    return runner, out
+
+
+def test_dense_decode_ragged_lengths_permuted_table():
+    """Contexts from one token to past several 64-block splits, on a scattered block table."""
+    w = M2.with_sizes("dense_dec", [1, 128, 129, 2049, 5000, 9999, 8192, 8193, 8320], [1] * 9, permuted_table=True)
+    runner, out = _dense_decode(w)
+    _all_rows(runner, out)
+
+
+def test_dense_decode_group_sizes():
+    for name, w in (("g16", WORKLOADS["m3d"].with_sizes("dense_dec_g16", [3000, 9001], [1, 1])),
+                    ("g8_d64", WORKLOADS["c0"].with_sizes("dense_dec_g8", [4096, 777, 8500], [1, 1, 1]))):
+        runner, out = _dense_decode(w)
+        _all_rows(runner, out)
+
+
+def test_dense_decode_equals_dense_prefill_kernel():
+    """Both dense calls on the same one-query batch."""
+    w = M2.with_sizes("dense_dec_eq", [700, 4097, 20000], [1, 1, 1], permuted_table=True)
+    runner, out = _dense_decode(w)
+    ref = torch.full_like(out, float("nan"))
+    ops.msa_dense_attn_prefill(runner.dims, runner.cache, runner.batch, runner.inputs.q, ref)
+    torch.cuda.synchronize()
+    diff = (out.float() - ref.float()).abs()
+    assert float(diff.max()) <= 2 * MAX_ABS and float(diff.mean()) <= MEAN_ABS
+
+
+def test_dense_decode_c2_full_size_sampled_sequences():
+    runner, out = _dense_decode(WORKLOADS["c2"])
+    for s in (0, 13, 31):
+        _compare(runner, out, s, [131071])
+    assert torch.isfinite(out.float()).all()
+
+
+def test_dense_decode_c4d_1m_one_sequence():
+    runner, out = _dense_decode(WORKLOADS["c4d"])
+    _compare(runner, out, 2, [(1 << 20) - 1])
+    assert torch.isfinite(out.float()).all()
