@@ -239,6 +239,10 @@ def main():
                     help="query rows (evenly spaced) on which to measure selection quality against dense attention; 0: skip")
     ap.add_argument("--dense-calls", type=int, default=3,
                     help="time the dense attention path on the same batch over this many calls after the timed region (0: skip)")
+    ap.add_argument("--rotate", type=int, default=None,
+                    help="timed steps rotate over this many cache copies (default: 2 for decode, 1 for prefill)")
+    ap.add_argument("--cold-steps", type=int, default=10,
+                    help="decode workloads: also time this many single steps, each after a 1 GiB write that evicts the Infinity Cache")
     ap.add_argument("--graph", choices=["on", "off"], default="off",
                     help="replay an unchunked step from a captured HIP graph (stage events then come from a serial pass)")
     args = ap.parse_args()
@@ -257,6 +261,12 @@ def main():
     torch.cuda.set_device(0)
     inputs = make_inputs(w, "cuda")
     runner = MsaRunner(inputs, chunk_rows=args.chunk_rows or None)
+    # Decode steps rotate over caches of their own (same contents, separate
+    # memory): a step's K_idx and K/V were last touched `rotate` steps ago,
+    # with the other copies' traffic (several times the 256 MB Infinity
+    # Cache) in between, so no step reads what the previous one left cached.
+    n_rot = max(1, args.rotate if args.rotate is not None else (2 if runner.decode else 1))
+    runners = [runner] + [MsaRunner(inputs, chunk_rows=args.chunk_rows or None) for _ in range(n_rot - 1)]
     work = algorithmic_work(w)
     stream = torch.cuda.current_stream()
 
@@ -271,12 +281,14 @@ def main():
     use_graph = args.graph == "on"
     if use_graph and runner.chunks:
         sys.exit("bench.py: --graph on needs an unchunked step (--chunk-rows 0)")
-    step = runner.step
+    steps = [r.step for r in runners]
     if use_graph:
-        runner.capture()
-        step = runner.replay
-    for _ in range(args.warmup):
-        step()
+        for r in runners:
+            r.capture()
+        steps = [r.replay for r in runners]
+    step = steps[0]
+    for i in range(args.warmup * n_rot):
+        steps[i % n_rot]()
     torch.cuda.synchronize()
 
     def staged_ms():
@@ -317,17 +329,19 @@ def main():
             pairs[-1][1] = e
 
     if not use_graph:
-        runner.hook = hook
+        for r in runners:
+            r.hook = hook
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_host = time.perf_counter()
     start.record(stream)
-    for _ in range(args.steps):
-        step()
+    for i in range(args.steps):
+        steps[i % n_rot]()
     end.record(stream)
     torch.cuda.synchronize()
     t_host = time.perf_counter() - t_host
-    runner.hook = None
+    for r in runners:
+        r.hook = None
     total_ms = start.elapsed_time(end)
     ms_per_step = total_ms / args.steps
     if pairs:
@@ -371,6 +385,30 @@ def main():
     roof["launches_per_step"] = launches_per_step
     roof["avg_launch_ms"] = avg_launch_ms
 
+    # Single decode steps, each timed right after reading a 1 GiB buffer
+    # (outside its events) that evicts the 256 MB Infinity Cache, beside the
+    # same isolated steps after reading 1 MiB.  A read evicts without leaving
+    # dirty lines whose write-back would load the next step.
+    cold = None
+    if runner.decode and args.cold_steps > 0:
+        def isolated(nbytes):
+            buf = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+            sink = torch.empty((), dtype=torch.float32, device="cuda")
+            times = []
+            for i in range(args.cold_steps):
+                torch.sum(buf, dim=0, out=sink)
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                step()
+                e1.record(stream)
+                torch.cuda.synchronize()
+                times.append(e0.elapsed_time(e1))
+            return float(np.median(times))
+        cold_med = isolated(1 << 30)
+        warm_med = isolated(1 << 20)
+        cold = {"steps": args.cold_steps, "median_ms_per_step": cold_med, "tokens_per_s": w.total_q / (cold_med / 1e3),
+                "evict_read_bytes": 1 << 30, "isolated_after_1mib_read_median_ms": warm_med}
+
     quality = selection_quality(runner, args.quality_rows) if args.quality_rows > 0 else None
     dense = None
     if args.dense_calls > 0:
@@ -402,11 +440,12 @@ def main():
         "stage_ms": stage_ms,
         "serial_ms_per_step": serial_ms,
         "pipeline": {"chunks": max(1, len(runner.chunks)), "streams": 2 if runner.chunks else 1,
-                     "hip_graph": use_graph},
+                     "hip_graph": use_graph, "cache_copies_rotated": n_rot},
         "step": step_info,
         "roofline": roof,
         "cpu_baseline": cpu,
         "selection_quality": quality,
+        "cold_cache": cold,
         "dense_attention": dense,
         "host_wall_s_timed_region": t_host,
     }
