@@ -154,10 +154,12 @@ def dense_attention(runner, n_calls: int):
         kv = sum(2.0 * 2 * w.head_dim * w.num_kv_heads * n for n in w.seq_lens)
         gbs = kv / (ms / 1e3) / 1e9
         return {"kernel": "msa_dense_attn_decode (dense_decode_kernel + dense_decode_merge_kernel)", "calls": n_calls,
-                "ms": ms, "algorithmic_bytes": kv, "achieved_gbs": gbs, "hbm_frac": gbs / HBM_PEAK_GBS}
+                "ms": ms, "algorithmic_bytes": kv, "achieved_gbs": gbs, "hbm_frac": gbs / HBM_PEAK_GBS,
+                "traffic": recorded_traffic(w.name, "dense", 1.0)}
     tflops = flops / (ms / 1e3) / 1e12
     return {"kernel": "msa_dense_attn_prefill (dense_prefill_kernel)", "calls": n_calls, "ms": ms,
-            "algorithmic_flops": flops, "achieved_tflops": tflops, "mfma_frac": tflops / BF16_PEAK_TFLOPS}
+            "algorithmic_flops": flops, "achieved_tflops": tflops, "mfma_frac": tflops / BF16_PEAK_TFLOPS,
+            "traffic": recorded_traffic(w.name, "dense", 1.0)}
 
 
 def cpu_baseline(inputs, runner, budget_s: float):
