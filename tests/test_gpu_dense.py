@@ -182,3 +182,54 @@ def test_dense_decode_c4d_1m_one_sequence():
     runner, out = _dense_decode(WORKLOADS["c4d"])
     _compare(runner, out, 2, [(1 << 20) - 1])
     assert torch.isfinite(out.float()).all()
+
+
+def _oracle_dense_without(inp, s, positions, absent):
+    """Dense attention over every causal block except the `absent` ones."""
+    positions = np.asarray(positions, dtype=np.int64)
+    rows = torch.from_numpy(seq_rows(inp, s, positions)).to(inp.q.device)
+    off = int(inp.tok_off[s])
+    length = int(positions.max()) + 1
+    k = bf16_bits(inp.k[off:off + length])
+    v = bf16_bits(inp.v[off:off + length])
+    q = bf16_bits(inp.q.index_select(0, rows))
+    w = inp.workload
+    nblk = (length + 127) // 128
+    sel = np.full((len(positions), w.num_kv_heads, nblk), -1, dtype=np.int32)
+    for r, t in enumerate(positions):
+        keep = [b for b in range(int(t) // 128 + 1) if b not in absent]
+        sel[r, :, :len(keep)] = keep
+    return rows, oracle.attend(positions, q, k, v, sel, w.block_size)
+
+
+@pytest.mark.parametrize("mode", ["prefill", "decode"])
+def test_dense_blocks_outside_the_cache_hold_no_keys(mode):
+    """Block-table entries outside [0, num_blocks) are skipped, as in the sparse calls."""
+    q_len = 700 if mode == "prefill" else 1
+    w = M2.with_sizes(f"dense_absent_{mode}", [3000], [q_len], permuted_table=True)
+    runner = MsaRunner(make_inputs(w, "cuda"))
+    runner.append()
+    absent = {3: -1, 7: runner.cache.k.shape[0], 10: -5}
+    for b, v in absent.items():
+        runner.cache.block_table[0, b] = v
+    out = torch.full_like(runner.inputs.q, float("nan"))
+    if mode == "prefill":
+        ops.msa_dense_attn_prefill(runner.dims, runner.cache, runner.batch, runner.inputs.q, out)
+    else:
+        need = ops.msa_workspace_size(runner.dims, runner.cache, runner.batch, ops.MSA_CALL_DENSE_ATTN_DECODE)
+        ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+        ops.msa_dense_attn_decode(runner.dims, runner.cache, runner.batch, runner.inputs.q, out, ws)
+    torch.cuda.synchronize()
+    pos = runner.inputs.positions(0)
+    rows, want = _oracle_dense_without(runner.inputs, 0, pos, set(absent))
+    got = out.index_select(0, rows).float().cpu().numpy().astype(np.float64)
+    err = np.abs(got - want)
+    assert float(err.max()) <= MAX_ABS and float(err.mean()) <= MEAN_ABS
+
+
+def test_dense_batch_with_sequences_without_queries():
+    """Sequences with no query rows this step take no part (and write nothing)."""
+    w = M2.with_sizes("dense_noq", [2000, 500, 4200, 129], [0, 300, 0, 129], permuted_table=True)
+    runner, out = _dense(w)
+    _all_rows(runner, out)
+    assert torch.isfinite(out.float()).all()
