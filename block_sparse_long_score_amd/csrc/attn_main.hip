@@ -23,9 +23,13 @@
 //               bf16 MFMA; rows whose local block this is mask the keys after
 //               the query.  Output per (row, slot, head): block-local softmax
 //               statistics and the normalised output in fp16 scaled by 2^-e;
-//   decode   decode_block: one workgroup per (slot, group, sequence), no staging;
-//   both     3. merge: per (row, head) a streaming log-sum-exp over the slots,
-//               rounded to bf16.
+//   decode   batches of >= 128 (sequence, group) pairs: decode_fused, one
+//               16-wave workgroup per pair, one wave per selected block, waves
+//               combined in LDS, output written directly; smaller batches:
+//               decode_block, one workgroup per (slot, group, sequence), no
+//               staging, then the merge below;
+//   prefill  3. merge: per (row, head) a streaming log-sum-exp over the slots,
+//   (and small decode) rounded to bf16.
 // The softmax works in base 2 with the scale folded into log2(e).
 //
 // MFMA mapping (32x32x16 bf16, wave64), per tile of 32 (row, head) pairs:
@@ -33,8 +37,9 @@
 //   O^T[D x 32 rows]        = V^T[D x keys] * P^T[keys x rows]
 // With keys on the M axis each lane owns one row, so row max/sum are in-lane
 // plus one exchange between wave halves, and the S^T accumulators rounded to
-// bf16 are directly the B operand of the P.V product; V is stored transposed
-// in LDS so its A operand is two 8-byte reads.
+// bf16 are directly the B operand of the P.V product.  The block's K and V
+// are staged row-major by asynchronous global->LDS copies; the V^T operand
+// is read with the LDS transpose load (attn_tiles.h).
 #include "attn_tiles.h"
 #include "msa_kernels.h"
 

@@ -232,7 +232,7 @@ __device__ __forceinline__ void softmax_rows(f32x16 (&sacc)[4], float c, float& 
   l = sum;
 }
 
-// Query rows of a 32-row tile as the B operand of block_scores: lane (row
+// Query rows of a 32-row tile as the B operand of tile_scores: lane (row
 // rho, half h) needs dims 16*ks + 8h .. +7 of row rho for every k-step ks.
 // They are loaded as 64-byte row segments: in load pair j, lane (h, a, b)
 // (a = bit 4 of the lane, b its low 4 bits) reads 16 bytes of tile row b
