@@ -197,6 +197,7 @@ def cpu_baseline(inputs, runner, budget_s: float):
         return t_sel + time.perf_counter() - t0
 
     decode = runner.decode
+    all_threads = oracle.num_threads()
     if decode:
         # whole decode rows (one per sequence), sequences taken in order until the budget is spent
         spent, n = 0.0, 0
@@ -205,8 +206,14 @@ def cpu_baseline(inputs, runner, budget_s: float):
             n += 1
             if spent >= budget_s:
                 break
-        sample = f"{n} of {w.num_seqs} decode rows (full {w.seq_lens[0]}-token context each)"
+        # one row per call: the scoring loop runs over that row's groups, its attention on one thread
+        used = min(all_threads, w.num_kv_heads)
+        sample = (f"{n} of {w.num_seqs} decode rows (full {w.seq_lens[0]}-token context each), one row per call: "
+                  f"scoring spread over the row's {w.num_kv_heads} groups, attention on one thread")
         value = n / spent
+        oracle.set_num_threads(1)
+        one = 1.0 / run_rows(0, np.array([w.seq_lens[0] - 1], np.int64))
+        sample1 = "1 decode row"
     else:
         s = 0
         n_q = w.q_lens[0]
@@ -221,8 +228,21 @@ def cpu_baseline(inputs, runner, budget_s: float):
             n = int(min(n_q, max(2 * n, n * budget_s / max(spent, 1e-3))))
         sample = f"{len(pos)} query rows evenly spaced over positions {first}..{w.seq_lens[0] - 1} (all groups/heads)"
         value = len(pos) / spent
-    return {"value": value, "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle", "sample": sample,
-            "seconds": round(spent, 2)}
+        used = all_threads
+        pos1 = pos[:: max(1, len(pos) // max(4, len(pos) // (2 * all_threads)))]
+        oracle.set_num_threads(1)
+        one = len(pos1) / run_rows(s, pos1)
+        sample1 = f"every {max(1, len(pos) // max(4, len(pos) // (2 * all_threads)))}th row of that sample ({len(pos1)} rows)"
+    oracle.set_num_threads(all_threads)
+    cpu = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), cpu)
+    except OSError:
+        pass
+    return {"value": value, "unit": "tokens/s", "cores": used, "kind": "oracle", "sample": sample,
+            "seconds": round(spent, 2), "value_1_thread": one, "sample_1_thread": sample1, "host_cpu": cpu,
+            "host_logical_cpus": os.cpu_count()}
 
 
 def main():

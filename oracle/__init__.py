@@ -65,8 +65,15 @@ def _load():
                   lib.msa_oracle_block_mass, lib.msa_oracle_selection_quality):
             f.restype = ctypes.c_int
         lib.msa_oracle_num_threads.restype = ctypes.c_int
+        lib.msa_oracle_set_num_threads.argtypes = [ctypes.c_int]
+        lib.msa_oracle_set_num_threads.restype = None
         _lib = lib
     return _lib
+
+
+def set_num_threads(n: int) -> None:
+    """Threads for the oracle's OpenMP loops from now on."""
+    _load().msa_oracle_set_num_threads(int(n))
 
 
 def num_threads() -> int:

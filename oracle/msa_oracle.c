@@ -75,6 +75,11 @@ static double bf16_to_double(uint16_t bits) {
   return (double)f;
 }
 
+/* Threads for the OpenMP loops below (n <= 0 leaves the setting unchanged). */
+void msa_oracle_set_num_threads(int n) {
+  if (n > 0) omp_set_num_threads(n);
+}
+
 int msa_oracle_num_threads(void) {
 #ifdef _OPENMP
   return omp_get_max_threads();
