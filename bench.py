@@ -12,7 +12,8 @@ The default workload is the 131,072-token prefill (48 query heads / 8 KV
 heads, head_dim 128, index dim 64), the context length the metric is quoted
 at; --workload selects another (c0 tiny prefill, c1 32K prefill, c2 decode of
 32 x 128K, c4d decode of 4 x 1M, c4p 8K chunk onto a 1M cache, m3p / m3d the
-same 128K prefill and 32 x 128K decode with M3's 64 query / 4 KV heads).
+same 128K prefill and 32 x 128K decode with M3's 64 query / 4 KV heads, c1n / c2n
+c1 / c2 with needles planted for the rows whose selection quality is measured).
 """
 from __future__ import annotations
 
@@ -250,7 +251,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="c3", choices=["c0", "c1", "c2", "c3", "c4d", "c4p", "m3p", "m3d"])
+    ap.add_argument("--workload", default="c3", choices=["c0", "c1", "c2", "c3", "c4d", "c4p", "m3p", "m3d", "c1n", "c2n"])
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calib-copy-mib", type=int, default=0,

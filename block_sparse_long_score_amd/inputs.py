@@ -19,6 +19,16 @@ Value recipe (one sub-stream per tensor, seed = 1000 + workload index):
     in any summation order and block selections can be compared bit for bit.
   - block table: identity for prefill workloads, a seeded random permutation
     of the physical blocks for decode workloads.
+
+Needle variant (workloads with needle_rows > 0).  On i.i.d. inputs the index
+keys carry nothing about where the attention mass lies, so selection recall
+and coverage sit at chance.  The needle variant plants keys that do: for
+each of `needle_rows` evenly spaced query rows r and each KV group g,
+`needles_per_group` keys at distinct positions in distinct earlier
+(non-local) blocks of r's context get K[i, g] = bf16(gain * Q[r, h]) for one
+head h of the group (a different head per needle) and K_idx[i] = Q_idx[r, g]
+(an exact copy, so index scores stay exact).  Everything else is the plain
+workload's draw.  Positions come from their own seeded sub-stream.
 """
 from __future__ import annotations
 
@@ -32,7 +42,7 @@ BLOCK = 128
 TOP_K = 16
 
 # Tensor ids of the sub-streams, in a fixed order.
-_STREAM_Q, _STREAM_K, _STREAM_V, _STREAM_QIDX, _STREAM_KIDX, _STREAM_TABLE = range(6)
+_STREAM_Q, _STREAM_K, _STREAM_V, _STREAM_QIDX, _STREAM_KIDX, _STREAM_TABLE, _STREAM_NEEDLE = range(7)
 
 
 @dataclasses.dataclass(frozen=True)
@@ -49,6 +59,9 @@ class Workload:
     seed: int
     block_size: int = BLOCK
     top_k: int = TOP_K
+    needle_rows: int = 0         # query rows that get planted needles (0: plain i.i.d. inputs)
+    needles_per_group: int = 4
+    needle_gain: float = 1.5
 
     @property
     def num_seqs(self) -> int:
@@ -70,12 +83,13 @@ class Workload:
     def max_blocks_per_seq(self) -> int:
         return max(math.ceil(n / self.block_size) for n in self.seq_lens)
 
-    def with_sizes(self, name: str, seq_lens, q_lens, permuted_table=None, seed=None) -> "Workload":
+    def with_sizes(self, name: str, seq_lens, q_lens, permuted_table=None, seed=None, needle_rows=None) -> "Workload":
         """Same head shapes with other sequence sizes (for parity cases)."""
         return dataclasses.replace(
             self, name=name, seq_lens=tuple(int(x) for x in seq_lens), q_lens=tuple(int(x) for x in q_lens),
             permuted_table=self.permuted_table if permuted_table is None else permuted_table,
-            seed=self.seed if seed is None else seed)
+            seed=self.seed if seed is None else seed,
+            needle_rows=self.needle_rows if needle_rows is None else needle_rows)
 
 
 _M2 = dict(num_q_heads=48, num_kv_heads=8, head_dim=128, index_dim=64)
@@ -100,6 +114,12 @@ WORKLOADS = {
                     seq_lens=(_ONE_M,) * 4, q_lens=(1,) * 4, permuted_table=True, seed=1004, **_M2),
     "c4p": Workload("c4p", "8192-token MSA prefill chunk appended to a 1,048,576-token cache",
                     seq_lens=(_ONE_M + 8192,), q_lens=(8192,), permuted_table=False, seed=1004, **_M2),
+    # The 32K prefill and the 32 x 128K decode with planted needles on 64 evenly spaced rows (every
+    # decode row): the selection-quality measurements on inputs where the indexer can find the mass.
+    "c1n": Workload("c1n", "M2-shaped MSA prefill, T=32768, 48q/8kv, needles planted for 64 rows",
+                    seq_lens=(32768,), q_lens=(32768,), permuted_table=False, seed=1001, needle_rows=64, **_M2),
+    "c2n": Workload("c2n", "MSA decode, 32 sequences x 131072 cached tokens, 48q/8kv, needles planted for every row",
+                    seq_lens=(131072,) * 32, q_lens=(1,) * 32, permuted_table=True, seed=1002, needle_rows=32, **_M2),
     # M3-shaped variants (64q/4kv, G = 16) of the 128K prefill and the 32 x 128K decode.
     "m3p": Workload("m3p", "M3-shaped MSA prefill, T=131072, 64q/4kv (G=16), D=128, d_idx=64",
                     seq_lens=(131072,), q_lens=(131072,), permuted_table=False, seed=1005, **_M3),
@@ -178,6 +198,45 @@ class Inputs:
         return torch.from_numpy(np.concatenate(rows)).to(self.k.device)
 
 
+def needle_rows_of(w: Workload) -> np.ndarray:
+    """Global query-row indices that carry needles: evenly spaced over all rows."""
+    if w.needle_rows <= 0 or w.total_q == 0:
+        return np.zeros(0, dtype=np.int64)
+    return np.unique(np.linspace(0, w.total_q - 1, min(w.needle_rows, w.total_q)).astype(np.int64))
+
+
+def needle_plan(w: Workload, seed: int | None = None) -> dict:
+    """Where the needles go: int64 arrays row, token (index into k/v/k_idx),
+    group, head, one entry per planted key.  Positions are distinct across
+    the whole workload, causal for their row and outside its local block."""
+    seed = w.seed if seed is None else seed
+    rng = np.random.default_rng(seed * 16 + _STREAM_NEEDLE)
+    cu = np.concatenate([[0], np.cumsum(w.q_lens)]).astype(np.int64)
+    off = np.concatenate([[0], np.cumsum(w.seq_lens)]).astype(np.int64)
+    B, G = w.block_size, w.group_size
+    used = set()
+    out = {"row": [], "token": [], "group": [], "head": []}
+    for r in needle_rows_of(w):
+        s = int(np.searchsorted(cu, r, side="right") - 1)
+        t = w.seq_lens[s] - int(cu[s + 1] - r)
+        c = t // B
+        if c == 0:
+            continue
+        for g in range(w.num_kv_heads):
+            blocks = rng.choice(c, size=min(w.needles_per_group, c), replace=False)
+            for n, b in enumerate(blocks):
+                for _ in range(8):
+                    tok = int(off[s] + b * B + rng.integers(0, B))
+                    if tok not in used:
+                        used.add(tok)
+                        out["row"].append(int(r))
+                        out["token"].append(tok)
+                        out["group"].append(g)
+                        out["head"].append(g * G + n % G)
+                        break
+    return {k: np.asarray(v, dtype=np.int64) for k, v in out.items()}
+
+
 def make_inputs(w: Workload, device="cpu", seed: int | None = None) -> Inputs:
     """Draw every tensor of workload `w` on `device` from its seeded sub-streams."""
     seed = w.seed if seed is None else seed
@@ -195,6 +254,11 @@ def make_inputs(w: Workload, device="cpu", seed: int | None = None) -> Inputs:
         table = perm.to(torch.int32).view(w.num_seqs, mb)
     else:
         table = torch.arange(num_blocks, device=dev, dtype=torch.int32).view(w.num_seqs, mb)
+    if w.needle_rows > 0:
+        plan = {key: torch.from_numpy(val).to(dev) for key, val in needle_plan(w, seed).items()}
+        if plan["token"].numel():
+            k[plan["token"], plan["group"]] = (q[plan["row"], plan["head"]].float() * w.needle_gain).to(torch.bfloat16)
+            k_idx[plan["token"]] = q_idx[plan["row"], plan["group"]]
     return Inputs(w, k, v, k_idx, q, q_idx, table.contiguous(), num_blocks)
 
 

@@ -18,7 +18,7 @@ import torch
 
 import oracle
 from block_sparse_long_score_amd import ops
-from block_sparse_long_score_amd.inputs import WORKLOADS, bf16_bits, make_inputs
+from block_sparse_long_score_amd.inputs import WORKLOADS, bf16_bits, make_inputs, needle_rows_of
 from block_sparse_long_score_amd.pipeline import MsaRunner
 from tests.gpu_helpers import oracle_rows, seq_rows
 
@@ -44,6 +44,9 @@ CASES = {
     "m3_shape": (WORKLOADS["m3p"].with_sizes("q_m3", [2600], [2600]), [5, 1000, 2047, 2048, 2599]),
     # 64 rows x 8 groups = 512 (row, group) pairs: the 4-wave mass kernel (smaller samples use 16 waves)
     "m2_many_rows": (WORKLOADS["c1"].with_sizes("q_m2b", [3000], [3000]), list(range(0, 3000, 47))[:64]),
+    # planted needles: the indexer can find the mass (rows = the needle rows of one sequence)
+    "needles": (WORKLOADS["c1n"].with_sizes("q_needles", [12000], [12000], needle_rows=16),
+                needle_rows_of(WORKLOADS["c1n"].with_sizes("q_needles", [12000], [12000], needle_rows=16)).tolist()),
 }
 
 
@@ -108,7 +111,7 @@ def test_block_mass_matches_oracle(name):
             np.testing.assert_allclose(got[i, :, : c + 1].sum(axis=-1), 1.0, atol=1e-4)
 
 
-@pytest.mark.parametrize("name", ["m2_prefill", "decode_batch", "m3_shape"])
+@pytest.mark.parametrize("name", ["m2_prefill", "decode_batch", "m3_shape", "needles"])
 def test_selection_quality_on_oracle_inputs(name):
     """Same float inputs on both sides: recall bit-exact, coverage and KL close."""
     runner, sample = _run(name)
@@ -134,7 +137,7 @@ def test_selection_quality_on_oracle_inputs(name):
         np.testing.assert_allclose(q[..., 2], kl, rtol=1e-4, atol=1e-4, err_msg=f"{name}: KL")
 
 
-@pytest.mark.parametrize("name", ["m2_prefill", "decode_batch"])
+@pytest.mark.parametrize("name", ["m2_prefill", "decode_batch", "needles"])
 def test_selection_quality_end_to_end(name):
     """The GPU's own mass, pooled scores and selections."""
     runner, sample = _run(name)
@@ -154,3 +157,24 @@ def test_selection_quality_end_to_end(name):
         assert np.all(np.abs(q[..., 1] - rec) <= 1.0 / 16 + 1e-6)
         assert np.mean(q[..., 1] == rec) >= 0.95
         assert np.all((q[..., 0] >= -1e-6) & (q[..., 0] <= 1 + 1e-5))
+
+
+def test_needles_are_found():
+    """With planted needles the indexer sees where the mass is: the needle rows'
+    selections cover far more of the dense attention mass than chance, and
+    the MSA outputs on those rows still match the oracle."""
+    runner, sample = _run("needles")
+    inp, dev = runner.inputs, runner.inputs.q.device
+    hkv = runner.dims.num_kv_heads
+    from tests.gpu_helpers import compare_rows
+    for s, pos, rows in sample:
+        compare_rows(runner, s, pos[pos >= 128])  # rows with at least one earlier block
+        rows_t, mass = _gpu_mass(runner, rows)
+        quality = torch.empty((len(rows), hkv, 3), dtype=torch.float32, device=dev)
+        ops.msa_selection_quality(runner.dims, runner.batch, rows_t, mass, runner.scores, runner.sel, quality)
+        torch.cuda.synchronize()
+        q = quality.cpu().numpy().astype(np.float64)
+        far = pos >= 16 * 128  # rows with more causal blocks than slots
+        chance = float(np.mean(16 / (pos[far] // 128 + 1)))  # uniform coverage share, and about chance recall
+        assert q[far, :, 0].mean() > chance + 0.2, "coverage should beat the uniform share"
+        assert q[far, :, 1].mean() > chance + 0.1, "recall should beat chance"
