@@ -16,6 +16,7 @@ STATUS_NAMES = {0: "MSA_OK", 1: "MSA_ERR_NULL_POINTER", 2: "MSA_ERR_BAD_SHAPE", 
 MSA_CALL_SPARSE_ATTN_PREFILL = 1
 MSA_CALL_SPARSE_ATTN_DECODE = 2
 MSA_CALL_DENSE_ATTN_DECODE = 3
+MSA_CALL_INDEX_SELECT = 4
 
 
 class MsaDims(ctypes.Structure):
@@ -57,6 +58,7 @@ def load() -> ctypes.CDLL:
         "msa_sparse_attn_decode": ([dims, cache, batch, vp, vp, vp, vp, sz, vp], ctypes.c_int),
         "msa_block_attn_mass": ([dims, cache, batch, vp, vp, i32, vp, i64, vp], ctypes.c_int),
         "msa_selection_quality": ([dims, batch, vp, i32, vp, vp, vp, i64, vp, vp], ctypes.c_int),
+        "msa_index_select": ([dims, cache, batch, vp, vp, vp, sz, vp], ctypes.c_int),
         "msa_dense_attn_prefill": ([dims, cache, batch, vp, vp, vp], ctypes.c_int),
         "msa_dense_attn_decode": ([dims, cache, batch, vp, vp, vp, sz, vp], ctypes.c_int),
         "msa_workspace_size": ([dims, cache, batch, i32], sz),

@@ -29,10 +29,11 @@ namespace msa {
 
 struct TopkArgs {
   Problem p;
-  const float* scores;
+  const float* scores;  // row R = r * hkv + g at scores + R * ld
   int64_t ld;
   int32_t* sel;
   int hkv_shift;
+  int64_t r_base;       // first (row, group) index of the batch: cu_q[0] * hkv
 };
 
 __device__ __forceinline__ int lanes_below(uint64_t mask) {
@@ -159,8 +160,9 @@ __global__ __launch_bounds__(256) void block_topk_kernel(TopkArgs a) {
   const Problem& p = a.p;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int64_t R = (int64_t)blockIdx.x * 4 + wave;
-  if (R >= ((int64_t)p.total_q << a.hkv_shift)) return;
+  const int64_t local = (int64_t)blockIdx.x * 4 + wave;
+  if (local >= ((int64_t)p.total_q << a.hkv_shift)) return;
+  const int64_t R = a.r_base + local;
   const int r = (int)(R >> a.hkv_shift);
   const int s = seq_of_row(p.cu_q, p.num_seqs, r);
   const int t = p.seq_lens[s] - (p.cu_q[s + 1] - r);
@@ -193,7 +195,7 @@ __global__ __launch_bounds__(kSplitWaves * 64) void block_topk_split_kernel(Topk
   const Problem& p = a.p;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int64_t R = blockIdx.x;
+  const int64_t R = a.r_base + blockIdx.x;
   const int r = (int)(R >> a.hkv_shift);
   const int s = seq_of_row(p.cu_q, p.num_seqs, r);
   const int t = p.seq_lens[s] - (p.cu_q[s + 1] - r);
@@ -255,17 +257,29 @@ __global__ __launch_bounds__(kSplitWaves * 64) void block_topk_split_kernel(Topk
 }
 
 hipError_t launch_block_topk(const Problem& p, const float* scores, int64_t ld, int32_t* sel, int64_t max_blocks,
-                             hipStream_t stream) {
+                             hipStream_t stream, int64_t first_row) {
   int hkv_shift = 0;
   while ((1 << hkv_shift) < p.hkv) ++hkv_shift;
   const int64_t rows = (int64_t)p.total_q << hkv_shift;
   if (rows == 0) return hipSuccess;
-  TopkArgs a{p, scores, ld, sel, hkv_shift};
+  TopkArgs a{p, scores, ld, sel, hkv_shift, first_row << hkv_shift};
   if (rows <= kSplitMaxRows && max_blocks > kSplitMinBlocks) {
     hipLaunchKernelGGL(block_topk_split_kernel, dim3((unsigned)rows), dim3(kSplitWaves * 64), 0, stream, a);
     return hipGetLastError();
   }
   hipLaunchKernelGGL(block_topk_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+__global__ void write_subbatch_kernel(int32_t* meta, int32_t seq_len, int32_t row_begin, int32_t row_end) {
+  meta[0] = seq_len;
+  meta[1] = row_begin;
+  meta[2] = row_end;
+}
+
+hipError_t launch_write_subbatch(int32_t* meta, int32_t seq_len, int32_t row_begin, int32_t row_end,
+                                 hipStream_t stream) {
+  hipLaunchKernelGGL(write_subbatch_kernel, dim3(1), dim3(1), 0, stream, meta, seq_len, row_begin, row_end);
   return hipGetLastError();
 }
 

@@ -15,6 +15,12 @@ namespace {
 
 thread_local std::string g_last_error;
 
+// msa_index_select: a 256-byte sub-batch descriptor, then the pooled scores
+// of one chunk of query rows; the suggested size keeps them within ~192 MB,
+// below the 256 MB Infinity Cache.
+constexpr int64_t kSelectMetaBytes = 256;
+constexpr int64_t kSelectScoresBudget = (int64_t)192 << 20;
+
 msa_status fail(msa_status st, const char* fmt, ...) {
   char buf[512];
   va_list ap;
@@ -244,6 +250,90 @@ msa_status msa_block_topk(const msa_dims* dims, const msa_batch* batch, const fl
                     "msa_block_topk launch");
 }
 
+msa_status msa_index_select(const msa_dims* dims, const msa_cache* cache, const msa_batch* batch, const void* q_idx,
+                            int32_t* sel, void* workspace, size_t ws_bytes, void* stream) {
+  MSA_TRY(check_dims(dims));
+  MSA_TRY(check_cache(cache));
+  MSA_TRY(check_batch(dims, batch, cache));
+  MSA_TRY(check_ptr(q_idx, "q_idx"));
+  MSA_TRY(check_ptr(sel, "sel"));
+  const int64_t ld = std::max<int64_t>(1, max_query_blocks(batch));
+  const int64_t row_bytes = (int64_t)dims->num_kv_heads * ld * (int64_t)sizeof(float);
+  if (!workspace || ws_bytes < (size_t)(kSelectMetaBytes + row_bytes))
+    return fail(MSA_ERR_WORKSPACE, "workspace of %zu bytes given, at least %lld needed (one query row)",
+                workspace ? ws_bytes : 0, (long long)(kSelectMetaBytes + row_bytes));
+  if (!aligned16(workspace)) return fail(MSA_ERR_MISALIGNED, "workspace is not 16-byte aligned");
+  const msa::Problem p = make_problem(dims, batch, cache);
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  const auto* qi = static_cast<const uint16_t*>(q_idx);
+  int32_t* meta = static_cast<int32_t*>(workspace);
+  float* scores = reinterpret_cast<float*>(static_cast<char*>(workspace) + kSelectMetaBytes);
+  // Rows per chunk: as many as the workspace holds pooled scores for.
+  const int64_t cap = std::max<int64_t>(1, (int64_t)(ws_bytes - kSelectMetaBytes) / row_bytes);
+  const int32_t* L = batch->seq_lens_host;
+  const int32_t* cu = batch->cu_q_host;
+  const int mbps = cache->max_blocks_per_seq;
+  // Score + select one chunk whose rows are [row_lo, row_lo + pc.total_q) of the batch.
+  auto run = [&](msa::Problem pc, const int32_t* lens_host, const int32_t* cu_host, int64_t row_lo,
+                 int64_t max_blocks) -> hipError_t {
+    // The chunk's pooled scores sit at the start of the workspace; row R = r * hkv + g of the
+    // batch is addressed globally, so the base is shifted back by the chunk's first row.
+    float* base = reinterpret_cast<float*>(reinterpret_cast<uintptr_t>(scores) -
+                                           (uintptr_t)(row_lo * dims->num_kv_heads * ld) * sizeof(float));
+    hipError_t e = msa::launch_index_score(pc, qi, base, ld, lens_host, cu_host, st);
+    if (e != hipSuccess) return e;
+    return msa::launch_block_topk(pc, base, ld, sel, max_blocks, st, row_lo);
+  };
+  int s = 0;
+  while (s < batch->num_seqs) {
+    const int nq = cu[s + 1] - cu[s];
+    if (nq == 0) { ++s; continue; }
+    if (nq > cap) {
+      // One long sequence: row ranges of it, each a one-sequence sub-batch (a prefill chunk).
+      for (int r0 = cu[s]; r0 < cu[s + 1]; r0 += (int)cap) {
+        const int r1 = (int)std::min<int64_t>(cu[s + 1], r0 + cap);
+        const int32_t len = L[s] - (cu[s + 1] - r1);  // the cache length seen by the chunk's last row
+        const int32_t lens_host[1] = {len};
+        const int32_t cu_host[2] = {r0, r1};
+        hipError_t e = msa::launch_write_subbatch(meta, len, r0, r1, st);
+        if (e != hipSuccess) return hip_status(e, "msa_index_select launch");
+        msa::Problem pc = p;
+        pc.num_seqs = 1;
+        pc.total_q = r1 - r0;
+        pc.max_q_per_seq = r1 - r0;
+        pc.seq_lens = meta;
+        pc.cu_q = meta + 1;
+        pc.block_table = p.block_table + (int64_t)s * mbps;
+        e = run(pc, lens_host, cu_host, r0, (len + 127) / 128);
+        if (e != hipSuccess) return hip_status(e, "msa_index_select launch");
+      }
+      ++s;
+      continue;
+    }
+    // Whole sequences while they fit: a sub-batch that points into the batch's own arrays.
+    int s1 = s;
+    int64_t rows = 0, max_blocks = 0;
+    int max_q = 0;
+    while (s1 < batch->num_seqs && rows + (cu[s1 + 1] - cu[s1]) <= cap) {
+      rows += cu[s1 + 1] - cu[s1];
+      max_q = std::max(max_q, cu[s1 + 1] - cu[s1]);
+      if (cu[s1 + 1] > cu[s1]) max_blocks = std::max<int64_t>(max_blocks, (L[s1] + 127) / 128);
+      ++s1;
+    }
+    msa::Problem pc = p;
+    pc.num_seqs = s1 - s;
+    pc.total_q = (int)rows;
+    pc.max_q_per_seq = max_q;
+    pc.seq_lens = batch->seq_lens + s;
+    pc.cu_q = batch->cu_q + s;
+    pc.block_table = p.block_table + (int64_t)s * mbps;
+    const hipError_t e = run(pc, L + s, cu + s, cu[s], max_blocks);
+    if (e != hipSuccess) return hip_status(e, "msa_index_select launch");
+    s = s1;
+  }
+  return ok();
+}
+
 msa_status msa_block_attn_mass(const msa_dims* dims, const msa_cache* cache, const msa_batch* batch, const void* q,
                                const int32_t* rows, int32_t n_rows, float* mass, int64_t ld, void* stream) {
   MSA_TRY(check_dims(dims));
@@ -329,6 +419,13 @@ size_t msa_workspace_size(const msa_dims* dims, const msa_cache* cache, const ms
       return msa::prefill_workspace_bytes(p);
     case MSA_CALL_SPARSE_ATTN_DECODE: ok(); return msa::decode_workspace_bytes(p);
     case MSA_CALL_DENSE_ATTN_DECODE: ok(); return msa::dense_decode_workspace_bytes(p, (int)max_query_blocks(batch));
+    case MSA_CALL_INDEX_SELECT: {
+      ok();
+      const int64_t ld = std::max<int64_t>(1, max_query_blocks(batch));
+      const int64_t row_bytes = (int64_t)dims->num_kv_heads * ld * (int64_t)sizeof(float);
+      const int64_t rows = std::max<int64_t>(1, std::min<int64_t>(batch->total_q, kSelectScoresBudget / row_bytes));
+      return (size_t)(kSelectMetaBytes + rows * row_bytes);
+    }
   }
   fail(MSA_ERR_BAD_SHAPE, "unknown call id %d", call);
   return 0;

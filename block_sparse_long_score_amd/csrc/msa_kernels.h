@@ -42,8 +42,14 @@ hipError_t launch_block_attn_mass(const Problem& p, const uint16_t* q, const int
 hipError_t launch_selection_quality(const Problem& p, const int32_t* rows, int32_t n_rows, const float* mass,
                                     const float* scores, const int32_t* sel, int64_t ld, float* quality,
                                     hipStream_t stream);
+// first_row: the batch's first query row (cu_q[0]); rows are addressed globally.
 hipError_t launch_block_topk(const Problem& p, const float* scores, int64_t ld, int32_t* sel, int64_t max_blocks,
-                             hipStream_t stream);
+                             hipStream_t stream, int64_t first_row = 0);
+
+// Writes {seq_len, row_begin, row_end} to meta: the device arrays of a
+// one-sequence sub-batch (seq_lens = meta, cu_q = meta + 1).
+hipError_t launch_write_subbatch(int32_t* meta, int32_t seq_len, int32_t row_begin, int32_t row_end,
+                                 hipStream_t stream);
 
 // Largest max_blocks_per_seq the prefill selection inversion supports (its
 // per-workgroup LDS histogram holds one counter per logical block).

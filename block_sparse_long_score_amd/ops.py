@@ -14,13 +14,13 @@ import numpy as np
 import torch
 
 from . import _lib
-from ._lib import (MSA_CALL_DENSE_ATTN_DECODE, MSA_CALL_SPARSE_ATTN_DECODE, MSA_CALL_SPARSE_ATTN_PREFILL, MsaBatch,
-                   MsaCache, MsaDims)
+from ._lib import (MSA_CALL_DENSE_ATTN_DECODE, MSA_CALL_INDEX_SELECT, MSA_CALL_SPARSE_ATTN_DECODE,
+                   MSA_CALL_SPARSE_ATTN_PREFILL, MsaBatch, MsaCache, MsaDims)
 
 __all__ = ["Dims", "Cache", "Batch", "MsaError", "msa_kv_append", "msa_index_score", "msa_block_topk",
            "msa_sparse_attn_prefill", "msa_sparse_attn_decode", "msa_dense_attn_prefill", "msa_dense_attn_decode",
-           "msa_block_attn_mass", "msa_selection_quality", "msa_workspace_size", "msa_abi_version",
-           "MSA_CALL_SPARSE_ATTN_PREFILL", "MSA_CALL_SPARSE_ATTN_DECODE", "MSA_CALL_DENSE_ATTN_DECODE"]
+           "msa_index_select", "msa_block_attn_mass", "msa_selection_quality", "msa_workspace_size", "msa_abi_version",
+           "MSA_CALL_SPARSE_ATTN_PREFILL", "MSA_CALL_SPARSE_ATTN_DECODE", "MSA_CALL_DENSE_ATTN_DECODE", "MSA_CALL_INDEX_SELECT"]
 
 
 class MsaError(RuntimeError):
@@ -171,6 +171,16 @@ def msa_sparse_attn_prefill(dims: Dims, cache: Cache, batch: Batch, q, sel, out,
 
 def msa_sparse_attn_decode(dims: Dims, cache: Cache, batch: Batch, q, sel, out, workspace, stream=None):
     _attn("msa_sparse_attn_decode", dims, cache, batch, q, sel, out, workspace, stream)
+
+
+def msa_index_select(dims: Dims, cache: Cache, batch: Batch, q_idx, sel, workspace, stream=None):
+    """Scoring, pooling and top-k in one call, chunked through `workspace` (uint8; the chunk
+    size follows its size); sel: int32 [total_q, Hkv, top_k], identical to the two calls'."""
+    L = _lib.load()
+    d, c, b = dims.c(), cache.c(), batch.c()
+    _check(L.msa_index_select(ctypes.byref(d), ctypes.byref(c), ctypes.byref(b), _ptr(q_idx, "q_idx", torch.bfloat16),
+                              _ptr(sel, "sel", torch.int32), _ptr(workspace, "workspace", torch.uint8),
+                              workspace.numel(), _stream(stream)))
 
 
 def msa_dense_attn_prefill(dims: Dims, cache: Cache, batch: Batch, q, out, stream=None):

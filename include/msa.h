@@ -125,7 +125,8 @@ typedef struct msa_batch {
 typedef enum msa_call {
   MSA_CALL_SPARSE_ATTN_PREFILL = 1,
   MSA_CALL_SPARSE_ATTN_DECODE = 2,
-  MSA_CALL_DENSE_ATTN_DECODE = 3
+  MSA_CALL_DENSE_ATTN_DECODE = 3,
+  MSA_CALL_INDEX_SELECT = 4
 } msa_call;
 
 /* ------------------------------------------------------------------------- *
@@ -177,6 +178,27 @@ msa_status msa_index_score(const msa_dims* dims, const msa_cache* cache, const m
  * ------------------------------------------------------------------------- */
 msa_status msa_block_topk(const msa_dims* dims, const msa_batch* batch, const float* block_scores,
                           int64_t ld, int32_t* sel, void* stream);
+
+/* ------------------------------------------------------------------------- *
+ * msa_index_select — msa_index_score followed by msa_block_topk ([M3-evo] §2
+ * steps 1–3) without handing the pooled scores to the caller: the batch is
+ * cut into chunks of query rows (whole sequences, or row ranges of one long
+ * sequence), and each chunk's pooled scores live in the workspace only
+ * until its selection is made.  sel is identical to the two calls'.
+ *   q_idx     : bf16 [total_q][Hkv][d_idx]
+ *   sel       : int32 [total_q][Hkv][top_k], as msa_block_topk
+ *   workspace : device scratch; it must hold 256 bytes plus the pooled
+ *               scores of one query row (Hkv x the blocks of the longest
+ *               sequence, fp32), and the rows per chunk are as many as it
+ *               holds.  msa_workspace_size(..., MSA_CALL_INDEX_SELECT) gives
+ *               a size that keeps a chunk's scores within about 192 MB (so
+ *               they stay in the 256 MB Infinity Cache) or the whole batch if
+ *               smaller.  Contents on entry are ignored.
+ * Errors: NULL_POINTER, BAD_SHAPE, UNSUPPORTED, MISALIGNED, CAPACITY,
+ *         WORKSPACE, HIP.
+ * ------------------------------------------------------------------------- */
+msa_status msa_index_select(const msa_dims* dims, const msa_cache* cache, const msa_batch* batch,
+                            const void* q_idx, int32_t* sel, void* workspace, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------- *
  * msa_sparse_attn_prefill — Main Branch ([M3-evo] §2 step 4 and the

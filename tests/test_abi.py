@@ -190,3 +190,25 @@ def test_dense_decode_validates_on_the_host(lib):
     one = lib.msa_workspace_size(dp, ctypes.byref(big), ctypes.byref(_Batch([1024], [1]).c), 3)
     three = lib.msa_workspace_size(dp, ctypes.byref(big), ctypes.byref(_Batch([128 * 64 * 3], [1]).c), 3)
     assert 2.9 * one < three < 3.1 * one
+
+
+def test_index_select_validates_on_the_host(lib):
+    d, c = _dims(), _cache()
+    b = _Batch([1024, 900], [300, 1])
+    dp, cp, bp = ctypes.byref(d), ctypes.byref(c), ctypes.byref(b.c)
+    need = lib.msa_workspace_size(dp, cp, bp, 4)
+    # a 256-byte descriptor plus every row's pooled scores (Hkv x 8 blocks, fp32): the batch fits in one chunk
+    assert need == 256 + 301 * 8 * 8 * 4
+    one_row = 256 + 8 * 8 * 4
+    assert lib.msa_index_select(dp, cp, bp, None, FAKE, FAKE, need, None) == NULLP
+    assert lib.msa_index_select(dp, cp, bp, FAKE, None, FAKE, need, None) == NULLP
+    assert lib.msa_index_select(dp, cp, bp, FAKE, FAKE, FAKE, one_row - 1, None) == WS
+    assert lib.msa_index_select(dp, cp, bp, FAKE, FAKE, None, need, None) == WS
+    assert lib.msa_index_select(dp, cp, bp, FAKE, FAKE, FAKE + 8, need, None) == MISAL
+    empty = _Batch([100, 5], [0, 0])
+    assert lib.msa_index_select(dp, cp, ctypes.byref(empty.c), FAKE, FAKE, FAKE, one_row, None) == OK
+    # long batches are capped near 192 MB of pooled scores per chunk
+    big_c = _cache(num_blocks=8192, mbps=8192)
+    big = _Batch([1 << 20], [1 << 16])
+    size = lib.msa_workspace_size(dp, ctypes.byref(big_c), ctypes.byref(big.c), 4)
+    assert (192 << 20) - 8 * 8192 * 4 < size - 256 <= 192 << 20

@@ -1,0 +1,75 @@
+"""msa_index_select (scoring, pooling and top-k in one call, chunked through
+the workspace) against the two separate calls: selections must be identical,
+with the suggested workspace and with small ones that force many chunks
+(row ranges of one long sequence, and runs of whole sequences)."""
+import sys
+
+import pytest
+import torch
+
+from block_sparse_long_score_amd import ops
+from block_sparse_long_score_amd.inputs import WORKLOADS, make_inputs
+from block_sparse_long_score_amd.pipeline import MsaRunner
+from tests.gpu_helpers import check_selection_invariants
+
+pytestmark = pytest.mark.gpu
+
+M2 = WORKLOADS["c1"]
+
+
+@pytest.fixture(autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def _announce(msg):
+    print(f"[gpu-case] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def _select(runner, rows_per_chunk=None):
+    """sel from msa_index_select; rows_per_chunk sizes the workspace (None: the suggested size)."""
+    w = runner.inputs.workload
+    if rows_per_chunk is None:
+        nbytes = ops.msa_workspace_size(runner.dims, runner.cache, runner.batch, ops.MSA_CALL_INDEX_SELECT)
+    else:
+        nbytes = 256 + rows_per_chunk * w.num_kv_heads * runner.ld * 4
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    sel = torch.full_like(runner.sel, 0x7777)
+    ops.msa_index_select(runner.dims, runner.cache, runner.batch, runner.inputs.q_idx, sel, ws)
+    torch.cuda.synchronize()
+    return sel
+
+
+CASES = {
+    "c0": WORKLOADS["c0"],
+    "ragged": M2.with_sizes("sel_ragged", [3001], [3001]),
+    "chunk_mid_block": M2.with_sizes("sel_chunk", [5000], [777]),
+    "multi_seq": M2.with_sizes("sel_multi", [2500, 129, 1, 4100, 2048], [2500, 60, 1, 900, 17], permuted_table=True),
+    "decode": M2.with_sizes("sel_decode", [1, 128, 129, 2049, 5000, 9999, 2048, 2049], [1] * 8, permuted_table=True),
+    "with_empty_seqs": M2.with_sizes("sel_empty", [2000, 500, 4200, 129], [0, 300, 0, 129], permuted_table=True),
+}
+
+
+@pytest.mark.parametrize("name", list(CASES))
+@pytest.mark.parametrize("rows_per_chunk", [None, 37, 1])
+def test_index_select_equals_score_then_topk(name, rows_per_chunk):
+    w = CASES[name]
+    if rows_per_chunk == 1 and w.total_q > 1000:
+        rows_per_chunk = 257  # one row per chunk only on the small batches (thousands of launches otherwise)
+    _announce(f"select {name} rows_per_chunk={rows_per_chunk}")
+    runner = MsaRunner(make_inputs(w, "cuda"))
+    runner.step()
+    sel = _select(runner, rows_per_chunk)
+    assert torch.equal(sel, runner.sel)
+
+
+@pytest.mark.parametrize("wl", ["c3", "c4p", "c2"])
+def test_index_select_full_size(wl):
+    _announce(f"select full size {wl}")
+    runner = MsaRunner(make_inputs(WORKLOADS[wl], "cuda"), chunk_rows=16384)
+    runner.step()
+    sel = _select(runner)
+    assert torch.equal(sel, runner.sel)
+    check_selection_invariants(runner)
