@@ -356,13 +356,20 @@ def main():
             r.hook = hook
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
+    # An event between consecutive steps on the caller's stream (every step
+    # ends joined to it) gives the per-step times for the median.
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps - 1)]
     t_host = time.perf_counter()
     start.record(stream)
     for i in range(args.steps):
         steps[i % n_rot]()
+        if i + 1 < args.steps:
+            marks[i].record(stream)
     end.record(stream)
     torch.cuda.synchronize()
     t_host = time.perf_counter() - t_host
+    bounds = [start] + marks + [end]
+    step_times = [a.elapsed_time(b) for a, b in zip(bounds, bounds[1:])]
     for r in runners:
         r.hook = None
     total_ms = start.elapsed_time(end)
@@ -451,6 +458,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": ms_per_step,
+        "median_ms_per_step": float(np.median(step_times)),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
