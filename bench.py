@@ -414,6 +414,9 @@ def main():
                      "prefill_tokens_per_s_without_append": tokens / ((ms_per_step - stage_ms["append"]) / 1e3)}
     roof["launches_per_step"] = launches_per_step
     roof["avg_launch_ms"] = avg_launch_ms
+    if traffic:  # the stage's measured HBM bytes per launch over its live launch time
+        roof["traffic_gbs"] = traffic["bytes_per_launch"] / (avg_launch_ms / 1e3) / 1e9
+        roof["traffic_hbm_frac"] = roof["traffic_gbs"] / HBM_PEAK_GBS
 
     # Single decode steps, each timed right after reading a 1 GiB buffer
     # (outside its events) that evicts the 256 MB Infinity Cache, beside the
