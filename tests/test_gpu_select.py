@@ -73,3 +73,48 @@ def test_index_select_full_size(wl):
     sel = _select(runner)
     assert torch.equal(sel, runner.sel)
     check_selection_invariants(runner)
+
+
+@pytest.mark.parametrize("kind", ["index_select", "dense_prefill", "dense_decode"])
+def test_graph_replays_equal_eager(kind):
+    """The calls allocate nothing and clear nothing with memsets, so they can be
+    captured in a HIP graph: every replay (with eager work in between) must
+    equal the eager call."""
+    decode = kind == "dense_decode"
+    w = (M2.with_sizes("graph_dec", [3000 + 113 * i for i in range(6)], [1] * 6, permuted_table=True) if decode
+         else M2.with_sizes("graph_pre", [5000], [2500]))
+    _announce(f"graph {kind}: {w.seq_lens[:3]} {w.q_lens[:3]}")
+    runner = MsaRunner(make_inputs(w, "cuda"))
+    runner.step()
+    inp = runner.inputs
+    if kind == "index_select":
+        # row-range chunks of 300 rows: the descriptor kernel runs before each chunk
+        ws = torch.empty(256 + 300 * w.num_kv_heads * runner.ld * 4, dtype=torch.uint8, device="cuda")
+        out = torch.empty_like(runner.sel)
+        call = lambda: ops.msa_index_select(runner.dims, runner.cache, runner.batch, inp.q_idx, out, ws)
+    elif kind == "dense_prefill":
+        out = torch.empty_like(inp.q)
+        call = lambda: ops.msa_dense_attn_prefill(runner.dims, runner.cache, runner.batch, inp.q, out)
+    else:
+        need = ops.msa_workspace_size(runner.dims, runner.cache, runner.batch, ops.MSA_CALL_DENSE_ATTN_DECODE)
+        ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+        out = torch.empty_like(inp.q)
+        call = lambda: ops.msa_dense_attn_decode(runner.dims, runner.cache, runner.batch, inp.q, out, ws)
+    call()
+    torch.cuda.synchronize()
+    eager = out.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call()
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call()
+    for i in range(4):
+        out.fill_(-1 if out.dtype == torch.int32 else float("nan"))
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), f"replay {i} differs from the eager call"
+        runner.step()  # eager work between replays
+        torch.cuda.synchronize()
