@@ -701,6 +701,8 @@ static hipError_t launch_main_t(const Problem& p, const uint16_t* q, const int32
     const unsigned n = (unsigned)(p.num_seqs * p.hkv);
     if (p.group <= 4)
       hipLaunchKernelGGL((decode_fused_kernel<D, 4>), dim3(n), dim3(1024), 0, stream, k);
+    else if (p.group <= 6)
+      hipLaunchKernelGGL((decode_fused_kernel<D, 6>), dim3(n), dim3(1024), 0, stream, k);
     else if (p.group <= 8)
       hipLaunchKernelGGL((decode_fused_kernel<D, 8>), dim3(n), dim3(1024), 0, stream, k);
     else
@@ -711,6 +713,8 @@ static hipError_t launch_main_t(const Problem& p, const uint16_t* q, const int32
     const dim3 dgrid(kTopK, p.hkv, p.num_seqs);
     if (p.group <= 4)
       hipLaunchKernelGGL((decode_block_kernel<D, 4>), dgrid, dim3(256), 0, stream, k);
+    else if (p.group <= 6)
+      hipLaunchKernelGGL((decode_block_kernel<D, 6>), dgrid, dim3(256), 0, stream, k);
     else if (p.group <= 8)
       hipLaunchKernelGGL((decode_block_kernel<D, 8>), dgrid, dim3(256), 0, stream, k);
     else

@@ -284,6 +284,12 @@ __device__ __forceinline__ void q_operand(const QRaw<D>& raw, bf16x8 (&bq)[D / 1
 
 // ------------------------------------------------------ decode, one wave
 
+// A raw buffer resource over `bytes` bytes from `base` (gfx9 descriptor
+// word 3); loads past the end return 0.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
 // One wave attends a decode query's G heads (G <= GM <= 16) to the keys of
 // one block after another, keeping a running softmax state.  Scores use the
 // 16x16x32 bf16 MFMA with 16 keys on M (K rows read straight from the cache)
@@ -291,12 +297,18 @@ __device__ __forceinline__ void q_operand(const QRaw<D>& raw, bf16x8 (&bq)[D / 1
 // owning D/64 output dims.  16x16x32 lane layout: A lane l holds
 // A[l%16][8*(l/16) .. +7], B lane l holds B[8*(l/16) .. +7][l%16], D lane l
 // register i holds D[4*(l/16) + i][l%16].
+// Steps of 16 keys, software-pipelined for G <= 8: the K and V rows of the
+// next step are requested before the current step is multiplied, so every
+// wave keeps loads in flight while it computes (two register sets of one step
+// each).
 template <int D, int GM>
 struct DecodeWave {
   static constexpr int VPL = D / 64;            // output dims per lane in P.V
   static constexpr int KS = D / 32;             // MFMA k-steps
-  static constexpr int SUB = GM > 8 ? 16 : 32;  // keys per online-softmax step (registers bound it at G = 16)
-  static constexpr int MT = SUB / 16;           // 16-key MFMA tiles per step
+  static constexpr int SUB = 16;                // keys per online-softmax step
+  static constexpr int NSTEP = kBlock / SUB;
+  // At G > 8 the 16 heads' accumulators leave no registers for a second step in flight.
+  static constexpr bool kPipelined = GM <= 8;
   float m_run = -__builtin_inff(), l_run = 0.f;  // head l16's running max (base 2) and sum
   float acc[GM][VPL];
 
@@ -322,94 +334,124 @@ struct DecodeWave {
     }
   }
 
-  // Keys [0, nvalid) of the block whose head-g rows start at k + base / v + base.
-  // p_w, alpha_w: this wave's LDS scratch for the P rows and the rescale factors.
+  // Requests the V rows (lane: dims lane*VPL ..) and the K operand rows of
+  // keys [c0, c0 + 16); keys at or past nvalid read key nvalid-1.  kr, vr:
+  // buffer resources over the block-head's K and V rows; ks_b: the key
+  // stride in bytes.  A V row's offset is the same in every lane (a scalar
+  // offset); each lane adds only its own dims.
+  __device__ __forceinline__ void issue(__amdgpu_buffer_rsrc_t kr, __amdgpu_buffer_rsrc_t vr, int ks_b, int nvalid,
+                                        int c0, uint32_t (&vreg)[SUB], bf16x8 (&ak)[KS]) const {
+    const int lane = threadIdx.x & 63;
+    const int l16 = lane & 15, q16 = lane >> 4;
+#pragma unroll
+    for (int kk = 0; kk < SUB; ++kk) {
+      const int soff = min(c0 + kk, nvalid - 1) * ks_b;
+      if constexpr (VPL == 2)
+        vreg[kk] = __builtin_amdgcn_raw_buffer_load_b32(vr, lane * 4, soff, 0);
+      else
+        vreg[kk] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(vr, lane * 2, soff, 0);
+    }
+    const int koff = min(c0 + l16, nvalid - 1) * ks_b + q16 * 16;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const auto x = __builtin_amdgcn_raw_buffer_load_b128(kr, koff + ks * 64, 0, 0);
+      ak[ks] = as_bf16x8(u32x4{x[0], x[1], x[2], x[3]});
+    }
+  }
+
+  // One step: scores of keys [c0, c0 + 16), the running softmax, and P.V.
+  __device__ __forceinline__ void step(int nvalid, int c0, const uint32_t (&vreg)[SUB], const bf16x8 (&ak)[KS],
+                                       const bf16x8 (&bq)[KS], float c, float (&p_w)[GM][SUB],
+                                       float (&alpha_w)[GM]) {
+    const int lane = threadIdx.x & 63;
+    const int l16 = lane & 15, q16 = lane >> 4;
+    f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak[ks], bq[ks], sacc, 0, 0, 0);
+    // lane (head l16, q16) holds keys c0 + 4*q16 + i
+    float sc[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sc[i] = c0 + 4 * q16 + i < nvalid ? sacc[i] : -__builtin_inff();
+    float mx = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_new = fmaxf(m_run, mx * c);  // finite: key c0 is valid
+    const float alpha = fast_exp2(m_run - m_new);
+    float psum = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float pe = fast_exp2(fmaf(sc[i], c, -m_new));
+      psum += pe;
+      if (l16 < GM) p_w[l16][4 * q16 + i] = pe;
+    }
+    psum += __shfl_xor(psum, 16);
+    psum += __shfl_xor(psum, 32);
+    l_run = fmaf(l_run, alpha, psum);
+    m_run = m_new;
+    if (q16 == 0 && l16 < GM) alpha_w[l16] = alpha;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+#pragma unroll
+    for (int j = 0; j < GM; ++j) {
+      const float al = alpha_w[j];
+#pragma unroll
+      for (int vv = 0; vv < VPL; ++vv) acc[j][vv] *= al;
+    }
+#pragma unroll
+    for (int k4 = 0; k4 < SUB / 4; ++k4) {
+      float vf[4][VPL];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        // keys past nvalid carry p = 0; their V (a valid row's) is zeroed too
+        const uint32_t w = c0 + k4 * 4 + i < nvalid ? vreg[k4 * 4 + i] : 0u;
+        vf[i][0] = bf16_to_f32(w & 0xffffu);
+        if constexpr (VPL == 2) vf[i][1] = bf16_to_f32(w >> 16);
+      }
+#pragma unroll
+      for (int j = 0; j < GM; ++j) {
+        const f32x4 pj = *reinterpret_cast<const f32x4*>(&p_w[j][k4 * 4]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int vv = 0; vv < VPL; ++vv) acc[j][vv] = fmaf(pj[i], vf[i][vv], acc[j][vv]);
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+  }
+
+  // Keys [0, nvalid) of the block whose head-g rows start at k + base / v + base
+  // (1 <= nvalid <= 128).  p_w, alpha_w: this wave's LDS scratch for the P rows
+  // and the rescale factors.  PIPE: request the next step before the current
+  // one is multiplied (needs the second register set).
+  template <bool PIPE = kPipelined>
   __device__ __forceinline__ void attend_block(const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
                                                int64_t base, int64_t key_stride, int nvalid, const bf16x8 (&bq)[KS],
                                                float c, float (&p_w)[GM][SUB], float (&alpha_w)[GM]) {
-    const int lane = threadIdx.x & 63;
-    const int l16 = lane & 15, q16 = lane >> 4;
-    const uint16_t* kb = k + base;
-    const uint16_t* vb = v + base;
-    for (int c0 = 0; c0 < nvalid; c0 += SUB) {
-      uint32_t vreg[SUB];
+    const int ks_b = (int)(key_stride * 2);
+    const uint32_t bytes = (uint32_t)((kBlock - 1) * ks_b + D * 2);
+    const __amdgpu_buffer_rsrc_t kb = buffer_rsrc(k + base, bytes), vb = buffer_rsrc(v + base, bytes);
+    if constexpr (PIPE) {
+      uint32_t vreg[2][SUB];
+      bf16x8 ak[2][KS];
+      issue(kb, vb, ks_b, nvalid, 0, vreg[0], ak[0]);
 #pragma unroll
-      for (int kk = 0; kk < SUB; ++kk) {
-        const int key = min(c0 + kk, nvalid - 1);
-        if constexpr (VPL == 2)
-          vreg[kk] = *reinterpret_cast<const uint32_t*>(vb + key * key_stride + lane * 2);
-        else
-          vreg[kk] = (uint32_t)vb[key * key_stride + lane];
+      for (int st = 0; st < NSTEP; ++st) {
+        const int c0 = st * SUB;
+        if (c0 >= nvalid) break;
+        if (st + 1 < NSTEP && c0 + SUB < nvalid)
+          issue(kb, vb, ks_b, nvalid, c0 + SUB, vreg[(st + 1) & 1], ak[(st + 1) & 1]);
+        step(nvalid, c0, vreg[st & 1], ak[st & 1], bq, c, p_w, alpha_w);
       }
-#pragma unroll
-      for (int kk = 0; kk < SUB; ++kk) vreg[kk] = c0 + kk < nvalid ? vreg[kk] : 0u;
-      float sc[4 * MT];
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        const int key = c0 + mt * 16 + l16;
-        const uint16_t* krow = kb + min(key, nvalid - 1) * key_stride + q16 * 8;
+    } else {
+      for (int c0 = 0; c0 < nvalid; c0 += SUB) {
+        uint32_t vreg[SUB];
         bf16x8 ak[KS];
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          const u32x4 x = load16(krow + ks * 32);
-          ak[ks] = as_bf16x8(key < nvalid ? x : u32x4{0u, 0u, 0u, 0u});
-        }
-        f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak[ks], bq[ks], sacc, 0, 0, 0);
-        // lane (head l16, q16) holds keys c0 + mt*16 + 4*q16 + i
-#pragma unroll
-        for (int i = 0; i < 4; ++i) sc[mt * 4 + i] = c0 + mt * 16 + 4 * q16 + i < nvalid ? sacc[i] : -__builtin_inff();
+        issue(kb, vb, ks_b, nvalid, c0, vreg, ak);
+        step(nvalid, c0, vreg, ak, bq, c, p_w, alpha_w);
       }
-      float mx = sc[0];
-#pragma unroll
-      for (int e = 1; e < 4 * MT; ++e) mx = fmaxf(mx, sc[e]);
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m_run, mx * c);  // finite: key c0 is valid
-      const float alpha = fast_exp2(m_run - m_new);
-      float psum = 0.f;
-#pragma unroll
-      for (int e = 0; e < 4 * MT; ++e) {
-        const float pe = fast_exp2(fmaf(sc[e], c, -m_new));
-        psum += pe;
-        if (l16 < GM) p_w[l16][(e >> 2) * 16 + 4 * q16 + (e & 3)] = pe;
-      }
-      psum += __shfl_xor(psum, 16);
-      psum += __shfl_xor(psum, 32);
-      l_run = fmaf(l_run, alpha, psum);
-      m_run = m_new;
-      if (q16 == 0 && l16 < GM) alpha_w[l16] = alpha;
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-#pragma unroll
-      for (int j = 0; j < GM; ++j) {
-        const float al = alpha_w[j];
-#pragma unroll
-        for (int vv = 0; vv < VPL; ++vv) acc[j][vv] *= al;
-      }
-#pragma unroll
-      for (int k4 = 0; k4 < SUB / 4; ++k4) {
-        __builtin_amdgcn_sched_barrier(0);  // four keys at a time: bounds live P and V registers
-        float vf[4][VPL];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          vf[i][0] = bf16_to_f32(vreg[k4 * 4 + i] & 0xffffu);
-          if constexpr (VPL == 2) vf[i][1] = bf16_to_f32(vreg[k4 * 4 + i] >> 16);
-        }
-#pragma unroll
-        for (int j = 0; j < GM; ++j) {
-          const f32x4 pj = *reinterpret_cast<const f32x4*>(&p_w[j][k4 * 4]);
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int vv = 0; vv < VPL; ++vv) acc[j][vv] = fmaf(pj[i], vf[i][vv], acc[j][vv]);
-        }
-      }
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
     }
   }
 

@@ -311,8 +311,8 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void dense_decode_kernel(DenseDe
     for (int b = b0 + w; b < b_end; b += kDecodeWaves) {
       const int phys = bt[b];
       if (phys < 0 || phys >= p.num_blocks) continue;  // absent blocks hold no keys
-      st.attend_block(p.k, p.v, ((int64_t)phys * kBlock * p.hkv + g) * D, (int64_t)p.hkv * D,
-                      min(kBlock, t - b * kBlock + 1), bq, p.scale_log2e, p_s[w], alpha_s[w]);
+      st.template attend_block<false>(p.k, p.v, ((int64_t)phys * kBlock * p.hkv + g) * D, (int64_t)p.hkv * D,
+                                      min(kBlock, t - b * kBlock + 1), bq, p.scale_log2e, p_s[w], alpha_s[w]);
     }
   }
   st.store(o_s[w], m_s[w], l_s[w]);
@@ -374,6 +374,8 @@ static void launch_dense_decode_t(const DenseDecodeArgs& a, hipStream_t stream) 
   const dim3 grid(a.n_split, a.p.hkv, a.p.num_seqs);
   if (a.p.group <= 4)
     hipLaunchKernelGGL((dense_decode_kernel<D, 4>), grid, dim3(64 * kDecodeWaves), 0, stream, a);
+  else if (a.p.group <= 6)
+    hipLaunchKernelGGL((dense_decode_kernel<D, 6>), grid, dim3(64 * kDecodeWaves), 0, stream, a);
   else if (a.p.group <= 8)
     hipLaunchKernelGGL((dense_decode_kernel<D, 8>), grid, dim3(64 * kDecodeWaves), 0, stream, a);
   else
