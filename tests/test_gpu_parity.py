@@ -118,6 +118,25 @@ def test_decode_large_batch_one_workgroup_per_group(shape):
     check_selection_invariants(runner)
 
 
+@pytest.mark.parametrize("group", [3, 5, 7])
+@pytest.mark.parametrize("path", ["decode_fused", "decode_split", "prefill"])
+def test_group_sizes_between_instantiations(group, path):
+    """Group sizes the kernels pad to the next instantiated head count
+    (3 -> 4, 5 -> 6, 7 -> 8): the padded heads must not leak into the output."""
+    import dataclasses
+    w0 = dataclasses.replace(M2, num_q_heads=8 * group)
+    if path == "decode_fused":
+        w = w0.with_sizes(f"g{group}_fused", _RAGGED, [1] * 16, permuted_table=True)
+        assert w.num_seqs * w.num_kv_heads >= 128
+    elif path == "decode_split":
+        w = w0.with_sizes(f"g{group}_split", _RAGGED[:8], [1] * 8, permuted_table=True)
+    else:
+        w = w0.with_sizes(f"g{group}_prefill", [2600, 300], [2600, 40], permuted_table=True)
+    runner = _run(w)
+    _all_rows(runner)
+    check_selection_invariants(runner)
+
+
 @pytest.mark.parametrize("case", ["decode_fused", "decode_split", "prefill"])
 def test_graph_replays_equal_eager_step(case):
     """A captured step replays to the eager step's results, replay after replay,
