@@ -256,12 +256,12 @@ __device__ __forceinline__ void load_q_raw(const uint16_t* __restrict__ qrow, QR
   const int h = lane >> 5, a16 = (lane >> 4) & 1;
   const uint64_t own = reinterpret_cast<uint64_t>(qrow);
   const uint64_t other = ((uint64_t)partner16((uint32_t)(own >> 32)) << 32) | partner16((uint32_t)own);
-  const uint16_t* rowA = reinterpret_cast<const uint16_t*>(a16 ? other : own);  // tile row b
-  const uint16_t* rowB = reinterpret_cast<const uint16_t*>(a16 ? own : other);  // tile row 16 + b
+  const uint64_t rowA = a16 ? other : own;  // tile row b
+  const uint64_t rowB = a16 ? own : other;  // tile row 16 + b
 #pragma unroll
   for (int j = 0; j < D / 32; ++j) {
-    raw.a[j] = load16(rowA + (4 * j + 2 * a16 + h) * 8);
-    raw.b[j] = load16(rowB + (4 * j + 2 * (1 - a16) + h) * 8);
+    raw.a[j] = load16_global(rowA + (uint64_t)((4 * j + 2 * a16 + h) * 16));
+    raw.b[j] = load16_global(rowB + (uint64_t)((4 * j + 2 * (1 - a16) + h) * 16));
   }
 }
 

@@ -64,6 +64,13 @@ __device__ __forceinline__ float swap_halves(float v) {
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 __device__ __forceinline__ u32x4 load16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+// A 16-byte global-memory load from an address held as an integer.  A pointer
+// rebuilt from an integer has no known address space, and the compiler would
+// emit a flat load, which also counts against the LDS wait counter, so every
+// later wait for an LDS read would wait for this load as well.
+__device__ __forceinline__ u32x4 load16_global(uint64_t addr) {
+  return *reinterpret_cast<const __attribute__((address_space(1))) u32x4*>(addr);
+}
 __device__ __forceinline__ void store16(void* p, const u32x4& v) { *reinterpret_cast<u32x4*>(p) = v; }
 
 // Sequence of a query row: largest s with cu_q[s] <= row (cu_q ascending).
