@@ -131,7 +131,7 @@ struct CsrArgs {
 // (after the scans): turn it into write positions and scatter the entries.
 template <bool FILL>
 __global__ __launch_bounds__(256) void csr_chunk_kernel(CsrArgs a) {
-  extern __shared__ int32_t hist[];  // [mbps]
+  extern __shared__ int32_t hist[];  // [mbps] counts, then [mbps] bytes: block b maps to a cached block
   const Problem& p = a.p;
   const int k = blockIdx.x, g = blockIdx.y, s = blockIdx.z;
   const int mbps = p.max_blocks_per_seq;
@@ -143,14 +143,22 @@ __global__ __launch_bounds__(256) void csr_chunk_kernel(CsrArgs a) {
   const int nrows = max(0, min(nq - i0, kCsrRows));
   const int64_t list0 = ((int64_t)s * p.hkv + g) * mbps;
   int32_t* mat = a.cnt_mat + (((int64_t)s * p.hkv + g) * a.csr_chunks + k) * mbps;
-
-  for (int b = threadIdx.x; b < mbps; b += blockDim.x) hist[b] = 0;
+  // The sequence's block table, read once: entry (t, b) is attended iff
+  // 0 <= b <= t/128 and block b maps to a cached block (entry_valid).
+  uint8_t* mapped = reinterpret_cast<uint8_t*>(hist + mbps);
+  const int32_t* table = p.block_table + (int64_t)s * mbps;
+  for (int b = threadIdx.x; b < mbps; b += blockDim.x) {
+    hist[b] = 0;
+    const int phys = table[b];
+    mapped[b] = phys >= 0 && phys < p.num_blocks;
+  }
   __syncthreads();
+  auto valid = [&](int b, int t) { return b >= 0 && b <= (t >> 7) && mapped[b]; };  // t < seq_len <= mbps * 128
   for (int idx = threadIdx.x; idx < nrows * kTopK; idx += blockDim.x) {
     const int i = i0 + (idx >> 4), slot = idx & 15;
     const int64_t R = ((int64_t)(row0 + i) << a.hkv_shift) + g;
     const int b = a.sel[R * kTopK + slot];
-    if (entry_valid(p, s, b, first_pos + i)) atomicAdd(&hist[b], 1);
+    if (valid(b, first_pos + i)) atomicAdd(&hist[b], 1);
   }
   __syncthreads();
   if (!FILL) {
@@ -163,7 +171,7 @@ __global__ __launch_bounds__(256) void csr_chunk_kernel(CsrArgs a) {
     const int i = i0 + (idx >> 4), slot = idx & 15;
     const int64_t R = ((int64_t)(row0 + i) << a.hkv_shift) + g;
     const int b = a.sel[R * kTopK + slot];
-    if (entry_valid(p, s, b, first_pos + i)) {
+    if (valid(b, first_pos + i)) {
       const int pos = atomicAdd(&hist[b], 1);
       a.entries[pos] = (int32_t)((R << 4) | slot);
       a.entry_of[R * kTopK + slot] = pos;
@@ -726,7 +734,7 @@ static hipError_t launch_main_t(const Problem& p, const uint16_t* q, const int32
               reinterpret_cast<int32_t*>(base + w.chunk_list), reinterpret_cast<int32_t*>(base + w.entries),
               reinterpret_cast<int32_t*>(base + w.entry_of), w.n_lists, w.csr_chunks, hs, w.chunk};
     const dim3 cgrid(w.csr_chunks, p.hkv, p.num_seqs);
-    const size_t lds = sizeof(int32_t) * p.max_blocks_per_seq;
+    const size_t lds = sizeof(int32_t) * p.max_blocks_per_seq + ((p.max_blocks_per_seq + 3) & ~3);
     const unsigned list_blocks = (unsigned)((w.n_lists + 255) / 256);
     hipLaunchKernelGGL((csr_chunk_kernel<false>), cgrid, dim3(256), lds, stream, c);
     hipLaunchKernelGGL(csr_colscan_kernel, dim3(list_blocks), dim3(256), 0, stream, c);
