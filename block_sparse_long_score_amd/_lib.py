@@ -17,6 +17,8 @@ MSA_CALL_SPARSE_ATTN_PREFILL = 1
 MSA_CALL_SPARSE_ATTN_DECODE = 2
 MSA_CALL_DENSE_ATTN_DECODE = 3
 MSA_CALL_INDEX_SELECT = 4
+MSA_CALL_SPARSE_ATTN_PREFILL_PLAN = 5
+MSA_CALL_SPARSE_ATTN_PREFILL_RUN = 6
 
 
 class MsaDims(ctypes.Structure):
@@ -56,6 +58,8 @@ def load() -> ctypes.CDLL:
         "msa_block_topk": ([dims, batch, vp, i64, vp, vp], ctypes.c_int),
         "msa_sparse_attn_prefill": ([dims, cache, batch, vp, vp, vp, vp, sz, vp], ctypes.c_int),
         "msa_sparse_attn_decode": ([dims, cache, batch, vp, vp, vp, vp, sz, vp], ctypes.c_int),
+        "msa_sparse_attn_prefill_plan": ([dims, cache, batch, vp, vp, sz, vp], ctypes.c_int),
+        "msa_sparse_attn_prefill_run": ([dims, cache, batch, vp, vp, vp, vp, vp, sz, vp], ctypes.c_int),
         "msa_block_attn_mass": ([dims, cache, batch, vp, vp, i32, vp, i64, vp], ctypes.c_int),
         "msa_selection_quality": ([dims, batch, vp, i32, vp, vp, vp, i64, vp, vp], ctypes.c_int),
         "msa_index_select": ([dims, cache, batch, vp, vp, vp, sz, vp], ctypes.c_int),

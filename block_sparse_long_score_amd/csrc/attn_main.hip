@@ -66,8 +66,11 @@ constexpr int64_t kFusedDecodeMinGroups = 128;
 
 // ---------------------------------------------------------------- workspace
 
+// Two regions: the plan (prefill only: the selection inversion) and the
+// partial outputs.  Offsets are relative to the start of their own region.
 struct MainWs {
-  size_t cnt_mat, list_cnt, off, coff, chunk_list, entries, entry_of, part_o, part_st, total;
+  size_t cnt_mat, list_cnt, off, coff, chunk_list, entries, entry_of, plan_total;
+  size_t part_o, part_st, part_total;
   int64_t n_lists, max_entries, max_kv_chunks;
   int csr_chunks;  // row chunks per sequence (grid x of the inversion kernels)
   int chunk;       // entries per kvouter workgroup
@@ -91,14 +94,21 @@ static MainWs main_layout(const Problem& p, bool decode) {
     w.entries = o;    o = align256(o + sizeof(int32_t) * (w.max_entries + 1));
     w.entry_of = o;   o = align256(o + sizeof(int32_t) * w.max_entries);
   }
+  w.plan_total = o;
+  o = 0;
   w.part_o = o;  o = align256(o + sizeof(uint16_t) * parts * p.head_dim);
   w.part_st = o; o = align256(o + sizeof(float) * 2 * parts);
-  w.total = o;
+  w.part_total = o;
   return w;
 }
 
-size_t prefill_workspace_bytes(const Problem& p) { return main_layout(p, false).total; }
-size_t decode_workspace_bytes(const Problem& p) { return main_layout(p, true).total; }
+size_t prefill_plan_bytes(const Problem& p) { return main_layout(p, false).plan_total; }
+size_t prefill_run_bytes(const Problem& p) { return main_layout(p, false).part_total; }
+size_t prefill_workspace_bytes(const Problem& p) {
+  const MainWs w = main_layout(p, false);
+  return w.plan_total + w.part_total;
+}
+size_t decode_workspace_bytes(const Problem& p) { return main_layout(p, true).part_total; }
 
 // An entry (query at position t of sequence s, selected logical block b) is
 // attended iff b is causal for t and the block table names a cached block.
@@ -695,16 +705,61 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
 
 // ------------------------------------------------------------------ launch
 
+// Selection inversion into the plan region: per (sequence, group, block) lists
+// of the (row, slot) entries that selected the block, and the kvouter chunks.
+static hipError_t launch_plan(const Problem& p, const int32_t* sel, void* plan, hipStream_t stream) {
+  const MainWs w = main_layout(p, false);
+  char* base = static_cast<char*>(plan);
+  CsrArgs c{p, sel,
+            reinterpret_cast<int32_t*>(base + w.cnt_mat), reinterpret_cast<int32_t*>(base + w.list_cnt),
+            reinterpret_cast<int32_t*>(base + w.off), reinterpret_cast<int32_t*>(base + w.coff),
+            reinterpret_cast<int32_t*>(base + w.chunk_list), reinterpret_cast<int32_t*>(base + w.entries),
+            reinterpret_cast<int32_t*>(base + w.entry_of), w.n_lists, w.csr_chunks, hkv_shift_of(p), w.chunk};
+  const dim3 cgrid(w.csr_chunks, p.hkv, p.num_seqs);
+  const size_t lds = sizeof(int32_t) * p.max_blocks_per_seq + ((p.max_blocks_per_seq + 3) & ~3);
+  const unsigned list_blocks = (unsigned)((w.n_lists + 255) / 256);
+  hipLaunchKernelGGL((csr_chunk_kernel<false>), cgrid, dim3(256), lds, stream, c);
+  hipLaunchKernelGGL(csr_colscan_kernel, dim3(list_blocks), dim3(256), 0, stream, c);
+  hipLaunchKernelGGL(csr_scan_kernel, dim3(1), dim3(1024), 0, stream, c);
+  hipLaunchKernelGGL((csr_chunk_kernel<true>), cgrid, dim3(256), lds, stream, c);
+  hipLaunchKernelGGL(csr_chunk_map_kernel, dim3(list_blocks), dim3(256), 0, stream, c);
+  return hipGetLastError();
+}
+
 template <int D>
-static hipError_t launch_main_t(const Problem& p, const uint16_t* q, const int32_t* sel, uint16_t* out, void* ws,
-                                bool decode, hipStream_t stream) {
-  const MainWs w = main_layout(p, decode);
-  char* base = static_cast<char*>(ws);
+static hipError_t launch_merge_t(const Problem& p, const int32_t* sel, const int32_t* entry_of, const uint16_t* part_o,
+                                 const float* part_st, uint16_t* out, hipStream_t stream) {
   const int hs = hkv_shift_of(p);
+  MergeArgs m{p, sel, entry_of, part_o, part_st, out, hs};
+  const int64_t threads = ((int64_t)p.total_q << hs) * p.group * (D / 8);
+  hipLaunchKernelGGL(merge_kernel<D>, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream, m);
+  return hipGetLastError();
+}
+
+// kvouter over a computed plan, then the merge.
+template <int D>
+static hipError_t launch_run_t(const Problem& p, const uint16_t* q, const int32_t* sel, const void* plan,
+                               uint16_t* out, void* part, hipStream_t stream) {
+  const MainWs w = main_layout(p, false);
+  const char* pb = static_cast<const char*>(plan);
+  char* wb = static_cast<char*>(part);
+  KvOuterArgs k{p, q, sel, reinterpret_cast<const int32_t*>(pb + w.entries), reinterpret_cast<const int32_t*>(pb + w.off),
+                reinterpret_cast<const int32_t*>(pb + w.coff), reinterpret_cast<const int32_t*>(pb + w.chunk_list),
+                reinterpret_cast<uint16_t*>(wb + w.part_o), out, reinterpret_cast<float*>(wb + w.part_st),
+                w.n_lists, hkv_shift_of(p), w.chunk};
+  hipLaunchKernelGGL(kvouter_kernel<D>, dim3((unsigned)w.max_kv_chunks), dim3(256), 0, stream, k);
+  return launch_merge_t<D>(p, sel, reinterpret_cast<const int32_t*>(pb + w.entry_of), k.part_o, k.part_st, out, stream);
+}
+
+template <int D>
+static hipError_t launch_decode_t(const Problem& p, const uint16_t* q, const int32_t* sel, uint16_t* out, void* ws,
+                                  hipStream_t stream) {
+  const MainWs w = main_layout(p, true);
+  char* base = static_cast<char*>(ws);
   KvOuterArgs k{p, q, sel, nullptr, nullptr, nullptr, nullptr,
                 reinterpret_cast<uint16_t*>(base + w.part_o), out, reinterpret_cast<float*>(base + w.part_st),
-                w.n_lists, hs, w.chunk};
-  if (decode && (int64_t)p.num_seqs * p.hkv >= kFusedDecodeMinGroups) {
+                w.n_lists, hkv_shift_of(p), w.chunk};
+  if ((int64_t)p.num_seqs * p.hkv >= kFusedDecodeMinGroups) {
     // Enough (sequence, group) pairs to fill the chip: one workgroup each, no merge pass.
     const unsigned n = (unsigned)(p.num_seqs * p.hkv);
     if (p.group <= 4)
@@ -717,55 +772,43 @@ static hipError_t launch_main_t(const Problem& p, const uint16_t* q, const int32
       hipLaunchKernelGGL((decode_fused_kernel<D, 16>), dim3(n), dim3(1024), 0, stream, k);
     return hipGetLastError();
   }
-  if (decode) {
-    const dim3 dgrid(kTopK, p.hkv, p.num_seqs);
-    if (p.group <= 4)
-      hipLaunchKernelGGL((decode_block_kernel<D, 4>), dgrid, dim3(256), 0, stream, k);
-    else if (p.group <= 6)
-      hipLaunchKernelGGL((decode_block_kernel<D, 6>), dgrid, dim3(256), 0, stream, k);
-    else if (p.group <= 8)
-      hipLaunchKernelGGL((decode_block_kernel<D, 8>), dgrid, dim3(256), 0, stream, k);
-    else
-      hipLaunchKernelGGL((decode_block_kernel<D, 16>), dgrid, dim3(256), 0, stream, k);
-  } else {
-    CsrArgs c{p, sel,
-              reinterpret_cast<int32_t*>(base + w.cnt_mat), reinterpret_cast<int32_t*>(base + w.list_cnt),
-              reinterpret_cast<int32_t*>(base + w.off), reinterpret_cast<int32_t*>(base + w.coff),
-              reinterpret_cast<int32_t*>(base + w.chunk_list), reinterpret_cast<int32_t*>(base + w.entries),
-              reinterpret_cast<int32_t*>(base + w.entry_of), w.n_lists, w.csr_chunks, hs, w.chunk};
-    const dim3 cgrid(w.csr_chunks, p.hkv, p.num_seqs);
-    const size_t lds = sizeof(int32_t) * p.max_blocks_per_seq + ((p.max_blocks_per_seq + 3) & ~3);
-    const unsigned list_blocks = (unsigned)((w.n_lists + 255) / 256);
-    hipLaunchKernelGGL((csr_chunk_kernel<false>), cgrid, dim3(256), lds, stream, c);
-    hipLaunchKernelGGL(csr_colscan_kernel, dim3(list_blocks), dim3(256), 0, stream, c);
-    hipLaunchKernelGGL(csr_scan_kernel, dim3(1), dim3(1024), 0, stream, c);
-    hipLaunchKernelGGL((csr_chunk_kernel<true>), cgrid, dim3(256), lds, stream, c);
-    hipLaunchKernelGGL(csr_chunk_map_kernel, dim3(list_blocks), dim3(256), 0, stream, c);
-    k.entries = c.entries;
-    k.off = c.off;
-    k.coff = c.coff;
-    k.chunk_list = c.chunk_list;
-    hipLaunchKernelGGL(kvouter_kernel<D>, dim3((unsigned)w.max_kv_chunks), dim3(256), 0, stream, k);
-  }
-  MergeArgs m{p, sel, decode ? nullptr : reinterpret_cast<const int32_t*>(base + w.entry_of), k.part_o, k.part_st,
-              out, hs};
-  const int64_t threads = ((int64_t)p.total_q << hs) * p.group * (D / 8);
-  hipLaunchKernelGGL(merge_kernel<D>, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream, m);
-  return hipGetLastError();
+  const dim3 dgrid(kTopK, p.hkv, p.num_seqs);
+  if (p.group <= 4)
+    hipLaunchKernelGGL((decode_block_kernel<D, 4>), dgrid, dim3(256), 0, stream, k);
+  else if (p.group <= 6)
+    hipLaunchKernelGGL((decode_block_kernel<D, 6>), dgrid, dim3(256), 0, stream, k);
+  else if (p.group <= 8)
+    hipLaunchKernelGGL((decode_block_kernel<D, 8>), dgrid, dim3(256), 0, stream, k);
+  else
+    hipLaunchKernelGGL((decode_block_kernel<D, 16>), dgrid, dim3(256), 0, stream, k);
+  return launch_merge_t<D>(p, sel, nullptr, k.part_o, k.part_st, out, stream);
+}
+
+hipError_t launch_attn_prefill_plan(const Problem& p, const int32_t* sel, void* plan, hipStream_t stream) {
+  if (p.total_q == 0) return hipSuccess;
+  return launch_plan(p, sel, plan, stream);
+}
+
+hipError_t launch_attn_prefill_run(const Problem& p, const uint16_t* q, const int32_t* sel, const void* plan,
+                                   uint16_t* out, void* part, hipStream_t stream) {
+  if (p.total_q == 0) return hipSuccess;
+  return p.head_dim == 128 ? launch_run_t<128>(p, q, sel, plan, out, part, stream)
+                           : launch_run_t<64>(p, q, sel, plan, out, part, stream);
 }
 
 hipError_t launch_attn_prefill(const Problem& p, const uint16_t* q, const int32_t* sel, uint16_t* out, void* ws,
                                hipStream_t stream) {
   if (p.total_q == 0) return hipSuccess;
-  return p.head_dim == 128 ? launch_main_t<128>(p, q, sel, out, ws, false, stream)
-                           : launch_main_t<64>(p, q, sel, out, ws, false, stream);
+  const hipError_t e = launch_plan(p, sel, ws, stream);
+  if (e != hipSuccess) return e;
+  return launch_attn_prefill_run(p, q, sel, ws, out, static_cast<char*>(ws) + prefill_plan_bytes(p), stream);
 }
 
 hipError_t launch_attn_decode(const Problem& p, const uint16_t* q, const int32_t* sel, uint16_t* out, void* ws,
                               hipStream_t stream) {
   if (p.total_q == 0) return hipSuccess;
-  return p.head_dim == 128 ? launch_main_t<128>(p, q, sel, out, ws, true, stream)
-                           : launch_main_t<64>(p, q, sel, out, ws, true, stream);
+  return p.head_dim == 128 ? launch_decode_t<128>(p, q, sel, out, ws, stream)
+                           : launch_decode_t<64>(p, q, sel, out, ws, stream);
 }
 
 }  // namespace msa

@@ -417,6 +417,14 @@ size_t msa_workspace_size(const msa_dims* dims, const msa_cache* cache, const ms
       if (check_prefill_capacity(dims, cache, batch) != MSA_OK) return 0;
       ok();
       return msa::prefill_workspace_bytes(p);
+    case MSA_CALL_SPARSE_ATTN_PREFILL_PLAN:
+      if (check_prefill_capacity(dims, cache, batch) != MSA_OK) return 0;
+      ok();
+      return msa::prefill_plan_bytes(p);
+    case MSA_CALL_SPARSE_ATTN_PREFILL_RUN:
+      if (check_prefill_capacity(dims, cache, batch) != MSA_OK) return 0;
+      ok();
+      return msa::prefill_run_bytes(p);
     case MSA_CALL_SPARSE_ATTN_DECODE: ok(); return msa::decode_workspace_bytes(p);
     case MSA_CALL_DENSE_ATTN_DECODE: ok(); return msa::dense_decode_workspace_bytes(p, (int)max_query_blocks(batch));
     case MSA_CALL_INDEX_SELECT: {
@@ -443,6 +451,39 @@ msa_status msa_sparse_attn_prefill(const msa_dims* dims, const msa_cache* cache,
   return hip_status(msa::launch_attn_prefill(p, static_cast<const uint16_t*>(q), sel, static_cast<uint16_t*>(out),
                                              workspace, static_cast<hipStream_t>(stream)),
                     "msa_sparse_attn_prefill launch");
+}
+
+msa_status msa_sparse_attn_prefill_plan(const msa_dims* dims, const msa_cache* cache, const msa_batch* batch,
+                                        const int32_t* sel, void* plan, size_t plan_bytes, void* stream) {
+  MSA_TRY(check_dims(dims));
+  MSA_TRY(check_cache(cache));
+  MSA_TRY(check_batch(dims, batch, cache));
+  MSA_TRY(check_ptr(sel, "sel"));
+  MSA_TRY(check_prefill_capacity(dims, cache, batch));
+  const msa::Problem p = make_problem(dims, batch, cache);
+  const size_t need = msa::prefill_plan_bytes(p);
+  if (!plan || plan_bytes < need)
+    return fail(MSA_ERR_WORKSPACE, "plan buffer of %zu bytes given, %zu needed", plan ? plan_bytes : 0, need);
+  if (!aligned16(plan)) return fail(MSA_ERR_MISALIGNED, "plan is not 16-byte aligned");
+  return hip_status(msa::launch_attn_prefill_plan(p, sel, plan, static_cast<hipStream_t>(stream)),
+                    "msa_sparse_attn_prefill_plan launch");
+}
+
+msa_status msa_sparse_attn_prefill_run(const msa_dims* dims, const msa_cache* cache, const msa_batch* batch,
+                                       const void* q, const int32_t* sel, const void* plan, void* out,
+                                       void* workspace, size_t ws_bytes, void* stream) {
+  MSA_TRY(check_attn(dims, cache, batch, q, sel, out));
+  MSA_TRY(check_ptr(plan, "plan"));
+  MSA_TRY(check_prefill_capacity(dims, cache, batch));
+  const msa::Problem p = make_problem(dims, batch, cache);
+  const size_t need = msa::prefill_run_bytes(p);
+  if (!workspace || ws_bytes < need)
+    return fail(MSA_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace ? ws_bytes : 0, need);
+  if (!aligned16(workspace)) return fail(MSA_ERR_MISALIGNED, "workspace is not 16-byte aligned");
+  return hip_status(msa::launch_attn_prefill_run(p, static_cast<const uint16_t*>(q), sel, plan,
+                                                 static_cast<uint16_t*>(out), workspace,
+                                                 static_cast<hipStream_t>(stream)),
+                    "msa_sparse_attn_prefill_run launch");
 }
 
 msa_status msa_sparse_attn_decode(const msa_dims* dims, const msa_cache* cache, const msa_batch* batch, const void* q,

@@ -55,10 +55,17 @@ hipError_t launch_write_subbatch(int32_t* meta, int32_t seq_len, int32_t row_beg
 // per-workgroup LDS histogram holds one counter per logical block).
 constexpr int kMaxPrefillBlocks = 16384;
 
-// Prefill Main Branch (blocks outer, queries inner) and its workspace.
+// Prefill Main Branch (blocks outer, queries inner) and its workspace: the
+// plan (selection inversion) followed by the partial outputs.  The one-call
+// form plans into the start of `ws` and runs with the partials after it.
 size_t prefill_workspace_bytes(const Problem& p);
+size_t prefill_plan_bytes(const Problem& p);
+size_t prefill_run_bytes(const Problem& p);
 hipError_t launch_attn_prefill(const Problem& p, const uint16_t* q, const int32_t* sel, uint16_t* out, void* ws,
                                hipStream_t stream);
+hipError_t launch_attn_prefill_plan(const Problem& p, const int32_t* sel, void* plan, hipStream_t stream);
+hipError_t launch_attn_prefill_run(const Problem& p, const uint16_t* q, const int32_t* sel, const void* plan,
+                                   uint16_t* out, void* part, hipStream_t stream);
 
 // Decode Main Branch (one query per sequence, split over its selected blocks).
 size_t decode_workspace_bytes(const Problem& p);

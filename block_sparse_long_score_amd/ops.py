@@ -15,12 +15,15 @@ import torch
 
 from . import _lib
 from ._lib import (MSA_CALL_DENSE_ATTN_DECODE, MSA_CALL_INDEX_SELECT, MSA_CALL_SPARSE_ATTN_DECODE,
-                   MSA_CALL_SPARSE_ATTN_PREFILL, MsaBatch, MsaCache, MsaDims)
+                   MSA_CALL_SPARSE_ATTN_PREFILL, MSA_CALL_SPARSE_ATTN_PREFILL_PLAN, MSA_CALL_SPARSE_ATTN_PREFILL_RUN,
+                   MsaBatch, MsaCache, MsaDims)
 
 __all__ = ["Dims", "Cache", "Batch", "MsaError", "msa_kv_append", "msa_index_score", "msa_block_topk",
-           "msa_sparse_attn_prefill", "msa_sparse_attn_decode", "msa_dense_attn_prefill", "msa_dense_attn_decode",
+           "msa_sparse_attn_prefill", "msa_sparse_attn_prefill_plan", "msa_sparse_attn_prefill_run",
+           "msa_sparse_attn_decode", "msa_dense_attn_prefill", "msa_dense_attn_decode",
            "msa_index_select", "msa_block_attn_mass", "msa_selection_quality", "msa_workspace_size", "msa_abi_version",
-           "MSA_CALL_SPARSE_ATTN_PREFILL", "MSA_CALL_SPARSE_ATTN_DECODE", "MSA_CALL_DENSE_ATTN_DECODE", "MSA_CALL_INDEX_SELECT"]
+           "MSA_CALL_SPARSE_ATTN_PREFILL", "MSA_CALL_SPARSE_ATTN_DECODE", "MSA_CALL_DENSE_ATTN_DECODE", "MSA_CALL_INDEX_SELECT",
+           "MSA_CALL_SPARSE_ATTN_PREFILL_PLAN", "MSA_CALL_SPARSE_ATTN_PREFILL_RUN"]
 
 
 class MsaError(RuntimeError):
@@ -167,6 +170,27 @@ def _attn(fn_name, dims, cache, batch, q, sel, out, workspace, stream):
 
 def msa_sparse_attn_prefill(dims: Dims, cache: Cache, batch: Batch, q, sel, out, workspace, stream=None):
     _attn("msa_sparse_attn_prefill", dims, cache, batch, q, sel, out, workspace, stream)
+
+
+def msa_sparse_attn_prefill_plan(dims: Dims, cache: Cache, batch: Batch, sel, plan, stream=None):
+    """plan: uint8, at least msa_workspace_size(..., MSA_CALL_SPARSE_ATTN_PREFILL_PLAN) bytes."""
+    L = _lib.load()
+    d, c, b = dims.c(), cache.c(), batch.c()
+    _check(L.msa_sparse_attn_prefill_plan(ctypes.byref(d), ctypes.byref(c), ctypes.byref(b),
+                                          _ptr(sel, "sel", torch.int32), _ptr(plan, "plan", torch.uint8),
+                                          plan.numel(), _stream(stream)))
+
+
+def msa_sparse_attn_prefill_run(dims: Dims, cache: Cache, batch: Batch, q, sel, plan, out, workspace, stream=None):
+    """plan: as written by msa_sparse_attn_prefill_plan for the same dims, cache, batch and sel;
+    workspace: uint8, at least msa_workspace_size(..., MSA_CALL_SPARSE_ATTN_PREFILL_RUN) bytes."""
+    L = _lib.load()
+    d, c, b = dims.c(), cache.c(), batch.c()
+    _check(L.msa_sparse_attn_prefill_run(ctypes.byref(d), ctypes.byref(c), ctypes.byref(b),
+                                         _ptr(q, "q", torch.bfloat16), _ptr(sel, "sel", torch.int32),
+                                         _ptr(plan, "plan", torch.uint8), _ptr(out, "out", torch.bfloat16),
+                                         _ptr(workspace, "workspace", torch.uint8), workspace.numel(),
+                                         _stream(stream)))
 
 
 def msa_sparse_attn_decode(dims: Dims, cache: Cache, batch: Batch, q, sel, out, workspace, stream=None):

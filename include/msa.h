@@ -66,7 +66,7 @@
 extern "C" {
 #endif
 
-#define MSA_ABI_VERSION 1
+#define MSA_ABI_VERSION 2
 
 typedef enum msa_status {
   MSA_OK = 0,
@@ -126,7 +126,9 @@ typedef enum msa_call {
   MSA_CALL_SPARSE_ATTN_PREFILL = 1,
   MSA_CALL_SPARSE_ATTN_DECODE = 2,
   MSA_CALL_DENSE_ATTN_DECODE = 3,
-  MSA_CALL_INDEX_SELECT = 4
+  MSA_CALL_INDEX_SELECT = 4,
+  MSA_CALL_SPARSE_ATTN_PREFILL_PLAN = 5,  /* the plan buffer of msa_sparse_attn_prefill_plan */
+  MSA_CALL_SPARSE_ATTN_PREFILL_RUN = 6    /* the workspace of msa_sparse_attn_prefill_run */
 } msa_call;
 
 /* ------------------------------------------------------------------------- *
@@ -221,6 +223,35 @@ msa_status msa_index_select(const msa_dims* dims, const msa_cache* cache, const 
 msa_status msa_sparse_attn_prefill(const msa_dims* dims, const msa_cache* cache,
                                    const msa_batch* batch, const void* q, const int32_t* sel,
                                    void* out, void* workspace, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------- *
+ * msa_sparse_attn_prefill_plan / msa_sparse_attn_prefill_run — the same
+ * Main Branch ([M3-evo] §2 step 4) in two calls, so that a caller can
+ * prepare the next batch's plan on another stream while this batch attends.
+ * Together they compute exactly what msa_sparse_attn_prefill computes (it is
+ * plan followed by run).
+ *   plan: inverts the selections into one list of (row, slot) entries per
+ *         (sequence, group, block) in `plan`, a device buffer of at least
+ *         msa_workspace_size(dims, cache, batch, MSA_CALL_SPARSE_ATTN_PREFILL_PLAN)
+ *         bytes owned by the caller; its contents on entry are ignored.
+ *   run:  attends every listed row to its block and merges the slots.  `plan`
+ *         must hold the result of msa_sparse_attn_prefill_plan for the same
+ *         dims, cache, batch and sel, unmodified since (run only reads it, so
+ *         one plan serves any number of runs); with anything else the result
+ *         is undefined.  `workspace` holds the partial outputs: at least
+ *         msa_workspace_size(dims, cache, batch, MSA_CALL_SPARSE_ATTN_PREFILL_RUN)
+ *         bytes, contents on entry ignored.  q, sel and out as in
+ *         msa_sparse_attn_prefill.
+ * Errors: NULL_POINTER, BAD_SHAPE, UNSUPPORTED, MISALIGNED, CAPACITY,
+ *         WORKSPACE, HIP.
+ * ------------------------------------------------------------------------- */
+msa_status msa_sparse_attn_prefill_plan(const msa_dims* dims, const msa_cache* cache,
+                                        const msa_batch* batch, const int32_t* sel,
+                                        void* plan, size_t plan_bytes, void* stream);
+msa_status msa_sparse_attn_prefill_run(const msa_dims* dims, const msa_cache* cache,
+                                       const msa_batch* batch, const void* q, const int32_t* sel,
+                                       const void* plan, void* out, void* workspace, size_t ws_bytes,
+                                       void* stream);
 
 /* ------------------------------------------------------------------------- *
  * msa_sparse_attn_decode — the same Main Branch computation for one query

@@ -212,3 +212,30 @@ def test_index_select_validates_on_the_host(lib):
     big = _Batch([1 << 20], [1 << 16])
     size = lib.msa_workspace_size(dp, ctypes.byref(big_c), ctypes.byref(big.c), 4)
     assert (192 << 20) - 8 * 8192 * 4 < size - 256 <= 192 << 20
+
+
+def test_prefill_plan_and_run_validate_on_the_host(lib):
+    d, c = _dims(), _cache()
+    b = _Batch([1024, 900], [300, 2])
+    dp, cp, bp = ctypes.byref(d), ctypes.byref(c), ctypes.byref(b.c)
+    whole = lib.msa_workspace_size(dp, cp, bp, 1)
+    plan = lib.msa_workspace_size(dp, cp, bp, 5)
+    run = lib.msa_workspace_size(dp, cp, bp, 6)
+    assert plan > 0 and run > 0 and plan + run == whole
+    # plan(sel, plan, plan_bytes, stream): every call below fails before any launch
+    assert lib.msa_sparse_attn_prefill_plan(dp, cp, bp, None, FAKE, plan, None) == NULLP
+    assert lib.msa_sparse_attn_prefill_plan(dp, cp, bp, FAKE, None, plan, None) == WS
+    assert lib.msa_sparse_attn_prefill_plan(dp, cp, bp, FAKE, FAKE, plan - 1, None) == WS
+    assert lib.msa_sparse_attn_prefill_plan(dp, cp, bp, FAKE, FAKE + 8, plan, None) == MISAL
+    # run(q, sel, plan, out, workspace, ws_bytes, stream)
+    assert lib.msa_sparse_attn_prefill_run(dp, cp, bp, None, FAKE, FAKE, FAKE, FAKE, run, None) == NULLP
+    assert lib.msa_sparse_attn_prefill_run(dp, cp, bp, FAKE, FAKE, None, FAKE, FAKE, run, None) == NULLP
+    assert lib.msa_sparse_attn_prefill_run(dp, cp, bp, FAKE, FAKE, FAKE + 8, FAKE, FAKE, run, None) == MISAL
+    assert lib.msa_sparse_attn_prefill_run(dp, cp, bp, FAKE, FAKE, FAKE, FAKE, FAKE, run - 1, None) == WS
+    assert lib.msa_sparse_attn_prefill_run(dp, cp, bp, FAKE, FAKE, FAKE, FAKE, None, run, None) == WS
+    # more blocks per sequence than one prefill call supports
+    big = _cache(num_blocks=20000, mbps=20000)
+    assert lib.msa_workspace_size(dp, ctypes.byref(big), bp, 5) == 0
+    assert lib.msa_sparse_attn_prefill_plan(dp, ctypes.byref(big), bp, FAKE, FAKE, 1 << 30, None) == CAP
+    assert lib.msa_sparse_attn_prefill_run(dp, ctypes.byref(big), bp, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30,
+                                           None) == CAP

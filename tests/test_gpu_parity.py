@@ -282,6 +282,29 @@ def test_pipelined_prefill_equals_serial():
     compare_rows(runner_p, 0, _sample_positions(5000, 0, 64, 5))
 
 
+def test_prefill_plan_then_run_equals_one_call():
+    """msa_sparse_attn_prefill_plan followed by msa_sparse_attn_prefill_run
+    writes exactly what msa_sparse_attn_prefill writes, and one plan serves
+    two runs."""
+    w = M2.with_sizes("planrun", [3001, 2500, 129], [3001, 700, 60], permuted_table=True)
+    runner = _run(w)
+    ref = runner.out.clone()
+    dims, cache, batch = runner.dims, runner.cache, runner.batch
+    plan = torch.empty(ops.msa_workspace_size(dims, cache, batch, ops.MSA_CALL_SPARSE_ATTN_PREFILL_PLAN),
+                       dtype=torch.uint8, device="cuda")
+    ws = torch.empty(ops.msa_workspace_size(dims, cache, batch, ops.MSA_CALL_SPARSE_ATTN_PREFILL_RUN),
+                     dtype=torch.uint8, device="cuda")
+    assert plan.numel() + ws.numel() == ops.msa_workspace_size(dims, cache, batch, ops.MSA_CALL_SPARSE_ATTN_PREFILL)
+    ops.msa_sparse_attn_prefill_plan(dims, cache, batch, runner.sel, plan)
+    for i in range(2):
+        out = torch.full_like(ref, float("nan"))
+        ws.fill_(0xFF)
+        ops.msa_sparse_attn_prefill_run(dims, cache, batch, runner.inputs.q, runner.sel, plan, out, ws)
+        torch.cuda.synchronize()
+        _announce(f"planrun: run {i}")
+        assert torch.equal(out.view(torch.int16), ref.view(torch.int16)), f"run {i} differs from the one-call output"
+
+
 def test_two_runs_are_identical():
     w = M2.with_sizes("det", [3000, 2000], [3000, 300])
     runner = _run(w)
