@@ -89,6 +89,22 @@ def test_multi_sequence_prefill_batch():
     check_selection_invariants(runner)
 
 
+@pytest.mark.parametrize("mode", ["many_rows", "single_rows"])
+def test_sequences_without_queries(mode):
+    """Sequences with no query rows this step take no part: the others'
+    selections and outputs are the oracle's, and all outputs are finite
+    (single_rows: one query in each sequence that has any, through the
+    prefill entry points, which allow empty sequences)."""
+    if mode == "many_rows":
+        w = M2.with_sizes("noq_prefill", [2000, 500, 4200, 129], [0, 300, 0, 129], permuted_table=True)
+    else:
+        w = M2.with_sizes("noq_single", [2000, 500, 4200, 129, 3000], [0, 1, 0, 1, 1], permuted_table=True)
+    runner = _run(w)
+    _all_rows(runner)
+    check_selection_invariants(runner)
+    assert torch.isfinite(runner.out.float()).all()
+
+
 def test_decode_batch_ragged_lengths():
     runner = _run(M2.with_sizes("decode", [1, 128, 129, 2049, 5000, 9999, 16 * 128, 16 * 128 + 1], [1] * 8,
                                 permuted_table=True))
