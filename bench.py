@@ -270,8 +270,8 @@ def main():
                     help="replay an unchunked step from a captured HIP graph (stage events then come from a serial pass)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this build measures one GPU only; the MSA hot path is not sharded across GPUs "
-              "(see the sharding paragraph of the design notes). Run with --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU only: the MSA hot path is not sharded across GPUs (sequences, KV groups "
+              "or context blocks would be the shard units). Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     import torch
