@@ -22,6 +22,7 @@ __all__ = ["Dims", "Cache", "Batch", "MsaError", "msa_kv_append", "msa_index_sco
            "msa_sparse_attn_prefill", "msa_sparse_attn_prefill_plan", "msa_sparse_attn_prefill_run",
            "msa_sparse_attn_decode", "msa_dense_attn_prefill", "msa_dense_attn_decode",
            "msa_index_select", "msa_block_attn_mass", "msa_selection_quality", "msa_workspace_size", "msa_abi_version",
+           "PreparedCall", "prepare",
            "MSA_CALL_SPARSE_ATTN_PREFILL", "MSA_CALL_SPARSE_ATTN_DECODE", "MSA_CALL_DENSE_ATTN_DECODE", "MSA_CALL_INDEX_SELECT",
            "MSA_CALL_SPARSE_ATTN_PREFILL_PLAN", "MSA_CALL_SPARSE_ATTN_PREFILL_RUN"]
 
@@ -127,28 +128,72 @@ def msa_abi_version() -> int:
     return int(_lib.load().msa_abi_version())
 
 
+# Argument marshalling of the calls a step repeats: each returns the C
+# arguments before the stream.  ctypes.byref keeps its struct alive.
+def _kv_append_args(dims, cache, batch, k_new, v_new, k_idx_new):
+    return (ctypes.byref(dims.c()), ctypes.byref(cache.c()), ctypes.byref(batch.c()),
+            _ptr(k_new, "k_new", torch.bfloat16), _ptr(v_new, "v_new", torch.bfloat16),
+            _ptr(k_idx_new, "k_idx_new", torch.bfloat16))
+
+
+def _index_score_args(dims, cache, batch, q_idx, block_scores):
+    return (ctypes.byref(dims.c()), ctypes.byref(cache.c()), ctypes.byref(batch.c()),
+            _ptr(q_idx, "q_idx", torch.bfloat16), _ptr(block_scores, "block_scores", torch.float32),
+            block_scores.shape[-1])
+
+
+def _block_topk_args(dims, batch, block_scores, sel):
+    return (ctypes.byref(dims.c()), ctypes.byref(batch.c()), _ptr(block_scores, "block_scores", torch.float32),
+            block_scores.shape[-1], _ptr(sel, "sel", torch.int32))
+
+
+def _attn_args(dims, cache, batch, q, sel, out, workspace):
+    return (ctypes.byref(dims.c()), ctypes.byref(cache.c()), ctypes.byref(batch.c()), _ptr(q, "q", torch.bfloat16),
+            _ptr(sel, "sel", torch.int32), _ptr(out, "out", torch.bfloat16),
+            _ptr(workspace, "workspace", torch.uint8), workspace.numel())
+
+
+_MARSHAL = {"msa_kv_append": _kv_append_args, "msa_index_score": _index_score_args,
+            "msa_block_topk": _block_topk_args, "msa_sparse_attn_prefill": _attn_args,
+            "msa_sparse_attn_decode": _attn_args}
+
+
+class PreparedCall:
+    """One C-ABI call with its arguments marshalled once, for loops that repeat
+    the same call on the same buffers (a decode or prefill step): calling it
+    costs one ctypes call (the library still validates every argument)
+    instead of rebuilding the structs and re-checking every tensor.  It keeps
+    the objects it was prepared from alive; their contents may change between
+    calls, their storage and shapes may not."""
+    __slots__ = ("_fn", "_args", "_keep")
+
+    def __init__(self, name, args, keep):
+        self._fn = getattr(_lib.load(), name)
+        self._args = args
+        self._keep = keep
+
+    def __call__(self, stream=None):
+        _check(self._fn(*self._args, _stream(stream)))
+
+
+def prepare(name: str, *args) -> PreparedCall:
+    """PreparedCall for one of msa_kv_append, msa_index_score, msa_block_topk,
+    msa_sparse_attn_prefill, msa_sparse_attn_decode, with the same positional
+    arguments as the function of that name (without the stream)."""
+    return PreparedCall(name, _MARSHAL[name](*args), args)
+
+
 def msa_kv_append(dims: Dims, cache: Cache, batch: Batch, k_new, v_new, k_idx_new, stream=None):
-    L = _lib.load()
-    d, c, b = dims.c(), cache.c(), batch.c()
-    _check(L.msa_kv_append(ctypes.byref(d), ctypes.byref(c), ctypes.byref(b), _ptr(k_new, "k_new", torch.bfloat16),
-                           _ptr(v_new, "v_new", torch.bfloat16), _ptr(k_idx_new, "k_idx_new", torch.bfloat16),
-                           _stream(stream)))
+    _check(_lib.load().msa_kv_append(*_kv_append_args(dims, cache, batch, k_new, v_new, k_idx_new), _stream(stream)))
 
 
 def msa_index_score(dims: Dims, cache: Cache, batch: Batch, q_idx, block_scores, stream=None):
     """block_scores: float32 [total_q, Hkv, ld]; entries after each row's block are left untouched."""
-    L = _lib.load()
-    d, c, b = dims.c(), cache.c(), batch.c()
-    _check(L.msa_index_score(ctypes.byref(d), ctypes.byref(c), ctypes.byref(b), _ptr(q_idx, "q_idx", torch.bfloat16),
-                             _ptr(block_scores, "block_scores", torch.float32), block_scores.shape[-1],
-                             _stream(stream)))
+    _check(_lib.load().msa_index_score(*_index_score_args(dims, cache, batch, q_idx, block_scores), _stream(stream)))
 
 
 def msa_block_topk(dims: Dims, batch: Batch, block_scores, sel, stream=None):
-    L = _lib.load()
-    d, b = dims.c(), batch.c()
-    _check(L.msa_block_topk(ctypes.byref(d), ctypes.byref(b), _ptr(block_scores, "block_scores", torch.float32),
-                            block_scores.shape[-1], _ptr(sel, "sel", torch.int32), _stream(stream)))
+    _check(_lib.load().msa_block_topk(*_block_topk_args(dims, batch, block_scores, sel), _stream(stream)))
 
 
 def msa_workspace_size(dims: Dims, cache: Cache, batch: Batch, call: int) -> int:
@@ -161,11 +206,7 @@ def msa_workspace_size(dims: Dims, cache: Cache, batch: Batch, call: int) -> int
 
 
 def _attn(fn_name, dims, cache, batch, q, sel, out, workspace, stream):
-    L = _lib.load()
-    d, c, b = dims.c(), cache.c(), batch.c()
-    _check(getattr(L, fn_name)(ctypes.byref(d), ctypes.byref(c), ctypes.byref(b), _ptr(q, "q", torch.bfloat16),
-                               _ptr(sel, "sel", torch.int32), _ptr(out, "out", torch.bfloat16),
-                               _ptr(workspace, "workspace", torch.uint8), workspace.numel(), _stream(stream)))
+    _check(getattr(_lib.load(), fn_name)(*_attn_args(dims, cache, batch, q, sel, out, workspace), _stream(stream)))
 
 
 def msa_sparse_attn_prefill(dims: Dims, cache: Cache, batch: Batch, q, sel, out, workspace, stream=None):

@@ -56,6 +56,7 @@ class MsaRunner:
         # (phase 0) and after (phase 1) each stage is enqueued in step(), with
         # the stream it is enqueued on (used to time a stage with events).
         self.hook = None
+        self._prepared, self._prepared_key = None, None
 
     def _fill_prefix(self):
         """Cache every token before the step's queries, one sequence at a time."""
@@ -71,20 +72,50 @@ class MsaRunner:
             lo, hi = int(off[s]), int(off[s] + prefix[s])
             ops.msa_kv_append(self.dims, self.cache, b, inp.k[lo:hi], inp.v[lo:hi], inp.k_idx[lo:hi])
 
+    def _calls(self):
+        """The step's C-ABI calls with their arguments marshalled once
+        (ops.prepare), so a step's host work stays far below its GPU time.
+        Rebuilt whenever one of the runner's buffers has been replaced."""
+        key = (id(self.cache), id(self.batch), id(self.scores), id(self.sel), id(self.out), id(self.workspace))
+        if key != self._prepared_key:
+            inp = self.inputs
+            attn = "msa_sparse_attn_decode" if self.decode else "msa_sparse_attn_prefill"
+            whole = {
+                "append": ops.prepare("msa_kv_append", self.dims, self.cache, self.batch, self.k_new, self.v_new,
+                                      self.k_idx_new),
+                "index_score": ops.prepare("msa_index_score", self.dims, self.cache, self.batch, inp.q_idx,
+                                           self.scores),
+                "block_topk": ops.prepare("msa_block_topk", self.dims, self.batch, self.scores, self.sel),
+                "attend": ops.prepare(attn, self.dims, self.cache, self.batch, inp.q, self.sel, self.out,
+                                      self.workspace),
+            }
+            chunks = []
+            for r0, r1, cb in self.chunks:
+                scores, sel = self.scores[r0:r1], self.sel[r0:r1]
+                chunks.append({
+                    "index_score": ops.prepare("msa_index_score", self.dims, self.cache, cb, inp.q_idx[r0:r1], scores),
+                    "block_topk": ops.prepare("msa_block_topk", self.dims, cb, scores, sel),
+                    "attend": ops.prepare("msa_sparse_attn_prefill", self.dims, self.cache, cb, inp.q[r0:r1], sel,
+                                          self.out[r0:r1], self.workspace),
+                })
+            self._prepared, self._prepared_key = (whole, chunks), key
+        return self._prepared
+
     # The four calls of one step, exposed separately so they can be timed.
     def append(self, stream=None):
-        ops.msa_kv_append(self.dims, self.cache, self.batch, self.k_new, self.v_new, self.k_idx_new, stream)
+        self._calls()[0]["append"](stream)
 
     def index_score(self, stream=None):
-        ops.msa_index_score(self.dims, self.cache, self.batch, self.inputs.q_idx, self.scores, stream)
+        self._calls()[0]["index_score"](stream)
 
     def block_topk(self, stream=None):
-        ops.msa_block_topk(self.dims, self.batch, self.scores, self.sel, stream)
+        self._calls()[0]["block_topk"](stream)
 
     def attend(self, sel=None, stream=None):
-        sel = self.sel if sel is None else sel
-        fn = ops.msa_sparse_attn_decode if self.decode else ops.msa_sparse_attn_prefill
-        fn(self.dims, self.cache, self.batch, self.inputs.q, sel, self.out, self.workspace, stream)
+        if sel is not None and sel is not self.sel:
+            fn = ops.msa_sparse_attn_decode if self.decode else ops.msa_sparse_attn_prefill
+            return fn(self.dims, self.cache, self.batch, self.inputs.q, sel, self.out, self.workspace, stream)
+        self._calls()[0]["attend"](stream)
 
     def _stage(self, name, stream, fn):
         if self.hook is None:
@@ -97,10 +128,13 @@ class MsaRunner:
         if self.chunks:
             return self.pipelined_step()
         st = stream if stream is not None else torch.cuda.current_stream()
-        self._stage("append", st, lambda: self.append(st))
-        self._stage("index_score", st, lambda: self.index_score(st))
-        self._stage("block_topk", st, lambda: self.block_topk(st))
-        self._stage("attend", st, lambda: self.attend(stream=st))
+        calls = self._calls()[0]
+        if self.hook is None:
+            for name in ("append", "index_score", "block_topk", "attend"):
+                calls[name](st)
+            return
+        for name in ("append", "index_score", "block_topk", "attend"):
+            self._stage(name, st, lambda: calls[name](st))
 
     def capture(self):
         """Record one unchunked step as a HIP graph, so that replay() issues
@@ -126,19 +160,16 @@ class MsaRunner:
         after each stage (chunk by chunk when chunked) so a caller can record
         an event there.  Used to time the stages one by one."""
         a = torch.cuda.current_stream()
-        inp = self.inputs
+        whole, chunks = self._calls()
         mark("start")
-        self.append(a)
+        whole["append"](a)
         mark("append")
-        parts = self.chunks or [(0, self.inputs.workload.total_q, self.batch)]
-        for r0, r1, cb in parts:
-            scores, sel = self.scores[r0:r1], self.sel[r0:r1]
-            ops.msa_index_score(self.dims, self.cache, cb, inp.q_idx[r0:r1], scores, a)
+        for calls in chunks or [whole]:
+            calls["index_score"](a)
             mark("index_score")
-            ops.msa_block_topk(self.dims, cb, scores, sel, a)
+            calls["block_topk"](a)
             mark("block_topk")
-            fn = ops.msa_sparse_attn_decode if self.decode else ops.msa_sparse_attn_prefill
-            fn(self.dims, self.cache, cb, inp.q[r0:r1], sel, self.out[r0:r1], self.workspace, a)
+            calls["attend"](a)
             mark("attend")
 
     def pipelined_step(self):
@@ -146,16 +177,13 @@ class MsaRunner:
         attention of consecutive chunks overlapped on two streams."""
         a = torch.cuda.current_stream()
         b = self.stream_b
-        inp = self.inputs
-        self._stage("append", a, lambda: self.append(a))
-        for i, (r0, r1, cb) in enumerate(self.chunks):
-            scores, sel = self.scores[r0:r1], self.sel[r0:r1]
-            self._stage("index_score", a,
-                        lambda: ops.msa_index_score(self.dims, self.cache, cb, inp.q_idx[r0:r1], scores, a))
-            self._stage("block_topk", a, lambda: ops.msa_block_topk(self.dims, cb, scores, sel, a))
+        whole, chunks = self._calls()
+        self._stage("append", a, lambda: whole["append"](a))
+        for i, calls in enumerate(chunks):
+            self._stage("index_score", a, lambda: calls["index_score"](a))
+            self._stage("block_topk", a, lambda: calls["block_topk"](a))
             self.events[i].record(a)
             b.wait_event(self.events[i])
-            self._stage("attend", b, lambda: ops.msa_sparse_attn_prefill(
-                self.dims, self.cache, cb, inp.q[r0:r1], sel, self.out[r0:r1], self.workspace, b))
+            self._stage("attend", b, lambda: calls["attend"](b))
         self.events[-1].record(b)
         a.wait_event(self.events[-1])

@@ -239,3 +239,23 @@ def test_prefill_plan_and_run_validate_on_the_host(lib):
     assert lib.msa_sparse_attn_prefill_plan(dp, ctypes.byref(big), bp, FAKE, FAKE, 1 << 30, None) == CAP
     assert lib.msa_sparse_attn_prefill_run(dp, ctypes.byref(big), bp, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30,
                                            None) == CAP
+
+
+def test_prepare_checks_tensors_once_on_the_host(lib):
+    """ops.prepare marshals a call's arguments up front: a wrong dtype or a
+    non-contiguous tensor is refused when the call is prepared (nothing is
+    launched here)."""
+    import torch
+    from block_sparse_long_score_amd import ops
+    dims = ops.Dims(48, 8, 128, 64)
+    batch = ops.Batch.make([300], [300], "cpu")
+    scores = torch.zeros((300, 8, 3), dtype=torch.float32)
+    sel = torch.zeros((300, 8, 16), dtype=torch.int32)
+    call = ops.prepare("msa_block_topk", dims, batch, scores, sel)
+    assert isinstance(call, ops.PreparedCall)
+    with pytest.raises(TypeError):
+        ops.prepare("msa_block_topk", dims, batch, scores.double(), sel)
+    with pytest.raises(ValueError):
+        ops.prepare("msa_block_topk", dims, batch, scores, sel.transpose(0, 1))
+    with pytest.raises(KeyError):
+        ops.prepare("msa_dense_attn_prefill", dims, batch, scores, sel)

@@ -321,6 +321,35 @@ def test_prefill_plan_then_run_equals_one_call():
         assert torch.equal(out.view(torch.int16), ref.view(torch.int16)), f"run {i} differs from the one-call output"
 
 
+@pytest.mark.parametrize("mode", ["prefill", "decode"])
+def test_prepared_step_equals_plain_calls(mode):
+    """The runner's step (C-ABI calls marshalled once) writes exactly what the
+    same four calls write through the plain binding, and it follows the
+    runner's buffers when they are replaced."""
+    if mode == "prefill":
+        w = M2.with_sizes("prep_p", [3000, 1500], [3000, 200], permuted_table=True)
+    else:
+        w = M2.with_sizes("prep_d", _RAGGED, [1] * 16, permuted_table=True)
+    runner = _run(w)
+    d, c, b, inp = runner.dims, runner.cache, runner.batch, runner.inputs
+    scores = torch.full_like(runner.scores, float("nan"))
+    sel = torch.full_like(runner.sel, -7)
+    out = torch.full_like(runner.out, float("nan"))
+    ops.msa_index_score(d, c, b, inp.q_idx, scores)
+    ops.msa_block_topk(d, b, scores, sel)
+    fn = ops.msa_sparse_attn_decode if runner.decode else ops.msa_sparse_attn_prefill
+    fn(d, c, b, inp.q, sel, out, runner.workspace)
+    torch.cuda.synchronize()
+    assert torch.equal(sel, runner.sel)
+    assert torch.equal(out.view(torch.int16), runner.out.view(torch.int16))
+    # replace the output buffer: the next step writes into the new one
+    ref = runner.out.clone()
+    runner.out = torch.full_like(ref, float("nan"))
+    runner.step()
+    torch.cuda.synchronize()
+    assert torch.equal(runner.out.view(torch.int16), ref.view(torch.int16))
+
+
 def test_two_runs_are_identical():
     w = M2.with_sizes("det", [3000, 2000], [3000, 300])
     runner = _run(w)
