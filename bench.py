@@ -14,6 +14,10 @@ at; --workload selects another (c0 tiny prefill, c1 32K prefill, c2 decode of
 32 x 128K, c4d decode of 4 x 1M, c4p 8K chunk onto a 1M cache, m3p / m3d the
 same 128K prefill and 32 x 128K decode with M3's 64 query / 4 KV heads, c1n / c2n
 c1 / c2 with needles planted for the rows whose selection quality is measured).
+With the default c3 headline, the same run then measures c1 and the 8K
+chunk onto a 1M cache (prefill) and the 32 x 128K and 4 x 1M decodes, each
+reported under "legs" with its tokens/s, whole-step fraction of peak and the
+roofline of its dominant stage (--legs selects others, or none).
 """
 from __future__ import annotations
 
@@ -90,15 +94,18 @@ def recorded_traffic(workload: str, stage: str, launches_per_step: float):
 
 
 def selection_quality(runner, n_rows: int):
-    """Coverage, recall and D_KL(P||Q) of the step's selections on evenly spaced
-    query rows, against the dense attention mass P (msa_block_attn_mass), with
-    the mass kernel timed by events.  After the timed region; not part of a step."""
+    """Coverage and recall of the step's selections on evenly spaced query rows
+    against the dense attention mass (msa_block_attn_mass), and the indexer's
+    D_KL(P||Q) over each row's candidate blocks, P the Main Branch's mass over
+    them (msa_block_attn_mass with the selections), with the dense mass kernel
+    timed by events.  After the timed region; not part of a step."""
     import torch
     from block_sparse_long_score_amd import ops
     w, dev = runner.inputs.workload, runner.inputs.q.device
     n = min(n_rows, w.total_q)
     rows = torch.from_numpy(np.unique(np.linspace(0, w.total_q - 1, n).astype(np.int32))).to(dev)
     mass = torch.empty((rows.numel(), w.num_kv_heads, runner.ld), dtype=torch.float32, device=dev)
+    sel_mass = torch.empty_like(mass)
     qual = torch.empty((rows.numel(), w.num_kv_heads, 3), dtype=torch.float32, device=dev)
     runner.step()  # the selections and scores of one step
     ops.msa_block_attn_mass(runner.dims, runner.cache, runner.batch, runner.inputs.q, rows, mass)  # warm-up
@@ -106,7 +113,8 @@ def selection_quality(runner, n_rows: int):
     e0.record()
     ops.msa_block_attn_mass(runner.dims, runner.cache, runner.batch, runner.inputs.q, rows, mass)
     e1.record()
-    ops.msa_selection_quality(runner.dims, runner.batch, rows, mass, runner.scores, runner.sel, qual)
+    ops.msa_block_attn_mass(runner.dims, runner.cache, runner.batch, runner.inputs.q, rows, sel_mass, sel=runner.sel)
+    ops.msa_selection_quality(runner.dims, runner.batch, rows, mass, sel_mass, runner.scores, runner.sel, qual)
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1)
     # positions of the sampled rows -> keys each (row, group) scans: t + 1 (read twice by the two passes)
@@ -118,7 +126,7 @@ def selection_quality(runner, n_rows: int):
     q = qual.cpu().numpy().astype(np.float64)
     blocks = pos // w.block_size + 1
     return {"rows": int(rows.numel()), "coverage_mean": float(q[..., 0].mean()), "recall_mean": float(q[..., 1].mean()),
-            "kl_mean": float(q[..., 2].mean()),
+            "kl_candidates_mean": float(q[..., 2].mean()),
             "uniform_coverage_mean": float(np.mean(np.minimum(w.top_k, blocks) / blocks)),
             "mass_kernel_ms": ms, "mass_kernel_gbs": 2 * k_bytes / (ms / 1e3) / 1e9}
 
@@ -246,6 +254,100 @@ def cpu_baseline(inputs, runner, budget_s: float):
             "host_logical_cpus": os.cpu_count()}
 
 
+def workload_leg(name: str, steps: int, warmup: int, chunk_rows: int):
+    """One more workload measured in the same run, after the headline one: its
+    steps timed back to back (decode steps rotating over two cache copies),
+    each launch of its dominant stage bracketed by events on its stream for
+    the roofline, and a serial stage breakdown.  Its buffers are freed before
+    returning."""
+    import torch
+    from block_sparse_long_score_amd.inputs import WORKLOADS, make_inputs
+    from block_sparse_long_score_amd.pipeline import MsaRunner
+
+    w = WORKLOADS[name]
+    inputs = make_inputs(w, "cuda")
+    runner = MsaRunner(inputs, chunk_rows=chunk_rows or None)
+    runners = [runner] + ([MsaRunner(inputs)] if runner.decode else [])
+    n_rot = len(runners)
+    stream = torch.cuda.current_stream()
+    for i in range(warmup * n_rot):
+        runners[i % n_rot].step()
+    torch.cuda.synchronize()
+
+    def serial_stages():
+        out, marks = {}, []
+
+        def mark(stage):
+            e = torch.cuda.Event(enable_timing=True)
+            e.record(stream)
+            marks.append((stage, e))
+
+        runner.staged_step(mark)
+        torch.cuda.synchronize()
+        for (_, e0), (stage, e1) in zip(marks, marks[1:]):
+            out[stage] = out.get(stage, 0.0) + e0.elapsed_time(e1)
+        return out
+
+    stage_ms = serial_stages()
+    dom = "index_score" if runner.decode else max(("index_score", "attend"), key=lambda k: stage_ms[k])
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for i in range(steps):
+        runners[i % n_rot].step()
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / steps
+    pairs = []
+
+    def hook(stage, st, phase):
+        if stage != dom:
+            return
+        e = torch.cuda.Event(enable_timing=True)
+        e.record(st)
+        if phase == 0:
+            pairs.append([e, None])
+        else:
+            pairs[-1][1] = e
+
+    for r in runners:
+        r.hook = hook
+    for i in range(steps):
+        runners[i % n_rot].step()
+    torch.cuda.synchronize()
+    for r in runners:
+        r.hook = None
+    launch_ms = float(np.mean([a.elapsed_time(b) for a, b in pairs]))
+    launches = len(pairs) / steps
+    work = algorithmic_work(w)
+    leg = {"workload": f"{w.name}: {w.description}", "mode": "decode" if runner.decode else "prefill",
+           "steps": steps, "warmup": warmup, "ms_per_step": ms, "tokens_per_s": w.total_q / (ms / 1e3),
+           "stage_ms_serial": stage_ms}
+    if runner.decode:
+        algo = (work["kidx_bytes"] + work["pooled_bytes"] / 2) / launches
+        gbs = algo / (launch_ms / 1e3) / 1e9
+        step_bytes = work["kidx_bytes"] + work["kv_bytes"] + work["io_bytes"] + work["pooled_bytes"]
+        leg["cache_copies_rotated"] = n_rot
+        leg["hbm_frac_whole_step"] = step_bytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBS
+        leg["algorithmic_bytes_per_step"] = step_bytes
+        leg["roofline"] = {"bound": "hbm", "stage": dom, "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                           "frac": gbs / HBM_PEAK_GBS, "avg_launch_ms": launch_ms,
+                           "algorithmic_bytes_per_launch": algo}
+    else:
+        algo = (work["index_flops"] if dom == "index_score" else work["main_flops"]) / launches
+        tf = algo / (launch_ms / 1e3) / 1e12
+        step_flops = work["index_flops"] + work["main_flops"]
+        leg["pipeline"] = {"chunks": max(1, len(runner.chunks)), "streams": 2 if runner.chunks else 1}
+        leg["mfma_frac_whole_step"] = step_flops / (ms / 1e3) / 1e12 / BF16_PEAK_TFLOPS
+        leg["algorithmic_flops_per_step"] = step_flops
+        leg["roofline"] = {"bound": "mfma", "stage": dom, "achieved": tf, "peak": BF16_PEAK_TFLOPS,
+                           "unit": "TFLOP/s", "frac": tf / BF16_PEAK_TFLOPS, "avg_launch_ms": launch_ms,
+                           "launches_per_step": launches, "algorithmic_flops_per_launch": algo}
+    del runners, runner, inputs
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return leg
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -268,6 +370,10 @@ def main():
                     help="decode workloads: also time this many single steps, each after a 1 GiB write that evicts the Infinity Cache")
     ap.add_argument("--graph", choices=["on", "off"], default="off",
                     help="replay an unchunked step from a captured HIP graph (stage events then come from a serial pass)")
+    ap.add_argument("--legs", default=None,
+                    help="comma-separated workloads also measured in the same run after the headline one "
+                         "(default with the c3 headline: c1,c4p,c2,c4d, so one run reports prefill and decode at "
+                         "128K and 1M; 'none' to skip)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the MSA hot path is not sharded across GPUs (sequences, KV groups "
@@ -465,6 +571,20 @@ def main():
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(inputs, runner, args.cpu_budget)
 
+    legs_arg = args.legs if args.legs is not None else ("c1,c4p,c2,c4d" if args.workload == "c3" else "none")
+    leg_names = [] if legs_arg == "none" else [n for n in legs_arg.split(",") if n and n != args.workload]
+    mode = "decode" if runner.decode else "prefill"
+    pipeline = {"chunks": max(1, len(runner.chunks)), "streams": 2 if runner.chunks else 1,
+                "hip_graph": use_graph, "cache_copies_rotated": n_rot}
+    legs = None
+    if leg_names:  # the headline workload's buffers are released first
+        del runners, runner, steps, step, inputs
+        import gc
+        gc.collect()
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        legs = {n: workload_leg(n, args.steps, args.warmup, args.chunk_rows) for n in leg_names}
+
     line = {
         "metric": METRIC,
         "value": value,
@@ -482,20 +602,20 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (seeded; Q/K/V ~ N(0,1) bf16, dyadic-integer Q_idx/K_idx)",
-        "config": {"workload": f"{w.name}: {w.description}", "mode": "decode" if runner.decode else "prefill",
+        "config": {"workload": f"{w.name}: {w.description}", "mode": mode,
                    "num_seqs": w.num_seqs, "seq_lens": w.seq_lens[0], "query_tokens_per_step": tokens,
                    "q_heads": w.num_q_heads, "kv_heads": w.num_kv_heads, "head_dim": w.head_dim,
                    "index_dim": w.index_dim, "block_size": w.block_size, "top_k": w.top_k},
         "stage_ms": stage_ms,
         "serial_ms_per_step": serial_ms,
-        "pipeline": {"chunks": max(1, len(runner.chunks)), "streams": 2 if runner.chunks else 1,
-                     "hip_graph": use_graph, "cache_copies_rotated": n_rot},
+        "pipeline": pipeline,
         "step": step_info,
         "roofline": roof,
         "cpu_baseline": cpu,
         "selection_quality": quality,
         "cold_cache": cold,
         "dense_attention": dense,
+        "legs": legs,
         "host_wall_s_timed_region": t_host,
     }
     print(json.dumps(line))

@@ -129,7 +129,7 @@ struct CsrArgs {
   int32_t* coff;
   int32_t* chunk_list;
   int32_t* entries;   // list order: (R << 4) | slot
-  int32_t* entry_of;  // [R * 16 + slot] -> position in entries (valid slots only)
+  int32_t* entry_of;  // [R * 16 + slot] -> position in entries, -1 for a slot that is not attended
   int64_t n_lists;
   int csr_chunks;
   int hkv_shift;
@@ -185,6 +185,8 @@ __global__ __launch_bounds__(256) void csr_chunk_kernel(CsrArgs a) {
       const int pos = atomicAdd(&hist[b], 1);
       a.entries[pos] = (int32_t)((R << 4) | slot);
       a.entry_of[R * kTopK + slot] = pos;
+    } else {
+      a.entry_of[R * kTopK + slot] = -1;  // not attended: the merge skips it
     }
   }
 }
@@ -618,7 +620,7 @@ __global__ __launch_bounds__(1024) void decode_fused_kernel(KvOuterArgs a) {
 struct MergeArgs {
   Problem p;
   const int32_t* sel;
-  const int32_t* entry_of;  // prefill: partial entry of (R, slot); decode: NULL (entry = R*16 + slot)
+  const int32_t* entry_of;  // prefill: partial entry of (R, slot), -1 if not attended; decode: NULL (entry = R*16 + slot)
   const uint16_t* part_o;
   const float* part_st;
   uint16_t* out;
@@ -627,8 +629,11 @@ struct MergeArgs {
 
 // One thread per (row, head, 8 consecutive output dims): log-sum-exp over
 // the row's attended slots, then the bf16 output.  A slot is attended iff its
-// block id is causal (0 <= b <= c); the kvouter pass wrote exactly those.  All
-// loads of the 16 slots are issued before any arithmetic.
+// block id is causal (0 <= b <= c) and the block table maps it to a cached
+// block (entry_valid); the attention pass wrote partials for exactly those.
+// Prefill reads that decision from the plan (entry_of = -1 otherwise), decode
+// from the block table.  All loads of the 16 slots are issued before any
+// arithmetic.
 template <int D>
 __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
   constexpr int C8 = D / 8;
@@ -657,9 +662,15 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
     for (int i = 0; i < 4; ++i) {
       const int j = j4 * 4 + i;
       const int bj = (int)bv[i];
-      const bool ok = bj >= 0 && bj <= c;
-      ok_mask |= (ok ? 1u : 0u) << j;
       const int64_t ent = a.entry_of ? (int64_t)(int32_t)ev[i] : R * kTopK + j;
+      bool ok = bj >= 0 && bj <= c;
+      if (a.entry_of) {
+        ok = ok && ent >= 0;
+      } else if (ok) {
+        const int phys = p.block_table[(int64_t)s * p.max_blocks_per_seq + bj];
+        ok = phys >= 0 && phys < p.num_blocks;
+      }
+      ok_mask |= (ok ? 1u : 0u) << j;
       prow[j] = (ok ? ent : 0) * G + hj;
     }
   }
@@ -696,7 +707,7 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
       }
     }
   }
-  const float inv = 1.0f / L;
+  const float inv = L > 0.f ? 1.0f / L : 0.f;  // no attended key (every selected block unmapped): 0
   u32x4 o;
 #pragma unroll
   for (int i = 0; i < 4; ++i) o[i] = pack_bf16x2(acc[2 * i] * inv, acc[2 * i + 1] * inv);

@@ -29,7 +29,7 @@ namespace msa {
 
 struct TopkArgs {
   Problem p;
-  const float* scores;  // row R = r * hkv + g at scores + R * ld
+  const float* scores;  // row R = r * hkv + g at scores + (R - r_base) * ld
   int64_t ld;
   int32_t* sel;
   int hkv_shift;
@@ -172,7 +172,7 @@ __global__ __launch_bounds__(256) void block_topk_kernel(TopkArgs a) {
     if (lane < kTopK) out[lane] = lane <= c ? lane : -1;
     return;
   }
-  const float* row = a.scores + R * a.ld;
+  const float* row = a.scores + (R - a.r_base) * a.ld;
   if (c <= kCached * 64)
     select_row<true>(row, c, out, surv_key[wave], surv_idx[wave]);
   else
@@ -205,7 +205,7 @@ __global__ __launch_bounds__(kSplitWaves * 64) void block_topk_split_kernel(Topk
     if (wave == 0 && lane < kTopK) out[lane] = lane <= c ? lane : -1;
     return;
   }
-  const float* row = a.scores + R * a.ld;
+  const float* row = a.scores + (R - a.r_base) * a.ld;
   // Shares are multiples of 64 candidates; a share of n <= 15 keeps all n.
   const int share = ((c + kSplitWaves * 64 - 1) / (kSplitWaves * 64)) * 64;
   const int lo = min(c, wave * share), n = min(share, c - lo);

@@ -39,6 +39,7 @@ struct IndexArgs {
   int tq;         // queries per tile = 32 * NCT / hkv
   int hkv_shift;  // log2(hkv)
   int kc;         // key blocks per workgroup
+  int64_t first_row;  // out holds rows [first_row, first_row + total_q) of the batch, from its start
 };
 
 // Pooled scores of one key block for every column tile, returned per lane
@@ -154,8 +155,9 @@ __global__ __launch_bounds__(256, 2) void index_score_kernel(IndexArgs a) {
         pool_block<DIDX, NCT, false>(kbase, bq, lim, runmax);
       }
     } else {
+      // A block the table does not map holds no keys: the max over no scores.
 #pragma unroll
-      for (int ct = 0; ct < NCT; ++ct) runmax[ct] = __builtin_nanf("");  // table precondition violated
+      for (int ct = 0; ct < NCT; ++ct) runmax[ct] = -__builtin_inff();
     }
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) {
@@ -174,7 +176,7 @@ __global__ __launch_bounds__(256, 2) void index_score_kernel(IndexArgs a) {
     const int64_t R = ((int64_t)(row0 + pos - first_pos) << a.hkv_shift) + (col & hkv_mask);
     float v = pooled_s[col * ld_s + j];
     v = (v == 0.0f) ? 0.0f : v;  // -0 and +0 are the same score
-    a.out[R * a.ld + kb0 + j] = v;
+    a.out[(R - (a.first_row << a.hkv_shift)) * a.ld + kb0 + j] = v;
   }
 }
 
@@ -348,7 +350,7 @@ __global__ __launch_bounds__(64 * WAVES, WAVES / 2) void index_score_shared_kern
       const int64_t R = ((int64_t)(row0 + pos - first_pos) << a.hkv_shift) + (col & hkv_mask);
       float v = pooled_s[col][j];
       v = (v == 0.0f) ? 0.0f : v;  // -0 and +0 are the same score
-      a.out[R * a.ld + kf + j] = v;
+      a.out[(R - (a.first_row << a.hkv_shift)) * a.ld + kf + j] = v;
     }
   };
 
@@ -365,6 +367,11 @@ __global__ __launch_bounds__(64 * WAVES, WAVES / 2) void index_score_shared_kern
     } else {
       const int lim[NCT] = {};
       shared_pool<DIDX, NCT, false>(kt, bq, lim, runmax);
+    }
+    const int phys = table[kb];
+    if (!(phys >= 0 && phys < p.num_blocks)) {  // an unmapped block holds no keys (its copy read block 0)
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct) runmax[ct] = -__builtin_inff();
     }
     const int slot = i % kSharedFlush;
 #pragma unroll
@@ -478,7 +485,7 @@ __global__ __launch_bounds__(256, 2) void index_score_stream_kernel(IndexArgs a)
       for (int r = 0; r < 16; ++r) runmax = fmaxf(runmax, acc[r]);
     }
     const int phys = table[kb];
-    if (!(phys >= 0 && phys < p.num_blocks)) runmax = __builtin_nanf("");  // table precondition violated
+    if (!(phys >= 0 && phys < p.num_blocks)) runmax = -__builtin_inff();  // an unmapped block holds no keys
     const float v = fmaxf(runmax, swap_halves(runmax));
     if (half == 0) pooled_s[l32 * ld_s + (kb - kb0)] = v;
   }
@@ -493,7 +500,7 @@ __global__ __launch_bounds__(256, 2) void index_score_stream_kernel(IndexArgs a)
     const int64_t R = ((int64_t)(row0 + pos - first_pos) << a.hkv_shift) + (col & hkv_mask);
     float v = pooled_s[col * ld_s + j];
     v = (v == 0.0f) ? 0.0f : v;  // -0 and +0 are the same score
-    a.out[R * a.ld + kb0 + j] = v;
+    a.out[(R - (a.first_row << a.hkv_shift)) * a.ld + kb0 + j] = v;
   }
 }
 
@@ -505,7 +512,8 @@ static hipError_t launch_index_t(const IndexArgs& a, dim3 grid, hipStream_t stre
 }
 
 hipError_t launch_index_score(const Problem& p, const uint16_t* q_idx, float* scores, int64_t ld,
-                              const int32_t* seq_lens_host, const int32_t* cu_q_host, hipStream_t stream) {
+                              const int32_t* seq_lens_host, const int32_t* cu_q_host, hipStream_t stream,
+                              int64_t first_row) {
   int hkv_shift = 0;
   while ((1 << hkv_shift) < p.hkv) ++hkv_shift;
   int max_q = 0;
@@ -529,7 +537,7 @@ hipError_t launch_index_score(const Problem& p, const uint16_t* q_idx, float* sc
     // 16 halves it and the pipelined 128K prefill step is ~3% faster); short
     // contexts keep 16 so the grid still fills the chip.
     const int kc = max_blocks >= 2048 ? 64 : (max_blocks >= 512 ? 32 : 16);
-    IndexArgs a{p, q_idx, scores, ld, tq, hkv_shift, kc};
+    IndexArgs a{p, q_idx, scores, ld, tq, hkv_shift, kc, first_row};
     dim3 grid((unsigned)max_tiles, (unsigned)((max_blocks + kc - 1) / kc), (unsigned)p.num_seqs);
     if (p.index_dim == 64)
       hipLaunchKernelGGL((index_score_shared_kernel<64, 2, 8>), grid, dim3(512), 0, stream, a);
@@ -554,7 +562,7 @@ hipError_t launch_index_score(const Problem& p, const uint16_t* q_idx, float* sc
   }
   // Decode tiles stream at least 2 blocks per wave so each wave's next block is in flight while it multiplies.
   int kc = (int)std::min<int64_t>(64, std::max<int64_t>(nct == 1 ? 8 : 4, (work / 8192 + 3) / 4 * 4));
-  IndexArgs a{p, q_idx, scores, ld, tq, hkv_shift, kc};
+  IndexArgs a{p, q_idx, scores, ld, tq, hkv_shift, kc, first_row};
   dim3 grid((unsigned)max_tiles, (unsigned)((max_blocks + kc - 1) / kc), (unsigned)p.num_seqs);
   if (nct == 1) {
     const size_t lds = (size_t)32 * (a.kc + 1) * sizeof(float);

@@ -276,13 +276,11 @@ msa_status msa_index_select(const msa_dims* dims, const msa_cache* cache, const 
   // Score + select one chunk whose rows are [row_lo, row_lo + pc.total_q) of the batch.
   auto run = [&](msa::Problem pc, const int32_t* lens_host, const int32_t* cu_host, int64_t row_lo,
                  int64_t max_blocks) -> hipError_t {
-    // The chunk's pooled scores sit at the start of the workspace; row R = r * hkv + g of the
-    // batch is addressed globally, so the base is shifted back by the chunk's first row.
-    float* base = reinterpret_cast<float*>(reinterpret_cast<uintptr_t>(scores) -
-                                           (uintptr_t)(row_lo * dims->num_kv_heads * ld) * sizeof(float));
-    hipError_t e = msa::launch_index_score(pc, qi, base, ld, lens_host, cu_host, st);
+    // The chunk's pooled scores sit at the start of the workspace, its first row (row_lo) first;
+    // q_idx and sel are addressed by the batch's own row numbers.
+    hipError_t e = msa::launch_index_score(pc, qi, scores, ld, lens_host, cu_host, st, row_lo);
     if (e != hipSuccess) return e;
-    return msa::launch_block_topk(pc, base, ld, sel, max_blocks, st, row_lo);
+    return msa::launch_block_topk(pc, scores, ld, sel, max_blocks, st, row_lo);
   };
   int s = 0;
   while (s < batch->num_seqs) {
@@ -335,11 +333,13 @@ msa_status msa_index_select(const msa_dims* dims, const msa_cache* cache, const 
 }
 
 msa_status msa_block_attn_mass(const msa_dims* dims, const msa_cache* cache, const msa_batch* batch, const void* q,
-                               const int32_t* rows, int32_t n_rows, float* mass, int64_t ld, void* stream) {
+                               const int32_t* sel, const int32_t* rows, int32_t n_rows, float* mass, int64_t ld,
+                               void* stream) {
   MSA_TRY(check_dims(dims));
   MSA_TRY(check_cache(cache));
   MSA_TRY(check_batch(dims, batch, cache));
   MSA_TRY(check_ptr(q, "q"));
+  if (sel) MSA_TRY(check_ptr(sel, "sel"));
   MSA_TRY(check_ptr(rows, "rows"));
   MSA_TRY(check_ptr(mass, "mass"));
   if (n_rows < 0) return fail(MSA_ERR_BAD_SHAPE, "n_rows=%d is negative", n_rows);
@@ -349,18 +349,19 @@ msa_status msa_block_attn_mass(const msa_dims* dims, const msa_cache* cache, con
   if (ld < need) return fail(MSA_ERR_BAD_SHAPE, "ld=%lld is less than the %lld blocks of the longest sequence",
                              (long long)ld, (long long)need);
   const msa::Problem p = make_problem(dims, batch, cache);
-  return hip_status(msa::launch_block_attn_mass(p, static_cast<const uint16_t*>(q), rows, n_rows, mass, ld,
+  return hip_status(msa::launch_block_attn_mass(p, static_cast<const uint16_t*>(q), sel, rows, n_rows, mass, ld,
                                                 static_cast<hipStream_t>(stream)),
                     "msa_block_attn_mass launch");
 }
 
 msa_status msa_selection_quality(const msa_dims* dims, const msa_batch* batch, const int32_t* rows, int32_t n_rows,
-                                 const float* mass, const float* block_scores, const int32_t* sel, int64_t ld,
-                                 float* quality, void* stream) {
+                                 const float* mass, const float* sel_mass, const float* block_scores,
+                                 const int32_t* sel, int64_t ld, float* quality, void* stream) {
   MSA_TRY(check_dims(dims));
   MSA_TRY(check_batch(dims, batch, nullptr));
   MSA_TRY(check_ptr(rows, "rows"));
   MSA_TRY(check_ptr(mass, "mass"));
+  MSA_TRY(check_ptr(sel_mass, "sel_mass"));
   MSA_TRY(check_ptr(block_scores, "block_scores"));
   MSA_TRY(check_ptr(sel, "sel"));
   MSA_TRY(check_ptr(quality, "quality"));
@@ -371,7 +372,7 @@ msa_status msa_selection_quality(const msa_dims* dims, const msa_batch* batch, c
   if (ld < need) return fail(MSA_ERR_BAD_SHAPE, "ld=%lld is less than the %lld blocks of the longest sequence",
                              (long long)ld, (long long)need);
   const msa::Problem p = make_problem(dims, batch, nullptr);
-  return hip_status(msa::launch_selection_quality(p, rows, n_rows, mass, block_scores, sel, ld, quality,
+  return hip_status(msa::launch_selection_quality(p, rows, n_rows, mass, sel_mass, block_scores, sel, ld, quality,
                                                   static_cast<hipStream_t>(stream)),
                     "msa_selection_quality launch");
 }

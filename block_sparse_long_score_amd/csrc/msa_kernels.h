@@ -32,17 +32,22 @@ hipError_t launch_kv_append(const Problem& p, uint16_t* k_cache, uint16_t* v_cac
                             const uint16_t* k_new, const uint16_t* v_new, const uint16_t* k_idx_new,
                             int max_q_per_seq, hipStream_t stream);
 
+// first_row: the batch's first query row (cu_q[0]); scores holds that row first.
 hipError_t launch_index_score(const Problem& p, const uint16_t* q_idx, float* scores, int64_t ld,
-                              const int32_t* seq_lens_host, const int32_t* cu_q_host, hipStream_t stream);
+                              const int32_t* seq_lens_host, const int32_t* cu_q_host, hipStream_t stream,
+                              int64_t first_row = 0);
 
-// max_blocks: blocks of the longest sequence (host-side), picks the kernel.
-// Selection quality against dense attention (sampled rows).
-hipError_t launch_block_attn_mass(const Problem& p, const uint16_t* q, const int32_t* rows, int32_t n_rows,
-                                  float* mass, int64_t ld, hipStream_t stream);
+// Selection quality (sampled rows): per-block attention mass over every
+// causal token (sel NULL) or over the selected blocks' tokens, and coverage,
+// recall and the indexer KL.
+hipError_t launch_block_attn_mass(const Problem& p, const uint16_t* q, const int32_t* sel, const int32_t* rows,
+                                  int32_t n_rows, float* mass, int64_t ld, hipStream_t stream);
 hipError_t launch_selection_quality(const Problem& p, const int32_t* rows, int32_t n_rows, const float* mass,
-                                    const float* scores, const int32_t* sel, int64_t ld, float* quality,
-                                    hipStream_t stream);
-// first_row: the batch's first query row (cu_q[0]); rows are addressed globally.
+                                    const float* sel_mass, const float* scores, const int32_t* sel, int64_t ld,
+                                    float* quality, hipStream_t stream);
+// max_blocks: blocks of the longest sequence (host-side), picks the kernel.
+// first_row: the batch's first query row (cu_q[0]); sel is addressed by the
+// batch's row numbers, scores from first_row on (its row 0 is row first_row).
 hipError_t launch_block_topk(const Problem& p, const float* scores, int64_t ld, int32_t* sel, int64_t max_blocks,
                              hipStream_t stream, int64_t first_row = 0);
 

@@ -6,20 +6,24 @@
 // D_KL(P || Q), and MSA is to be judged not only by speed but by selection
 // recall and by how much of the attention score the chosen blocks cover.
 //
-// block_mass_kernel: P for sampled query rows.  One workgroup per (sampled
-// row, group); its waves (4, or 16 for small samples) take the causal blocks
-// round-robin.  Scores of
-// the group's heads use the 16x16x32 bf16 MFMA with 16 keys on M (K rows read
-// straight from the block-major cache) and the heads on N (padded to 16), so
-// lane (head l%16, quarter l/16) holds 4 keys of one head per key tile.  Pass
-// 1 forms each head's softmax max and sum over all causal tokens (online, in
-// base 2); pass 2 recomputes the scores and sums exp2(z - max) / sum over each
-// block's tokens and over the group's heads.
+// block_mass_kernel: per-block attention mass for sampled query rows, over
+// one of two token sets: every causal token (the dense mass, for coverage
+// and recall), or the tokens of the row's selected blocks (the Main Branch's
+// own softmax: P of the KL, over the candidate blocks).  One workgroup per
+// (sampled row, group); its waves (4, or 16 for small samples) take the
+// blocks round-robin.  Scores of the group's heads use the 16x16x32 bf16 MFMA
+// with 16 keys on M (K rows read straight from the block-major cache) and the
+// heads on N (padded to 16), so lane (head l%16, quarter l/16) holds 4 keys
+// of one head per key tile.  Pass 1 forms each head's softmax max and sum
+// over the token set (online, in base 2); pass 2 recomputes the scores and
+// sums exp2(z - max) / sum over each block's tokens and over the group's
+// heads.
 //
 // selection_quality_kernel: one wave per (sampled row, group): coverage of
-// the selected blocks, recall of the top blocks by mass (exact K-th largest
-// mass found bit by bit with wave ballots, equal masses to the lower index),
-// and D_KL(P || softmax of the pooled index scores).
+// the selected blocks and recall of the top blocks by dense mass (exact K-th
+// largest mass found bit by bit with wave ballots, equal masses to the lower
+// index), and D_KL(P || Q) over the selected blocks, Q the softmax of their
+// pooled index scores.
 #include "msa_device.h"
 #include "msa_kernels.h"
 
@@ -28,6 +32,7 @@ namespace msa {
 struct MassArgs {
   Problem p;
   const uint16_t* q;
+  const int32_t* sel;  // NULL: every causal token; else the tokens of the row's selected blocks
   const int32_t* rows;
   int32_t n_rows;
   float* mass;
@@ -74,6 +79,17 @@ __global__ __launch_bounds__(64 * WAVES) void block_mass_kernel(MassArgs a) {
   }
   const int64_t key_stride = (int64_t)p.hkv * D;
   const int32_t* table = p.block_table + (int64_t)s * p.max_blocks_per_seq;
+  float* out = a.mass + ((int64_t)k * p.hkv + g) * a.ld;
+  // The blocks of the token set: causal blocks 0..c, or the row's selected
+  // slots (ids outside 0..c and unmapped blocks hold no keys).  Work item i of
+  // n_items is block i, or the block of slot i.
+  const int32_t* sel_row = a.sel ? a.sel + (((int64_t)r << a.hkv_shift) + g) * kTopK : nullptr;
+  const int n_items = a.sel ? kTopK : c + 1;
+  auto block_of = [&](int i) -> int { return sel_row ? sel_row[i] : i; };
+  if (sel_row) {  // blocks that are not selected carry no mass
+    for (int b = threadIdx.x; b <= c; b += blockDim.x) out[b] = 0.f;
+    __syncthreads();
+  }
 
   // Base-2 scaled scores of key tile kt of a block with nvalid causal keys:
   // lane (head l16, q4) gets keys 16*kt + 4*q4 + i; keys past nvalid are -inf.
@@ -91,9 +107,11 @@ __global__ __launch_bounds__(64 * WAVES) void block_mass_kernel(MassArgs a) {
     return sc;
   };
 
-  // Pass 1: per head, max and sum of 2^z over every causal token.
+  // Pass 1: per head, max and sum of 2^z over every token of the set.
   float m = -__builtin_inff(), l = 0.f;
-  for (int b = wave; b <= c; b += WAVES) {
+  for (int i = wave; i < n_items; i += WAVES) {
+    const int b = block_of(i);
+    if (b < 0 || b > c) continue;
     const int phys = table[b];
     if (phys < 0 || phys >= p.num_blocks) continue;
     const uint16_t* kb = p.k + ((int64_t)phys * kBlock * p.hkv + g) * D;
@@ -130,8 +148,9 @@ __global__ __launch_bounds__(64 * WAVES) void block_mass_kernel(MassArgs a) {
   const float inv_l = 1.0f / L;
 
   // Pass 2: mass of each block, summed over the group's heads.
-  float* out = a.mass + ((int64_t)k * p.hkv + g) * a.ld;
-  for (int b = wave; b <= c; b += WAVES) {
+  for (int i = wave; i < n_items; i += WAVES) {
+    const int b = block_of(i);
+    if (b < 0 || b > c) continue;
     const int phys = table[b];
     if (phys < 0 || phys >= p.num_blocks) continue;
     const uint16_t* kb = p.k + ((int64_t)phys * kBlock * p.hkv + g) * D;
@@ -155,7 +174,8 @@ struct QualityArgs {
   Problem p;
   const int32_t* rows;
   int32_t n_rows;
-  const float* mass;
+  const float* mass;      // dense mass per block (coverage, recall)
+  const float* sel_mass;  // the Main Branch's mass over the selected blocks (P of the KL)
   const float* scores;
   const int32_t* sel;
   int64_t ld;
@@ -224,24 +244,18 @@ __global__ __launch_bounds__(256) void selection_quality_kernel(QualityArgs a) {
   const bool member = sel_ok && (kb > T || (kb == T && eq_below < need));
   const float recall = (float)__popcll(__ballot(member)) / (float)K;
 
-  // D_KL(P || Q), Q = softmax of the pooled scores over the n blocks:
-  // sum P ln P - sum P S + lse(S) * sum P.
-  float smax = -__builtin_inff();
-  for (int b = lane; b < n; b += 64) smax = fmaxf(smax, S[b]);
-  smax = wave_max(smax);
-  float se = 0.f, spl = 0.f, sps = 0.f, sp = 0.f;
-  for (int b = lane; b < n; b += 64) {
-    const float pb = P[b], sb = S[b];
-    se += expf(sb - smax);
-    if (pb > 0.f) spl += pb * logf(pb);
-    sps += pb * sb;
-    sp += pb;
-  }
-  se = wave_sum(se);
-  spl = wave_sum(spl);
-  sps = wave_sum(sps);
-  sp = wave_sum(sp);
-  const float kl = spl - sps + (smax + logf(se)) * sp;
+  // D_KL(P || Q) over the selected blocks (lane j < 16 holds slot j): P the
+  // Main Branch's mass, Q the softmax of the pooled scores over the same
+  // blocks.  KL = sum P ln P - sum P S + lse(S) * sum P, over blocks with
+  // P > 0 (an unmapped block has P = 0 and score -inf: Q = 0, no term).
+  const float pb = sel_ok ? a.sel_mass[w * a.ld + bj] : 0.f;
+  const float sb = sel_ok ? S[bj] : -__builtin_inff();
+  const float smax = wave_max(sb);
+  const float se = wave_sum(sel_ok && sb > -__builtin_inff() ? expf(sb - smax) : 0.f);
+  const float spl = wave_sum(pb > 0.f ? pb * logf(pb) : 0.f);
+  const float sps = wave_sum(pb > 0.f ? pb * sb : 0.f);
+  const float sp = wave_sum(pb > 0.f ? pb : 0.f);
+  const float kl = sp > 0.f ? spl - sps + (smax + logf(se)) * sp : 0.f;
   if (lane == 0) {
     float* q = a.quality + w * 3;
     q[0] = coverage;
@@ -250,12 +264,12 @@ __global__ __launch_bounds__(256) void selection_quality_kernel(QualityArgs a) {
   }
 }
 
-hipError_t launch_block_attn_mass(const Problem& p, const uint16_t* q, const int32_t* rows, int32_t n_rows,
-                                  float* mass, int64_t ld, hipStream_t stream) {
+hipError_t launch_block_attn_mass(const Problem& p, const uint16_t* q, const int32_t* sel, const int32_t* rows,
+                                  int32_t n_rows, float* mass, int64_t ld, hipStream_t stream) {
   int hkv_shift = 0;
   while ((1 << hkv_shift) < p.hkv) ++hkv_shift;
   if (n_rows == 0) return hipSuccess;
-  MassArgs a{p, q, rows, n_rows, mass, ld, hkv_shift};
+  MassArgs a{p, q, sel, rows, n_rows, mass, ld, hkv_shift};
   const int64_t pairs = (int64_t)n_rows << hkv_shift;
   const dim3 grid((unsigned)pairs);
   // Few (row, group) pairs (decode-sized samples): 16 waves each to keep enough loads in flight.
@@ -273,12 +287,12 @@ hipError_t launch_block_attn_mass(const Problem& p, const uint16_t* q, const int
 }
 
 hipError_t launch_selection_quality(const Problem& p, const int32_t* rows, int32_t n_rows, const float* mass,
-                                    const float* scores, const int32_t* sel, int64_t ld, float* quality,
-                                    hipStream_t stream) {
+                                    const float* sel_mass, const float* scores, const int32_t* sel, int64_t ld,
+                                    float* quality, hipStream_t stream) {
   int hkv_shift = 0;
   while ((1 << hkv_shift) < p.hkv) ++hkv_shift;
   if (n_rows == 0) return hipSuccess;
-  QualityArgs a{p, rows, n_rows, mass, scores, sel, ld, quality, hkv_shift};
+  QualityArgs a{p, rows, n_rows, mass, sel_mass, scores, sel, ld, quality, hkv_shift};
   const int64_t waves = (int64_t)n_rows << hkv_shift;
   hipLaunchKernelGGL(selection_quality_kernel, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, stream, a);
   return hipGetLastError();

@@ -48,7 +48,7 @@ class Dims:
                        self.top_k, self.softmax_scale)
 
 
-@dataclasses.dataclass
+@dataclasses.dataclass(frozen=True)
 class Cache:
     """Block-major cache: k, v bf16 [num_blocks, 128, Hkv, D]; k_idx bf16
     [num_blocks, 128, d_idx]; block_table int32 [num_seqs, max_blocks_per_seq]."""
@@ -71,7 +71,7 @@ class Cache:
                         self.k.shape[0], self.block_table.shape[1])
 
 
-@dataclasses.dataclass
+@dataclasses.dataclass(frozen=True)
 class Batch:
     """seq_lens: tokens per sequence after this step's append; the queries of
     sequence s are its last cu_q[s+1]-cu_q[s] positions."""
@@ -158,13 +158,26 @@ _MARSHAL = {"msa_kv_append": _kv_append_args, "msa_index_score": _index_score_ar
             "msa_sparse_attn_decode": _attn_args}
 
 
+def _buffers(obj):
+    """The tensors and host arrays whose addresses a call's arguments carry."""
+    if isinstance(obj, Cache):
+        return [obj.k, obj.v, obj.k_idx, obj.block_table]
+    if isinstance(obj, Batch):
+        return [obj.seq_lens, obj.cu_q, obj.seq_lens_host, obj.cu_q_host]
+    if isinstance(obj, (torch.Tensor, np.ndarray)):
+        return [obj]
+    return []
+
+
 class PreparedCall:
     """One C-ABI call with its arguments marshalled once, for loops that repeat
     the same call on the same buffers (a decode or prefill step): calling it
     costs one ctypes call (the library still validates every argument)
     instead of rebuilding the structs and re-checking every tensor.  It keeps
-    the objects it was prepared from alive; their contents may change between
-    calls, their storage and shapes may not."""
+    every tensor and host array whose address it captured alive (not only
+    the Cache / Batch wrappers, whose fields could be reassigned), so the
+    captured addresses stay valid for as long as the call exists; their
+    contents may change between calls."""
     __slots__ = ("_fn", "_args", "_keep")
 
     def __init__(self, name, args, keep):
@@ -180,7 +193,8 @@ def prepare(name: str, *args) -> PreparedCall:
     """PreparedCall for one of msa_kv_append, msa_index_score, msa_block_topk,
     msa_sparse_attn_prefill, msa_sparse_attn_decode, with the same positional
     arguments as the function of that name (without the stream)."""
-    return PreparedCall(name, _MARSHAL[name](*args), args)
+    keep = tuple(b for a in args for b in _buffers(a))
+    return PreparedCall(name, _MARSHAL[name](*args), keep)
 
 
 def msa_kv_append(dims: Dims, cache: Cache, batch: Batch, k_new, v_new, k_idx_new, stream=None):
@@ -266,22 +280,26 @@ def msa_dense_attn_decode(dims: Dims, cache: Cache, batch: Batch, q, out, worksp
                                    workspace.numel(), _stream(stream)))
 
 
-def msa_block_attn_mass(dims: Dims, cache: Cache, batch: Batch, q, rows, mass, stream=None):
-    """mass: float32 [n_rows, Hkv, ld]; rows: int32 [n_rows] query-row indices of the batch."""
+def msa_block_attn_mass(dims: Dims, cache: Cache, batch: Batch, q, rows, mass, sel=None, stream=None):
+    """mass: float32 [n_rows, Hkv, ld]; rows: int32 [n_rows] query-row indices of the batch.
+    sel None: the dense mass over every causal token; sel (int32 [total_q, Hkv, top_k]): the
+    Main Branch's mass over the tokens of the selected blocks."""
     L = _lib.load()
     d, c, b = dims.c(), cache.c(), batch.c()
+    sel_ptr = None if sel is None else _ptr(sel, "sel", torch.int32)
     _check(L.msa_block_attn_mass(ctypes.byref(d), ctypes.byref(c), ctypes.byref(b), _ptr(q, "q", torch.bfloat16),
-                                 _ptr(rows, "rows", torch.int32), rows.numel(), _ptr(mass, "mass", torch.float32),
-                                 mass.shape[-1], _stream(stream)))
+                                 sel_ptr, _ptr(rows, "rows", torch.int32), rows.numel(),
+                                 _ptr(mass, "mass", torch.float32), mass.shape[-1], _stream(stream)))
 
 
-def msa_selection_quality(dims: Dims, batch: Batch, rows, mass, block_scores, sel, quality, stream=None):
-    """quality: float32 [n_rows, Hkv, 3] = (coverage, recall, kl)."""
+def msa_selection_quality(dims: Dims, batch: Batch, rows, mass, sel_mass, block_scores, sel, quality, stream=None):
+    """quality: float32 [n_rows, Hkv, 3] = (coverage, recall, kl); mass is the dense mass,
+    sel_mass the Main Branch's mass over the selected blocks (msa_block_attn_mass with sel)."""
     L = _lib.load()
     d, b = dims.c(), batch.c()
-    if block_scores.shape[-1] != mass.shape[-1]:
-        raise ValueError("mass and block_scores must share the row pitch ld")
+    if block_scores.shape[-1] != mass.shape[-1] or sel_mass.shape[-1] != mass.shape[-1]:
+        raise ValueError("mass, sel_mass and block_scores must share the row pitch ld")
     _check(L.msa_selection_quality(ctypes.byref(d), ctypes.byref(b), _ptr(rows, "rows", torch.int32), rows.numel(),
-                                   _ptr(mass, "mass", torch.float32),
+                                   _ptr(mass, "mass", torch.float32), _ptr(sel_mass, "sel_mass", torch.float32),
                                    _ptr(block_scores, "block_scores", torch.float32), _ptr(sel, "sel", torch.int32),
                                    mass.shape[-1], _ptr(quality, "quality", torch.float32), _stream(stream)))

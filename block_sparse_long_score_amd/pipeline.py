@@ -75,10 +75,15 @@ class MsaRunner:
     def _calls(self):
         """The step's C-ABI calls with their arguments marshalled once
         (ops.prepare), so a step's host work stays far below its GPU time.
-        Rebuilt whenever one of the runner's buffers has been replaced."""
-        key = (id(self.cache), id(self.batch), id(self.scores), id(self.sel), id(self.out), id(self.workspace))
+        Rebuilt whenever one of the runner's buffers has been replaced: the
+        key is the identity of each object the calls were prepared from.
+        Cache and Batch are frozen, so their tensors cannot be swapped behind
+        an unchanged wrapper, and each prepared call keeps the buffers it
+        captured alive, so no identity is reused while it exists."""
+        inp = self.inputs
+        key = tuple(map(id, (self.cache, self.batch, self.scores, self.sel, self.out, self.workspace, self.k_new,
+                             self.v_new, self.k_idx_new, inp.q, inp.q_idx)))
         if key != self._prepared_key:
-            inp = self.inputs
             attn = "msa_sparse_attn_decode" if self.decode else "msa_sparse_attn_prefill"
             whole = {
                 "append": ops.prepare("msa_kv_append", self.dims, self.cache, self.batch, self.k_new, self.v_new,

@@ -37,10 +37,13 @@
  *   a thread-local human-readable detail of the last failure.
  * - Per-token device metadata (block_table entries, the device copies of
  *   seq_lens and cu_q) cannot be read by the host without a synchronisation;
- *   it is a precondition that they equal their host mirrors and that every
- *   block_table entry a call touches lies in [0, num_blocks).  Kernels guard
- *   every physical block id against num_blocks and skip out-of-range blocks
- *   rather than touch memory outside the cache.
+ *   it is a precondition that seq_lens and cu_q equal their host mirrors.
+ *   A block_table entry outside [0, num_blocks) is never dereferenced: the
+ *   logical block it names holds no keys.  msa_index_score gives such a
+ *   block the pooled score -inf (the max over no keys), so msa_block_topk
+ *   picks it only as the forced local block or when fewer than top_k - 1
+ *   earlier blocks hold keys; every attention call skips it; and a row whose
+ *   selected blocks all hold no keys gets output 0.
  *
  * Positions, blocks and groups
  * ----------------------------
@@ -66,7 +69,7 @@
 extern "C" {
 #endif
 
-#define MSA_ABI_VERSION 2
+#define MSA_ABI_VERSION 3
 
 typedef enum msa_status {
   MSA_OK = 0,
@@ -265,49 +268,62 @@ msa_status msa_sparse_attn_decode(const msa_dims* dims, const msa_cache* cache,
                                   void* out, void* workspace, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------- *
- * msa_block_attn_mass — dense attention mass per block for a sample of query
- * rows ([M3-evo] §2, the paragraph on training the indexer: the Main Branch's
- * group-averaged importance distribution P over the candidate blocks).  For
- * sampled row k (query row r = rows[k] at position t, local block c = t/128)
- * and group g:
- *     P[k][g][b] = (1/G) * sum over the group's heads h of
- *                  sum over tokens i of block b, i <= t, of softmax_i(z_h),
- *     z_h,i = softmax_scale * (q[r][h] . k[i][g]) over ALL causal tokens i,
+ * msa_block_attn_mass — attention mass per block for a sample of query rows
+ * ([M3-evo] §2: MSA is judged by how much of the attention its chosen blocks
+ * cover, and in training the Main Branch forms a group-averaged importance
+ * distribution P over the candidate blocks).  For sampled row k (query row
+ * r = rows[k] at position t, local block c = t/128) and group g, with I the
+ * token set:
+ *     mass[k][g][b] = (1/G) * sum over the group's heads h of
+ *                     sum over tokens i of block b in I of softmax_i(z_h),
+ *     z_h,i = softmax_scale * (q[r][h] . k[i][g]), softmax over i in I,
  * for b = 0..c (entries b > c are not written).  fp32 arithmetic.
+ *   sel == NULL : I = every causal token i <= t (the dense mass);
+ *   sel != NULL : I = the tokens i <= t of the blocks in sel[r][g] (the Main
+ *                 Branch's own softmax of msa_sparse_attn_prefill), so the
+ *                 mass is P over the candidate blocks: it sums to 1 over the
+ *                 selected blocks and is 0 on every other block b <= c.
  *   q    : bf16 [total_q][Hq][D] (the Main Branch queries)
+ *   sel  : NULL, or int32 [total_q][Hkv][top_k] as from msa_block_topk
  *   rows : int32 [n_rows], query-row indices into the batch; a row outside
  *          [0, total_q) is skipped (its outputs are not written).
  *   mass : fp32 [n_rows][Hkv][ld], ld >= the blocks of the longest sequence.
- * Reads K of every causal block through the block table (twice: once for
- * the softmax statistics, once for the masses).  Meant for sampled rows: the
- * work is that of dense attention without the values.
+ * Reads K of every block of I through the block table (twice: once for the
+ * softmax statistics, once for the masses).  Meant for sampled rows: with
+ * sel == NULL the work is that of dense attention without the values.
  * Errors: NULL_POINTER, BAD_SHAPE, UNSUPPORTED, MISALIGNED, CAPACITY, HIP.
  * ------------------------------------------------------------------------- */
 msa_status msa_block_attn_mass(const msa_dims* dims, const msa_cache* cache, const msa_batch* batch,
-                               const void* q, const int32_t* rows, int32_t n_rows, float* mass, int64_t ld,
-                               void* stream);
+                               const void* q, const int32_t* sel, const int32_t* rows, int32_t n_rows,
+                               float* mass, int64_t ld, void* stream);
 
 /* ------------------------------------------------------------------------- *
  * msa_selection_quality — how well the selections of the sampled rows match
- * the dense attention ([M3-evo] §2: MSA is judged by selection recall and by
- * the share of attention score the chosen blocks cover; the indexer is
- * trained with D_KL(P || Q)).  For sampled row k and group g, with P the
- * mass from msa_block_attn_mass and c = t/128:
- *   coverage = sum of P[b] over the selected blocks;
- *   recall   = |selected AND top| / |top|, top = the min(top_k, c+1) blocks
- *              of largest P (equal masses go to the lower block index);
- *   kl       = sum over b <= c with P[b] > 0 of P[b] (ln P[b] - ln Q[b]),
- *              Q = softmax over b <= c of the pooled index scores.
+ * the attention, and the indexer's training target ([M3-evo] §2: MSA is
+ * judged by selection recall and by the share of attention score the chosen
+ * blocks cover; the indexer is trained by D_KL(P || Q), P the Main Branch's
+ * group-averaged importance over the candidate blocks, Q the indexer's
+ * distribution).  For sampled row k and group g, with c = t/128, S the
+ * selected blocks (ids in 0..c), M the dense mass and P the candidate mass
+ * (msa_block_attn_mass without and with sel):
+ *   coverage = sum of M[b] over b in S;
+ *   recall   = |S AND top| / |top|, top = the min(top_k, c+1) blocks of
+ *              largest M (equal masses go to the lower block index);
+ *   kl       = sum over b in S with P[b] > 0 of P[b] (ln P[b] - ln Q[b]),
+ *              Q[b] = exp(score[b]) / sum over b' in S of exp(score[b']),
+ *              the softmax of the pooled index scores over the same blocks.
  *   rows         : int32 [n_rows] as for msa_block_attn_mass
- *   mass         : fp32 [n_rows][Hkv][ld]
+ *   mass         : fp32 [n_rows][Hkv][ld], the dense mass M
+ *   sel_mass     : fp32 [n_rows][Hkv][ld], the candidate mass P
  *   block_scores : fp32 [total_q][Hkv][ld] from msa_index_score
  *   sel          : int32 [total_q][Hkv][top_k] from msa_block_topk
  *   quality      : fp32 [n_rows][Hkv][3] = (coverage, recall, kl)
  * Errors: NULL_POINTER, BAD_SHAPE, UNSUPPORTED, MISALIGNED, HIP.
  * ------------------------------------------------------------------------- */
 msa_status msa_selection_quality(const msa_dims* dims, const msa_batch* batch, const int32_t* rows,
-                                 int32_t n_rows, const float* mass, const float* block_scores,
-                                 const int32_t* sel, int64_t ld, float* quality, void* stream);
+                                 int32_t n_rows, const float* mass, const float* sel_mass,
+                                 const float* block_scores, const int32_t* sel, int64_t ld, float* quality,
+                                 void* stream);
 
 /* ------------------------------------------------------------------------- *
  * msa_dense_attn_prefill — dense causal attention over the same cache

@@ -11,9 +11,10 @@ Text-01、M1、M2 到 M3", §2: index scoring against a shared K_idx, max-poolin
 into 128-token blocks, top-16 selection with the local block forced in, and
 exact softmax attention over the selected tokens.  The same section's
 training and evaluation quantities are here too: the dense attention mass per
-block (the group-averaged importance P) and a selection's coverage of it,
-recall of its largest blocks and D_KL(P || Q) against the indexer's
-softmax Q over the pooled scores.
+block with a selection's coverage of it and recall of its largest blocks,
+and the indexer's training target, D_KL(P || Q) between the Main Branch's
+group-averaged importance P over the candidate (selected) blocks and the
+indexer's softmax Q over the same blocks.
 
 All tensors are numpy arrays in plain logical order for ONE sequence:
 bf16 inputs are passed as ``uint16`` bit patterns, keys are indexed by token
@@ -60,9 +61,12 @@ def _load():
         lib.msa_oracle_select.argtypes = [i64, p, p, i32, i64, i32, i32, p]
         lib.msa_oracle_attend.argtypes = [i64, p, p, i32, i32, i32, p, p, i64, p, i32, i32, dbl, p]
         lib.msa_oracle_block_mass.argtypes = [i64, p, p, i32, i32, i32, p, i64, i32, dbl, p, i64]
-        lib.msa_oracle_selection_quality.argtypes = [i64, p, p, p, p, i32, i64, i32, i32, p, p, p]
+        lib.msa_oracle_selection_quality.argtypes = [i64, p, p, p, i32, i64, i32, i32, p, p]
+        lib.msa_oracle_selected_mass.argtypes = [i64, p, p, i32, i32, i32, p, i64, p, i32, i32, dbl, p, i64]
+        lib.msa_oracle_indexer_kl.argtypes = [i64, p, p, p, p, i32, i64, i32, i32, p]
         for f in (lib.msa_oracle_block_scores, lib.msa_oracle_select, lib.msa_oracle_attend,
-                  lib.msa_oracle_block_mass, lib.msa_oracle_selection_quality):
+                  lib.msa_oracle_block_mass, lib.msa_oracle_selection_quality, lib.msa_oracle_selected_mass,
+                  lib.msa_oracle_indexer_kl):
             f.restype = ctypes.c_int
         lib.msa_oracle_num_threads.restype = ctypes.c_int
         lib.msa_oracle_set_num_threads.argtypes = [ctypes.c_int]
@@ -196,22 +200,64 @@ def block_mass(pos, q, k, block_size: int = 128, scale: float | None = None, ld:
     return out
 
 
-def selection_quality(pos, mass, pooled, sel, block_size: int = 128):
-    """Step 6: (coverage, recall, kl), each float64 [n, G].
+def selection_quality(pos, mass, sel, block_size: int = 128):
+    """Step 6: (coverage, recall), each float64 [n, G], of the selections
+    against the dense mass.
 
-    mass : float64 [n, G, ld] (converted if given as float32); pooled : float32
-    [n, G, ld] index scores; sel : int32 [n, G, top_k].
+    mass : float64 [n, G, ld] (converted if given as float32); sel : int32 [n, G, top_k].
     """
     pos = np.ascontiguousarray(pos, dtype=np.int64)
     mass = np.ascontiguousarray(mass, dtype=np.float64)
-    pooled = np.ascontiguousarray(pooled, dtype=np.float32)
     sel = np.ascontiguousarray(sel, dtype=np.int32)
     n, groups, ld = mass.shape
-    if pooled.shape != mass.shape:
-        raise ValueError("mass and pooled scores must have the same shape")
     top_k = sel.shape[2]
-    cov, rec, kl = (np.empty((n, groups), dtype=np.float64) for _ in range(3))
-    rc = _load().msa_oracle_selection_quality(n, _ptr(pos), _ptr(mass), _ptr(pooled), _ptr(sel), groups, ld,
-                                              block_size, top_k, _ptr(cov), _ptr(rec), _ptr(kl))
+    cov, rec = (np.empty((n, groups), dtype=np.float64) for _ in range(2))
+    rc = _load().msa_oracle_selection_quality(n, _ptr(pos), _ptr(mass), _ptr(sel), groups, ld, block_size, top_k,
+                                              _ptr(cov), _ptr(rec))
     _check(rc, "selection_quality")
-    return cov, rec, kl
+    return cov, rec
+
+
+def selected_mass(pos, q, k, sel, block_size: int = 128, scale: float | None = None,
+                  ld: int | None = None) -> np.ndarray:
+    """Step 7: float64 [n, G, ld], the Main Branch's group-averaged softmax mass
+    of each selected block (its softmax runs over the selected tokens only);
+    0 for every block that is not selected.
+
+    q : uint16 [n, Hq, D]; k : uint16 [L, G, D]; sel : int32 [n, G, top_k].
+    """
+    pos = np.ascontiguousarray(pos, dtype=np.int64)
+    q, k = _u16(q), _u16(k)
+    sel = np.ascontiguousarray(sel, dtype=np.int32)
+    n, hq, d = q.shape
+    groups = k.shape[1]
+    if scale is None:
+        scale = 1.0 / float(np.sqrt(d))
+    if ld is None:
+        ld = int(pos.max()) // block_size + 1 if n else 1
+    out = np.empty((n, groups, ld), dtype=np.float64)
+    rc = _load().msa_oracle_selected_mass(n, _ptr(pos), _ptr(q), hq, groups, d, _ptr(k), k.shape[0], _ptr(sel),
+                                          block_size, sel.shape[2], float(scale), _ptr(out), ld)
+    _check(rc, "selected_mass")
+    return out
+
+
+def indexer_kl(pos, sel_mass, pooled, sel, block_size: int = 128) -> np.ndarray:
+    """Step 8: float64 [n, G], D_KL(P || Q) over each row's selected blocks,
+    P = sel_mass (step 7), Q = softmax of the pooled index scores over the
+    same blocks.
+
+    sel_mass : float64 [n, G, ld]; pooled : float32 [n, G, ld]; sel : int32 [n, G, top_k].
+    """
+    pos = np.ascontiguousarray(pos, dtype=np.int64)
+    sel_mass = np.ascontiguousarray(sel_mass, dtype=np.float64)
+    pooled = np.ascontiguousarray(pooled, dtype=np.float32)
+    sel = np.ascontiguousarray(sel, dtype=np.int32)
+    n, groups, ld = sel_mass.shape
+    if pooled.shape != sel_mass.shape:
+        raise ValueError("sel_mass and pooled scores must have the same shape")
+    kl = np.empty((n, groups), dtype=np.float64)
+    rc = _load().msa_oracle_indexer_kl(n, _ptr(pos), _ptr(sel_mass), _ptr(pooled), _ptr(sel), groups, ld,
+                                       block_size, sel.shape[2], _ptr(kl))
+    _check(rc, "indexer_kl")
+    return kl

@@ -39,18 +39,27 @@
  * are given in plain logical order (token i at index i), independently of any
  * cache layout.  Rows are independent; OpenMP spreads them over host cores.
  *
- * Selection quality (same page, §2: the indexer is trained by aligning its
- * distribution Q with the Main Branch's group-averaged importance P by
- * D_KL(P||Q), and MSA is judged by selection recall and by how much of the
- * attention mass the chosen blocks cover):
- *     5. mass       P_b = (1/G) sum over the group's heads of the DENSE causal
- *                   softmax probabilities of the tokens of block b;
- *     6. quality    coverage = sum of P over the selected blocks; recall = the
- *                   share of the min(top_k, c+1) largest-P blocks (ties to the
- *                   lower index) that were selected; D_KL(P||Q) with Q the
- *                   softmax over the pooled index scores of blocks 0..c.
- * Readings (listed in the design notes): P and Q range over every causal
- * block including the local one; Q uses the raw pooled scores (no
+ * Selection quality and the indexer's training target (same page, §2: MSA
+ * is judged by selection recall and by how much of the attention the chosen
+ * blocks cover; in training, the Main Branch forms a group-averaged
+ * importance distribution P over the candidate blocks, the indexer predicts a
+ * distribution Q, and the two are aligned by D_KL(P||Q)):
+ *     5. dense mass  the DENSE causal softmax probabilities of the tokens of
+ *                    block b, summed per block and averaged over the group's
+ *                    heads (every causal block);
+ *     6. quality     coverage = dense mass on the selected blocks; recall =
+ *                    the share of the min(top_k, c+1) largest-mass blocks
+ *                    (ties to the lower index) that were selected;
+ *     7. P           the Main Branch's own softmax (over the tokens of the
+ *                    selected blocks only, as in step 4), summed per selected
+ *                    block and averaged over the group's heads: P is a
+ *                    distribution over the candidate blocks;
+ *     8. D_KL(P||Q)  with Q the indexer's distribution over the same
+ *                    candidate blocks: the softmax of their pooled index
+ *                    scores.
+ * Readings (listed in the design notes): coverage and recall use the dense
+ * mass, over every causal block including the local one; the KL's P and Q
+ * range over the selected blocks; Q uses the raw pooled scores (no
  * temperature); natural logarithms.
  */
 #include <math.h>
@@ -339,18 +348,16 @@ int msa_oracle_block_mass(int64_t n_rows, const int64_t* pos, const uint16_t* q,
  *   coverage = sum of P_b over the selected blocks (ids >= 0);
  *   recall   = |selected AND top| / |top|, top = the K = min(top_k, c+1)
  *              blocks of largest P (repeated argmax, strictly greater wins, so
- *              equal masses go to the lower index);
- *   kl       = sum over b <= c with P_b > 0 of P_b * (ln P_b - ln Q_b), where
- *              Q = softmax over b <= c of the pooled index scores.
- * mass is double [n_rows][n_groups][ld]; pooled float [n_rows][n_groups][ld];
- * sel int32 [n_rows][n_groups][top_k].  Outputs double [n_rows][n_groups].
+ *              equal masses go to the lower index).
+ * mass is double [n_rows][n_groups][ld]; sel int32 [n_rows][n_groups][top_k].
+ * Outputs double [n_rows][n_groups].
  */
-int msa_oracle_selection_quality(int64_t n_rows, const int64_t* pos, const double* mass, const float* pooled,
-                                 const int32_t* sel, int n_groups, int64_t ld, int block_size, int top_k,
-                                 double* coverage, double* recall, double* kl) {
-  if (n_rows < 0 || n_groups <= 0 || ld <= 0 || block_size <= 0 || top_k <= 0 || !pos || !coverage || !recall || !kl)
+int msa_oracle_selection_quality(int64_t n_rows, const int64_t* pos, const double* mass, const int32_t* sel,
+                                 int n_groups, int64_t ld, int block_size, int top_k, double* coverage,
+                                 double* recall) {
+  if (n_rows < 0 || n_groups <= 0 || ld <= 0 || block_size <= 0 || top_k <= 0 || !pos || !coverage || !recall)
     return ORACLE_BAD_ARG;
-  if (n_rows > 0 && (!mass || !pooled || !sel)) return ORACLE_BAD_ARG;
+  if (n_rows > 0 && (!mass || !sel)) return ORACLE_BAD_ARG;
   for (int64_t r = 0; r < n_rows; ++r)
     if (pos[r] < 0 || pos[r] / block_size >= ld) return ORACLE_BAD_ARG;
   int status = ORACLE_OK;
@@ -368,7 +375,6 @@ int msa_oracle_selection_quality(int64_t n_rows, const int64_t* pos, const doubl
       for (int g = 0; g < n_groups; ++g) {
         const int64_t row = r * n_groups + g;
         const double* P = mass + row * ld;
-        const float* S = pooled + row * ld;
         const int32_t* s = sel + row * (int64_t)top_k;
         double cov = 0.0;
         for (int j = 0; j < top_k; ++j)
@@ -385,22 +391,132 @@ int msa_oracle_selection_quality(int64_t n_rows, const int64_t* pos, const doubl
         int64_t hits = 0;
         for (int j = 0; j < top_k; ++j)
           if (s[j] >= 0 && s[j] <= c && taken[s[j]]) ++hits;
-        /* ln Q_b = S_b - log sum_b' exp(S_b'). */
-        double smax = -INFINITY;
-        for (int64_t b = 0; b <= c; ++b)
-          if (S[b] > smax) smax = S[b];
-        double sum = 0.0;
-        for (int64_t b = 0; b <= c; ++b) sum += exp((double)S[b] - smax);
-        const double lse = smax + log(sum);
-        double d = 0.0;
-        for (int64_t b = 0; b <= c; ++b)
-          if (P[b] > 0.0) d += P[b] * (log(P[b]) - ((double)S[b] - lse));
         coverage[row] = cov;
         recall[row] = (double)hits / (double)K;
-        kl[row] = d;
       }
     }
     free(taken);
   }
   return status;
+}
+
+/*
+ * Step 7: the Main Branch's importance of each candidate block.  For each
+ * row (position t) and group g, every head h of the group takes the softmax
+ * of z_i = scale * q_h.k_i over the tokens it attends in step 4 (the tokens
+ * i <= t of the blocks in sel[r][g]); the mass of a selected block is the sum
+ * of those probabilities over its tokens, averaged over the G heads.
+ * out: double [n_rows][n_groups][ld]; blocks that are not selected (and
+ * blocks after the row's own block) are 0, so each row sums to 1 over its
+ * selected blocks.  sel int32 [n_rows][n_groups][top_k], -1 = unused slot.
+ */
+int msa_oracle_selected_mass(int64_t n_rows, const int64_t* pos, const uint16_t* q, int n_q_heads, int n_groups,
+                             int head_dim, const uint16_t* k, int64_t n_keys, const int32_t* sel, int block_size,
+                             int top_k, double scale, double* out, int64_t ld) {
+  if (n_rows < 0 || n_groups <= 0 || n_q_heads <= 0 || n_q_heads % n_groups != 0 || head_dim <= 0 ||
+      block_size <= 0 || top_k <= 0 || ld <= 0 || !pos || !out)
+    return ORACLE_BAD_ARG;
+  if (n_rows > 0 && (!q || !k || !sel)) return ORACLE_BAD_ARG;
+  for (int64_t r = 0; r < n_rows; ++r) {
+    if (pos[r] < 0 || pos[r] >= n_keys || pos[r] / block_size >= ld) return ORACLE_BAD_ARG;
+    for (int g = 0; g < n_groups; ++g)
+      for (int j = 0; j < top_k; ++j) {
+        const int32_t b = sel[(r * n_groups + g) * (int64_t)top_k + j];
+        if (b < -1 || b > pos[r] / block_size) return ORACLE_BAD_SEL;
+      }
+  }
+  const int group_size = n_q_heads / n_groups;
+  int status = ORACLE_OK;
+#pragma omp parallel
+  {
+    double* z = (double*)malloc(sizeof(double) * (size_t)top_k * (size_t)block_size);
+    int64_t* blk = (int64_t*)malloc(sizeof(int64_t) * (size_t)top_k * (size_t)block_size);
+    if (!z || !blk) {
+#pragma omp atomic write
+      status = ORACLE_NO_MEMORY;
+    }
+#pragma omp for schedule(dynamic, 4)
+    for (int64_t r = 0; r < n_rows; ++r) {
+      if (!z || !blk) continue;
+      const int64_t t = pos[r];
+      for (int g = 0; g < n_groups; ++g) {
+        double* mass = out + (r * n_groups + g) * ld;
+        for (int64_t b = 0; b < ld; ++b) mass[b] = 0.0;
+        const int32_t* s = sel + (r * n_groups + g) * (int64_t)top_k;
+        for (int j = 0; j < group_size; ++j) {
+          const int h = g * group_size + j;
+          const uint16_t* qh = q + (r * n_q_heads + h) * (int64_t)head_dim;
+          /* The scores of the attended tokens, as in step 4. */
+          int64_t n = 0;
+          double zmax = -INFINITY;
+          for (int jj = 0; jj < top_k; ++jj) {
+            if (s[jj] < 0) continue;
+            for (int64_t i = (int64_t)s[jj] * block_size; i < (int64_t)(s[jj] + 1) * block_size && i <= t; ++i) {
+              const uint16_t* key = k + (i * n_groups + g) * (int64_t)head_dim;
+              double dot = 0.0;
+              for (int d = 0; d < head_dim; ++d) dot += bf16_to_double(qh[d]) * bf16_to_double(key[d]);
+              z[n] = dot * scale;
+              blk[n] = s[jj];
+              if (z[n] > zmax) zmax = z[n];
+              ++n;
+            }
+          }
+          double denom = 0.0;
+          for (int64_t m = 0; m < n; ++m) { /* softmax over the attended tokens */
+            z[m] = exp(z[m] - zmax);
+            denom += z[m];
+          }
+          for (int64_t m = 0; m < n; ++m) mass[blk[m]] += z[m] / denom / group_size;
+        }
+      }
+    }
+    free(z);
+    free(blk);
+  }
+  return status;
+}
+
+/*
+ * Step 8: D_KL(P || Q) over the candidate blocks of each row and group.
+ *   P = sel_mass (step 7) on the selected blocks;
+ *   Q_b = exp(S_b) / sum over the selected blocks b' of exp(S_b'), S the
+ *         pooled index scores (step 2);
+ *   kl = sum over selected b with P_b > 0 of P_b * (ln P_b - ln Q_b).
+ * sel_mass double [n_rows][n_groups][ld]; pooled float [n_rows][n_groups][ld];
+ * sel int32 [n_rows][n_groups][top_k].  Output double [n_rows][n_groups].
+ */
+int msa_oracle_indexer_kl(int64_t n_rows, const int64_t* pos, const double* sel_mass, const float* pooled,
+                          const int32_t* sel, int n_groups, int64_t ld, int block_size, int top_k, double* kl) {
+  if (n_rows < 0 || n_groups <= 0 || ld <= 0 || block_size <= 0 || top_k <= 0 || !pos || !kl) return ORACLE_BAD_ARG;
+  if (n_rows > 0 && (!sel_mass || !pooled || !sel)) return ORACLE_BAD_ARG;
+  for (int64_t r = 0; r < n_rows; ++r) {
+    if (pos[r] < 0 || pos[r] / block_size >= ld) return ORACLE_BAD_ARG;
+    for (int g = 0; g < n_groups; ++g)
+      for (int j = 0; j < top_k; ++j) {
+        const int32_t b = sel[(r * n_groups + g) * (int64_t)top_k + j];
+        if (b < -1 || b > pos[r] / block_size) return ORACLE_BAD_SEL;
+      }
+  }
+#pragma omp parallel for schedule(dynamic, 16)
+  for (int64_t r = 0; r < n_rows; ++r) {
+    for (int g = 0; g < n_groups; ++g) {
+      const int64_t row = r * n_groups + g;
+      const double* P = sel_mass + row * ld;
+      const float* S = pooled + row * ld;
+      const int32_t* s = sel + row * (int64_t)top_k;
+      /* ln Q_b = S_b - log sum over the candidates of exp(S_b'). */
+      double smax = -INFINITY;
+      for (int j = 0; j < top_k; ++j)
+        if (s[j] >= 0 && S[s[j]] > smax) smax = S[s[j]];
+      double sum = 0.0;
+      for (int j = 0; j < top_k; ++j)
+        if (s[j] >= 0) sum += exp((double)S[s[j]] - smax);
+      const double lse = smax + log(sum);
+      double d = 0.0;
+      for (int j = 0; j < top_k; ++j)
+        if (s[j] >= 0 && P[s[j]] > 0.0) d += P[s[j]] * (log(P[s[j]]) - ((double)S[s[j]] - lse));
+      kl[row] = d;
+    }
+  }
+  return ORACLE_OK;
 }

@@ -11,6 +11,7 @@ import torch
 
 import oracle
 from block_sparse_long_score_amd.inputs import bf16_bits
+from oracle import scores_matmul
 
 MAX_ABS = 2e-2   # spec tolerance on attention outputs (bf16 in, fp32 accumulate)
 MEAN_ABS = 2e-3
@@ -96,3 +97,53 @@ def check_selection_invariants(runner):
     d = np.diff(sel, axis=2)
     assert np.all((d > 0) | ~np.broadcast_to(valid[:, :, 1:], d.shape)), "not strictly ascending"
     assert np.all((sel >= 0) | ~np.broadcast_to(valid, sel.shape))
+
+
+def compare_row_range(runner, s, r0, r1, check_out=True, batch=2048):
+    """Every query row of sequence s with row index (within the sequence) in
+    [r0, r1) against the oracle, in batches: pooled scores bit for bit (steps
+    1-2 by the pinned matrix-product form of the oracle), selections bit for
+    bit (the oracle's select on the oracle's scores), and, with check_out,
+    the outputs within the tolerance (the oracle's attention over all of the
+    sequence's keys).  Returns (max_abs, mean_abs) over the range, or None."""
+    inp = runner.inputs
+    w = inp.workload
+    first = w.seq_lens[s] - w.q_lens[s]
+    off = int(inp.tok_off[s])
+    last_pos = first + r1 - 1
+    k_idx = bf16_bits(inp.k_idx[off:off + last_pos + 1])
+    if check_out:
+        k = bf16_bits(inp.k[off:off + last_pos + 1])
+        v = bf16_bits(inp.v[off:off + last_pos + 1])
+    ld = runner.ld
+    worst, total, count = 0.0, 0.0, 0
+    for b0 in range(r0, r1, batch):
+        b1 = min(r1, b0 + batch)
+        pos = np.arange(first + b0, first + b1, dtype=np.int64)
+        rows = torch.arange(int(inp.cu_q[s]) + b0, int(inp.cu_q[s]) + b1, device=inp.q.device)
+        q_idx = bf16_bits(inp.q_idx.index_select(0, rows))
+        pooled = scores_matmul.block_scores(int(pos[0]), q_idx, k_idx, w.block_size, ld)
+        gpu_scores = runner.scores.index_select(0, rows).cpu().numpy()
+        c = pos // w.block_size
+        causal = np.arange(ld)[None, None, :] <= c[:, None, None]
+        bad = np.argwhere(causal & (gpu_scores.view(np.uint32) != pooled.view(np.uint32)))
+        assert bad.size == 0, (f"pooled scores differ at {len(bad)} entries, first: position {pos[bad[0][0]]} "
+                               f"group {bad[0][1]} block {bad[0][2]}")
+        sel = oracle.select(pos, pooled, w.block_size, w.top_k)
+        gpu_sel = runner.sel.index_select(0, rows).cpu().numpy()
+        bad = np.argwhere(np.any(gpu_sel != sel, axis=-1))
+        assert bad.size == 0, (f"selection mismatch at {len(bad)} (row, group) pairs, first: position "
+                               f"{pos[bad[0][0]]} group {bad[0][1]}: gpu {gpu_sel[tuple(bad[0])]} "
+                               f"oracle {sel[tuple(bad[0])]}")
+        if not check_out:
+            continue
+        out = oracle.attend(pos, bf16_bits(inp.q.index_select(0, rows)), k, v, sel, w.block_size)
+        err = np.abs(runner.out.index_select(0, rows).float().cpu().numpy().astype(np.float64) - out)
+        worst = max(worst, float(err.max()))
+        total += float(err.sum())
+        count += err.size
+    if not check_out:
+        return None
+    max_abs, mean_abs = worst, total / count
+    assert max_abs <= MAX_ABS and mean_abs <= MEAN_ABS, (max_abs, mean_abs)
+    return max_abs, mean_abs

@@ -145,16 +145,20 @@ def test_quality_entry_points_validate_on_the_host(lib):
     b = _Batch([1024, 900], [1, 1])
     dp, cp, bp = ctypes.byref(d), ctypes.byref(c), ctypes.byref(b.c)
     # block mass: null / misaligned pointers, negative counts, short rows
-    assert lib.msa_block_attn_mass(dp, cp, bp, None, FAKE, 4, FAKE, 16, None) == NULLP
-    assert lib.msa_block_attn_mass(dp, cp, bp, FAKE, FAKE + 4, 4, FAKE, 16, None) == MISAL
-    assert lib.msa_block_attn_mass(dp, cp, bp, FAKE, FAKE, -1, FAKE, 16, None) == SHAPE
-    assert lib.msa_block_attn_mass(dp, cp, bp, FAKE, FAKE, 4, FAKE, 7, None) == SHAPE  # 8 blocks needed
-    assert lib.msa_block_attn_mass(dp, cp, bp, FAKE, FAKE, 0, FAKE, 16, None) == OK  # nothing to do
+    # (the dense mass with sel NULL, the candidate mass with a selection)
+    for sel in (None, FAKE):
+        assert lib.msa_block_attn_mass(dp, cp, bp, None, sel, FAKE, 4, FAKE, 16, None) == NULLP
+        assert lib.msa_block_attn_mass(dp, cp, bp, FAKE, sel, FAKE + 4, 4, FAKE, 16, None) == MISAL
+        assert lib.msa_block_attn_mass(dp, cp, bp, FAKE, sel, FAKE, -1, FAKE, 16, None) == SHAPE
+        assert lib.msa_block_attn_mass(dp, cp, bp, FAKE, sel, FAKE, 4, FAKE, 7, None) == SHAPE  # 8 blocks needed
+        assert lib.msa_block_attn_mass(dp, cp, bp, FAKE, sel, FAKE, 0, FAKE, 16, None) == OK  # nothing to do
+    assert lib.msa_block_attn_mass(dp, cp, bp, FAKE, FAKE + 8, FAKE, 4, FAKE, 16, None) == MISAL
     # selection quality
-    assert lib.msa_selection_quality(dp, bp, FAKE, 4, FAKE, FAKE, None, 16, FAKE, None) == NULLP
-    assert lib.msa_selection_quality(dp, bp, FAKE, -2, FAKE, FAKE, FAKE, 16, FAKE, None) == SHAPE
-    assert lib.msa_selection_quality(dp, bp, FAKE, 4, FAKE, FAKE, FAKE, 3, FAKE, None) == SHAPE
-    assert lib.msa_selection_quality(dp, bp, FAKE, 0, FAKE, FAKE, FAKE, 16, FAKE, None) == OK
+    assert lib.msa_selection_quality(dp, bp, FAKE, 4, FAKE, FAKE, FAKE, None, 16, FAKE, None) == NULLP
+    assert lib.msa_selection_quality(dp, bp, FAKE, 4, FAKE, None, FAKE, FAKE, 16, FAKE, None) == NULLP
+    assert lib.msa_selection_quality(dp, bp, FAKE, -2, FAKE, FAKE, FAKE, FAKE, 16, FAKE, None) == SHAPE
+    assert lib.msa_selection_quality(dp, bp, FAKE, 4, FAKE, FAKE, FAKE, FAKE, 3, FAKE, None) == SHAPE
+    assert lib.msa_selection_quality(dp, bp, FAKE, 0, FAKE, FAKE, FAKE, FAKE, 16, FAKE, None) == OK
 
 
 def test_dense_attention_validates_on_the_host(lib):

@@ -109,10 +109,13 @@ def test_no_write_outside_any_buffer(name):
         extra = {"dense output": dense}
     rows = torch.from_numpy(np.unique(np.linspace(0, w.total_q - 1, 8).astype(np.int32))).cuda()
     mass = Guarded((rows.numel(), w.num_kv_heads, runner.ld), torch.float32)
+    sel_mass = Guarded((rows.numel(), w.num_kv_heads, runner.ld), torch.float32)
     quality = Guarded((rows.numel(), w.num_kv_heads, 3), torch.float32)
     ops.msa_block_attn_mass(runner.dims, runner.cache, runner.batch, inputs.q, rows, mass.view)
-    ops.msa_selection_quality(runner.dims, runner.batch, rows, mass.view, runner.scores, runner.sel, quality.view)
+    ops.msa_block_attn_mass(runner.dims, runner.cache, runner.batch, inputs.q, rows, sel_mass.view, sel=runner.sel)
+    ops.msa_selection_quality(runner.dims, runner.batch, rows, mass.view, sel_mass.view, runner.scores, runner.sel,
+                              quality.view)
     torch.cuda.synchronize()
-    extra.update({"attention mass": mass, "quality": quality})
+    extra.update({"attention mass": mass, "candidate mass": sel_mass, "quality": quality})
     for what, g in {**guards, **extra}.items():
         assert g.intact(), f"{name}: write outside the {what}"

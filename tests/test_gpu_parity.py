@@ -11,10 +11,12 @@ import numpy as np
 import pytest
 import torch
 
+import oracle
+
 from block_sparse_long_score_amd import ops
 from block_sparse_long_score_amd.inputs import WORKLOADS, bf16_bits, make_inputs
 from block_sparse_long_score_amd.pipeline import MsaRunner
-from tests.gpu_helpers import check_selection_invariants, compare_rows, oracle_rows, seq_rows
+from tests.gpu_helpers import check_selection_invariants, compare_row_range, compare_rows, oracle_rows, seq_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -360,6 +362,63 @@ def test_two_runs_are_identical():
     assert torch.equal(out1.view(torch.int16), runner.out.view(torch.int16))
 
 
+@pytest.mark.parametrize("mode", ["prefill", "decode_split", "decode_fused"])
+def test_sparse_blocks_outside_the_cache_hold_no_keys(mode):
+    """Block-table entries outside [0, num_blocks) name blocks that hold no keys:
+    their pooled score is -inf (the max over no keys), so they are selected only
+    when fewer than 15 earlier blocks hold keys (or as the local block), and the
+    Main Branch attends none of their tokens.  The oracle sees the same batch
+    with those blocks' keys removed."""
+    if mode == "prefill":  # rows at blocks 17..23: at block 17 only 14 earlier blocks hold keys
+        w = M2.with_sizes("sparse_absent_prefill", [3000], [700], permuted_table=True)
+    elif mode == "decode_split":  # the last sequence's own (local) block is unmapped too
+        w = M2.with_sizes("sparse_absent_split", [3000, 2200, 5000], [1, 1, 1], permuted_table=True)
+    else:
+        w = M2.with_sizes("sparse_absent_fused", [2100 + 150 * i for i in range(16)], [1] * 16, permuted_table=True)
+    _announce(f"{w.name}: seq_lens={w.seq_lens[:4]} q_lens={w.q_lens[:4]} (unmapped table entries)")
+    runner = MsaRunner(make_inputs(w, "cuda"))
+    runner.append()
+    nb = runner.cache.k.shape[0]
+    absent = {s: {3: -1, 7: nb, 10: -5} for s in range(w.num_seqs)}
+    if mode == "decode_split":
+        absent[2][(5000 - 1) // 128] = nb + 100
+    for s, bad in absent.items():
+        for b, v in bad.items():
+            runner.cache.block_table[s, b] = v
+    runner.index_score()
+    runner.block_topk()
+    runner.attend()
+    torch.cuda.synchronize()
+    inp = runner.inputs
+    for s in range(w.num_seqs):
+        pos = inp.positions(s)
+        rows = torch.from_numpy(seq_rows(inp, s, pos)).to(inp.q.device)
+        pooled, _, _ = oracle_rows(inp, s, pos, attend=False)
+        gone = sorted(absent[s])
+        for i, t in enumerate(pos):
+            for b in gone:
+                if b <= int(t) // 128:
+                    pooled[i, :, b] = -np.inf
+        sel = oracle.select(pos, pooled, w.block_size, w.top_k)
+        gpu_sel = runner.sel.index_select(0, rows).cpu().numpy()
+        np.testing.assert_array_equal(gpu_sel, sel, err_msg=f"{w.name} sequence {s}: selections")
+        gpu_scores = runner.scores.index_select(0, rows).cpu().numpy()
+        for i, t in enumerate(pos):
+            c = int(t) // 128
+            np.testing.assert_array_equal(gpu_scores[i, :, : c + 1], pooled[i, :, : c + 1])
+        if mode == "prefill":
+            assert np.any(np.isin(sel, gone)), "some row should select an unmapped block"
+        attended = np.where(np.isin(sel, gone), -1, sel)
+        off = int(inp.tok_off[s])
+        length = int(pos.max()) + 1
+        want = oracle.attend(pos, bf16_bits(inp.q.index_select(0, rows)), bf16_bits(inp.k[off:off + length]),
+                             bf16_bits(inp.v[off:off + length]), attended, w.block_size)
+        got = runner.out.index_select(0, rows).float().cpu().numpy().astype(np.float64)
+        assert np.all(np.isfinite(want)), "every row keeps at least one block with keys"
+        err = np.abs(got - want)
+        assert float(err.max()) <= 2e-2 and float(err.mean()) <= 2e-3, (s, float(err.max()), float(err.mean()))
+
+
 # ----------------------------------------------------------- full sizes
 
 
@@ -376,6 +435,17 @@ def test_c1_full_size_sampled_rows():
     compare_rows(runner, 0, _sample_positions(32768, 0, 384, 1))
 
 
+@pytest.mark.slow
+@pytest.mark.parametrize("part", range(4))
+def test_c1_full_size_every_row(part):
+    """The 32,768-token prefill as the bench runs it: every row's pooled scores,
+    selections and outputs against the oracle, a quarter of the rows per case."""
+    runner = _run(WORKLOADS["c1"], chunk_rows=BENCH_CHUNK_ROWS)
+    r0 = part * 8192
+    max_abs, mean_abs = compare_row_range(runner, 0, r0, r0 + 8192)
+    _announce(f"c1 rows {r0}..{r0 + 8191}: max_abs {max_abs:.3g} mean_abs {mean_abs:.3g}")
+
+
 def test_c2_full_size_decode_all_rows():
     runner = _run(WORKLOADS["c2"])
     check_selection_invariants(runner)
@@ -388,6 +458,18 @@ def test_c3_full_size_sampled_rows():
     assert len(runner.chunks) == 8
     check_selection_invariants(runner)
     compare_rows(runner, 0, _sample_positions(131072, 0, 256, 3))
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("part", range(4))
+def test_c3_full_size_every_selection(part):
+    """The 131,072-token prefill as the bench runs it: every row's pooled scores
+    and block selections (all 8 groups) bit for bit against the oracle, a
+    quarter of the rows per case; outputs are checked on sampled rows above."""
+    runner = _run(WORKLOADS["c3"], chunk_rows=BENCH_CHUNK_ROWS)
+    r0 = part * 32768
+    compare_row_range(runner, 0, r0, r0 + 32768, check_out=False, batch=4096)
+    _announce(f"c3 rows {r0}..{r0 + 32767}: every pooled score and selection equal")
 
 
 def test_m3p_full_size_sampled_rows():

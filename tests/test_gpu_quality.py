@@ -1,12 +1,14 @@
 """Parity of the selection-quality calls (msa_block_attn_mass,
 msa_selection_quality) with the CPU oracle.
 
-- Block mass: fp32 on the GPU against the oracle's double-precision dense
-  softmax (max |diff| <= 1e-6 + 1e-4 |P|).
-- Quality: fed the oracle's own mass (rounded to float), pooled scores and
+- Block mass: fp32 on the GPU against the oracle's double-precision softmax
+  (max |diff| <= 1e-6 + 1e-4 |P|), over every causal token (the dense mass)
+  and over the tokens of the oracle's selected blocks (the Main Branch's mass
+  over the candidate blocks, P of the indexer KL).
+- Quality: fed the oracle's own masses (rounded to float), pooled scores and
   selections, the GPU must give the oracle's recall exactly (both decide from
   the same float values) and its coverage and KL within float rounding.
-- End to end on the GPU's own mass, scores and selections: coverage and KL
+- End to end on the GPU's own masses, scores and selections: coverage and KL
   close to the oracle's; recall equal except where two masses sit within
   float rounding of each other.
 """
@@ -60,14 +62,26 @@ def _sample(runner, positions):
     return out
 
 
-def _oracle_mass(inp, s, pos, ld):
-    w = inp.workload
+def _oracle_q_k(inp, s, pos):
     off = int(inp.tok_off[s])
     length = int(pos.max()) + 1
     rows = torch.from_numpy(seq_rows(inp, s, pos)).to(inp.q.device)
-    q = bf16_bits(inp.q.index_select(0, rows))
-    k = bf16_bits(inp.k[off:off + length])
-    return oracle.block_mass(pos, q, k, w.block_size, ld=ld)
+    return bf16_bits(inp.q.index_select(0, rows)), bf16_bits(inp.k[off:off + length])
+
+
+def _oracle_mass(inp, s, pos, ld):
+    q, k = _oracle_q_k(inp, s, pos)
+    return oracle.block_mass(pos, q, k, inp.workload.block_size, ld=ld)
+
+
+def _oracle_sel_mass(inp, s, pos, sel, ld):
+    q, k = _oracle_q_k(inp, s, pos)
+    return oracle.selected_mass(pos, q, k, sel, inp.workload.block_size, ld=ld)
+
+
+def _oracle_quality(pos, mass, sel_mass, pooled, sel):
+    cov, rec = oracle.selection_quality(pos, mass, sel)
+    return cov, rec, oracle.indexer_kl(pos, sel_mass, pooled, sel)
 
 
 def _run(name):
@@ -86,13 +100,20 @@ def _pad(pooled, ld):
     return out
 
 
-def _gpu_mass(runner, rows):
+def _gpu_mass(runner, rows, sel=None):
     dev = runner.inputs.q.device
     rows_t = torch.from_numpy(np.asarray(rows, np.int32)).to(dev)
     mass = torch.full((len(rows), runner.dims.num_kv_heads, runner.ld), float("nan"), dtype=torch.float32, device=dev)
-    ops.msa_block_attn_mass(runner.dims, runner.cache, runner.batch, runner.inputs.q, rows_t, mass)
+    ops.msa_block_attn_mass(runner.dims, runner.cache, runner.batch, runner.inputs.q, rows_t, mass, sel=sel)
     torch.cuda.synchronize()
     return rows_t, mass
+
+
+def _batch_sel(runner, rows, sel):
+    """A [total_q, Hkv, top_k] selection tensor holding `sel` (from the oracle) at `rows`, -1 elsewhere."""
+    full = torch.full_like(runner.sel, -1)
+    full[torch.from_numpy(np.asarray(rows, np.int64)).to(full.device)] = torch.from_numpy(sel).to(full.device)
+    return full
 
 
 @pytest.mark.parametrize("name", list(CASES))
@@ -111,6 +132,27 @@ def test_block_mass_matches_oracle(name):
             np.testing.assert_allclose(got[i, :, : c + 1].sum(axis=-1), 1.0, atol=1e-4)
 
 
+@pytest.mark.parametrize("name", list(CASES))
+def test_candidate_mass_matches_oracle(name):
+    """The Main Branch's mass over the oracle's selected blocks (P of the indexer KL)."""
+    runner, sample = _run(name)
+    for s, pos, rows in sample:
+        _, sel, _ = oracle_rows(runner.inputs, s, pos, attend=False)
+        _, mass = _gpu_mass(runner, rows, sel=_batch_sel(runner, rows, sel))
+        want = _oracle_sel_mass(runner.inputs, s, pos, sel, runner.ld)
+        got = mass.cpu().numpy().astype(np.float64)
+        for i, t in enumerate(pos):
+            c = int(t) // 128
+            err = np.abs(got[i, :, : c + 1] - want[i, :, : c + 1])
+            assert np.all(err <= 1e-6 + 1e-4 * want[i, :, : c + 1]), \
+                f"{name}: candidate mass of position {t} off by {err.max():.3g}"
+            assert np.all(np.isnan(got[i, :, c + 1:])), "blocks after the local block must not be written"
+            np.testing.assert_allclose(got[i, :, : c + 1].sum(axis=-1), 1.0, atol=1e-4)
+            for g in range(runner.dims.num_kv_heads):
+                off = np.setdiff1d(np.arange(c + 1), sel[i, g][sel[i, g] >= 0])
+                assert np.all(got[i, g, off] == 0.0), "blocks that are not selected carry no mass"
+
+
 @pytest.mark.parametrize("name", ["m2_prefill", "decode_batch", "m3_shape", "needles"])
 def test_selection_quality_on_oracle_inputs(name):
     """Same float inputs on both sides: recall bit-exact, coverage and KL close."""
@@ -121,37 +163,46 @@ def test_selection_quality_on_oracle_inputs(name):
         pooled, sel, _ = oracle_rows(inp, s, pos, attend=False)
         pooled = _pad(pooled, runner.ld)
         mass = _oracle_mass(inp, s, pos, runner.ld).astype(np.float32)
+        sel_mass = _oracle_sel_mass(inp, s, pos, sel, runner.ld).astype(np.float32)
         scores_full = torch.zeros_like(runner.scores)
-        sel_full = torch.full_like(runner.sel, -1)
         rows_t = torch.from_numpy(np.asarray(rows, np.int64)).to(dev)
         scores_full[rows_t] = torch.from_numpy(pooled).to(dev)
-        sel_full[rows_t] = torch.from_numpy(sel).to(dev)
         quality = torch.empty((len(rows), hkv, 3), dtype=torch.float32, device=dev)
         ops.msa_selection_quality(runner.dims, runner.batch, rows_t.int(), torch.from_numpy(mass).to(dev),
-                                  scores_full, sel_full, quality)
+                                  torch.from_numpy(sel_mass).to(dev), scores_full, _batch_sel(runner, rows, sel),
+                                  quality)
         torch.cuda.synchronize()
         q = quality.cpu().numpy().astype(np.float64)
-        cov, rec, kl = oracle.selection_quality(pos, mass.astype(np.float64), pooled, sel)
+        cov, rec, kl = _oracle_quality(pos, mass.astype(np.float64), sel_mass.astype(np.float64), pooled, sel)
         np.testing.assert_array_equal(q[..., 1], rec, err_msg=f"{name}: recall")
         np.testing.assert_allclose(q[..., 0], cov, rtol=0, atol=2e-6, err_msg=f"{name}: coverage")
         np.testing.assert_allclose(q[..., 2], kl, rtol=1e-4, atol=1e-4, err_msg=f"{name}: KL")
 
 
+def _gpu_quality(runner, rows):
+    """Coverage, recall and KL from the GPU's own masses, scores and selections."""
+    dev = runner.inputs.q.device
+    rows_t, mass = _gpu_mass(runner, rows)
+    _, sel_mass = _gpu_mass(runner, rows, sel=runner.sel)
+    quality = torch.empty((len(rows), runner.dims.num_kv_heads, 3), dtype=torch.float32, device=dev)
+    ops.msa_selection_quality(runner.dims, runner.batch, rows_t, mass, sel_mass, runner.scores, runner.sel, quality)
+    torch.cuda.synchronize()
+    return quality.cpu().numpy().astype(np.float64)
+
+
 @pytest.mark.parametrize("name", ["m2_prefill", "decode_batch", "needles"])
 def test_selection_quality_end_to_end(name):
-    """The GPU's own mass, pooled scores and selections."""
+    """The GPU's own masses, pooled scores and selections."""
     runner, sample = _run(name)
-    inp, dev = runner.inputs, runner.inputs.q.device
-    hkv = runner.dims.num_kv_heads
+    inp = runner.inputs
     for s, pos, rows in sample:
-        rows_t, mass = _gpu_mass(runner, rows)
-        quality = torch.empty((len(rows), hkv, 3), dtype=torch.float32, device=dev)
-        ops.msa_selection_quality(runner.dims, runner.batch, rows_t, mass, runner.scores, runner.sel, quality)
-        torch.cuda.synchronize()
-        q = quality.cpu().numpy().astype(np.float64)
+        q = _gpu_quality(runner, rows)
         pooled, sel, _ = oracle_rows(inp, s, pos, attend=False)
+        gpu_sel = runner.sel.index_select(0, torch.from_numpy(np.asarray(rows, np.int64)).to(inp.q.device))
+        np.testing.assert_array_equal(gpu_sel.cpu().numpy(), sel, err_msg=f"{name}: selections")
         omass = _oracle_mass(inp, s, pos, runner.ld)
-        cov, rec, kl = oracle.selection_quality(pos, omass, _pad(pooled, runner.ld), sel)
+        osel_mass = _oracle_sel_mass(inp, s, pos, sel, runner.ld)
+        cov, rec, kl = _oracle_quality(pos, omass, osel_mass, _pad(pooled, runner.ld), sel)
         np.testing.assert_allclose(q[..., 0], cov, rtol=0, atol=1e-4, err_msg=f"{name}: coverage")
         np.testing.assert_allclose(q[..., 2], kl, rtol=1e-3, atol=1e-3, err_msg=f"{name}: KL")
         assert np.all(np.abs(q[..., 1] - rec) <= 1.0 / 16 + 1e-6)
@@ -164,16 +215,10 @@ def test_needles_are_found():
     selections cover far more of the dense attention mass than chance, and
     the MSA outputs on those rows still match the oracle."""
     runner, sample = _run("needles")
-    inp, dev = runner.inputs, runner.inputs.q.device
-    hkv = runner.dims.num_kv_heads
     from tests.gpu_helpers import compare_rows
     for s, pos, rows in sample:
         compare_rows(runner, s, pos[pos >= 128])  # rows with at least one earlier block
-        rows_t, mass = _gpu_mass(runner, rows)
-        quality = torch.empty((len(rows), hkv, 3), dtype=torch.float32, device=dev)
-        ops.msa_selection_quality(runner.dims, runner.batch, rows_t, mass, runner.scores, runner.sel, quality)
-        torch.cuda.synchronize()
-        q = quality.cpu().numpy().astype(np.float64)
+        q = _gpu_quality(runner, rows)
         far = pos >= 16 * 128  # rows with more causal blocks than slots
         chance = float(np.mean(16 / (pos[far] // 128 + 1)))  # uniform coverage share, and about chance recall
         assert q[far, :, 0].mean() > chance + 0.2, "coverage should beat the uniform share"

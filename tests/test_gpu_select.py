@@ -7,10 +7,12 @@ import sys
 import pytest
 import torch
 
+import numpy as np
+
 from block_sparse_long_score_amd import ops
 from block_sparse_long_score_amd.inputs import WORKLOADS, make_inputs
 from block_sparse_long_score_amd.pipeline import MsaRunner
-from tests.gpu_helpers import check_selection_invariants
+from tests.gpu_helpers import check_selection_invariants, oracle_rows, seq_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -65,14 +67,30 @@ def test_index_select_equals_score_then_topk(name, rows_per_chunk):
     assert torch.equal(sel, runner.sel)
 
 
+def _sampled_positions(w, s, count, seed):
+    first, n = w.seq_lens[s] - w.q_lens[s], w.seq_lens[s]
+    rng = np.random.default_rng(seed)
+    fixed = [p for p in (first, 2047, 2048, n - 1) if first <= p < n]
+    return np.unique(np.concatenate([fixed, rng.integers(first, n, size=count)]).astype(np.int64))
+
+
 @pytest.mark.parametrize("wl", ["c3", "c4p", "c2"])
 def test_index_select_full_size(wl):
+    """msa_index_select at full size: equal to the two calls on every row, and to
+    the oracle on sampled rows of every sequence."""
     _announce(f"select full size {wl}")
-    runner = MsaRunner(make_inputs(WORKLOADS[wl], "cuda"), chunk_rows=16384)
+    w = WORKLOADS[wl]
+    runner = MsaRunner(make_inputs(w, "cuda"), chunk_rows=16384)
     runner.step()
     sel = _select(runner)
     assert torch.equal(sel, runner.sel)
     check_selection_invariants(runner)
+    for s in range(w.num_seqs):
+        pos = _sampled_positions(w, s, 128 if w.q_lens[s] > 1 else 0, 7 + s)
+        _, want, _ = oracle_rows(runner.inputs, s, pos, attend=False)
+        rows = torch.from_numpy(seq_rows(runner.inputs, s, pos)).to(sel.device)
+        got = sel.index_select(0, rows).cpu().numpy()
+        np.testing.assert_array_equal(got, want, err_msg=f"{wl} sequence {s}: msa_index_select against the oracle")
 
 
 @pytest.mark.parametrize("kind", ["index_select", "dense_prefill", "dense_decode"])

@@ -41,8 +41,20 @@ MUTANTS = [
      "mass[i / block_size > 0 ? i / block_size - 1 : 0] += z[i] / denom / group_size;"),
     ("recall ties go to the higher index", "if (!taken[b] && (best < 0 || P[b] > P[best])) best = b;",
      "if (!taken[b] && (best < 0 || P[b] >= P[best])) best = b;"),
-    ("KL with the logarithm ratio flipped", "if (P[b] > 0.0) d += P[b] * (log(P[b]) - ((double)S[b] - lse));",
-     "if (P[b] > 0.0) d += P[b] * (((double)S[b] - lse) - log(P[b]));"),
+    ("KL with the logarithm ratio flipped",
+     "if (s[j] >= 0 && P[s[j]] > 0.0) d += P[s[j]] * (log(P[s[j]]) - ((double)S[s[j]] - lse));",
+     "if (s[j] >= 0 && P[s[j]] > 0.0) d += P[s[j]] * (((double)S[s[j]] - lse) - log(P[s[j]]));"),
+    ("indexer softmax over every causal block instead of the candidates",
+     "        if (s[j] >= 0) sum += exp((double)S[s[j]] - smax);",
+     "        if (s[j] >= 0) sum += exp((double)S[s[j]] - smax);\n"
+     "      for (int64_t b = 0; b <= pos[r] / block_size; ++b) sum += exp((double)S[b] - smax);"),
+    ("candidate mass includes tokens after the query",
+     "for (int64_t i = (int64_t)s[jj] * block_size; i < (int64_t)(s[jj] + 1) * block_size && i <= t; ++i) {",
+     "for (int64_t i = (int64_t)s[jj] * block_size; i < (int64_t)(s[jj] + 1) * block_size && i < n_keys; ++i) {"),
+    ("candidate mass not averaged over the group", "mass[blk[m]] += z[m] / denom / group_size;",
+     "mass[blk[m]] += z[m] / denom;"),
+    ("candidate mass credited to the next slot's block", "blk[n] = s[jj];",
+     "blk[n] = s[jj + 1 < top_k && s[jj + 1] >= 0 ? jj + 1 : jj];"),
     ("coverage misses the last selected block", "for (int j = 0; j < top_k; ++j)\n          if (s[j] >= 0) cov += P[s[j]];",
      "for (int j = 0; j + 1 < top_k; ++j)\n          if (s[j] >= 0) cov += P[s[j]];"),
 ]
@@ -63,6 +75,8 @@ PINS = [
     quality.test_all_blocks_selected_covers_everything,
     quality.test_kl_hand_example,
     quality.test_kl_vanishes_when_the_indexer_matches_and_is_nonnegative,
+    quality.test_selected_mass_hand_example,
+    lambda o: quality.test_selected_mass_is_attention_over_the_selection(o, 7, 700, 16, 5, 6, 2, 32),
 ]
 
 
