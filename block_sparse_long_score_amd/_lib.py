@@ -58,6 +58,7 @@ def load() -> ctypes.CDLL:
         "msa_block_topk": ([dims, batch, vp, i64, vp, vp], ctypes.c_int),
         "msa_sparse_attn_prefill": ([dims, cache, batch, vp, vp, vp, vp, sz, vp], ctypes.c_int),
         "msa_sparse_attn_decode": ([dims, cache, batch, vp, vp, vp, vp, sz, vp], ctypes.c_int),
+        "msa_sparse_attn_decode_noalloc": ([dims, cache, batch, vp, vp, vp, vp], ctypes.c_int),
         "msa_sparse_attn_prefill_plan": ([dims, cache, batch, vp, vp, sz, vp], ctypes.c_int),
         "msa_sparse_attn_prefill_run": ([dims, cache, batch, vp, vp, vp, vp, vp, sz, vp], ctypes.c_int),
         "msa_block_attn_mass": ([dims, cache, batch, vp, vp, vp, i32, vp, i64, vp], ctypes.c_int),

@@ -40,6 +40,8 @@
 // bf16 are directly the B operand of the P.V product.  The block's K and V
 // are staged row-major by asynchronous global->LDS copies; the V^T operand
 // is read with the LDS transpose load (attn_tiles.h).
+#include <mutex>
+
 #include "attn_tiles.h"
 #include "msa_kernels.h"
 
@@ -109,6 +111,56 @@ size_t prefill_workspace_bytes(const Problem& p) {
   return w.plan_total + w.part_total;
 }
 size_t decode_workspace_bytes(const Problem& p) { return main_layout(p, true).part_total; }
+
+// ------------------------------------------------- decode without allocation
+
+// The split decode (fewer than kFusedDecodeMinGroups (sequence, group) pairs)
+// keeps one partial row per (pair, slot, head) in scratch memory; larger
+// batches use decode_fused_kernel, which needs none.  So the scratch of the
+// largest split decode, 127 pairs at G = 16 and D = 128, serves every decode
+// batch: 127 * 16 * 16 partial rows of 128 fp16 values and 8 bytes of
+// statistics each.
+constexpr size_t kDecodeScratchBytes = ((size_t)127 * 16 * 16 * 128 * 2 + 255) / 256 * 256 +
+                                       ((size_t)127 * 16 * 16 * 2 * 4 + 255) / 256 * 256;
+
+// The scratch of msa_sparse_attn_decode_noalloc.  Each GPU holds its own copy
+// from the library's first use on it until the process ends.  Host code never
+// uses this name as an address (on the host it is only a stand-in for the
+// symbol): kernels receive the device address that decode_scratch() looked up
+// for the GPU they run on.
+static __device__ __align__(256) unsigned char scratch[kDecodeScratchBytes];
+
+size_t decode_scratch_capacity() { return kDecodeScratchBytes; }
+
+size_t decode_scratch_need(const Problem& p) {
+  return (int64_t)p.num_seqs * p.hkv >= kFusedDecodeMinGroups ? 0 : decode_workspace_bytes(p);
+}
+
+// Device address of `scratch` on `device`, looked up once per device (with
+// that device current) and kept for the life of the process.
+hipError_t decode_scratch(int device, void** addr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* table[kMaxDevices] = {};
+  if (device < 0 || device >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!table[device]) {
+    int current = 0;
+    hipError_t e = hipGetDevice(&current);
+    if (e != hipSuccess) return e;
+    if (current != device && (e = hipSetDevice(device)) != hipSuccess) return e;
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (current != device) {
+      const hipError_t e2 = hipSetDevice(current);
+      if (e == hipSuccess) e = e2;
+    }
+    if (e != hipSuccess) return e;
+    table[device] = ptr;
+  }
+  *addr = table[device];
+  return hipSuccess;
+}
 
 // An entry (query at position t of sequence s, selected logical block b) is
 // attended iff b is causal for t and the block table names a cached block.

@@ -501,4 +501,25 @@ msa_status msa_sparse_attn_decode(const msa_dims* dims, const msa_cache* cache, 
                     "msa_sparse_attn_decode launch");
 }
 
+msa_status msa_sparse_attn_decode_noalloc(const msa_dims* dims, const msa_cache* cache, const msa_batch* batch,
+                                          const void* q, const int32_t* sel, void* out, void* stream) {
+  MSA_TRY(check_attn(dims, cache, batch, q, sel, out));
+  MSA_TRY(check_one_query_per_sequence(batch));
+  const msa::Problem p = make_problem(dims, batch, cache);
+  const size_t need = msa::decode_scratch_need(p);
+  if (need > msa::decode_scratch_capacity())
+    return fail(MSA_ERR_WORKSPACE, "this decode needs %zu bytes of scratch; the library's static scratch holds %zu",
+                need, msa::decode_scratch_capacity());
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  int device = 0;
+  hipError_t e = st ? hipStreamGetDevice(st, &device) : hipGetDevice(&device);
+  if (e != hipSuccess) return hip_status(e, "msa_sparse_attn_decode_noalloc: device of the stream");
+  void* ws = nullptr;
+  if ((e = msa::decode_scratch(device, &ws)) != hipSuccess)
+    return hip_status(e, "msa_sparse_attn_decode_noalloc: scratch address");
+  return hip_status(msa::launch_attn_decode(p, static_cast<const uint16_t*>(q), sel, static_cast<uint16_t*>(out), ws,
+                                            st),
+                    "msa_sparse_attn_decode_noalloc launch");
+}
+
 }  // extern "C"

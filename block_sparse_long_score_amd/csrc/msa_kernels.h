@@ -76,6 +76,12 @@ hipError_t launch_attn_prefill_run(const Problem& p, const uint16_t* q, const in
 size_t decode_workspace_bytes(const Problem& p);
 hipError_t launch_attn_decode(const Problem& p, const uint16_t* q, const int32_t* sel, uint16_t* out, void* ws,
                               hipStream_t stream);
+// The library's static decode scratch (for callers that cannot allocate): the
+// bytes this batch needs of it (0 when the one-workgroup-per-pair kernel runs),
+// its capacity, and its device address on `device` (looked up once per device).
+size_t decode_scratch_need(const Problem& p);
+size_t decode_scratch_capacity();
+hipError_t decode_scratch(int device, void** addr);
 
 // Dense causal attention over the same cache (queries outer, no workspace).
 hipError_t launch_dense_prefill(const Problem& p, const uint16_t* q, uint16_t* out, hipStream_t stream);

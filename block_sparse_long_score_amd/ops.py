@@ -20,7 +20,7 @@ from ._lib import (MSA_CALL_DENSE_ATTN_DECODE, MSA_CALL_INDEX_SELECT, MSA_CALL_S
 
 __all__ = ["Dims", "Cache", "Batch", "MsaError", "msa_kv_append", "msa_index_score", "msa_block_topk",
            "msa_sparse_attn_prefill", "msa_sparse_attn_prefill_plan", "msa_sparse_attn_prefill_run",
-           "msa_sparse_attn_decode", "msa_dense_attn_prefill", "msa_dense_attn_decode",
+           "msa_sparse_attn_decode", "msa_sparse_attn_decode_noalloc", "msa_dense_attn_prefill", "msa_dense_attn_decode",
            "msa_index_select", "msa_block_attn_mass", "msa_selection_quality", "msa_workspace_size", "msa_abi_version",
            "PreparedCall", "prepare",
            "MSA_CALL_SPARSE_ATTN_PREFILL", "MSA_CALL_SPARSE_ATTN_DECODE", "MSA_CALL_DENSE_ATTN_DECODE", "MSA_CALL_INDEX_SELECT",
@@ -250,6 +250,16 @@ def msa_sparse_attn_prefill_run(dims: Dims, cache: Cache, batch: Batch, q, sel, 
 
 def msa_sparse_attn_decode(dims: Dims, cache: Cache, batch: Batch, q, sel, out, workspace, stream=None):
     _attn("msa_sparse_attn_decode", dims, cache, batch, q, sel, out, workspace, stream)
+
+
+def msa_sparse_attn_decode_noalloc(dims: Dims, cache: Cache, batch: Batch, q, sel, out, stream=None):
+    """msa_sparse_attn_decode with the library's static scratch instead of a workspace
+    (for callers that cannot allocate); calls that overlap on one GPU race."""
+    L = _lib.load()
+    d, c, b = dims.c(), cache.c(), batch.c()
+    _check(L.msa_sparse_attn_decode_noalloc(ctypes.byref(d), ctypes.byref(c), ctypes.byref(b),
+                                            _ptr(q, "q", torch.bfloat16), _ptr(sel, "sel", torch.int32),
+                                            _ptr(out, "out", torch.bfloat16), _stream(stream)))
 
 
 def msa_index_select(dims: Dims, cache: Cache, batch: Batch, q_idx, sel, workspace, stream=None):

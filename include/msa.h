@@ -268,6 +268,30 @@ msa_status msa_sparse_attn_decode(const msa_dims* dims, const msa_cache* cache,
                                   void* out, void* workspace, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------- *
+ * msa_sparse_attn_decode_noalloc — msa_sparse_attn_decode without a caller
+ * workspace, for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation).  It
+ * computes exactly what msa_sparse_attn_decode computes (same kernels, same
+ * results bit for bit).  Its scratch memory is a static array inside the
+ * library: about 8.2 MB per GPU, held from the first call on that GPU until
+ * the process ends, enough for every decode batch (batches of 128 or more
+ * (sequence, group) pairs need none; smaller ones need
+ * msa_workspace_size(..., MSA_CALL_SPARSE_ATTN_DECODE) bytes of it, at most
+ * the array's size).  The call allocates nothing and calls no allocating
+ * routine.  Every call on one GPU shares that GPU's array: calls that overlap
+ * in time on one GPU (on different streams, or from different threads without
+ * ordering) race and may return wrong results; calls ordered on one stream are
+ * safe.  The array keeps the last call's contents; no call relies on them.
+ *   q, sel, out : as msa_sparse_attn_decode.
+ * Errors: NULL_POINTER, BAD_SHAPE, UNSUPPORTED, MISALIGNED, CAPACITY,
+ *         WORKSPACE (a batch that would need more scratch than the array
+ *         holds), HIP.
+ * ------------------------------------------------------------------------- */
+msa_status msa_sparse_attn_decode_noalloc(const msa_dims* dims, const msa_cache* cache,
+                                          const msa_batch* batch, const void* q, const int32_t* sel,
+                                          void* out, void* stream);
+
+/* ------------------------------------------------------------------------- *
  * msa_block_attn_mass — attention mass per block for a sample of query rows
  * ([M3-evo] §2: MSA is judged by how much of the attention its chosen blocks
  * cover, and in training the Main Branch forms a group-averaged importance

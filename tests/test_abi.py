@@ -131,6 +131,20 @@ def test_attention_validation(lib):
     assert lib.msa_workspace_size(ctypes.byref(d), ctypes.byref(c), ctypes.byref(b.c), 7) == 0
 
 
+def test_noalloc_decode_validates_on_the_host(lib):
+    """The allocation-free decode rejects what msa_sparse_attn_decode rejects, before any HIP call."""
+    d, c = _dims(), _cache()
+    b = _Batch([1024, 900], [1, 2])
+    args = (ctypes.byref(d), ctypes.byref(c), ctypes.byref(b.c))
+    assert lib.msa_sparse_attn_decode_noalloc(*args, FAKE, FAKE, FAKE, None) == SHAPE  # two queries in sequence 1
+    b1 = _Batch([1024, 900], [1, 1])
+    args1 = (ctypes.byref(d), ctypes.byref(c), ctypes.byref(b1.c))
+    assert lib.msa_sparse_attn_decode_noalloc(*args1, None, FAKE, FAKE, None) == NULLP
+    assert lib.msa_sparse_attn_decode_noalloc(*args1, FAKE, FAKE + 4, FAKE, None) == MISAL
+    assert lib.msa_sparse_attn_decode_noalloc(ctypes.byref(_dims(head_dim=96)), ctypes.byref(c), ctypes.byref(b1.c),
+                                              FAKE, FAKE, FAKE, None) == UNSUP
+
+
 def test_workspace_grows_with_queries(lib):
     d, c = _dims(), _cache(num_blocks=4096, mbps=1024)
     sizes = [lib.msa_workspace_size(ctypes.byref(d), ctypes.byref(c), ctypes.byref(_Batch([n], [n]).c), 1)
