@@ -312,7 +312,7 @@ def workload_leg(name: str, steps: int, warmup: int, chunk_rows: int):
     for r in runners:
         r.hook = hook
     for i in range(steps):
-        runners[i % n_rot].step()
+        runners[i % n_rot].step(fused=False)  # the four calls one by one, so the stage can be bracketed
     torch.cuda.synchronize()
     for r in runners:
         r.hook = None
@@ -321,7 +321,9 @@ def workload_leg(name: str, steps: int, warmup: int, chunk_rows: int):
     work = algorithmic_work(w)
     leg = {"workload": f"{w.name}: {w.description}", "mode": "decode" if runner.decode else "prefill",
            "steps": steps, "warmup": warmup, "ms_per_step": ms, "tokens_per_s": w.total_q / (ms / 1e3),
-           "stage_ms_serial": stage_ms}
+           "stage_ms_serial": stage_ms,
+           "step_calls": "msa_decode_step" if runner.decode else "msa_kv_append + msa_index_score + msa_block_topk + "
+                                                                 "msa_sparse_attn_prefill per chunk"}
     if runner.decode:
         algo = (work["kidx_bytes"] + work["pooled_bytes"] / 2) / launches
         gbs = algo / (launch_ms / 1e3) / 1e9
@@ -488,7 +490,7 @@ def main():
         for r in runners:
             r.hook = hook
         for i in range(args.steps):
-            steps[i % n_rot]()
+            runners[i % n_rot].step(fused=False)  # decode: the four calls one by one, so the scan can be bracketed
         torch.cuda.synchronize()
         for r in runners:
             r.hook = None
@@ -596,7 +598,13 @@ def main():
         "median_ms_per_step": float(np.median(step_times)),
         "timing": {"value": f"{args.steps} steps back to back, events at the two ends only",
                    "median_ms_per_step": f"a second pass of {args.steps} steps, an event between consecutive steps",
-                   "roofline": f"a third pass of {args.steps} steps, events around each launch of the dominant stage"},
+                   "roofline": f"a third pass of {args.steps} steps, events around each launch of the dominant stage"
+                               + (" (the step's four calls issued one by one instead of msa_decode_step)"
+                                  if mode == "decode" else "")},
+        "step_calls": ("msa_decode_step (the append fused into the K_idx scan; then selection, attention and "
+                       "merge in one kernel below 128 (sequence, group) pairs, else the top-k kernel and the "
+                       "one-workgroup-per-pair attention)" if mode == "decode" else
+                       "msa_kv_append, then per chunk msa_index_score, msa_block_topk, msa_sparse_attn_prefill"),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

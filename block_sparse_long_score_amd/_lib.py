@@ -19,6 +19,7 @@ MSA_CALL_DENSE_ATTN_DECODE = 3
 MSA_CALL_INDEX_SELECT = 4
 MSA_CALL_SPARSE_ATTN_PREFILL_PLAN = 5
 MSA_CALL_SPARSE_ATTN_PREFILL_RUN = 6
+MSA_CALL_DECODE_STEP = 7
 
 
 class MsaDims(ctypes.Structure):
@@ -59,6 +60,7 @@ def load() -> ctypes.CDLL:
         "msa_sparse_attn_prefill": ([dims, cache, batch, vp, vp, vp, vp, sz, vp], ctypes.c_int),
         "msa_sparse_attn_decode": ([dims, cache, batch, vp, vp, vp, vp, sz, vp], ctypes.c_int),
         "msa_sparse_attn_decode_noalloc": ([dims, cache, batch, vp, vp, vp, vp], ctypes.c_int),
+        "msa_decode_step": ([dims, cache, batch, vp, vp, vp, vp, vp, vp, i64, vp, vp, vp, sz, vp], ctypes.c_int),
         "msa_sparse_attn_prefill_plan": ([dims, cache, batch, vp, vp, sz, vp], ctypes.c_int),
         "msa_sparse_attn_prefill_run": ([dims, cache, batch, vp, vp, vp, vp, vp, sz, vp], ctypes.c_int),
         "msa_block_attn_mass": ([dims, cache, batch, vp, vp, vp, i32, vp, i64, vp], ctypes.c_int),

@@ -44,6 +44,7 @@
 
 #include "attn_tiles.h"
 #include "msa_kernels.h"
+#include "topk_rows.h"
 
 namespace msa {
 
@@ -325,6 +326,16 @@ struct KvOuterArgs {
   int chunk;
 };
 
+// The fused decode step's second kernel: the selection is made in-kernel
+// from the pooled scores (and written out), and the split path merges the
+// slots of a row in the workgroup that finishes last.
+struct StepArgs {
+  const float* scores;  // pooled scores [total_q][hkv][ld]
+  int64_t ld;
+  int32_t* sel_out;     // [total_q][hkv][16]
+  int32_t* counters;    // split path: finished slots per (row, group); zero on entry
+};
+
 // One (row, head) pair of a tile: where its query lives and how its keys are masked.
 struct TileRow {
   bool valid;
@@ -487,20 +498,34 @@ __global__ __launch_bounds__(256, 2) void kvouter_kernel(KvOuterArgs a) {
 // 16x16x32 bf16 MFMA lane layout: A lane l holds A[l%16][8*(l/16) .. +7],
 // B lane l holds B[8*(l/16) .. +7][l%16], D lane l register i holds
 // D[4*(l/16) + i][l%16].
+// LDS of one slot's decode attention (decode_block_partial).
 template <int D, int GM>
-__global__ __launch_bounds__(256) void decode_block_kernel(KvOuterArgs a) {
+struct DecodeBlockLds {
+  float s_s[GM][kBlock];
+  float red_s[4][GM][D];
+  float stat_s[GM][4];
+};
+
+// One workgroup (4 waves) attends the sequence's single query (the group's G
+// heads) at position t to block b (logical; it must satisfy entry_valid) and
+// writes the partial rows (R*16 + slot)*G + head.
+template <int D, bool COHERENT>
+__device__ __forceinline__ u32x4 merge_slots(uint32_t ok_mask, const int64_t (&prow)[kTopK], const uint16_t* part_o,
+                                             const float* part_st, int d8);
+__device__ __forceinline__ void coherent_store(void* p, uint32_t v);
+
+// COHERENT: the partials are stored with device-coherent stores (for a merge
+// by another workgroup of the same kernel); the values are the same.
+template <int D, int GM, bool COHERENT = false>
+__device__ __forceinline__ void decode_block_partial(const KvOuterArgs& a, DecodeBlockLds<D, GM>& sh, int s, int g,
+                                                     int64_t R, int slot, int b, int t) {
   constexpr int VPL = D / 64;  // output dims per lane in P.V
   constexpr int KS = D / 32;   // MFMA k-steps
-  __shared__ float s_s[GM][kBlock];
-  __shared__ float red_s[4][GM][D];
-  __shared__ float stat_s[GM][4];
+  auto& s_s = sh.s_s;
+  auto& red_s = sh.red_s;
+  auto& stat_s = sh.stat_s;
   const Problem& p = a.p;
   const int G = p.group;
-  const int slot = blockIdx.x, g = blockIdx.y, s = blockIdx.z;
-  const int64_t R = ((int64_t)p.cu_q[s] << a.hkv_shift) + g;
-  const int b = a.sel[R * kTopK + slot];
-  const int t = p.seq_lens[s] - 1;
-  if (!entry_valid(p, s, b, t)) return;
   const int phys = p.block_table[(int64_t)s * p.max_blocks_per_seq + b];
   const int nvalid = min(kBlock, t - b * kBlock + 1);
   const int64_t key_stride = (int64_t)p.hkv * D;
@@ -616,12 +641,97 @@ __global__ __launch_bounds__(256) void decode_block_kernel(KvOuterArgs a) {
     const u32x4 w{pack_f16x2(x[0] * f, x[1] * f), pack_f16x2(x[2] * f, x[3] * f), pack_f16x2(x[4] * f, x[5] * f),
                   pack_f16x2(x[6] * f, x[7] * f)};
     const int64_t prow = (R * kTopK + slot) * G + j;
-    store16(a.part_o + prow * D + p8 * 8, w);
+    if constexpr (COHERENT) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) coherent_store(a.part_o + prow * D + p8 * 8 + 2 * i, w[i]);
+    } else {
+      store16(a.part_o + prow * D + p8 * 8, w);
+    }
   }
   if (tid < G) {
     const int64_t prow = (R * kTopK + slot) * G + tid;
-    *reinterpret_cast<f32x2*>(a.part_st + prow * 2) = f32x2{stat_s[tid][0] + __log2f(stat_s[tid][1]), stat_s[tid][2]};
+    const f32x2 st{stat_s[tid][0] + __log2f(stat_s[tid][1]), stat_s[tid][2]};
+    if constexpr (COHERENT) {
+      coherent_store(a.part_st + prow * 2, __float_as_uint(st[0]));
+      coherent_store(a.part_st + prow * 2 + 1, __float_as_uint(st[1]));
+    } else {
+      *reinterpret_cast<f32x2*>(a.part_st + prow * 2) = st;
+    }
   }
+}
+
+template <int D, int GM>
+__global__ __launch_bounds__(256) void decode_block_kernel(KvOuterArgs a) {
+  __shared__ DecodeBlockLds<D, GM> sh;
+  const Problem& p = a.p;
+  const int slot = blockIdx.x, g = blockIdx.y, s = blockIdx.z;
+  const int64_t R = ((int64_t)p.cu_q[s] << a.hkv_shift) + g;
+  const int b = a.sel[R * kTopK + slot];
+  const int t = p.seq_lens[s] - 1;
+  if (!entry_valid(p, s, b, t)) return;
+  decode_block_partial<D, GM>(a, sh, s, g, R, slot, b, t);
+}
+
+
+// The fused decode step, small batches: one workgroup per (slot, group,
+// sequence), as decode_block_kernel, that first makes its row's selection
+// from the pooled scores (every slot's workgroup computes the same one with
+// split_select_row, the msa_block_topk rule; slot 0's writes it out), then
+// attends its slot's block.  The row's 16 workgroups count themselves on a
+// per-row counter; the last one merges the 16 slots exactly as merge_kernel
+// does and sets the counter back to 0.  Partial stores are released and
+// acquired at device scope around the counter, so the merge sees every
+// workgroup's partial whichever XCD wrote it.
+template <int D, int GM>
+__global__ __launch_bounds__(256) void decode_step_block_kernel(KvOuterArgs a, StepArgs sa) {
+  constexpr int C8 = D / 8;
+  __shared__ DecodeBlockLds<D, GM> sh;
+  __shared__ uint32_t surv_key[4][64];
+  __shared__ int32_t surv_idx[4][64];
+  __shared__ int32_t cand[4][kKeep];
+  __shared__ int32_t sel_s[kTopK];
+  __shared__ int last_s;
+  const Problem& p = a.p;
+  const int G = p.group;
+  const int slot = blockIdx.x, g = blockIdx.y, s = blockIdx.z;
+  const int r = p.cu_q[s];
+  const int64_t R = ((int64_t)r << a.hkv_shift) + g;
+  const int t = p.seq_lens[s] - 1;
+  const int c = t >> 7;
+  const int tid = threadIdx.x;
+  if (c + 1 <= kTopK) {
+    if (tid < kTopK) sel_s[tid] = tid <= c ? tid : -1;
+  } else {
+    split_select_row<4, 32>(sa.scores + R * sa.ld, c, sel_s, surv_key, surv_idx, cand);  // <= 2048 per wave in registers
+    if (tid == 0) sel_s[kKeep] = c;
+  }
+  __syncthreads();
+  if (slot == 0 && tid < kTopK) sa.sel_out[R * kTopK + tid] = sel_s[tid];
+  const int b = sel_s[slot];
+  if (entry_valid(p, s, b, t)) decode_block_partial<D, GM, true>(a, sh, s, g, R, slot, b, t);
+
+  // The partials were stored device-coherently; every wave waits until its
+  // stores have completed before the row's counter is incremented, so the
+  // workgroup that sees 15 finished before it reads complete partials (with
+  // device-coherent loads).  No cache maintenance is needed.
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (tid == 0)
+    last_s = __hip_atomic_fetch_add(sa.counters + R, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == kTopK - 1;
+  __syncthreads();
+  if (!last_s) return;
+  uint32_t ok_mask = 0;
+#pragma unroll
+  for (int j = 0; j < kTopK; ++j) ok_mask |= (entry_valid(p, s, sel_s[j], t) ? 1u : 0u) << j;
+  for (int idx = tid; idx < G * C8; idx += blockDim.x) {
+    const int hj = idx / C8, d8 = idx - hj * C8;
+    int64_t prow[kTopK];
+#pragma unroll
+    for (int j = 0; j < kTopK; ++j) prow[j] = ((ok_mask >> j & 1u) ? R * kTopK + j : 0) * G + hj;
+    store16(a.out_direct + ((int64_t)r * p.hq + g * G + hj) * D + d8 * 8,
+            merge_slots<D, true>(ok_mask, prow, a.part_o, a.part_st, d8));
+  }
+  if (tid == 0) sa.counters[R] = 0;
 }
 
 // Decode of a large batch: one workgroup of 16 waves per (sequence, group);
@@ -679,13 +789,94 @@ struct MergeArgs {
   int hkv_shift;
 };
 
+// Log-sum-exp combination of one (row, head)'s attended slots for 8
+// consecutive output dims d8*8 .. +7: slot j (bit j of ok_mask) holds the
+// partial row prow[j] (normalised output * 2^-e, fp16) and its statistics
+// (log2 of the slot's softmax mass, e).  Returns the 8 outputs as bf16.  All
+// loads of the 16 slots are issued before any arithmetic.
+// Relaxed device-scope loads and stores of the partials that one kernel's
+// workgroups exchange (the fused decode step's merge): on gfx950 they go to
+// the device-coherent level, past any XCD's L2, so no cache write-back or
+// invalidation is needed around them.
+__device__ __forceinline__ uint32_t coherent_load(const void* p) {
+  return __hip_atomic_load(static_cast<const uint32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void coherent_store(void* p, uint32_t v) {
+  __hip_atomic_store(static_cast<uint32_t*>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+template <int D, bool COHERENT = false>
+__device__ __forceinline__ u32x4 merge_slots(uint32_t ok_mask, const int64_t (&prow)[kTopK], const uint16_t* part_o,
+                                             const float* part_st, int d8) {
+  // Slot j's weight is its softmax mass 2^lse_j relative to the largest.
+  float M = -__builtin_inff();
+  f32x2 sj[kTopK];
+  u32x4 yc[COHERENT ? kTopK : 1];
+  if constexpr (COHERENT) {  // every slot's statistics and partial row in flight at once
+#pragma unroll
+    for (int j = 0; j < kTopK; ++j) {
+      const bool ok = ok_mask >> j & 1u;
+      const float* st = part_st + (ok ? prow[j] : 0) * 2;
+      const uint16_t* y = part_o + (ok ? prow[j] : 0) * D + d8 * 8;
+      sj[j] = f32x2{__uint_as_float(coherent_load(st)), __uint_as_float(coherent_load(st + 1))};
+      yc[j] = u32x4{coherent_load(y), coherent_load(y + 2), coherent_load(y + 4), coherent_load(y + 6)};
+    }
+#pragma unroll
+    for (int j = 0; j < kTopK; ++j) {
+      if (!(ok_mask >> j & 1u)) {
+        sj[j] = f32x2{-__builtin_inff(), 0.f};
+        yc[j] = u32x4{0u, 0u, 0u, 0u};
+      }
+      M = fmaxf(M, sj[j][0]);
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < kTopK; ++j) {
+      sj[j] = (ok_mask >> j & 1u) ? *reinterpret_cast<const f32x2*>(part_st + prow[j] * 2)
+                                  : f32x2{-__builtin_inff(), 0.f};
+      M = fmaxf(M, sj[j][0]);
+    }
+  }
+  float L = 0.f;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int h8 = 0; h8 < kTopK; h8 += 8) {
+    __builtin_amdgcn_sched_barrier(0);  // eight slots' loads in flight at a time
+    u32x4 y[8];
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) {
+      const int j = h8 + jj;
+      if constexpr (COHERENT)
+        y[jj] = yc[j];
+      else
+        y[jj] = (ok_mask >> j & 1u) ? load16(part_o + prow[j] * D + d8 * 8) : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) {
+      const int j = h8 + jj;
+      const float w = (ok_mask >> j & 1u) ? fast_exp2(sj[j][0] - M) : 0.f;
+      L += w;
+      const float wy = ldexpf(w, (int)sj[j][1]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        acc[2 * i] += wy * f16_lo(y[jj][i]);
+        acc[2 * i + 1] += wy * f16_hi(y[jj][i]);
+      }
+    }
+  }
+  const float inv = L > 0.f ? 1.0f / L : 0.f;  // no attended key (every selected block unmapped): 0
+  u32x4 o;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) o[i] = pack_bf16x2(acc[2 * i] * inv, acc[2 * i + 1] * inv);
+  return o;
+}
+
 // One thread per (row, head, 8 consecutive output dims): log-sum-exp over
 // the row's attended slots, then the bf16 output.  A slot is attended iff its
 // block id is causal (0 <= b <= c) and the block table maps it to a cached
 // block (entry_valid); the attention pass wrote partials for exactly those.
 // Prefill reads that decision from the plan (entry_of = -1 otherwise), decode
-// from the block table.  All loads of the 16 slots are issued before any
-// arithmetic.
+// from the block table.
 template <int D>
 __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
   constexpr int C8 = D / 8;
@@ -726,44 +917,7 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
       prow[j] = (ok ? ent : 0) * G + hj;
     }
   }
-  // Slot j's weight is its softmax mass 2^lse_j relative to the largest.
-  float M = -__builtin_inff();
-  f32x2 sj[kTopK];
-#pragma unroll
-  for (int j = 0; j < kTopK; ++j) {
-    sj[j] = (ok_mask >> j & 1u) ? *reinterpret_cast<const f32x2*>(a.part_st + prow[j] * 2)
-                                : f32x2{-__builtin_inff(), 0.f};
-    M = fmaxf(M, sj[j][0]);
-  }
-  float L = 0.f;
-  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int h8 = 0; h8 < kTopK; h8 += 8) {
-    __builtin_amdgcn_sched_barrier(0);  // eight slots' loads in flight at a time
-    u32x4 y[8];
-#pragma unroll
-    for (int jj = 0; jj < 8; ++jj) {
-      const int j = h8 + jj;
-      y[jj] = (ok_mask >> j & 1u) ? load16(a.part_o + prow[j] * D + d8 * 8) : u32x4{0u, 0u, 0u, 0u};
-    }
-#pragma unroll
-    for (int jj = 0; jj < 8; ++jj) {
-      const int j = h8 + jj;
-      const float w = (ok_mask >> j & 1u) ? fast_exp2(sj[j][0] - M) : 0.f;
-      L += w;
-      const float wy = ldexpf(w, (int)sj[j][1]);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        acc[2 * i] += wy * f16_lo(y[jj][i]);
-        acc[2 * i + 1] += wy * f16_hi(y[jj][i]);
-      }
-    }
-  }
-  const float inv = L > 0.f ? 1.0f / L : 0.f;  // no attended key (every selected block unmapped): 0
-  u32x4 o;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) o[i] = pack_bf16x2(acc[2 * i] * inv, acc[2 * i + 1] * inv);
-  store16(a.out + ((int64_t)r * p.hq + g * G + hj) * D + d8 * 8, o);
+  store16(a.out + ((int64_t)r * p.hq + g * G + hj) * D + d8 * 8, merge_slots<D>(ok_mask, prow, a.part_o, a.part_st, d8));
 }
 
 // ------------------------------------------------------------------ launch
@@ -872,6 +1026,55 @@ hipError_t launch_attn_decode(const Problem& p, const uint16_t* q, const int32_t
   if (p.total_q == 0) return hipSuccess;
   return p.head_dim == 128 ? launch_decode_t<128>(p, q, sel, out, ws, stream)
                            : launch_decode_t<64>(p, q, sel, out, ws, stream);
+}
+
+// ------------------------------------------------------- fused decode step
+
+// Workspace of the fused decode step: the split decode's partial rows, then
+// one counter per (row, group).
+size_t decode_step_workspace_bytes(const Problem& p) {
+  return decode_workspace_bytes(p) + align256(sizeof(int32_t) * (size_t)p.total_q * p.hkv);
+}
+
+int32_t* decode_step_counters(const Problem& p, void* ws) {
+  if ((int64_t)p.num_seqs * p.hkv >= kFusedDecodeMinGroups) return nullptr;  // the fused path merges in LDS
+  return reinterpret_cast<int32_t*>(static_cast<char*>(ws) + decode_workspace_bytes(p));
+}
+
+template <int D>
+static hipError_t launch_step_attn_t(const Problem& p, const uint16_t* q, const float* scores, int64_t ld,
+                                     int32_t* sel, uint16_t* out, void* ws, int64_t max_blocks, hipStream_t stream) {
+  const MainWs w = main_layout(p, true);
+  char* base = static_cast<char*>(ws);
+  KvOuterArgs k{p, q, sel, nullptr, nullptr, nullptr, nullptr,
+                reinterpret_cast<uint16_t*>(base + w.part_o), out, reinterpret_cast<float*>(base + w.part_st),
+                w.n_lists, hkv_shift_of(p), w.chunk};
+  const StepArgs sa{scores, ld, sel, decode_step_counters(p, ws)};
+  if (!sa.counters) {
+    // Batches that fill the chip with one workgroup per (sequence, group): the
+    // selection as its own short kernel (made inside each workgroup, it would
+    // delay every workgroup's attention by its latency), then the attention.
+    const hipError_t e = launch_block_topk(p, scores, ld, sel, max_blocks, stream);
+    if (e != hipSuccess) return e;
+    return launch_decode_t<D>(p, q, sel, out, ws, stream);
+  }
+  const dim3 dgrid(kTopK, p.hkv, p.num_seqs);
+  if (p.group <= 4)
+    hipLaunchKernelGGL((decode_step_block_kernel<D, 4>), dgrid, dim3(256), 0, stream, k, sa);
+  else if (p.group <= 6)
+    hipLaunchKernelGGL((decode_step_block_kernel<D, 6>), dgrid, dim3(256), 0, stream, k, sa);
+  else if (p.group <= 8)
+    hipLaunchKernelGGL((decode_step_block_kernel<D, 8>), dgrid, dim3(256), 0, stream, k, sa);
+  else
+    hipLaunchKernelGGL((decode_step_block_kernel<D, 16>), dgrid, dim3(256), 0, stream, k, sa);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_step_attn(const Problem& p, const uint16_t* q, const float* scores, int64_t ld, int32_t* sel,
+                                   uint16_t* out, void* ws, int64_t max_blocks, hipStream_t stream) {
+  if (p.total_q == 0) return hipSuccess;
+  return p.head_dim == 128 ? launch_step_attn_t<128>(p, q, scores, ld, sel, out, ws, max_blocks, stream)
+                           : launch_step_attn_t<64>(p, q, scores, ld, sel, out, ws, max_blocks, stream);
 }
 
 }  // namespace msa

@@ -394,8 +394,22 @@ __global__ __launch_bounds__(64 * WAVES, WAVES / 2) void index_score_shared_kern
 // prefill kernel), is read into registers, and the wave's next block is
 // requested into the same region before this one is multiplied, so one block
 // per wave is always in flight without a workgroup barrier.
-template <int DIDX>
-__global__ __launch_bounds__(256, 2) void index_score_stream_kernel(IndexArgs a) {
+// The fused decode step's append (APPEND): each sequence's new token (its
+// single query row) is written into the cache by the workgroup that scores
+// the token's block, before any of its waves copies that block, and that
+// workgroup clears the sequence's rows of the attention kernel's counters.
+struct StepAppend {
+  uint16_t* k_cache;
+  uint16_t* v_cache;
+  uint16_t* k_idx_cache;
+  const uint16_t* k_new;      // bf16 [total_q][hkv][D]
+  const uint16_t* v_new;
+  const uint16_t* k_idx_new;  // bf16 [total_q][d_idx]
+  int32_t* counters;          // [total_q][hkv] or NULL
+};
+
+template <int DIDX, bool APPEND>
+__global__ __launch_bounds__(256, 2) void index_score_stream_kernel(IndexArgs a, StepAppend ap) {
   constexpr int KS = DIDX / 16;          // 32x32x16 MFMA k-steps
   constexpr int BLK = kBlock * DIDX;     // bf16 elements of one K_idx block
   constexpr int CPR = DIDX / 8;          // 16-byte chunks per row
@@ -404,7 +418,12 @@ __global__ __launch_bounds__(256, 2) void index_score_stream_kernel(IndexArgs a)
   extern __shared__ float pooled_s[];  // [32][kc + 1]
   const Problem& p = a.p;
 
-  const int s = blockIdx.z;
+  // APPEND: the grid is (tile, sequence, key chunk) with the chunks in reverse
+  // order, so every sequence's last chunk (the one that appends the new
+  // token before scoring it) is dispatched first and its extra work
+  // overlaps the rest of the scan instead of lengthening its tail.
+  const int s = APPEND ? blockIdx.y : blockIdx.z;
+  const int key_chunk = APPEND ? (int)(gridDim.z - 1 - blockIdx.z) : (int)blockIdx.y;
   const int row0 = p.cu_q[s];
   const int nq = p.cu_q[s + 1] - row0;
   if (nq <= 0) return;
@@ -416,7 +435,7 @@ __global__ __launch_bounds__(256, 2) void index_score_stream_kernel(IndexArgs a)
   if ((int)blockIdx.x >= n_tiles) return;
   const int p0 = tile0 + (n_tiles - 1 - (int)blockIdx.x) * tq;
   const int c_tile = p0 >> 7;
-  const int kb0 = blockIdx.y * a.kc;
+  const int kb0 = key_chunk * a.kc;
   if (kb0 > c_tile) return;
   const int nkb = min(a.kc, c_tile + 1 - kb0);
 
@@ -451,6 +470,30 @@ __global__ __launch_bounds__(256, 2) void index_score_stream_kernel(IndexArgs a)
                                        16, 0, 0);
     }
   };
+  if constexpr (APPEND) {
+    const int t_new = seq_len - 1;  // one query per sequence: the new token
+    if ((t_new >> 7) >= kb0 && (t_new >> 7) < kb0 + nkb) {
+      const int phys = table[t_new >> 7];
+      if (phys >= 0 && phys < p.num_blocks) {  // (an unmapped block holds no keys, as in msa_kv_append)
+        const int kv_vec = (p.hkv * p.head_dim) >> 3;  // 16-byte vectors of one token's K (and V)
+        constexpr int ki_vec = DIDX >> 3;
+        const int64_t slot = (int64_t)phys * kBlock + (t_new & 127);
+        for (int v = threadIdx.x; v < 2 * kv_vec + ki_vec; v += blockDim.x) {
+          if (v < kv_vec)
+            store16(ap.k_cache + (slot * kv_vec + v) * 8, load16(ap.k_new + ((int64_t)row0 * kv_vec + v) * 8));
+          else if (v < 2 * kv_vec)
+            store16(ap.v_cache + (slot * kv_vec + v - kv_vec) * 8,
+                    load16(ap.v_new + ((int64_t)row0 * kv_vec + v - kv_vec) * 8));
+          else
+            store16(ap.k_idx_cache + (slot * ki_vec + v - 2 * kv_vec) * 8,
+                    load16(ap.k_idx_new + ((int64_t)row0 * ki_vec + v - 2 * kv_vec) * 8));
+        }
+      }
+      if (ap.counters && (int)threadIdx.x < p.hkv) ap.counters[((int64_t)row0 << a.hkv_shift) + threadIdx.x] = 0;
+      __builtin_amdgcn_s_waitcnt(0);  // this wave's stores have completed
+      __syncthreads();                // and every wave's, before the block is copied
+    }
+  }
   int kb = kb0 + wave;
   if (kb < kb0 + nkb) dma(kb);
   for (; kb < kb0 + nkb; kb += 4) {
@@ -511,9 +554,9 @@ static hipError_t launch_index_t(const IndexArgs& a, dim3 grid, hipStream_t stre
   return hipGetLastError();
 }
 
-hipError_t launch_index_score(const Problem& p, const uint16_t* q_idx, float* scores, int64_t ld,
-                              const int32_t* seq_lens_host, const int32_t* cu_q_host, hipStream_t stream,
-                              int64_t first_row) {
+static hipError_t launch_index_impl(const Problem& p, const uint16_t* q_idx, float* scores, int64_t ld,
+                                    const int32_t* seq_lens_host, const int32_t* cu_q_host, hipStream_t stream,
+                                    int64_t first_row, const StepAppend* append) {
   int hkv_shift = 0;
   while ((1 << hkv_shift) < p.hkv) ++hkv_shift;
   int max_q = 0;
@@ -522,6 +565,7 @@ hipError_t launch_index_score(const Problem& p, const uint16_t* q_idx, float* sc
   // Prefill-shaped batches: 512 columns per workgroup sharing each K_idx block.
   constexpr int kSharedCols = 8 * 32 * 2;  // 8 waves x 64 columns
   if (max_q * p.hkv > 4 * kSharedCols) {
+    if (append) return hipErrorInvalidValue;  // the append is fused only into the one-tile-per-sequence scan
     const int tq = kSharedCols / p.hkv;
     int max_tiles = 0, max_blocks = 0;
     for (int s = 0; s < p.num_seqs; ++s) {
@@ -566,13 +610,37 @@ hipError_t launch_index_score(const Problem& p, const uint16_t* q_idx, float* sc
   dim3 grid((unsigned)max_tiles, (unsigned)((max_blocks + kc - 1) / kc), (unsigned)p.num_seqs);
   if (nct == 1) {
     const size_t lds = (size_t)32 * (a.kc + 1) * sizeof(float);
+    if (append) {
+      const dim3 agrid(grid.x, grid.z, grid.y);  // (tile, sequence, chunk): see the kernel
+      if (p.index_dim == 64)
+        hipLaunchKernelGGL((index_score_stream_kernel<64, true>), agrid, dim3(256), lds, stream, a, *append);
+      else
+        hipLaunchKernelGGL((index_score_stream_kernel<32, true>), agrid, dim3(256), lds, stream, a, *append);
+      return hipGetLastError();
+    }
+    const StepAppend none{};
     if (p.index_dim == 64)
-      hipLaunchKernelGGL((index_score_stream_kernel<64>), grid, dim3(256), lds, stream, a);
+      hipLaunchKernelGGL((index_score_stream_kernel<64, false>), grid, dim3(256), lds, stream, a, none);
     else
-      hipLaunchKernelGGL((index_score_stream_kernel<32>), grid, dim3(256), lds, stream, a);
+      hipLaunchKernelGGL((index_score_stream_kernel<32, false>), grid, dim3(256), lds, stream, a, none);
     return hipGetLastError();
   }
+  if (append) return hipErrorInvalidValue;  // the append is fused only into the one-tile-per-sequence scan
   return p.index_dim == 64 ? launch_index_t<64, 4>(a, grid, stream) : launch_index_t<32, 4>(a, grid, stream);
+}
+
+hipError_t launch_index_score(const Problem& p, const uint16_t* q_idx, float* scores, int64_t ld,
+                              const int32_t* seq_lens_host, const int32_t* cu_q_host, hipStream_t stream,
+                              int64_t first_row) {
+  return launch_index_impl(p, q_idx, scores, ld, seq_lens_host, cu_q_host, stream, first_row, nullptr);
+}
+
+hipError_t launch_decode_append_score(const Problem& p, uint16_t* k_cache, uint16_t* v_cache, uint16_t* k_idx_cache,
+                                      const uint16_t* k_new, const uint16_t* v_new, const uint16_t* k_idx_new,
+                                      const uint16_t* q_idx, float* scores, int64_t ld, int32_t* counters,
+                                      const int32_t* seq_lens_host, const int32_t* cu_q_host, hipStream_t stream) {
+  const StepAppend ap{k_cache, v_cache, k_idx_cache, k_new, v_new, k_idx_new, counters};
+  return launch_index_impl(p, q_idx, scores, ld, seq_lens_host, cu_q_host, stream, 0, &ap);
 }
 
 }  // namespace msa

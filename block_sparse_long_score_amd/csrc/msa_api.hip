@@ -428,6 +428,7 @@ size_t msa_workspace_size(const msa_dims* dims, const msa_cache* cache, const ms
       return msa::prefill_run_bytes(p);
     case MSA_CALL_SPARSE_ATTN_DECODE: ok(); return msa::decode_workspace_bytes(p);
     case MSA_CALL_DENSE_ATTN_DECODE: ok(); return msa::dense_decode_workspace_bytes(p, (int)max_query_blocks(batch));
+    case MSA_CALL_DECODE_STEP: ok(); return msa::decode_step_workspace_bytes(p);
     case MSA_CALL_INDEX_SELECT: {
       ok();
       const int64_t ld = std::max<int64_t>(1, max_query_blocks(batch));
@@ -499,6 +500,42 @@ msa_status msa_sparse_attn_decode(const msa_dims* dims, const msa_cache* cache, 
   return hip_status(msa::launch_attn_decode(p, static_cast<const uint16_t*>(q), sel, static_cast<uint16_t*>(out),
                                             workspace, static_cast<hipStream_t>(stream)),
                     "msa_sparse_attn_decode launch");
+}
+
+msa_status msa_decode_step(const msa_dims* dims, const msa_cache* cache, const msa_batch* batch, const void* k_new,
+                           const void* v_new, const void* k_idx_new, const void* q_idx, const void* q,
+                           float* block_scores, int64_t ld, int32_t* sel, void* out, void* workspace,
+                           size_t ws_bytes, void* stream) {
+  MSA_TRY(check_dims(dims));
+  MSA_TRY(check_cache(cache));
+  MSA_TRY(check_batch(dims, batch, cache));
+  MSA_TRY(check_one_query_per_sequence(batch));
+  MSA_TRY(check_ptr(k_new, "k_new"));
+  MSA_TRY(check_ptr(v_new, "v_new"));
+  MSA_TRY(check_ptr(k_idx_new, "k_idx_new"));
+  MSA_TRY(check_ptr(q_idx, "q_idx"));
+  MSA_TRY(check_ptr(q, "q"));
+  MSA_TRY(check_ptr(block_scores, "block_scores"));
+  MSA_TRY(check_ptr(sel, "sel"));
+  MSA_TRY(check_ptr(out, "out"));
+  const int64_t need_ld = max_query_blocks(batch);
+  if (ld < need_ld) return fail(MSA_ERR_BAD_SHAPE, "ld=%lld is less than the %lld blocks of the longest sequence",
+                                (long long)ld, (long long)need_ld);
+  const msa::Problem p = make_problem(dims, batch, cache);
+  const size_t need = msa::decode_step_workspace_bytes(p);
+  if (!workspace || ws_bytes < need)
+    return fail(MSA_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace ? ws_bytes : 0, need);
+  if (!aligned16(workspace)) return fail(MSA_ERR_MISALIGNED, "workspace is not 16-byte aligned");
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e = msa::launch_decode_append_score(
+      p, static_cast<uint16_t*>(cache->k), static_cast<uint16_t*>(cache->v), static_cast<uint16_t*>(cache->k_idx),
+      static_cast<const uint16_t*>(k_new), static_cast<const uint16_t*>(v_new),
+      static_cast<const uint16_t*>(k_idx_new), static_cast<const uint16_t*>(q_idx), block_scores, ld,
+      msa::decode_step_counters(p, workspace), batch->seq_lens_host, batch->cu_q_host, st);
+  if (e != hipSuccess) return hip_status(e, "msa_decode_step launch (append and scoring)");
+  return hip_status(msa::launch_decode_step_attn(p, static_cast<const uint16_t*>(q), block_scores, ld, sel,
+                                                 static_cast<uint16_t*>(out), workspace, need_ld, st),
+                    "msa_decode_step launch (selection and attention)");
 }
 
 msa_status msa_sparse_attn_decode_noalloc(const msa_dims* dims, const msa_cache* cache, const msa_batch* batch,

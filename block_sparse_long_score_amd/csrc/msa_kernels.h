@@ -76,6 +76,22 @@ hipError_t launch_attn_prefill_run(const Problem& p, const uint16_t* q, const in
 size_t decode_workspace_bytes(const Problem& p);
 hipError_t launch_attn_decode(const Problem& p, const uint16_t* q, const int32_t* sel, uint16_t* out, void* ws,
                               hipStream_t stream);
+// The fused decode step (one query row per sequence): the append of each
+// sequence's new token fused into the K_idx scan (which also clears the
+// attention kernel's counters), then, for batches of fewer than 128
+// (sequence, group) pairs, the selection, the attention and the merge in one
+// kernel (larger batches: the top-k kernel, then the one-workgroup-per-pair
+// attention).  Results equal msa_kv_append, msa_index_score, msa_block_topk
+// and msa_sparse_attn_decode in sequence, bit for bit.  max_blocks: blocks of
+// the longest sequence (host-side).
+size_t decode_step_workspace_bytes(const Problem& p);
+int32_t* decode_step_counters(const Problem& p, void* ws);  // NULL when the batch needs none
+hipError_t launch_decode_append_score(const Problem& p, uint16_t* k_cache, uint16_t* v_cache, uint16_t* k_idx_cache,
+                                      const uint16_t* k_new, const uint16_t* v_new, const uint16_t* k_idx_new,
+                                      const uint16_t* q_idx, float* scores, int64_t ld, int32_t* counters,
+                                      const int32_t* seq_lens_host, const int32_t* cu_q_host, hipStream_t stream);
+hipError_t launch_decode_step_attn(const Problem& p, const uint16_t* q, const float* scores, int64_t ld, int32_t* sel,
+                                   uint16_t* out, void* ws, int64_t max_blocks, hipStream_t stream);
 // The library's static decode scratch (for callers that cannot allocate): the
 // bytes this batch needs of it (0 when the one-workgroup-per-pair kernel runs),
 // its capacity, and its device address on `device` (looked up once per device).

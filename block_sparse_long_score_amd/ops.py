@@ -14,17 +14,17 @@ import numpy as np
 import torch
 
 from . import _lib
-from ._lib import (MSA_CALL_DENSE_ATTN_DECODE, MSA_CALL_INDEX_SELECT, MSA_CALL_SPARSE_ATTN_DECODE,
+from ._lib import (MSA_CALL_DECODE_STEP, MSA_CALL_DENSE_ATTN_DECODE, MSA_CALL_INDEX_SELECT, MSA_CALL_SPARSE_ATTN_DECODE,
                    MSA_CALL_SPARSE_ATTN_PREFILL, MSA_CALL_SPARSE_ATTN_PREFILL_PLAN, MSA_CALL_SPARSE_ATTN_PREFILL_RUN,
                    MsaBatch, MsaCache, MsaDims)
 
 __all__ = ["Dims", "Cache", "Batch", "MsaError", "msa_kv_append", "msa_index_score", "msa_block_topk",
            "msa_sparse_attn_prefill", "msa_sparse_attn_prefill_plan", "msa_sparse_attn_prefill_run",
            "msa_sparse_attn_decode", "msa_sparse_attn_decode_noalloc", "msa_dense_attn_prefill", "msa_dense_attn_decode",
-           "msa_index_select", "msa_block_attn_mass", "msa_selection_quality", "msa_workspace_size", "msa_abi_version",
+           "msa_index_select", "msa_decode_step", "msa_block_attn_mass", "msa_selection_quality", "msa_workspace_size", "msa_abi_version",
            "PreparedCall", "prepare",
            "MSA_CALL_SPARSE_ATTN_PREFILL", "MSA_CALL_SPARSE_ATTN_DECODE", "MSA_CALL_DENSE_ATTN_DECODE", "MSA_CALL_INDEX_SELECT",
-           "MSA_CALL_SPARSE_ATTN_PREFILL_PLAN", "MSA_CALL_SPARSE_ATTN_PREFILL_RUN"]
+           "MSA_CALL_SPARSE_ATTN_PREFILL_PLAN", "MSA_CALL_SPARSE_ATTN_PREFILL_RUN", "MSA_CALL_DECODE_STEP"]
 
 
 class MsaError(RuntimeError):
@@ -153,9 +153,18 @@ def _attn_args(dims, cache, batch, q, sel, out, workspace):
             _ptr(workspace, "workspace", torch.uint8), workspace.numel())
 
 
+def _decode_step_args(dims, cache, batch, k_new, v_new, k_idx_new, q_idx, q, block_scores, sel, out, workspace):
+    return (ctypes.byref(dims.c()), ctypes.byref(cache.c()), ctypes.byref(batch.c()),
+            _ptr(k_new, "k_new", torch.bfloat16), _ptr(v_new, "v_new", torch.bfloat16),
+            _ptr(k_idx_new, "k_idx_new", torch.bfloat16), _ptr(q_idx, "q_idx", torch.bfloat16),
+            _ptr(q, "q", torch.bfloat16), _ptr(block_scores, "block_scores", torch.float32), block_scores.shape[-1],
+            _ptr(sel, "sel", torch.int32), _ptr(out, "out", torch.bfloat16),
+            _ptr(workspace, "workspace", torch.uint8), workspace.numel())
+
+
 _MARSHAL = {"msa_kv_append": _kv_append_args, "msa_index_score": _index_score_args,
             "msa_block_topk": _block_topk_args, "msa_sparse_attn_prefill": _attn_args,
-            "msa_sparse_attn_decode": _attn_args}
+            "msa_sparse_attn_decode": _attn_args, "msa_decode_step": _decode_step_args}
 
 
 def _buffers(obj):
@@ -191,8 +200,8 @@ class PreparedCall:
 
 def prepare(name: str, *args) -> PreparedCall:
     """PreparedCall for one of msa_kv_append, msa_index_score, msa_block_topk,
-    msa_sparse_attn_prefill, msa_sparse_attn_decode, with the same positional
-    arguments as the function of that name (without the stream)."""
+    msa_sparse_attn_prefill, msa_sparse_attn_decode, msa_decode_step, with the
+    same positional arguments as the function of that name (without the stream)."""
     keep = tuple(b for a in args for b in _buffers(a))
     return PreparedCall(name, _MARSHAL[name](*args), keep)
 
@@ -250,6 +259,15 @@ def msa_sparse_attn_prefill_run(dims: Dims, cache: Cache, batch: Batch, q, sel, 
 
 def msa_sparse_attn_decode(dims: Dims, cache: Cache, batch: Batch, q, sel, out, workspace, stream=None):
     _attn("msa_sparse_attn_decode", dims, cache, batch, q, sel, out, workspace, stream)
+
+
+def msa_decode_step(dims: Dims, cache: Cache, batch: Batch, k_new, v_new, k_idx_new, q_idx, q, block_scores, sel, out,
+                    workspace, stream=None):
+    """One decode step (msa_kv_append, msa_index_score, msa_block_topk and msa_sparse_attn_decode in
+    sequence, same results) as two kernels; workspace: uint8, at least
+    msa_workspace_size(..., MSA_CALL_DECODE_STEP) bytes."""
+    _check(_lib.load().msa_decode_step(*_decode_step_args(dims, cache, batch, k_new, v_new, k_idx_new, q_idx, q,
+                                                          block_scores, sel, out, workspace), _stream(stream)))
 
 
 def msa_sparse_attn_decode_noalloc(dims: Dims, cache: Cache, batch: Batch, q, sel, out, stream=None):

@@ -23,7 +23,11 @@ from .inputs import Inputs
 
 
 class MsaRunner:
-    def __init__(self, inputs: Inputs, chunk_rows: int | None = None):
+    """fused_decode (decode batches; default on): a step is one msa_decode_step
+    call (append, scoring, selection and attention in two kernels) instead of
+    the four separate calls; results are the same bit for bit."""
+
+    def __init__(self, inputs: Inputs, chunk_rows: int | None = None, fused_decode: bool = True):
         w = inputs.workload
         dev = inputs.q.device
         self.inputs = inputs
@@ -31,6 +35,7 @@ class MsaRunner:
         self.cache = ops.Cache.allocate(self.dims, inputs.num_blocks, inputs.block_table)
         self.batch = ops.Batch.make(w.seq_lens, w.q_lens, dev)
         self.decode = all(n == 1 for n in w.q_lens)
+        self.fused_decode = self.decode and fused_decode
         self._fill_prefix()
         rows = inputs.new_token_rows()
         self.k_new = inputs.k.index_select(0, rows).contiguous()
@@ -48,9 +53,10 @@ class MsaRunner:
                 self.chunks.append((r0, r1, ops.Batch.make([first + r1], [r1 - r0], dev)))
             self.stream_b = torch.cuda.Stream(device=dev)  # default priority
             self.events = [torch.cuda.Event() for _ in range(len(self.chunks) + 1)]
-        call = ops.MSA_CALL_SPARSE_ATTN_DECODE if self.decode else ops.MSA_CALL_SPARSE_ATTN_PREFILL
         ws_batch = self.chunks[0][2] if self.chunks else self.batch
-        self.workspace = torch.empty(ops.msa_workspace_size(self.dims, self.cache, ws_batch, call),
+        calls = ([ops.MSA_CALL_SPARSE_ATTN_DECODE, ops.MSA_CALL_DECODE_STEP] if self.decode
+                 else [ops.MSA_CALL_SPARSE_ATTN_PREFILL])
+        self.workspace = torch.empty(max(ops.msa_workspace_size(self.dims, self.cache, ws_batch, c) for c in calls),
                                      dtype=torch.uint8, device=dev)
         # Optional observer: hook(stage, stream, phase) is called right before
         # (phase 0) and after (phase 1) each stage is enqueued in step(), with
@@ -94,6 +100,10 @@ class MsaRunner:
                 "attend": ops.prepare(attn, self.dims, self.cache, self.batch, inp.q, self.sel, self.out,
                                       self.workspace),
             }
+            if self.decode:
+                whole["decode_step"] = ops.prepare("msa_decode_step", self.dims, self.cache, self.batch, self.k_new,
+                                                   self.v_new, self.k_idx_new, inp.q_idx, inp.q, self.scores,
+                                                   self.sel, self.out, self.workspace)
             chunks = []
             for r0, r1, cb in self.chunks:
                 scores, sel = self.scores[r0:r1], self.sel[r0:r1]
@@ -129,11 +139,16 @@ class MsaRunner:
         fn()
         self.hook(name, stream, 1)
 
-    def step(self, stream=None):
+    def step(self, stream=None, fused: bool | None = None):
+        """One step.  fused (decode only; default: the runner's fused_decode):
+        one msa_decode_step call, else the four calls one by one (the hook, if
+        set, then sees each of them)."""
         if self.chunks:
             return self.pipelined_step()
         st = stream if stream is not None else torch.cuda.current_stream()
         calls = self._calls()[0]
+        if self.decode and (self.fused_decode if fused is None else fused):
+            return self._stage("decode_step", st, lambda: calls["decode_step"](st))
         if self.hook is None:
             for name in ("append", "index_score", "block_topk", "attend"):
                 calls[name](st)

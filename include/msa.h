@@ -131,7 +131,8 @@ typedef enum msa_call {
   MSA_CALL_DENSE_ATTN_DECODE = 3,
   MSA_CALL_INDEX_SELECT = 4,
   MSA_CALL_SPARSE_ATTN_PREFILL_PLAN = 5,  /* the plan buffer of msa_sparse_attn_prefill_plan */
-  MSA_CALL_SPARSE_ATTN_PREFILL_RUN = 6    /* the workspace of msa_sparse_attn_prefill_run */
+  MSA_CALL_SPARSE_ATTN_PREFILL_RUN = 6,   /* the workspace of msa_sparse_attn_prefill_run */
+  MSA_CALL_DECODE_STEP = 7                /* the workspace of msa_decode_step */
 } msa_call;
 
 /* ------------------------------------------------------------------------- *
@@ -266,6 +267,35 @@ msa_status msa_sparse_attn_prefill_run(const msa_dims* dims, const msa_cache* ca
 msa_status msa_sparse_attn_decode(const msa_dims* dims, const msa_cache* cache,
                                   const msa_batch* batch, const void* q, const int32_t* sel,
                                   void* out, void* workspace, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------- *
+ * msa_decode_step — one whole decode step of MSA ([M3-evo] §2, the four
+ * inference steps, for one new token per sequence): the calls msa_kv_append,
+ * msa_index_score, msa_block_topk and msa_sparse_attn_decode in sequence,
+ * with the same arguments and the same results bit for bit (block_scores,
+ * sel, out and the cache), in fewer kernels: the append of each sequence's
+ * new token is fused into the K_idx scan, and for batches of fewer than 128
+ * (sequence, group) pairs the block selection, the attention and the merge
+ * of the 16 slots run as one kernel (the workgroup that finishes a row last
+ * merges it; two kernels instead of five).  Larger batches run the top-k
+ * and the one-workgroup-per-pair attention after the fused scan (three
+ * instead of four).  Fewer launches shorten a step whose work is one
+ * HBM-bound scan followed by latency-bound tails.
+ *   Requires cu_q[s+1] - cu_q[s] == 1 for every s (BAD_SHAPE otherwise).
+ *   k_new, v_new, k_idx_new : as msa_kv_append
+ *   q_idx                   : as msa_index_score
+ *   q, sel, out             : as msa_sparse_attn_decode (sel is written)
+ *   block_scores, ld        : as msa_index_score (written)
+ *   workspace : device scratch of at least
+ *               msa_workspace_size(dims, cache, batch, MSA_CALL_DECODE_STEP)
+ *               bytes; contents on entry are ignored.
+ * Errors: NULL_POINTER, BAD_SHAPE, UNSUPPORTED, MISALIGNED, CAPACITY,
+ *         WORKSPACE, HIP.
+ * ------------------------------------------------------------------------- */
+msa_status msa_decode_step(const msa_dims* dims, const msa_cache* cache, const msa_batch* batch,
+                           const void* k_new, const void* v_new, const void* k_idx_new,
+                           const void* q_idx, const void* q, float* block_scores, int64_t ld,
+                           int32_t* sel, void* out, void* workspace, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------- *
  * msa_sparse_attn_decode_noalloc — msa_sparse_attn_decode without a caller

@@ -128,7 +128,7 @@ def test_attention_validation(lib):
     needp = lib.msa_workspace_size(ctypes.byref(d), ctypes.byref(c), ctypes.byref(b.c), 1)
     assert lib.msa_sparse_attn_prefill(*args, FAKE, needp - 1, None) == WS
     assert lib.msa_sparse_attn_prefill(*args, FAKE + 8, needp, None) == MISAL
-    assert lib.msa_workspace_size(ctypes.byref(d), ctypes.byref(c), ctypes.byref(b.c), 7) == 0
+    assert lib.msa_workspace_size(ctypes.byref(d), ctypes.byref(c), ctypes.byref(b.c), 99) == 0
 
 
 def test_noalloc_decode_validates_on_the_host(lib):
@@ -143,6 +143,28 @@ def test_noalloc_decode_validates_on_the_host(lib):
     assert lib.msa_sparse_attn_decode_noalloc(*args1, FAKE, FAKE + 4, FAKE, None) == MISAL
     assert lib.msa_sparse_attn_decode_noalloc(ctypes.byref(_dims(head_dim=96)), ctypes.byref(c), ctypes.byref(b1.c),
                                               FAKE, FAKE, FAKE, None) == UNSUP
+
+
+def test_decode_step_validates_on_the_host(lib):
+    """msa_decode_step rejects what its four calls reject, before any HIP call."""
+    d, c = _dims(), _cache()
+    b2 = _Batch([1024, 900], [1, 2])
+    b1 = _Batch([1024, 900], [1, 1])
+    need = lib.msa_workspace_size(ctypes.byref(d), ctypes.byref(c), ctypes.byref(b1.c), 7)
+    assert need >= lib.msa_workspace_size(ctypes.byref(d), ctypes.byref(c), ctypes.byref(b1.c), 2)
+
+    def call(b, ptrs=(FAKE,) * 5, ld=8, sel=FAKE, out=FAKE, ws=FAKE, nbytes=None, dims=d):
+        return lib.msa_decode_step(ctypes.byref(dims), ctypes.byref(c), ctypes.byref(b.c), *ptrs[:4], ptrs[4], FAKE,
+                                   ld, sel, out, ws, need if nbytes is None else nbytes, None)
+
+    assert call(b2) == SHAPE                               # two queries in sequence 1
+    assert call(b1, ptrs=(None, FAKE, FAKE, FAKE, FAKE)) == NULLP
+    assert call(b1, ptrs=(FAKE, FAKE, FAKE + 4, FAKE, FAKE)) == MISAL
+    assert call(b1, ld=7) == SHAPE                         # 8 blocks needed
+    assert call(b1, sel=None) == NULLP
+    assert call(b1, nbytes=need - 1) == WS
+    assert call(b1, ws=None) == WS
+    assert call(b1, dims=_dims(index_dim=48)) == UNSUP
 
 
 def test_workspace_grows_with_queries(lib):

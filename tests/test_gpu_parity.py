@@ -352,6 +352,63 @@ def test_prepared_step_equals_plain_calls(mode):
     assert torch.equal(runner.out.view(torch.int16), ref.view(torch.int16))
 
 
+_STEP_CASES = {
+    "split_m2": lambda: M2.with_sizes("step_split", [9999, 130, 2049, 5000, 1, 70000], [1] * 6, permuted_table=True),
+    "fused_m2": lambda: M2.with_sizes("step_fused", _RAGGED, [1] * 16, permuted_table=True),
+    "split_g16": lambda: WORKLOADS["m3d"].with_sizes("step_g16", [_RAGGED[i % 16] + 13 * i for i in range(31)],
+                                                     [1] * 31, permuted_table=True),
+    "fused_g16": lambda: WORKLOADS["m3d"].with_sizes("step_g16f", [_RAGGED[i % 16] + 13 * i for i in range(32)],
+                                                     [1] * 32, permuted_table=True),
+    "split_d64": lambda: WORKLOADS["c0"].with_sizes("step_d64", [_RAGGED[i % 16] for i in range(20)], [1] * 20,
+                                                    permuted_table=True),
+}
+
+
+@pytest.mark.parametrize("case", list(_STEP_CASES))
+@pytest.mark.parametrize("unmapped", [False, True])
+def test_decode_step_equals_separate_calls(case, unmapped):
+    """msa_decode_step (append fused into the scan; selection, attention and the
+    last-arriver merge in one kernel) writes exactly what msa_kv_append,
+    msa_index_score, msa_block_topk and msa_sparse_attn_decode write: pooled
+    scores, selections, outputs and the cache, bit for bit, on two calls in a
+    row with different queries (the merge counters must be back at zero for
+    the second, and no partial of the first may be read)."""
+    w = _STEP_CASES[case]()
+    _announce(f"decode step {case} unmapped={unmapped}: num_seqs={w.num_seqs} Hq={w.num_q_heads} "
+              f"Hkv={w.num_kv_heads} D={w.head_dim}")
+    runner = MsaRunner(make_inputs(w, "cuda"))
+    if unmapped:  # some logical blocks of every sequence hold no keys
+        for s in range(w.num_seqs):
+            for b in (2, 5, 17):
+                if b < runner.cache.block_table.shape[1]:
+                    runner.cache.block_table[s, b] = -1
+    bufs = (runner.scores, runner.sel, runner.out, runner.cache.k, runner.cache.v, runner.cache.k_idx)
+
+    def snapshot():
+        return [t.clone() for t in bufs]
+
+    def poison():
+        runner.scores.fill_(float("nan"))
+        runner.sel.fill_(-7)
+        runner.out.fill_(float("nan"))
+
+    for i in range(2):
+        if i == 1:  # new queries: every partial row differs from the first call's
+            runner.inputs.q.neg_()
+            runner.inputs.q_idx.neg_()
+        poison()
+        runner.step(fused=False)
+        torch.cuda.synchronize()
+        ref = snapshot()
+        poison()
+        runner.step(fused=True)
+        torch.cuda.synchronize()
+        for name, got, want in zip(("scores", "sel", "out", "k cache", "v cache", "k_idx cache"), bufs, ref):
+            assert torch.equal(got.view(torch.uint8), want.view(torch.uint8)), f"{case} call {i}: {name} differs"
+    if not unmapped:
+        check_selection_invariants(runner)
+
+
 def test_two_runs_are_identical():
     w = M2.with_sizes("det", [3000, 2000], [3000, 300])
     runner = _run(w)
