@@ -8,7 +8,9 @@ from __future__ import annotations
 import ctypes
 import os
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmsa.so")
+# MSA_LIBRARY names another build of the same library (the host-sanitizer
+# build of the CPU tests); by default the in-tree libmsa.so.
+LIB_PATH = os.environ.get("MSA_LIBRARY") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmsa.so")
 
 MSA_OK = 0
 STATUS_NAMES = {0: "MSA_OK", 1: "MSA_ERR_NULL_POINTER", 2: "MSA_ERR_BAD_SHAPE", 3: "MSA_ERR_UNSUPPORTED",

@@ -5,6 +5,7 @@
 #include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
+#include <string.h>
 
 #include <string>
 
@@ -190,7 +191,12 @@ int32_t msa_abi_version(void) { return MSA_ABI_VERSION; }
 const char* msa_last_error(void) { return g_last_error.c_str(); }
 
 const char* msa_status_string(msa_status status) {
-  switch (status) {
+  // A C caller may pass any int: read the argument's bits instead of using a
+  // value of enum type outside its enumerators' range.
+  static_assert(sizeof(msa_status) == sizeof(int32_t), "msa_status is a 32-bit integer");
+  int32_t code;
+  memcpy(&code, &status, sizeof code);
+  switch (code) {
     case MSA_OK: return "MSA_OK";
     case MSA_ERR_NULL_POINTER: return "MSA_ERR_NULL_POINTER";
     case MSA_ERR_BAD_SHAPE: return "MSA_ERR_BAD_SHAPE";
