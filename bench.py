@@ -333,7 +333,7 @@ def workload_leg(name: str, steps: int, warmup: int, chunk_rows: int):
         leg["algorithmic_bytes_per_step"] = step_bytes
         leg["roofline"] = {"bound": "hbm", "stage": dom, "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                            "frac": gbs / HBM_PEAK_GBS, "avg_launch_ms": launch_ms,
-                           "algorithmic_bytes_per_launch": algo}
+                           "algorithmic_bytes_per_launch": algo, "traffic": recorded_traffic(w.name, dom, launches)}
     else:
         algo = (work["index_flops"] if dom == "index_score" else work["main_flops"]) / launches
         tf = algo / (launch_ms / 1e3) / 1e12
@@ -343,7 +343,8 @@ def workload_leg(name: str, steps: int, warmup: int, chunk_rows: int):
         leg["algorithmic_flops_per_step"] = step_flops
         leg["roofline"] = {"bound": "mfma", "stage": dom, "achieved": tf, "peak": BF16_PEAK_TFLOPS,
                            "unit": "TFLOP/s", "frac": tf / BF16_PEAK_TFLOPS, "avg_launch_ms": launch_ms,
-                           "launches_per_step": launches, "algorithmic_flops_per_launch": algo}
+                           "launches_per_step": launches, "algorithmic_flops_per_launch": algo,
+                           "traffic": recorded_traffic(w.name, dom, launches)}
     del runners, runner, inputs
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
