@@ -509,16 +509,34 @@ struct DecodeBlockLds {
 // One workgroup (4 waves) attends the sequence's single query (the group's G
 // heads) at position t to block b (logical; it must satisfy entry_valid) and
 // writes the partial rows (R*16 + slot)*G + head.
-template <int D, bool COHERENT>
+template <int D, bool COHERENT, bool NT = false>
 __device__ __forceinline__ u32x4 merge_slots(uint32_t ok_mask, const int64_t (&prow)[kTopK], const uint16_t* part_o,
                                              const float* part_st, int d8);
-__device__ __forceinline__ void coherent_store(void* p, uint32_t v);
+
+// Device-coherent 16- and 8-byte loads and stores (gfx950 "sc1" buffer
+// accesses: they reach the level every XCD reads, past any XCD's L2, so no
+// cache write-back or invalidation is needed around them) of the partials
+// that one kernel's workgroups exchange (the fused decode step's merge).
+// Offsets are in bytes from the array's start.
+constexpr int kCoherent = 16;
+__device__ __forceinline__ void coherent_store16(void* base, uint32_t off, const u32x4& v) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, buffer_rsrc(base, 0x7fffffffu), off, 0, kCoherent);
+}
+__device__ __forceinline__ void coherent_store8(void* base, uint32_t off, const u32x2& v) {
+  __builtin_amdgcn_raw_buffer_store_b64(v, buffer_rsrc(base, 0x7fffffffu), off, 0, kCoherent);
+}
+__device__ __forceinline__ u32x4 coherent_load16(const void* base, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(buffer_rsrc(base, 0x7fffffffu), off, 0, kCoherent);
+}
+__device__ __forceinline__ u32x2 coherent_load8(const void* base, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b64(buffer_rsrc(base, 0x7fffffffu), off, 0, kCoherent);
+}
 
 // COHERENT: the partials are stored with device-coherent stores (for a merge
 // by another workgroup of the same kernel); the values are the same.
 template <int D, int GM, bool COHERENT = false>
-__device__ __forceinline__ void decode_block_partial(const KvOuterArgs& a, DecodeBlockLds<D, GM>& sh, int s, int g,
-                                                     int64_t R, int slot, int b, int t) {
+__device__ __forceinline__ void decode_block_partial(const KvOuterArgs& a, DecodeBlockLds<D, GM>& sh, int g,
+                                                     int64_t R, int slot, int b, int t, int phys) {
   constexpr int VPL = D / 64;  // output dims per lane in P.V
   constexpr int KS = D / 32;   // MFMA k-steps
   auto& s_s = sh.s_s;
@@ -526,7 +544,6 @@ __device__ __forceinline__ void decode_block_partial(const KvOuterArgs& a, Decod
   auto& stat_s = sh.stat_s;
   const Problem& p = a.p;
   const int G = p.group;
-  const int phys = p.block_table[(int64_t)s * p.max_blocks_per_seq + b];
   const int nvalid = min(kBlock, t - b * kBlock + 1);
   const int64_t key_stride = (int64_t)p.hkv * D;
   const uint16_t* kb = p.k + ((int64_t)phys * kBlock * p.hkv + g) * D;
@@ -534,15 +551,15 @@ __device__ __forceinline__ void decode_block_partial(const KvOuterArgs& a, Decod
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, q16 = lane >> 4;
 
-  // V rows of this wave's keys (lane: dims lane*VPL ..), issued first.
+  // V rows of this wave's keys (lane: dims lane*VPL ..), issued first; K and V by non-temporal loads (read once).
   uint32_t vreg[32];
 #pragma unroll
   for (int k = 0; k < 32; ++k) {
     const int kk = wave * 32 + k;
     if constexpr (VPL == 2)
-      vreg[k] = kk < nvalid ? *reinterpret_cast<const uint32_t*>(vb + kk * key_stride + lane * 2) : 0u;
+      vreg[k] = kk < nvalid ? __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(vb + kk * key_stride + lane * 2)) : 0u;
     else
-      vreg[k] = kk < nvalid ? (uint32_t)vb[kk * key_stride + lane] : 0u;
+      vreg[k] = kk < nvalid ? (uint32_t)__builtin_nontemporal_load(vb + kk * key_stride + lane) : 0u;
   }
   // K rows (A operand) for the wave's two 16-key tiles, and the heads' Q (B operand).
   bf16x8 ak[2][KS], bq[KS];
@@ -551,9 +568,10 @@ __device__ __forceinline__ void decode_block_partial(const KvOuterArgs& a, Decod
     const int key = wave * 32 + mt * 16 + l16;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
-      ak[mt][ks] = as_bf16x8(key < nvalid ? load16(kb + key * key_stride + ks * 32 + q16 * 8) : u32x4{0u, 0u, 0u, 0u});
+      ak[mt][ks] = as_bf16x8(key < nvalid ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kb + key * key_stride + ks * 32 + q16 * 8))
+                                          : u32x4{0u, 0u, 0u, 0u});
   }
-  const uint16_t* qh = a.q + ((int64_t)p.cu_q[s] * p.hq + g * G + l16) * D;
+  const uint16_t* qh = a.q + ((R >> a.hkv_shift) * p.hq + g * G + l16) * D;
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks)
     bq[ks] = as_bf16x8(l16 < G ? load16(qh + ks * 32 + q16 * 8) : u32x4{0u, 0u, 0u, 0u});
@@ -641,19 +659,16 @@ __device__ __forceinline__ void decode_block_partial(const KvOuterArgs& a, Decod
     const u32x4 w{pack_f16x2(x[0] * f, x[1] * f), pack_f16x2(x[2] * f, x[3] * f), pack_f16x2(x[4] * f, x[5] * f),
                   pack_f16x2(x[6] * f, x[7] * f)};
     const int64_t prow = (R * kTopK + slot) * G + j;
-    if constexpr (COHERENT) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) coherent_store(a.part_o + prow * D + p8 * 8 + 2 * i, w[i]);
-    } else {
+    if constexpr (COHERENT)
+      coherent_store16(a.part_o, (uint32_t)((prow * D + p8 * 8) * 2), w);
+    else
       store16(a.part_o + prow * D + p8 * 8, w);
-    }
   }
   if (tid < G) {
     const int64_t prow = (R * kTopK + slot) * G + tid;
     const f32x2 st{stat_s[tid][0] + __log2f(stat_s[tid][1]), stat_s[tid][2]};
     if constexpr (COHERENT) {
-      coherent_store(a.part_st + prow * 2, __float_as_uint(st[0]));
-      coherent_store(a.part_st + prow * 2 + 1, __float_as_uint(st[1]));
+      coherent_store8(a.part_st, (uint32_t)(prow * 8), u32x2{__float_as_uint(st[0]), __float_as_uint(st[1])});
     } else {
       *reinterpret_cast<f32x2*>(a.part_st + prow * 2) = st;
     }
@@ -668,8 +683,10 @@ __global__ __launch_bounds__(256) void decode_block_kernel(KvOuterArgs a) {
   const int64_t R = ((int64_t)p.cu_q[s] << a.hkv_shift) + g;
   const int b = a.sel[R * kTopK + slot];
   const int t = p.seq_lens[s] - 1;
-  if (!entry_valid(p, s, b, t)) return;
-  decode_block_partial<D, GM>(a, sh, s, g, R, slot, b, t);
+  if (b < 0 || b > (t >> 7)) return;
+  const int phys = p.block_table[(int64_t)s * p.max_blocks_per_seq + b];
+  if (!(phys >= 0 && phys < p.num_blocks)) return;  // entry_valid
+  decode_block_partial<D, GM>(a, sh, g, R, slot, b, t, phys);
 }
 
 
@@ -677,19 +694,31 @@ __global__ __launch_bounds__(256) void decode_block_kernel(KvOuterArgs a) {
 // sequence), as decode_block_kernel, that first makes its row's selection
 // from the pooled scores (every slot's workgroup computes the same one with
 // split_select_row, the msa_block_topk rule; slot 0's writes it out), then
-// attends its slot's block.  The row's 16 workgroups count themselves on a
-// per-row counter; the last one merges the 16 slots exactly as merge_kernel
-// does and sets the counter back to 0.  Partial stores are released and
-// acquired at device scope around the counter, so the merge sees every
-// workgroup's partial whichever XCD wrote it.
+// attends its slot's block.  While the scores load, the sequence's block
+// table row is loaded into LDS (rows of up to kStepTab blocks), so the
+// selected blocks' cache addresses and validity need no further round trip to
+// memory.  The row's 16 workgroups count themselves on a per-row counter; the
+// last one merges the 16 slots exactly as merge_kernel does and sets the
+// counter back to 0.  The partials are exchanged through device-coherent
+// stores and loads, so the merge sees every workgroup's partial whichever XCD
+// wrote it.
+constexpr int kStepTab = 8192;  // block-table entries staged in LDS (1M tokens)
+
 template <int D, int GM>
 __global__ __launch_bounds__(256) void decode_step_block_kernel(KvOuterArgs a, StepArgs sa) {
   constexpr int C8 = D / 8;
-  __shared__ DecodeBlockLds<D, GM> sh;
+  constexpr int TV = kStepTab / 256;  // table entries per thread
+  __shared__ union {
+    int32_t tab[kStepTab];       // selection phase: the sequence's block table row
+    DecodeBlockLds<D, GM> attn;  // attention phase
+  } lds;
   __shared__ uint32_t surv_key[4][64];
   __shared__ int32_t surv_idx[4][64];
   __shared__ int32_t cand[4][kKeep];
+  __shared__ uint32_t cand_key[4][kKeep];
   __shared__ int32_t sel_s[kTopK];
+  __shared__ int32_t phys_s[kTopK];
+  __shared__ uint32_t ok_s;
   __shared__ int last_s;
   const Problem& p = a.p;
   const int G = p.group;
@@ -699,16 +728,39 @@ __global__ __launch_bounds__(256) void decode_step_block_kernel(KvOuterArgs a, S
   const int t = p.seq_lens[s] - 1;
   const int c = t >> 7;
   const int tid = threadIdx.x;
+  const int32_t* table = p.block_table + (int64_t)s * p.max_blocks_per_seq;
+  const bool tab_lds = c < kStepTab;
+  int32_t tv[TV];
+  if (tab_lds) {  // requested before the scores, consumed after the selection
+#pragma unroll
+    for (int j = 0; j < TV; ++j) tv[j] = j * 256 + tid <= c ? table[j * 256 + tid] : -1;
+  }
   if (c + 1 <= kTopK) {
     if (tid < kTopK) sel_s[tid] = tid <= c ? tid : -1;
   } else {
-    split_select_row<4, 32>(sa.scores + R * sa.ld, c, sel_s, surv_key, surv_idx, cand);  // <= 2048 per wave in registers
+    // <= 2048 candidates per wave in registers
+    split_select_row<4, 32>(sa.scores + R * sa.ld, c, sel_s, surv_key, surv_idx, cand, cand_key);
     if (tid == 0) sel_s[kKeep] = c;
   }
+  if (tab_lds) {
+#pragma unroll
+    for (int j = 0; j < TV; ++j)
+      if (j * 256 + tid <= c) lds.tab[j * 256 + tid] = tv[j];
+  }
   __syncthreads();
+  if (tid < 64) {  // wave 0: each slot's cache block and whether it is attended (entry_valid)
+    const int bj = tid < kTopK ? sel_s[tid] : -1;
+    const bool causal = bj >= 0 && bj <= c;
+    const int phys = causal ? (tab_lds ? lds.tab[bj] : table[bj]) : -1;
+    const bool ok = causal && phys >= 0 && phys < p.num_blocks;
+    const uint64_t m = __ballot(ok);
+    if (tid < kTopK) phys_s[tid] = phys;
+    if (tid == 0) ok_s = (uint32_t)m;
+  }
+  __syncthreads();  // (the table's LDS is free from here on)
   if (slot == 0 && tid < kTopK) sa.sel_out[R * kTopK + tid] = sel_s[tid];
-  const int b = sel_s[slot];
-  if (entry_valid(p, s, b, t)) decode_block_partial<D, GM, true>(a, sh, s, g, R, slot, b, t);
+  const uint32_t ok_mask = ok_s;
+  if (ok_mask >> slot & 1u) decode_block_partial<D, GM, true>(a, lds.attn, g, R, slot, sel_s[slot], t, phys_s[slot]);
 
   // The partials were stored device-coherently; every wave waits until its
   // stores have completed before the row's counter is incremented, so the
@@ -720,9 +772,6 @@ __global__ __launch_bounds__(256) void decode_step_block_kernel(KvOuterArgs a, S
     last_s = __hip_atomic_fetch_add(sa.counters + R, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == kTopK - 1;
   __syncthreads();
   if (!last_s) return;
-  uint32_t ok_mask = 0;
-#pragma unroll
-  for (int j = 0; j < kTopK; ++j) ok_mask |= (entry_valid(p, s, sel_s[j], t) ? 1u : 0u) << j;
   for (int idx = tid; idx < G * C8; idx += blockDim.x) {
     const int hj = idx / C8, d8 = idx - hj * C8;
     int64_t prow[kTopK];
@@ -794,18 +843,7 @@ struct MergeArgs {
 // partial row prow[j] (normalised output * 2^-e, fp16) and its statistics
 // (log2 of the slot's softmax mass, e).  Returns the 8 outputs as bf16.  All
 // loads of the 16 slots are issued before any arithmetic.
-// Relaxed device-scope loads and stores of the partials that one kernel's
-// workgroups exchange (the fused decode step's merge): on gfx950 they go to
-// the device-coherent level, past any XCD's L2, so no cache write-back or
-// invalidation is needed around them.
-__device__ __forceinline__ uint32_t coherent_load(const void* p) {
-  return __hip_atomic_load(static_cast<const uint32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void coherent_store(void* p, uint32_t v) {
-  __hip_atomic_store(static_cast<uint32_t*>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-template <int D, bool COHERENT = false>
+template <int D, bool COHERENT = false, bool NT>
 __device__ __forceinline__ u32x4 merge_slots(uint32_t ok_mask, const int64_t (&prow)[kTopK], const uint16_t* part_o,
                                              const float* part_st, int d8) {
   // Slot j's weight is its softmax mass 2^lse_j relative to the largest.
@@ -816,10 +854,10 @@ __device__ __forceinline__ u32x4 merge_slots(uint32_t ok_mask, const int64_t (&p
 #pragma unroll
     for (int j = 0; j < kTopK; ++j) {
       const bool ok = ok_mask >> j & 1u;
-      const float* st = part_st + (ok ? prow[j] : 0) * 2;
-      const uint16_t* y = part_o + (ok ? prow[j] : 0) * D + d8 * 8;
-      sj[j] = f32x2{__uint_as_float(coherent_load(st)), __uint_as_float(coherent_load(st + 1))};
-      yc[j] = u32x4{coherent_load(y), coherent_load(y + 2), coherent_load(y + 4), coherent_load(y + 6)};
+      const int64_t pr = ok ? prow[j] : 0;
+      const u32x2 st = coherent_load8(part_st, (uint32_t)(pr * 8));
+      sj[j] = f32x2{__uint_as_float(st[0]), __uint_as_float(st[1])};
+      yc[j] = coherent_load16(part_o, (uint32_t)((pr * D + d8 * 8) * 2));
     }
 #pragma unroll
     for (int j = 0; j < kTopK; ++j) {
@@ -849,7 +887,12 @@ __device__ __forceinline__ u32x4 merge_slots(uint32_t ok_mask, const int64_t (&p
       if constexpr (COHERENT)
         y[jj] = yc[j];
       else
-        y[jj] = (ok_mask >> j & 1u) ? load16(part_o + prow[j] * D + d8 * 8) : u32x4{0u, 0u, 0u, 0u};
+        if (!(ok_mask >> j & 1u))
+        y[jj] = u32x4{0u, 0u, 0u, 0u};
+      else if constexpr (NT)
+        y[jj] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(part_o + prow[j] * D + d8 * 8));
+      else
+        y[jj] = load16(part_o + prow[j] * D + d8 * 8);
     }
 #pragma unroll
     for (int jj = 0; jj < 8; ++jj) {
@@ -876,8 +919,8 @@ __device__ __forceinline__ u32x4 merge_slots(uint32_t ok_mask, const int64_t (&p
 // block id is causal (0 <= b <= c) and the block table maps it to a cached
 // block (entry_valid); the attention pass wrote partials for exactly those.
 // Prefill reads that decision from the plan (entry_of = -1 otherwise), decode
-// from the block table.
-template <int D>
+// from the block table.  NT (decode): the partial rows by non-temporal loads.
+template <int D, bool NT>
 __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
   constexpr int C8 = D / 8;
   const Problem& p = a.p;
@@ -917,7 +960,7 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
       prow[j] = (ok ? ent : 0) * G + hj;
     }
   }
-  store16(a.out + ((int64_t)r * p.hq + g * G + hj) * D + d8 * 8, merge_slots<D>(ok_mask, prow, a.part_o, a.part_st, d8));
+  store16(a.out + ((int64_t)r * p.hq + g * G + hj) * D + d8 * 8, merge_slots<D, false, NT>(ok_mask, prow, a.part_o, a.part_st, d8));
 }
 
 // ------------------------------------------------------------------ launch
@@ -949,7 +992,11 @@ static hipError_t launch_merge_t(const Problem& p, const int32_t* sel, const int
   const int hs = hkv_shift_of(p);
   MergeArgs m{p, sel, entry_of, part_o, part_st, out, hs};
   const int64_t threads = ((int64_t)p.total_q << hs) * p.group * (D / 8);
-  hipLaunchKernelGGL(merge_kernel<D>, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream, m);
+  const dim3 grid((unsigned)((threads + 255) / 256));
+  if (entry_of)  // prefill
+    hipLaunchKernelGGL((merge_kernel<D, false>), grid, dim3(256), 0, stream, m);
+  else
+    hipLaunchKernelGGL((merge_kernel<D, true>), grid, dim3(256), 0, stream, m);
   return hipGetLastError();
 }
 

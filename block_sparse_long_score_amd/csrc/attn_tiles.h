@@ -334,7 +334,7 @@ struct DecodeWave {
     }
   }
 
-  // Requests the V rows (lane: dims lane*VPL ..) and the K operand rows of
+  // Requests (non-temporal loads) the V rows (lane: dims lane*VPL ..) and the K operand rows of
   // keys [c0, c0 + 16); keys at or past nvalid read key nvalid-1.  kr, vr:
   // buffer resources over the block-head's K and V rows; ks_b: the key
   // stride in bytes.  A V row's offset is the same in every lane (a scalar
@@ -347,14 +347,14 @@ struct DecodeWave {
     for (int kk = 0; kk < SUB; ++kk) {
       const int soff = min(c0 + kk, nvalid - 1) * ks_b;
       if constexpr (VPL == 2)
-        vreg[kk] = __builtin_amdgcn_raw_buffer_load_b32(vr, lane * 4, soff, 0);
+        vreg[kk] = __builtin_amdgcn_raw_buffer_load_b32(vr, lane * 4, soff, kLoadNT);
       else
-        vreg[kk] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(vr, lane * 2, soff, 0);
+        vreg[kk] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(vr, lane * 2, soff, kLoadNT);
     }
     const int koff = min(c0 + l16, nvalid - 1) * ks_b + q16 * 16;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      const auto x = __builtin_amdgcn_raw_buffer_load_b128(kr, koff + ks * 64, 0, 0);
+      const auto x = __builtin_amdgcn_raw_buffer_load_b128(kr, koff + ks * 64, 0, kLoadNT);
       ak[ks] = as_bf16x8(u32x4{x[0], x[1], x[2], x[3]});
     }
   }

@@ -75,6 +75,7 @@ __global__ __launch_bounds__(kSplitWaves * 64) void block_topk_split_kernel(Topk
   __shared__ uint32_t surv_key[kSplitWaves][64];
   __shared__ int32_t surv_idx[kSplitWaves][64];
   __shared__ int32_t cand[kSplitWaves][kKeep];
+  __shared__ uint32_t cand_key[kSplitWaves][kKeep];
   const Problem& p = a.p;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -88,7 +89,7 @@ __global__ __launch_bounds__(kSplitWaves * 64) void block_topk_split_kernel(Topk
     if (wave == 0 && lane < kTopK) out[lane] = lane <= c ? lane : -1;
     return;
   }
-  split_select_row<kSplitWaves>(a.scores + (R - a.r_base) * a.ld, c, out, surv_key, surv_idx, cand);
+  split_select_row<kSplitWaves>(a.scores + (R - a.r_base) * a.ld, c, out, surv_key, surv_idx, cand, cand_key);
   if (wave == 0 && lane == 0) out[kKeep] = c;
 }
 

@@ -389,9 +389,9 @@ __global__ __launch_bounds__(64 * WAVES, WAVES / 2) void index_score_shared_kern
 }
 
 // Decode-shaped batches (one 32-column tile per sequence): each wave streams
-// its own key blocks.  A block arrives by direct global-to-LDS loads into the
-// wave's own 16 KB LDS region (coalesced 1 KB runs, swizzled as in the
-// prefill kernel), is read into registers, and the wave's next block is
+// its own key blocks.  A block arrives by direct non-temporal global-to-LDS
+// loads into the wave's own 16 KB LDS region (coalesced 1 KB runs, swizzled
+// as in the prefill kernel), is read into registers, and the wave's next block is
 // requested into the same region before this one is multiplied, so one block
 // per wave is always in flight without a workgroup barrier.
 // The fused decode step's append (APPEND): each sequence's new token (its
@@ -467,7 +467,7 @@ __global__ __launch_bounds__(256, 2) void index_score_stream_kernel(IndexArgs a,
       __builtin_amdgcn_global_load_lds(static_cast<const void*>(src + row * DIDX + chunk * 8),
                                        reinterpret_cast<__attribute__((address_space(3))) void*>(
                                            reinterpret_cast<uintptr_t>(region + run * 512)),
-                                       16, 0, 0);
+                                       16, 0, kLoadNT);
     }
   };
   if constexpr (APPEND) {

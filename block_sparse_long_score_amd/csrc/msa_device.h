@@ -10,6 +10,13 @@ namespace msa {
 constexpr int kBlock = 128;  // tokens per KV block
 constexpr int kTopK = 16;    // blocks kept per query and group
 constexpr int kWave = 64;    // CDNA wavefront width
+// Cache-policy bits of a non-temporal load (gfx950 "nt").  Decode streams
+// read-once data (the context's K_idx, the selected blocks' K/V, the partial
+// rows) with it: 16 KB blocks in random order stream at ~6.5 TB/s this way
+// against ~5.7 TB/s with plain loads.  Prefill keeps plain loads, because its
+// K/V blocks and partial rows are read again soon enough for the Infinity
+// Cache to serve some of them.
+constexpr int kLoadNT = 2;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));

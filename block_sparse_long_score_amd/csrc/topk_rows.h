@@ -55,10 +55,11 @@ __device__ __forceinline__ void load_batch(const float* __restrict__ row, int c,
 
 // Selection for one row.  Rows with c <= 64 * NC candidates keep their keys
 // in registers (one batch of loads); longer rows are streamed in batches of
-// 64 * NC (NC per lane).
+// 64 * NC (NC per lane).  out_key (optional): each kept block's order key,
+// beside its index in out.
 template <bool CACHED, bool WRITE_LOCAL = true, int NC = kCached>
 __device__ void select_row(const float* __restrict__ row, int c, int32_t* __restrict__ out, uint32_t* surv_key,
-                           int32_t* surv_idx) {
+                           int32_t* surv_idx, uint32_t* out_key = nullptr) {
   const int lane = threadIdx.x & 63;
   const int nj = (c + 63) / 64;
   uint32_t keys[NC];
@@ -102,7 +103,10 @@ __device__ void select_row(const float* __restrict__ row, int c, int32_t* __rest
     const bool take = have && (k > T || (k == T && lanes_below(eq) < need));
     const uint64_t tm = __ballot(take);
     // 4. ascending output, local block last.
-    if (take) out[lanes_below(tm)] = idx;
+    if (take) {
+      out[lanes_below(tm)] = idx;
+      if (out_key) out_key[lanes_below(tm)] = k;
+    }
   } else {
     // Massive ties: exact k-th largest over all candidates, bit by bit.
     auto key_at = [&](int j) -> uint32_t {
@@ -125,7 +129,10 @@ __device__ void select_row(const float* __restrict__ row, int c, int32_t* __rest
       const uint64_t eq = __ballot(k == T);
       const bool take = k > T || (k == T && ties + lanes_below(eq) < need);
       const uint64_t tm = __ballot(take);
-      if (take) out[taken + lanes_below(tm)] = j * 64 + lane;
+      if (take) {
+        out[taken + lanes_below(tm)] = j * 64 + lane;
+        if (out_key) out_key[taken + lanes_below(tm)] = k;
+      }
       taken += __popcll(tm);
       ties += __popcll(eq);
     }
@@ -139,12 +146,14 @@ __device__ void select_row(const float* __restrict__ row, int c, int32_t* __rest
 // candidates (ties to the lower index); the overall top 15 lies in the union
 // of these, which wave 0 then searches in ascending block order with the same
 // exact threshold and tie rule, writing out[0..15) ascending.  out may be
-// global or LDS memory.  The selection is unique, so it depends on neither NW
-// nor NC (the candidates per lane each wave holds in registers).
+// global or LDS memory.  Each wave's candidates keep their keys beside their
+// indices (cand, cand_key), so the union is searched without reading the row
+// again.  The selection is unique, so it depends on neither NW nor NC (the
+// candidates per lane each wave holds in registers).
 template <int NW, int NC = kCached>
 __device__ __forceinline__ void split_select_row(const float* __restrict__ row, int c, int32_t* out,
                                                  uint32_t (*surv_key)[64], int32_t (*surv_idx)[64],
-                                                 int32_t (*cand)[kKeep]) {
+                                                 int32_t (*cand)[kKeep], uint32_t (*cand_key)[kKeep]) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   // Shares are multiples of 64 candidates; a share of n <= 15 keeps all n.
@@ -152,9 +161,9 @@ __device__ __forceinline__ void split_select_row(const float* __restrict__ row, 
   const int lo = min(c, wave * share), n = min(share, c - lo);
   if (n > 0) {
     if (n <= NC * 64)
-      select_row<true, false, NC>(row + lo, n, cand[wave], surv_key[wave], surv_idx[wave]);
+      select_row<true, false, NC>(row + lo, n, cand[wave], surv_key[wave], surv_idx[wave], cand_key[wave]);
     else
-      select_row<false, false, NC>(row + lo, n, cand[wave], surv_key[wave], surv_idx[wave]);
+      select_row<false, false, NC>(row + lo, n, cand[wave], surv_key[wave], surv_idx[wave], cand_key[wave]);
   }
   __syncthreads();
   if (wave != 0) return;
@@ -169,7 +178,7 @@ __device__ __forceinline__ void split_select_row(const float* __restrict__ row, 
     const int lo_w = min(c, w * share), n_w = min(share, c - lo_w);
     const bool have = w < NW && k < min(n_w, kKeep);
     idx[j] = have ? lo_w + cand[w][k] : -1;
-    key[j] = have ? order_key(row[idx[j]]) : 0u;
+    key[j] = have ? cand_key[w][k] : 0u;
   }
   // Exact 15th-largest key over the candidates, bit by bit.
   uint32_t T = 0;
