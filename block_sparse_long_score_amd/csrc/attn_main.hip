@@ -60,7 +60,8 @@ static int hkv_shift_of(const Problem& p) {
 
 // Entries (row, slot) per kvouter workgroup: ~1536 (row, head) pairs, so
 // each staged block serves ~48 row tiles before it is dropped.
-static int kv_chunk(const Problem& p) { return std::max(16, 1536 / p.group); }
+constexpr int kKvMaxChunk = 1536;  // (entry, head) rows per kvouter workgroup, at most
+static int kv_chunk(const Problem& p) { return std::max(16, kKvMaxChunk / p.group); }
 
 // Decode batches with at least this many (sequence, group) pairs use one
 // 16-wave workgroup per pair (decode_fused_kernel, any G <= 16); smaller ones split each
@@ -367,6 +368,12 @@ __global__ __launch_bounds__(256, 2) void kvouter_kernel(KvOuterArgs a) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int half = lane >> 5, l32 = lane & 31;
+  // Entry codes are requested one tile ahead with unconditional loads (a row
+  // past the list end reads the last entry's code): the wait for a code then
+  // leaves the block copy, the query loads and the partial stores in flight.
+  const int rows = n_ent * G;
+  auto code_of = [&](int tile) -> int32_t { return a.entries[e0 + min(tile * 32 + l32, rows - 1) / G]; };
+  int32_t code_cur = code_of(wave), code_nxt = code_of(wave + 4);
   {  // the block's K and V into LDS, asynchronously (keys past the sequence end are never attended)
     const int64_t key_stride = (int64_t)p.hkv * D;
     const DmaLane<D, 4> dl = dma_lane<D, 4>(wave, lane, key_stride);
@@ -374,14 +381,13 @@ __global__ __launch_bounds__(256, 2) void kvouter_kernel(KvOuterArgs a) {
     block_dma<D, 4, false>(k_s, dl, wave, p.k + base, key_stride, valid);
     block_dma<D, 4, true>(v_s, dl, wave, p.v + base, key_stride, valid);
   }
-  const int rows = n_ent * G;
-  auto tile_row = [&](int tile) -> TileRow {
+  auto tile_row = [&](int tile, int32_t code32) -> TileRow {
     TileRow tr;
     const int rr = tile * 32 + l32;
     tr.valid = rr < rows;
     const int ei = tr.valid ? rr / G : 0;
     const int hj = tr.valid ? rr - ei * G : 0;
-    const int64_t code = tr.valid ? (int64_t)a.entries[e0 + ei] : 0;
+    const int64_t code = tr.valid ? (int64_t)code32 : 0;
     tr.R = code >> 4;
     tr.prow = (int64_t)(e0 + ei) * G + hj;
     const int64_t r = tr.R >> a.hkv_shift;
@@ -395,18 +401,21 @@ __global__ __launch_bounds__(256, 2) void kvouter_kernel(KvOuterArgs a) {
   // The first tile's rows and queries load while the block is in flight.
   int tile = wave;
   const bool has_tiles = tile * 32 < rows;
-  TileRow cur{};
+  // Unconditional, so the compiler can count the loads in flight: rows past
+  // the list end (and a wave with no tiles) read a valid row's query;
+  // nothing of theirs is stored.
+  TileRow cur = tile_row(tile, code_cur);
   QRaw<D> raw;
-  if (has_tiles) {
-    cur = tile_row(tile);
-    load_q_raw<D>(cur.q, raw);  // rows past the list end read a valid row's query; nothing of theirs is stored
-  }
+  load_q_raw<D>(cur.q, raw);
   __builtin_amdgcn_s_waitcnt(0);  // this wave's copies have landed
   __syncthreads();                // and everyone's
   if (!has_tiles) return;
   lds_byte* kb = opaque_lds(k_s);
   lds_byte* vb = opaque_lds(v_s);
   const OpLane<D> ol = op_lane<D>(lane);
+  // This workgroup's partial rows (entry e0's first head on) and statistics.
+  const auto out_o = buffer_rsrc(a.part_o + (int64_t)e0 * G * D, (uint32_t)(rows * D * 2));
+  const auto out_st = buffer_rsrc(a.part_st + (int64_t)e0 * G * 2, (uint32_t)(rows * 8));
   for (; tile * 32 < rows; tile += 4) {
     bf16x8 bq[D / 16];
     q_operand<D>(raw, bq);
@@ -414,9 +423,10 @@ __global__ __launch_bounds__(256, 2) void kvouter_kernel(KvOuterArgs a) {
     const int nxt = tile + 4;
     TileRow next = cur;
     if (nxt * 32 < rows) {
-      next = tile_row(nxt);
+      next = tile_row(nxt, code_nxt);
       load_q_raw<D>(next.q, raw);
     }
+    code_nxt = code_of(nxt + 4);
 
     f32x16 sacc[4];
     tile_scores<D>(kb, ol, bq, sacc);
@@ -455,11 +465,14 @@ __global__ __launch_bounds__(256, 2) void kvouter_kernel(KvOuterArgs a) {
     // 32n + 16 + 8h .. +7 (c2), and a swap of c2 with the lane 16 away lets
     // four lanes cover 32 consecutive dims of one row in each store: the
     // first store writes tile rows 0..15, the second rows 16..31.
+    // Stores are unconditional buffer stores relative to this workgroup's
+    // rows: a tile row past the list end is out of the resource's range, so
+    // the hardware drops it.  (Branches around the stores would keep the
+    // compiler from counting them, and the next tile's wait for its query
+    // loads would then wait for these stores as well.)
     const int a16 = l32 >> 4, b16 = l32 & 15;
-    const int64_t prow0 = (int64_t)e0 * G + (int64_t)tile * 32;
-    const bool okA = tile * 32 + b16 < rows, okB = tile * 32 + 16 + b16 < rows;
-    uint16_t* dstA = a.part_o + (prow0 + b16) * D + 8 * half + 16 * a16;
-    uint16_t* dstB = a.part_o + (prow0 + 16 + b16) * D + 8 * half + 16 * (1 - a16);
+    const uint32_t offA = (uint32_t)(((tile * 32 + b16) * D + 8 * half + 16 * a16) * 2);
+    const uint32_t offB = (uint32_t)(((tile * 32 + 16 + b16) * D + 8 * half + 16 * (1 - a16)) * 2);
 #pragma unroll
     for (int n = 0; n < D / 32; ++n) {
       const f32x16& o = oacc[n];
@@ -477,10 +490,11 @@ __global__ __launch_bounds__(256, 2) void kvouter_kernel(KvOuterArgs a) {
         const auto t = __builtin_amdgcn_permlane16_swap(c2[i], c2[i], false, false);
         c2[i] = a16 ? t[0] : t[1];
       }
-      if (okA) store16(dstA + 32 * n, a16 ? c2 : c1);
-      if (okB) store16(dstB + 32 * n, a16 ? c1 : c2);
+      __builtin_amdgcn_raw_buffer_store_b128(a16 ? c2 : c1, out_o, offA + 64 * n, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b128(a16 ? c1 : c2, out_o, offB + 64 * n, 0, 0);
     }
-    if (cur.valid && half == 0) *reinterpret_cast<f32x2*>(a.part_st + cur.prow * 2) = f32x2{m + __log2f(l), (float)ex};
+    const u32x2 st{__float_as_uint(m + __log2f(l)), __float_as_uint((float)ex)};
+    __builtin_amdgcn_raw_buffer_store_b64(st, out_st, half == 0 ? (uint32_t)((tile * 32 + l32) * 8) : 0xfffffff8u, 0, 0);
     cur = next;
   }
 }

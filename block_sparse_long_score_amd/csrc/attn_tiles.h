@@ -258,10 +258,12 @@ __device__ __forceinline__ void load_q_raw(const uint16_t* __restrict__ qrow, QR
   const uint64_t other = ((uint64_t)partner16((uint32_t)(own >> 32)) << 32) | partner16((uint32_t)own);
   const uint64_t rowA = a16 ? other : own;  // tile row b
   const uint64_t rowB = a16 ? own : other;  // tile row 16 + b
+  const uint64_t baseA = rowA + (uint64_t)((2 * a16 + h) * 16);
+  const uint64_t baseB = rowB + (uint64_t)((2 * (1 - a16) + h) * 16);
 #pragma unroll
-  for (int j = 0; j < D / 32; ++j) {
-    raw.a[j] = load16_global(rowA + (uint64_t)((4 * j + 2 * a16 + h) * 16));
-    raw.b[j] = load16_global(rowB + (uint64_t)((4 * j + 2 * (1 - a16) + h) * 16));
+  for (int j = 0; j < D / 32; ++j) {  // one address per row, the 64-byte steps as immediate offsets
+    raw.a[j] = load16_global(baseA + (uint64_t)(64 * j));
+    raw.b[j] = load16_global(baseB + (uint64_t)(64 * j));
   }
 }
 

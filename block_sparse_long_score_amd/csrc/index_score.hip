@@ -140,8 +140,9 @@ __global__ __launch_bounds__(256, 2) void index_score_kernel(IndexArgs a) {
   }
 
   const int32_t* table = p.block_table + (int64_t)s * p.max_blocks_per_seq;
+  const int tab = lane < nkb ? table[kb0 + lane] : -1;  // the chunk's table entries, one per lane (kc <= 64)
   for (int kb = kb0 + wave; kb < kb0 + nkb; kb += 4) {
-    const int phys = table[kb];
+    const int phys = __builtin_amdgcn_readlane(tab, kb - kb0);
     float runmax[NCT];
     if (phys >= 0 && phys < p.num_blocks) {
       const uint16_t* kbase = p.k_idx + (int64_t)phys * kBlock * DIDX + half * 8;
@@ -271,6 +272,7 @@ __global__ __launch_bounds__(64 * WAVES, WAVES / 2) void index_score_shared_kern
   constexpr int BLK = kBlock * DIDX;      // bf16 elements of one K_idx block
   __shared__ __attribute__((aligned(1024))) uint16_t kbuf[2][BLK];
   __shared__ float pooled_s[NC][kSharedFlush + 1];
+  __shared__ int32_t tab_s[64];
   const Problem& p = a.p;
 
   const int s = blockIdx.z;
@@ -320,9 +322,13 @@ __global__ __launch_bounds__(64 * WAVES, WAVES / 2) void index_score_shared_kern
   constexpr int CPR = DIDX / 8;                // 16-byte chunks per row
   constexpr int RUNS = BLK * 2 / 1024;         // 1 KB runs per block
   static_assert(RUNS % WAVES == 0, "runs per wave");
+  // The chunk's block-table entries (kc <= 64) are staged in LDS once, so
+  // each block's copy is requested without a dependent global load.
   const int32_t* table = p.block_table + (int64_t)s * p.max_blocks_per_seq;
+  if (wave == 0) tab_s[lane] = lane < nkb ? table[kb0 + lane] : -1;
+  __syncthreads();
   auto dma = [&](int kb, int buf) {
-    const int phys = table[kb];
+    const int phys = tab_s[kb - kb0];
     const uint16_t* src = p.k_idx + (int64_t)((phys >= 0 && phys < p.num_blocks) ? phys : 0) * BLK;
 #pragma unroll
     for (int k = 0; k < RUNS / WAVES; ++k) {
@@ -368,7 +374,7 @@ __global__ __launch_bounds__(64 * WAVES, WAVES / 2) void index_score_shared_kern
       const int lim[NCT] = {};
       shared_pool<DIDX, NCT, false>(kt, bq, lim, runmax);
     }
-    const int phys = table[kb];
+    const int phys = tab_s[kb - kb0];
     if (!(phys >= 0 && phys < p.num_blocks)) {  // an unmapped block holds no keys (its copy read block 0)
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct) runmax[ct] = -__builtin_inff();
@@ -456,9 +462,10 @@ __global__ __launch_bounds__(256, 2) void index_score_stream_kernel(IndexArgs a,
   }
 
   const int32_t* table = p.block_table + (int64_t)s * p.max_blocks_per_seq;
+  const int tab = lane < nkb ? table[kb0 + lane] : -1;  // the chunk's table entries, one per lane (kc <= 64)
   uint16_t* region = kbuf[wave];
   auto dma = [&](int kb) {
-    const int phys = table[kb];
+    const int phys = __builtin_amdgcn_readlane(tab, kb - kb0);
     const uint16_t* src = p.k_idx + (int64_t)((phys >= 0 && phys < p.num_blocks) ? phys : 0) * BLK;
 #pragma unroll
     for (int run = 0; run < RUNS; ++run) {
@@ -527,7 +534,7 @@ __global__ __launch_bounds__(256, 2) void index_score_stream_kernel(IndexArgs a,
 #pragma unroll
       for (int r = 0; r < 16; ++r) runmax = fmaxf(runmax, acc[r]);
     }
-    const int phys = table[kb];
+    const int phys = __builtin_amdgcn_readlane(tab, kb - kb0);
     if (!(phys >= 0 && phys < p.num_blocks)) runmax = -__builtin_inff();  // an unmapped block holds no keys
     const float v = fmaxf(runmax, swap_halves(runmax));
     if (half == 0) pooled_s[l32 * ld_s + (kb - kb0)] = v;
@@ -580,6 +587,7 @@ static hipError_t launch_index_impl(const Problem& p, const uint16_t* q_idx, flo
     // once, so longer chunks cut that traffic (at 1024 blocks, 32 instead of
     // 16 halves it and the pipelined 128K prefill step is ~3% faster); short
     // contexts keep 16 so the grid still fills the chip.
+    // (kc <= 64 always: the kernels hold a chunk's block-table entries one per lane.)
     const int kc = max_blocks >= 2048 ? 64 : (max_blocks >= 512 ? 32 : 16);
     IndexArgs a{p, q_idx, scores, ld, tq, hkv_shift, kc, first_row};
     dim3 grid((unsigned)max_tiles, (unsigned)((max_blocks + kc - 1) / kc), (unsigned)p.num_seqs);
@@ -605,6 +613,7 @@ static hipError_t launch_index_impl(const Problem& p, const uint16_t* q_idx, flo
     work += (int64_t)tiles * ((t0 / kBlock + (L - 1) / kBlock) / 2 + 1);
   }
   // Decode tiles stream at least 2 blocks per wave so each wave's next block is in flight while it multiplies.
+  // (At most 64 blocks per chunk: one block-table entry per lane.)
   int kc = (int)std::min<int64_t>(64, std::max<int64_t>(nct == 1 ? 8 : 4, (work / 8192 + 3) / 4 * 4));
   IndexArgs a{p, q_idx, scores, ld, tq, hkv_shift, kc, first_row};
   dim3 grid((unsigned)max_tiles, (unsigned)((max_blocks + kc - 1) / kc), (unsigned)p.num_seqs);
