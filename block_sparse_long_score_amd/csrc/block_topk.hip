@@ -93,6 +93,37 @@ __global__ __launch_bounds__(kSplitWaves * 64) void block_topk_split_kernel(Topk
   if (wave == 0 && lane == 0) out[kKeep] = c;
 }
 
+// Many long rows (a prefill chunk over a long cache): one workgroup of 4
+// waves per row, each wave holding its quarter of the row (up to 36
+// candidates per lane, rows of up to 9216 blocks) in registers, so the row is
+// read from memory once; the one-wave kernel would read rows longer than
+// 1024 blocks twice.  Same selection rule as the split kernel.
+constexpr int kRowWaves = 4;
+constexpr int kRowCached = 36;
+
+__global__ __launch_bounds__(kRowWaves * 64) void block_topk_row4_kernel(TopkArgs a) {
+  __shared__ uint32_t surv_key[kRowWaves][64];
+  __shared__ int32_t surv_idx[kRowWaves][64];
+  __shared__ int32_t cand[kRowWaves][kKeep];
+  __shared__ uint32_t cand_key[kRowWaves][kKeep];
+  const Problem& p = a.p;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t R = a.r_base + blockIdx.x;
+  const int r = (int)(R >> a.hkv_shift);
+  const int s = seq_of_row(p.cu_q, p.num_seqs, r);
+  const int t = p.seq_lens[s] - (p.cu_q[s + 1] - r);
+  const int c = t >> 7;
+  int32_t* out = a.sel + R * kTopK;
+  if (c + 1 <= kTopK) {  // every causal block is kept
+    if (wave == 0 && lane < kTopK) out[lane] = lane <= c ? lane : -1;
+    return;
+  }
+  split_select_row<kRowWaves, kRowCached>(a.scores + (R - a.r_base) * a.ld, c, out, surv_key, surv_idx, cand,
+                                          cand_key);
+  if (wave == 0 && lane == 0) out[kKeep] = c;
+}
+
 hipError_t launch_block_topk(const Problem& p, const float* scores, int64_t ld, int32_t* sel, int64_t max_blocks,
                              hipStream_t stream, int64_t first_row) {
   int hkv_shift = 0;
@@ -102,6 +133,10 @@ hipError_t launch_block_topk(const Problem& p, const float* scores, int64_t ld, 
   TopkArgs a{p, scores, ld, sel, hkv_shift, first_row << hkv_shift};
   if (rows <= kSplitMaxRows && max_blocks > kSplitMinBlocks) {
     hipLaunchKernelGGL(block_topk_split_kernel, dim3((unsigned)rows), dim3(kSplitWaves * 64), 0, stream, a);
+    return hipGetLastError();
+  }
+  if (max_blocks > (int64_t)kCached * 64) {
+    hipLaunchKernelGGL(block_topk_row4_kernel, dim3((unsigned)rows), dim3(kRowWaves * 64), 0, stream, a);
     return hipGetLastError();
   }
   hipLaunchKernelGGL(block_topk_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, stream, a);

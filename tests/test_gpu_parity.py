@@ -235,7 +235,7 @@ def test_topk_on_oracle_scores_with_ties(n_rows):
     """The selection kernel alone, fed block scores written by the oracle
     (real rows) and by hand (massive ties, +/-0, long rows past the register
     cache).  64 long rows take the split (16 waves per row) kernel, 1100 the
-    one-wave-per-row kernel."""
+    four-waves-per-row kernel (rows over 1024 blocks, many rows)."""
     w = M2.with_sizes("topk", [9000], [9000])
     inp = make_inputs(w, "cuda")
     runner = MsaRunner(inp)
