@@ -230,12 +230,13 @@ def test_decode_equals_prefill_last_row():
     compare_rows(runner_d, 0, [4499])
 
 
-@pytest.mark.parametrize("n_rows", [64, 1100])
-def test_topk_on_oracle_scores_with_ties(n_rows):
+@pytest.mark.parametrize("n_rows,ld", [(64, 8300), (1100, 8300), (1100, 10000)])
+def test_topk_on_oracle_scores_with_ties(n_rows, ld):
     """The selection kernel alone, fed block scores written by the oracle
     (real rows) and by hand (massive ties, +/-0, long rows past the register
     cache).  64 long rows take the split (16 waves per row) kernel, 1100 the
-    four-waves-per-row kernel (rows over 1024 blocks, many rows)."""
+    four-waves-per-row kernel (rows over 1024 blocks, many rows), which holds
+    rows of up to 9216 blocks in registers and streams longer ones."""
     w = M2.with_sizes("topk", [9000], [9000])
     inp = make_inputs(w, "cuda")
     runner = MsaRunner(inp)
@@ -250,7 +251,6 @@ def test_topk_on_oracle_scores_with_ties(n_rows):
 
     import oracle
     rng = np.random.default_rng(3)
-    ld = 8300
     pos = np.sort(rng.integers(2048, ld * 128, size=n_rows)).astype(np.int64)
     pos[:3] = [ld * 128 - 1, 1024 * 128 + 5, 1024 * 128 - 1]
     vals = rng.integers(-3, 4, size=(n_rows, 1, ld)).astype(np.float32) / 4
@@ -263,7 +263,7 @@ def test_topk_on_oracle_scores_with_ties(n_rows):
     b = ops.Batch.make(wt.seq_lens, wt.q_lens, "cuda")
     scores = torch.from_numpy(vals).cuda()
     got = torch.empty((n_rows, 1, 16), dtype=torch.int32, device="cuda")
-    _announce(f"topk on hand-made scores, {n_rows} rows up to 8300 blocks")
+    _announce(f"topk on hand-made scores, {n_rows} rows up to {ld} blocks")
     ops.msa_block_topk(d, b, scores, got)
     torch.cuda.synchronize()
     np.testing.assert_array_equal(got.cpu().numpy(), want)
