@@ -354,7 +354,7 @@ def workload_leg(name: str, steps: int, warmup: int, chunk_rows: int):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=40)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="c3", choices=["c0", "c1", "c2", "c3", "c4d", "c4p", "m3p", "m3d", "c1n", "c2n"])
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for cpu_baseline")
