@@ -253,6 +253,7 @@ def test_topk_on_oracle_scores_with_ties(n_rows, ld):
     rng = np.random.default_rng(3)
     pos = np.sort(rng.integers(2048, ld * 128, size=n_rows)).astype(np.int64)
     pos[:3] = [ld * 128 - 1, 1024 * 128 + 5, 1024 * 128 - 1]
+    pos[-6:] = [0, 130, 2047, 2100, 5000, 8191]  # short rows: every block kept, or candidates in one wave only
     vals = rng.integers(-3, 4, size=(n_rows, 1, ld)).astype(np.float32) / 4
     vals[0] = 0.0                      # every block ties
     vals[1, 0, ::2] = -0.0             # signed zeros tie with +0
