@@ -255,12 +255,25 @@ __device__ __forceinline__ void shared_pool(const uint16_t* __restrict__ kt, con
   reduce(kBlock / 16 - 1, acc[1]);
 }
 
-// The running maxima of the four lanes that share a column (lanes l%16 + 16j).
-__device__ __forceinline__ float column_max16(float v) {
-  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  v = fmaxf(v, __uint_as_float((threadIdx.x & 32) ? a[0] : a[1]));
-  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return fmaxf(v, __uint_as_float((threadIdx.x & 16) ? b[0] : b[1]));
+// Monotone map float -> uint32 (a < b as numbers <=> key(a) < key(b), with
+// -0 just below +0) and its inverse.
+__device__ __forceinline__ uint32_t pool_key(float x) {
+  const uint32_t u = __float_as_uint(x);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float key_to_float(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+
+// The largest of the four lanes that share a column (lanes l%16 + 16j), on
+// pool keys: each swap leaves a lane's own value and its partner's in the two
+// results, so one integer max combines them, with no select and no float
+// canonicalisation.
+__device__ __forceinline__ uint32_t column_max_key16(uint32_t k) {
+  const auto a = __builtin_amdgcn_permlane32_swap(k, k, false, false);
+  k = max(a[0], a[1]);  // lanes l and l ^ 32
+  const auto b = __builtin_amdgcn_permlane16_swap(k, k, false, false);
+  return max(b[0], b[1]);  // and l ^ 16
 }
 
 template <int DIDX, int NCTW, int WAVES>
@@ -271,8 +284,10 @@ __global__ __launch_bounds__(64 * WAVES, WAVES / 2) void index_score_shared_kern
   constexpr int NC = WAVES * NCW;         // columns per workgroup
   constexpr int BLK = kBlock * DIDX;      // bf16 elements of one K_idx block
   __shared__ __attribute__((aligned(1024))) uint16_t kbuf[2][BLK];
-  __shared__ float pooled_s[NC][kSharedFlush + 1];
+  __shared__ uint32_t pooled_s[NC][kSharedFlush + 1];  // pool keys of the pooled scores
   __shared__ int32_t tab_s[64];
+  __shared__ int64_t colrow_s[NC];  // each column's row of pooled scores (offset into a.out)
+  __shared__ int32_t colpos_s[NC];  // each column's query position (-1: no query in this column)
   const Problem& p = a.p;
 
   const int s = blockIdx.z;
@@ -302,13 +317,11 @@ __global__ __launch_bounds__(64 * WAVES, WAVES / 2) void index_score_shared_kern
   // This lane's column in every 16-column tile and its Q_idx operand
   // (dims 32*ks + 8*q4 .. +7).
   bf16x8 bq[NCT][KS];
-  int col_pos[NCT];
 #pragma unroll
   for (int ct = 0; ct < NCT; ++ct) {
     const int col = wave * NCW + ct * 16 + l16;
     const int pos = p0 + (col >> a.hkv_shift);
     const bool valid = pos >= first_pos && pos < seq_len;
-    col_pos[ct] = pos;
     const int64_t R = ((int64_t)(row0 + pos - first_pos) << a.hkv_shift) + (col & hkv_mask);
     const uint16_t* src = a.q_idx + R * DIDX + q4 * 8;
 #pragma unroll
@@ -326,6 +339,13 @@ __global__ __launch_bounds__(64 * WAVES, WAVES / 2) void index_score_shared_kern
   // each block's copy is requested without a dependent global load.
   const int32_t* table = p.block_table + (int64_t)s * p.max_blocks_per_seq;
   if (wave == 0) tab_s[lane] = lane < nkb ? table[kb0 + lane] : -1;
+  for (int col = threadIdx.x; col < NC; col += blockDim.x) {
+    const int pos = p0 + (col >> a.hkv_shift);
+    const bool ok = pos >= first_pos && pos < seq_len;
+    const int64_t R = ((int64_t)(row0 + pos - first_pos) << a.hkv_shift) + (col & hkv_mask);
+    colrow_s[col] = ok ? (R - (a.first_row << a.hkv_shift)) * a.ld : 0;
+    colpos_s[col] = ok ? pos : -1;
+  }
   __syncthreads();
   auto dma = [&](int kb, int buf) {
     const int phys = tab_s[kb - kb0];
@@ -347,16 +367,24 @@ __global__ __launch_bounds__(64 * WAVES, WAVES / 2) void index_score_shared_kern
 
   // Each valid (query, group) row writes the staged pooled scores of blocks
   // [kf, kf + n) it can see (b <= its own block) as one contiguous run.
+  auto store = [&](int col, int kf, int j) {
+    if (kf + j > (colpos_s[col] >> 7)) return;  // no query in the column, or a block after its own
+    float v = key_to_float(pooled_s[col][j]);
+    v = (v == 0.0f) ? 0.0f : v;  // -0 and +0 are the same score
+    a.out[colrow_s[col] + kf + j] = v;
+  };
   auto flush = [&](int kf, int n) {
-    for (int idx = threadIdx.x; idx < NC * n; idx += blockDim.x) {
-      const int col = idx / n;
-      const int j = idx - col * n;
-      const int pos = p0 + (col >> a.hkv_shift);
-      if (pos < first_pos || pos >= seq_len || kf + j > (pos >> 7)) continue;
-      const int64_t R = ((int64_t)(row0 + pos - first_pos) << a.hkv_shift) + (col & hkv_mask);
-      float v = pooled_s[col][j];
-      v = (v == 0.0f) ? 0.0f : v;  // -0 and +0 are the same score
-      a.out[(R - (a.first_row << a.hkv_shift)) * a.ld + kf + j] = v;
+    constexpr int kThreads = 64 * WAVES;
+    // The thread index passes through an empty asm so the compiler derives
+    // the flush's addresses here rather than holding them (in registers it
+    // would spill) across the whole key-block loop.
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));
+    if (n == kSharedFlush) {  // a full flush: each thread keeps one block slot, columns step by kThreads / n
+      const int j = tid % kSharedFlush;
+      for (int col = tid / kSharedFlush; col < NC; col += kThreads / kSharedFlush) store(col, kf, j);
+    } else {
+      for (int idx = tid; idx < NC * n; idx += kThreads) store(idx / n, kf, idx % n);
     }
   };
 
@@ -368,7 +396,7 @@ __global__ __launch_bounds__(64 * WAVES, WAVES / 2) void index_score_shared_kern
     if (kb >= unmasked_end) {
       int lim[NCT];
 #pragma unroll
-      for (int ct = 0; ct < NCT; ++ct) lim[ct] = col_pos[ct] - kb * kBlock;
+      for (int ct = 0; ct < NCT; ++ct) lim[ct] = colpos_s[wave * NCW + ct * 16 + l16] - kb * kBlock;
       shared_pool<DIDX, NCT, true>(kt, bq, lim, runmax);
     } else {
       const int lim[NCT] = {};
@@ -382,8 +410,8 @@ __global__ __launch_bounds__(64 * WAVES, WAVES / 2) void index_score_shared_kern
     const int slot = i % kSharedFlush;
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) {
-      const float v = column_max16(runmax[ct]);
-      if (q4 == 0) pooled_s[wave * NCW + ct * 16 + l16][slot] = v;
+      const uint32_t k = column_max_key16(pool_key(runmax[ct]));
+      if (q4 == 0) pooled_s[wave * NCW + ct * 16 + l16][slot] = k;
     }
     __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of the next block have landed
     __syncthreads();
