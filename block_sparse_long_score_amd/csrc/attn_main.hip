@@ -347,9 +347,18 @@ struct TileRow {
   const uint16_t* q;
 };
 
+// 16-byte LDS accesses at a byte offset from a base.
+__device__ __forceinline__ void lds_store16(lds_byte* base, uint32_t off, u32x4 v) {
+  *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(const_cast<__attribute__((address_space(3))) char*>(base + off)) = v;
+}
+__device__ __forceinline__ u32x4 lds_load16(lds_byte* base, uint32_t off) {
+  return *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(base + off);
+}
+
 template <int D>
 __global__ __launch_bounds__(256, 2) void kvouter_kernel(KvOuterArgs a) {
   __shared__ uint16_t k_s[kBlock * D], v_s[kBlock * D];
+  __shared__ u32x4 stage_s[4 * 256];  // output staging, 4 KB per wave (two workgroups still fit a CU's 160 KB)
   const Problem& p = a.p;
   const int G = p.group;
   if ((int)blockIdx.x >= a.coff[a.n_lists]) return;
@@ -416,6 +425,21 @@ __global__ __launch_bounds__(256, 2) void kvouter_kernel(KvOuterArgs a) {
   // This workgroup's partial rows (entry e0's first head on) and statistics.
   const auto out_o = buffer_rsrc(a.part_o + (int64_t)e0 * G * D, (uint32_t)(rows * D * 2));
   const auto out_st = buffer_rsrc(a.part_st + (int64_t)e0 * G * 2, (uint32_t)(rows * 8));
+  // Output staging: the wave's 4 KB hold 64 dims of the tile's 32 rows (128
+  // bytes a row) at a time, their 16-byte chunks XOR-swizzled by row (chunk c
+  // of row r at r*128 + (c ^ (r/2 % 8))*16) so that neither the writes nor
+  // the reads meet a bank twice in a group of 16 lanes.  Read back with eight
+  // lanes per row, each store writes eight whole 128-byte row halves.
+  lds_byte* stg = opaque_lds(reinterpret_cast<const uint16_t*>(stage_s)) + wave * 4096;
+  uint32_t st_w[4], st_r[4];  // c1, c2 of an even and an odd dim tile; four row groups
+#pragma unroll
+  for (int c = 0; c < 4; ++c) st_w[c] = (uint32_t)(l32 * 128 + (((4 * (c >> 1) + 2 * (c & 1) + half) ^ ((l32 >> 1) & 7)) * 16));
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int row = 8 * k + (lane >> 3);
+    st_r[k] = (uint32_t)(row * 128 + (((lane & 7) ^ ((row >> 1) & 7)) * 16));
+  }
+  const uint32_t st_g = (uint32_t)((lane >> 3) * D * 2 + (lane & 7) * 16);
   for (; tile * 32 < rows; tile += 4) {
     bf16x8 bq[D / 16];
     q_operand<D>(raw, bq);
@@ -459,39 +483,36 @@ __global__ __launch_bounds__(256, 2) void kvouter_kernel(KvOuterArgs a) {
     amax = fmaxf(amax, swap_halves(amax)) * inv_l;
     const int ex = amax > 0.f ? (int)((__float_as_uint(amax) >> 23) & 0xff) - 126 : 0;
     const float f = ldexpf(inv_l, -ex);
-    // Partial rows in natural dim order, stored as 64-byte row segments.
-    // Lane (row rho, half h) holds dims 32n + 8*(i/4) + 4h + (i%4) of oacc[n];
-    // a swap across the wave halves gives it dims 32n + 8h .. +7 (c1) and
-    // 32n + 16 + 8h .. +7 (c2), and a swap of c2 with the lane 16 away lets
-    // four lanes cover 32 consecutive dims of one row in each store: the
-    // first store writes tile rows 0..15, the second rows 16..31.
+    // Partial rows in natural dim order.  Lane (row rho, half h) holds dims
+    // 32n + 8*(i/4) + 4h + (i%4) of oacc[n]; a swap across the wave halves
+    // gives it dims 32n + 8h .. +7 (c1) and 32n + 16 + 8h .. +7 (c2), which go
+    // to the staging rows; two dim tiles (64 dims) make one round through it.
     // Stores are unconditional buffer stores relative to this workgroup's
     // rows: a tile row past the list end is out of the resource's range, so
     // the hardware drops it.  (Branches around the stores would keep the
     // compiler from counting them, and the next tile's wait for its query
-    // loads would then wait for these stores as well.)
-    const int a16 = l32 >> 4, b16 = l32 & 15;
-    const uint32_t offA = (uint32_t)(((tile * 32 + b16) * D + 8 * half + 16 * a16) * 2);
-    const uint32_t offB = (uint32_t)(((tile * 32 + 16 + b16) * D + 8 * half + 16 * (1 - a16)) * 2);
+    // loads would then wait for these stores as well.)  The LDS accesses of
+    // one wave complete in order, so a round's writes never overtake the
+    // previous round's reads.
 #pragma unroll
-    for (int n = 0; n < D / 32; ++n) {
-      const f32x16& o = oacc[n];
-      uint32_t w[8];
+    for (int ph = 0; ph < D / 64; ++ph) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) w[i] = pack_f16x2(o[2 * i] * f, o[2 * i + 1] * f);
-      const auto s0 = __builtin_amdgcn_permlane32_swap(w[0], w[2], false, false);
-      const auto s1 = __builtin_amdgcn_permlane32_swap(w[1], w[3], false, false);
-      const auto s2 = __builtin_amdgcn_permlane32_swap(w[4], w[6], false, false);
-      const auto s3 = __builtin_amdgcn_permlane32_swap(w[5], w[7], false, false);
-      const u32x4 c1{s0[0], s1[0], s0[1], s1[1]};
-      u32x4 c2{s2[0], s3[0], s2[1], s3[1]};
+      for (int n2 = 0; n2 < 2; ++n2) {
+        const f32x16& o = oacc[2 * ph + n2];
+        uint32_t w[8];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const auto t = __builtin_amdgcn_permlane16_swap(c2[i], c2[i], false, false);
-        c2[i] = a16 ? t[0] : t[1];
+        for (int i = 0; i < 8; ++i) w[i] = pack_f16x2(o[2 * i] * f, o[2 * i + 1] * f);
+        const auto s0 = __builtin_amdgcn_permlane32_swap(w[0], w[2], false, false);
+        const auto s1 = __builtin_amdgcn_permlane32_swap(w[1], w[3], false, false);
+        const auto s2 = __builtin_amdgcn_permlane32_swap(w[4], w[6], false, false);
+        const auto s3 = __builtin_amdgcn_permlane32_swap(w[5], w[7], false, false);
+        lds_store16(stg, st_w[2 * n2], u32x4{s0[0], s1[0], s0[1], s1[1]});
+        lds_store16(stg, st_w[2 * n2 + 1], u32x4{s2[0], s3[0], s2[1], s3[1]});
       }
-      __builtin_amdgcn_raw_buffer_store_b128(a16 ? c2 : c1, out_o, offA + 64 * n, 0, 0);
-      __builtin_amdgcn_raw_buffer_store_b128(a16 ? c1 : c2, out_o, offB + 64 * n, 0, 0);
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        __builtin_amdgcn_raw_buffer_store_b128(lds_load16(stg, st_r[k]), out_o,
+                                               st_g + (uint32_t)((tile * 32 + 8 * k) * D * 2 + ph * 128), 0, 0);
     }
     const u32x2 st{__float_as_uint(m + __log2f(l)), __float_as_uint((float)ex)};
     __builtin_amdgcn_raw_buffer_store_b64(st, out_st, half == 0 ? (uint32_t)((tile * 32 + l32) * 8) : 0xfffffff8u, 0, 0);

@@ -233,55 +233,29 @@ __device__ __forceinline__ void softmax_rows(f32x16 (&sacc)[4], float c, float& 
 }
 
 // Query rows of a 32-row tile as the B operand of tile_scores: lane (row
-// rho, half h) needs dims 16*ks + 8h .. +7 of row rho for every k-step ks.
-// They are loaded as 64-byte row segments: in load pair j, lane (h, a, b)
-// (a = bit 4 of the lane, b its low 4 bits) reads 16 bytes of tile row b
-// (first load) and of tile row 16 + b (second load), so four lanes cover 32
-// consecutive dims of one row per load.  q_operand() then swaps with the
-// lane 16 away to give every lane its own row.  Loads are issued early
-// (load_q_raw) and the swaps done when the operand is needed.
+// rho, half h) needs dims 16*ks + 8h .. +7 of row rho for every k-step ks,
+// 16 bytes at byte 32*ks + 16h of its own row, so the loads land in operand
+// order (one address per lane, the k-steps as immediate offsets; the two
+// lanes of a row read 32 consecutive bytes per load).  Loads are issued early
+// (load_q_raw, into registers the next tile's math does not touch) and taken
+// as the operand when it is needed (q_operand).
 template <int D>
 struct QRaw {
-  u32x4 a[D / 32], b[D / 32];
+  u32x4 q[D / 16];
 };
-
-__device__ __forceinline__ uint32_t partner16(uint32_t x) {
-  const auto t = __builtin_amdgcn_permlane16_swap(x, x, false, false);
-  return (threadIdx.x & 16) ? t[0] : t[1];
-}
 
 template <int D>
 __device__ __forceinline__ void load_q_raw(const uint16_t* __restrict__ qrow, QRaw<D>& raw) {
-  const int lane = threadIdx.x & 63;
-  const int h = lane >> 5, a16 = (lane >> 4) & 1;
-  const uint64_t own = reinterpret_cast<uint64_t>(qrow);
-  const uint64_t other = ((uint64_t)partner16((uint32_t)(own >> 32)) << 32) | partner16((uint32_t)own);
-  const uint64_t rowA = a16 ? other : own;  // tile row b
-  const uint64_t rowB = a16 ? own : other;  // tile row 16 + b
-  const uint64_t baseA = rowA + (uint64_t)((2 * a16 + h) * 16);
-  const uint64_t baseB = rowB + (uint64_t)((2 * (1 - a16) + h) * 16);
+  const int h = (threadIdx.x >> 5) & 1;
+  const uint64_t base = reinterpret_cast<uint64_t>(qrow) + (uint64_t)(16 * h);
 #pragma unroll
-  for (int j = 0; j < D / 32; ++j) {  // one address per row, the 64-byte steps as immediate offsets
-    raw.a[j] = load16_global(baseA + (uint64_t)(64 * j));
-    raw.b[j] = load16_global(baseB + (uint64_t)(64 * j));
-  }
+  for (int ks = 0; ks < D / 16; ++ks) raw.q[ks] = load16_global(base + (uint64_t)(32 * ks));
 }
 
 template <int D>
 __device__ __forceinline__ void q_operand(const QRaw<D>& raw, bf16x8 (&bq)[D / 16]) {
-  const bool a16 = (threadIdx.x & 16) != 0;
 #pragma unroll
-  for (int j = 0; j < D / 32; ++j) {
-    u32x4 x, y;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const auto t = __builtin_amdgcn_permlane16_swap(raw.a[j][i], raw.b[j][i], false, false);
-      x[i] = a16 ? t[1] : t[0];  // dims 32j + 8h .. +7 of this lane's row
-      y[i] = a16 ? t[0] : t[1];  // dims 32j + 16 + 8h .. +7
-    }
-    bq[2 * j] = as_bf16x8(x);
-    bq[2 * j + 1] = as_bf16x8(y);
-  }
+  for (int ks = 0; ks < D / 16; ++ks) bq[ks] = as_bf16x8(raw.q[ks]);
 }
 
 // ------------------------------------------------------ decode, one wave
