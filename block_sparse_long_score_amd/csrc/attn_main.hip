@@ -998,6 +998,70 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
   store16(a.out + ((int64_t)r * p.hq + g * G + hj) * D + d8 * 8, merge_slots<D, false, NT>(ok_mask, prow, a.part_o, a.part_st, d8));
 }
 
+// Prefill merge: one thread per (row, head, 8 consecutive output dims), as
+// merge_kernel, but the plan's entry_of alone says which slots were attended
+// (-1 otherwise) and where their partial rows are, so no block ids, sequence
+// or block table are read.  The statistics and partial rows of all 16 slots
+// are requested with unconditional loads before any arithmetic (a slot that
+// was not attended reads partial row `head` of the region, which always
+// exists, and its values are discarded), so each thread waits for memory
+// once.  Returns the same outputs as merge_slots, slot by slot in order.
+template <int D>
+__global__ __launch_bounds__(256) void merge_prefill_kernel(MergeArgs a) {
+  constexpr int C8 = D / 8;  // a power of two
+  const Problem& p = a.p;
+  const int G = p.group;
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t n = ((int64_t)p.total_q << a.hkv_shift) * G * C8;
+  if (idx >= n) return;
+  // (row, head) pairs number total_q * hq < 2^31 (the output holds D values for each).
+  const int d8 = (int)(idx & (C8 - 1));
+  const int rest = (int)(idx / C8);
+  const int R = rest / G;
+  const int hj = rest - R * G;
+  const int r = R >> a.hkv_shift;
+  const int g = R & ((1 << a.hkv_shift) - 1);
+
+  int32_t ent[kTopK];
+#pragma unroll
+  for (int j4 = 0; j4 < kTopK / 4; ++j4) {
+    const u32x4 ev = load16(a.entry_of + (int64_t)R * kTopK + j4 * 4);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ent[j4 * 4 + i] = (int32_t)ev[i];
+  }
+  f32x2 st[kTopK];
+  u32x4 y[kTopK];
+#pragma unroll
+  for (int j = 0; j < kTopK; ++j) {
+    const int64_t pr = (int64_t)max(ent[j], 0) * G + hj;
+    st[j] = *reinterpret_cast<const f32x2*>(a.part_st + pr * 2);
+    y[j] = load16(a.part_o + pr * D + d8 * 8);
+  }
+  float M = -__builtin_inff();
+#pragma unroll
+  for (int j = 0; j < kTopK; ++j) M = ent[j] >= 0 ? fmaxf(M, st[j][0]) : M;
+  float L = 0.f;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < kTopK; ++j) {
+    const bool ok = ent[j] >= 0;
+    const float w = ok ? fast_exp2(st[j][0] - M) : 0.f;
+    L += w;
+    const float wy = ldexpf(w, ok ? (int)st[j][1] : 0);
+    const u32x4 v = ok ? y[j] : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      acc[2 * i] += wy * f16_lo(v[i]);
+      acc[2 * i + 1] += wy * f16_hi(v[i]);
+    }
+  }
+  const float inv = L > 0.f ? 1.0f / L : 0.f;  // no attended key (every selected block unmapped): 0
+  u32x4 o;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) o[i] = pack_bf16x2(acc[2 * i] * inv, acc[2 * i + 1] * inv);
+  store16(a.out + ((int64_t)r * p.hq + g * G + hj) * D + d8 * 8, o);
+}
+
 // ------------------------------------------------------------------ launch
 
 // Selection inversion into the plan region: per (sequence, group, block) lists
@@ -1029,7 +1093,7 @@ static hipError_t launch_merge_t(const Problem& p, const int32_t* sel, const int
   const int64_t threads = ((int64_t)p.total_q << hs) * p.group * (D / 8);
   const dim3 grid((unsigned)((threads + 255) / 256));
   if (entry_of)  // prefill
-    hipLaunchKernelGGL((merge_kernel<D, false>), grid, dim3(256), 0, stream, m);
+    hipLaunchKernelGGL((merge_prefill_kernel<D>), grid, dim3(256), 0, stream, m);
   else
     hipLaunchKernelGGL((merge_kernel<D, true>), grid, dim3(256), 0, stream, m);
   return hipGetLastError();
