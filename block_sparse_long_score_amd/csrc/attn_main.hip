@@ -493,7 +493,10 @@ __global__ __launch_bounds__(256, 2) void kvouter_kernel(KvOuterArgs a) {
     // compiler from counting them, and the next tile's wait for its query
     // loads would then wait for these stores as well.)  The LDS accesses of
     // one wave complete in order, so a round's writes never overtake the
-    // previous round's reads.
+    // previous round's reads.  The partial rows and statistics are written
+    // once and read once by the merge, so they are stored non-temporally:
+    // they then stream past the caches instead of evicting the queries
+    // (whole lines, so no partial-line merging is left to the caches).
 #pragma unroll
     for (int ph = 0; ph < D / 64; ++ph) {
 #pragma unroll
@@ -512,10 +515,10 @@ __global__ __launch_bounds__(256, 2) void kvouter_kernel(KvOuterArgs a) {
 #pragma unroll
       for (int k = 0; k < 4; ++k)
         __builtin_amdgcn_raw_buffer_store_b128(lds_load16(stg, st_r[k]), out_o,
-                                               st_g + (uint32_t)((tile * 32 + 8 * k) * D * 2 + ph * 128), 0, 0);
+                                               st_g + (uint32_t)((tile * 32 + 8 * k) * D * 2 + ph * 128), 0, kLoadNT);
     }
     const u32x2 st{__float_as_uint(m + __log2f(l)), __float_as_uint((float)ex)};
-    __builtin_amdgcn_raw_buffer_store_b64(st, out_st, half == 0 ? (uint32_t)((tile * 32 + l32) * 8) : 0xfffffff8u, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b64(st, out_st, half == 0 ? (uint32_t)((tile * 32 + l32) * 8) : 0xfffffff8u, 0, kLoadNT);
     cur = next;
   }
 }

@@ -14,8 +14,9 @@ constexpr int kWave = 64;    // CDNA wavefront width
 // read-once data (the context's K_idx, the selected blocks' K/V, the partial
 // rows) with it: 16 KB blocks in random order stream at ~6.5 TB/s this way
 // against ~5.7 TB/s with plain loads.  Prefill keeps plain loads, because its
-// K/V blocks and partial rows are read again soon enough for the Infinity
-// Cache to serve some of them.
+// K/V blocks and queries are read again soon enough for the Infinity Cache to
+// serve some of them, but stores its partial rows (whole 128-byte lines,
+// written once, read once) with the same bit.
 constexpr int kLoadNT = 2;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
