@@ -39,7 +39,8 @@ constexpr int kKeep = kTopK - 1;  // non-local blocks kept per row
 constexpr int kCached = 16;       // candidates per lane held in registers (rows with c <= 1024)
 
 // Keys of candidates j*64 + lane for j in [j0, j0 + NC): one batch of
-// independent loads (0 beyond the last candidate).
+// independent loads (0 beyond the last candidate).  Each row is read once
+// (or once per pass when streamed), so the loads are non-temporal.
 template <int NC>
 __device__ __forceinline__ void load_batch(const float* __restrict__ row, int c, int j0, uint32_t (&keys)[NC]) {
   const int lane = threadIdx.x & 63;
@@ -47,7 +48,7 @@ __device__ __forceinline__ void load_batch(const float* __restrict__ row, int c,
 #pragma unroll
   for (int j = 0; j < NC; ++j) {
     const int b = (j0 + j) * 64 + lane;
-    v[j] = b < c ? row[b] : 0.f;
+    v[j] = b < c ? __builtin_nontemporal_load(&row[b]) : 0.f;
   }
 #pragma unroll
   for (int j = 0; j < NC; ++j) keys[j] = (j0 + j) * 64 + lane < c ? order_key(v[j]) : 0u;
