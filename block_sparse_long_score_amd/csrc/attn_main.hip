@@ -58,9 +58,10 @@ static int hkv_shift_of(const Problem& p) {
   return s;
 }
 
-// Entries (row, slot) per kvouter workgroup: ~1536 (row, head) pairs, so
-// each staged block serves ~48 row tiles before it is dropped.
-constexpr int kKvMaxChunk = 1536;  // (entry, head) rows per kvouter workgroup, at most
+// Entries (row, slot) per kvouter workgroup: ~3072 (row, head) pairs, so
+// each staged block serves ~96 row tiles before it is dropped (a list of a
+// 16384-row chunk at 128K context fits one workgroup).
+constexpr int kKvMaxChunk = 3072;  // (entry, head) rows per kvouter workgroup, at most
 static int kv_chunk(const Problem& p) { return std::max(16, kKvMaxChunk / p.group); }
 
 // Decode batches with at least this many (sequence, group) pairs use one
