@@ -526,7 +526,7 @@ def main():
         algo = (work["index_flops"] if dom == "index_score" else work["main_flops"]) / launches_per_step
         achieved = algo / (avg_launch_ms / 1e3) / 1e12
         name = ("msa_index_score (index_score_shared_kernel: scoring + block max-pool)" if dom == "index_score"
-                else "msa_sparse_attn_prefill (selection inversion, kvouter_kernel, merge_kernel)")
+                else "msa_sparse_attn_prefill (selection inversion, kvouter_kernel, merge_prefill_kernel)")
         roof = {"bound": "mfma", "kernel": name, "achieved": achieved, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": achieved / BF16_PEAK_TFLOPS, "traffic": traffic, "algorithmic_flops_per_launch": algo}
         step_flops = work["index_flops"] + work["main_flops"]
