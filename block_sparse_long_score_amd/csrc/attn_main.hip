@@ -870,7 +870,7 @@ __global__ __launch_bounds__(1024) void decode_fused_kernel(KvOuterArgs a) {
 struct MergeArgs {
   Problem p;
   const int32_t* sel;
-  const int32_t* entry_of;  // prefill: partial entry of (R, slot), -1 if not attended; decode: NULL (entry = R*16 + slot)
+  const int32_t* entry_of;  // merge_prefill_kernel: partial entry of (R, slot), -1 if not attended; merge_kernel (decode): unused
   const uint16_t* part_o;
   const float* part_st;
   uint16_t* out;
@@ -953,13 +953,13 @@ __device__ __forceinline__ u32x4 merge_slots(uint32_t ok_mask, const int64_t (&p
   return o;
 }
 
-// One thread per (row, head, 8 consecutive output dims): log-sum-exp over
-// the row's attended slots, then the bf16 output.  A slot is attended iff its
-// block id is causal (0 <= b <= c) and the block table maps it to a cached
-// block (entry_valid); the attention pass wrote partials for exactly those.
-// Prefill reads that decision from the plan (entry_of = -1 otherwise), decode
-// from the block table.  NT (decode): the partial rows by non-temporal loads.
-template <int D, bool NT>
+// Decode (the split path): one thread per (row, head, 8 consecutive output
+// dims): log-sum-exp over the row's attended slots, then the bf16 output.  A
+// slot is attended iff its block id is causal (0 <= b <= c) and the block
+// table maps it to a cached block (entry_valid); decode_block_kernel wrote
+// partial rows (R*16 + slot)*G + head for exactly those.  The partial rows
+// are read once, by non-temporal loads.
+template <int D>
 __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
   constexpr int C8 = D / 8;
   const Problem& p = a.p;
@@ -982,24 +982,20 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
 #pragma unroll
   for (int j4 = 0; j4 < kTopK / 4; ++j4) {
     const u32x4 bv = load16(a.sel + R * kTopK + j4 * 4);
-    const u32x4 ev = a.entry_of ? load16(a.entry_of + R * kTopK + j4 * 4) : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int j = j4 * 4 + i;
       const int bj = (int)bv[i];
-      const int64_t ent = a.entry_of ? (int64_t)(int32_t)ev[i] : R * kTopK + j;
       bool ok = bj >= 0 && bj <= c;
-      if (a.entry_of) {
-        ok = ok && ent >= 0;
-      } else if (ok) {
+      if (ok) {
         const int phys = p.block_table[(int64_t)s * p.max_blocks_per_seq + bj];
         ok = phys >= 0 && phys < p.num_blocks;
       }
       ok_mask |= (ok ? 1u : 0u) << j;
-      prow[j] = (ok ? ent : 0) * G + hj;
+      prow[j] = (ok ? R * kTopK + j : 0) * G + hj;
     }
   }
-  store16(a.out + ((int64_t)r * p.hq + g * G + hj) * D + d8 * 8, merge_slots<D, false, NT>(ok_mask, prow, a.part_o, a.part_st, d8));
+  store16(a.out + ((int64_t)r * p.hq + g * G + hj) * D + d8 * 8, merge_slots<D, false, true>(ok_mask, prow, a.part_o, a.part_st, d8));
 }
 
 // Prefill merge: one thread per (row, head, 8 consecutive output dims), as
@@ -1099,7 +1095,7 @@ static hipError_t launch_merge_t(const Problem& p, const int32_t* sel, const int
   if (entry_of)  // prefill
     hipLaunchKernelGGL((merge_prefill_kernel<D>), grid, dim3(256), 0, stream, m);
   else
-    hipLaunchKernelGGL((merge_kernel<D, true>), grid, dim3(256), 0, stream, m);
+    hipLaunchKernelGGL((merge_kernel<D>), grid, dim3(256), 0, stream, m);
   return hipGetLastError();
 }
 
