@@ -247,57 +247,91 @@ __global__ __launch_bounds__(256) void csr_chunk_kernel(CsrArgs a) {
 }
 
 // Per list: exclusive prefix over the row chunks (in place) and the total.
+// The column is read kU entries at a time (clamped, so the loads issue
+// together) rather than one dependent load per row chunk.
 __global__ __launch_bounds__(256) void csr_colscan_kernel(CsrArgs a) {
+  constexpr int kU = 8;
   const int64_t list = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (list >= a.n_lists) return;
   const int mbps = a.p.max_blocks_per_seq;
   const int64_t sg = list / mbps, b = list - sg * mbps;
   int32_t* col = a.cnt_mat + sg * a.csr_chunks * mbps + b;
   int run = 0;
-  for (int k = 0; k < a.csr_chunks; ++k) {
-    const int v = col[(int64_t)k * mbps];
-    col[(int64_t)k * mbps] = run;
-    run += v;
+  for (int k0 = 0; k0 < a.csr_chunks; k0 += kU) {
+    int v[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) v[u] = col[(int64_t)min(k0 + u, a.csr_chunks - 1) * mbps];
+#pragma unroll
+    for (int u = 0; u < kU; ++u)
+      if (k0 + u < a.csr_chunks) {
+        col[(int64_t)(k0 + u) * mbps] = run;
+        run += v[u];
+      }
   }
   a.list_cnt[list] = run;
 }
 
 // One workgroup: exclusive scans of the list sizes (entry offsets) and of the
-// per-list kvouter chunk counts (chunk offsets).
+// per-list kvouter chunk counts (chunk offsets).  Each thread owns a run of
+// consecutive lists (read kU at a time), the runs' totals are scanned within
+// each wave by lane shuffles and across the 16 waves through LDS, then each
+// thread writes its run's offsets.  Offsets are 32-bit, as the plan stores them.
 __global__ __launch_bounds__(1024) void csr_scan_kernel(CsrArgs a) {
-  __shared__ int64_t sums[2][1024];
-  const int tid = threadIdx.x;
+  constexpr int kU = 8;
+  __shared__ int32_t wave_sum[2][16];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t n = a.n_lists;
   const int64_t per = (n + 1023) / 1024;
   const int64_t lo = std::min<int64_t>(n, tid * per), hi = std::min<int64_t>(n, lo + per);
-  int64_t se = 0, sc = 0;
-  for (int64_t i = lo; i < hi; ++i) {
-    const int c = a.list_cnt[i];
-    se += c;
-    sc += (c + a.chunk - 1) / a.chunk;
+  const int chunk = a.chunk;
+  int32_t se = 0, sc = 0;
+  for (int64_t i0 = lo; i0 < hi; i0 += kU) {
+    int32_t c[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) c[u] = a.list_cnt[std::min<int64_t>(i0 + u, hi - 1)];
+#pragma unroll
+    for (int u = 0; u < kU; ++u)
+      if (i0 + u < hi) {
+        se += c[u];
+        sc += (c[u] + chunk - 1) / chunk;
+      }
   }
-  sums[0][tid] = se;
-  sums[1][tid] = sc;
+  int32_t ie = se, ic = sc;  // inclusive scan over the wave's lanes
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int32_t te = __shfl_up(ie, d), tc = __shfl_up(ic, d);
+    if (lane >= d) {
+      ie += te;
+      ic += tc;
+    }
+  }
+  if (lane == 63) {
+    wave_sum[0][wave] = ie;
+    wave_sum[1][wave] = ic;
+  }
   __syncthreads();
-  for (int d = 1; d < 1024; d <<= 1) {  // inclusive Hillis-Steele scan
-    int64_t ve = 0, vc = 0;
-    if (tid >= d) { ve = sums[0][tid - d]; vc = sums[1][tid - d]; }
-    __syncthreads();
-    sums[0][tid] += ve;
-    sums[1][tid] += vc;
-    __syncthreads();
+  int32_t be = 0, bc = 0;  // the earlier waves' totals
+  for (int w = 0; w < wave; ++w) {
+    be += wave_sum[0][w];
+    bc += wave_sum[1][w];
   }
-  int64_t e = sums[0][tid] - se, c = sums[1][tid] - sc;
-  for (int64_t i = lo; i < hi; ++i) {
-    const int k = a.list_cnt[i];
-    a.off[i] = (int32_t)e;
-    a.coff[i] = (int32_t)c;
-    e += k;
-    c += (k + a.chunk - 1) / a.chunk;
+  int32_t e = be + ie - se, c = bc + ic - sc;  // exclusive prefix of this thread's run
+  for (int64_t i0 = lo; i0 < hi; i0 += kU) {
+    int32_t k[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) k[u] = a.list_cnt[std::min<int64_t>(i0 + u, hi - 1)];
+#pragma unroll
+    for (int u = 0; u < kU; ++u)
+      if (i0 + u < hi) {
+        a.off[i0 + u] = e;
+        a.coff[i0 + u] = c;
+        e += k[u];
+        c += (k[u] + chunk - 1) / chunk;
+      }
   }
   if (tid == 1023) {
-    a.off[n] = (int32_t)sums[0][1023];
-    a.coff[n] = (int32_t)sums[1][1023];
+    a.off[n] = be + ie;
+    a.coff[n] = bc + ic;
   }
 }
 
