@@ -219,11 +219,27 @@ __global__ __launch_bounds__(256) void csr_chunk_kernel(CsrArgs a) {
   }
   __syncthreads();
   auto valid = [&](int b, int t) { return b >= 0 && b <= (t >> 7) && mapped[b]; };  // t < seq_len <= mbps * 128
-  for (int idx = threadIdx.x; idx < nrows * kTopK; idx += blockDim.x) {
-    const int i = i0 + (idx >> 4), slot = idx & 15;
-    const int64_t R = ((int64_t)(row0 + i) << a.hkv_shift) + g;
-    const int b = a.sel[R * kTopK + slot];
-    if (valid(b, first_pos + i)) atomicAdd(&hist[b], 1);
+  // The chunk's (row, slot) entries, kU per thread requested together
+  // (clamped to the last entry, so the loads issue as one batch).
+  constexpr int kU = 8;
+  const int n_items = nrows * kTopK;
+  const int stride = (int)blockDim.x;
+  auto load_batch = [&](int base, int (&bb)[kU]) {
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int idx = min(base + u * stride, n_items - 1);
+      const int64_t R = ((int64_t)(row0 + i0 + (idx >> 4)) << a.hkv_shift) + g;
+      bb[u] = a.sel[R * kTopK + (idx & 15)];
+    }
+  };
+  for (int base = threadIdx.x; base < n_items; base += stride * kU) {
+    int bb[kU];
+    load_batch(base, bb);
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int idx = base + u * stride;
+      if (idx < n_items && valid(bb[u], first_pos + i0 + (idx >> 4))) atomicAdd(&hist[bb[u]], 1);
+    }
   }
   __syncthreads();
   if (!FILL) {
@@ -232,16 +248,22 @@ __global__ __launch_bounds__(256) void csr_chunk_kernel(CsrArgs a) {
   }
   for (int b = threadIdx.x; b < mbps; b += blockDim.x) hist[b] = a.off[list0 + b] + mat[b];
   __syncthreads();
-  for (int idx = threadIdx.x; idx < nrows * kTopK; idx += blockDim.x) {
-    const int i = i0 + (idx >> 4), slot = idx & 15;
-    const int64_t R = ((int64_t)(row0 + i) << a.hkv_shift) + g;
-    const int b = a.sel[R * kTopK + slot];
-    if (valid(b, first_pos + i)) {
-      const int pos = atomicAdd(&hist[b], 1);
-      a.entries[pos] = (int32_t)((R << 4) | slot);
-      a.entry_of[R * kTopK + slot] = pos;
-    } else {
-      a.entry_of[R * kTopK + slot] = -1;  // not attended: the merge skips it
+  for (int base = threadIdx.x; base < n_items; base += stride * kU) {
+    int bb[kU];
+    load_batch(base, bb);
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int idx = base + u * stride;
+      if (idx >= n_items) continue;
+      const int i = i0 + (idx >> 4), slot = idx & 15;
+      const int64_t R = ((int64_t)(row0 + i) << a.hkv_shift) + g;
+      if (valid(bb[u], first_pos + i)) {
+        const int pos = atomicAdd(&hist[bb[u]], 1);
+        a.entries[pos] = (int32_t)((R << 4) | slot);
+        a.entry_of[R * kTopK + slot] = pos;
+      } else {
+        a.entry_of[R * kTopK + slot] = -1;  // not attended: the merge skips it
+      }
     }
   }
 }
