@@ -892,7 +892,11 @@ __global__ __launch_bounds__(1024) void decode_fused_kernel(KvOuterArgs a) {
   __shared__ float p_s[kTopK][GM][W::SUB];
   __shared__ float alpha_s[kTopK][GM];
   __shared__ float m_s[kTopK][GM], l_s[kTopK][GM];
-  __shared__ float o_s[kTopK][GM][D];
+  __shared__ __attribute__((aligned(16))) float o_s[kTopK][GM][D];
+  // Each wave's K staging: inside its own o_s rows when they are large
+  // enough (they are written only after the wave's last step), else apart.
+  constexpr bool kStageInOut = GM * D * 4 >= W::STAGE * 2;
+  __shared__ __attribute__((aligned(16))) uint16_t kst_s[kStageInOut ? 1 : kTopK][kStageInOut ? 1 : W::STAGE];
   const Problem& p = a.p;
   const int G = p.group;
   const int g = blockIdx.x & ((1 << a.hkv_shift) - 1);
@@ -907,8 +911,9 @@ __global__ __launch_bounds__(1024) void decode_fused_kernel(KvOuterArgs a) {
     const int phys = p.block_table[(int64_t)s * p.max_blocks_per_seq + b];
     bf16x8 bq[W::KS];
     st.load_q(a.q + ((int64_t)r * p.hq + g * G) * D, G, bq);
+    uint16_t* stage = kStageInOut ? reinterpret_cast<uint16_t*>(&o_s[w][0][0]) : &kst_s[kStageInOut ? 0 : w][0];
     st.attend_block(p.k, p.v, ((int64_t)phys * kBlock * p.hkv + g) * D, (int64_t)p.hkv * D,
-                    min(kBlock, t - b * kBlock + 1), bq, p.scale_log2e, p_s[w], alpha_s[w]);
+                    min(kBlock, t - b * kBlock + 1), bq, p.scale_log2e, p_s[w], alpha_s[w], stage);
   }
   st.store(o_s[w], m_s[w], l_s[w]);
   __syncthreads();

@@ -275,14 +275,24 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, 
 // register i holds D[4*(l/16) + i][l%16].
 // Steps of 16 keys, software-pipelined for G <= 8: the K and V rows of the
 // next step are requested before the current step is multiplied, so every
-// wave keeps loads in flight while it computes (two register sets of one step
-// each).
+// wave keeps loads in flight while it computes (two register sets of V, one
+// LDS region of K).  A step's 16 K rows reach the wave's own LDS region by
+// direct global-to-LDS loads of whole rows (each load instruction moves
+// 64 / (D/8) rows of D*2 contiguous bytes; 16-byte chunks XOR-swizzled by
+// row), and the A operand is read from there: loaded straight into operand
+// order, each instruction would read only 64 bytes of each of 16 rows.
 template <int D, int GM>
 struct DecodeWave {
   static constexpr int VPL = D / 64;            // output dims per lane in P.V
   static constexpr int KS = D / 32;             // MFMA k-steps
   static constexpr int SUB = 16;                // keys per online-softmax step
   static constexpr int NSTEP = kBlock / SUB;
+  static constexpr int CPR = D / 8;             // 16-byte chunks per K row
+  static constexpr int RPI = 64 / CPR;          // K rows per load instruction
+  static constexpr int STAGE = SUB * D;         // bf16 elements of a step's staged K rows
+  // Chunk c of staged row r sits at chunk position c ^ swz(r): a step's 16
+  // rows then cover every bank once for any one logical chunk.
+  static __device__ __forceinline__ int swz(int r) { return (r / (256 / (D * 2))) & (CPR - 1); }  // D <= 128
   // At G > 8 the 16 heads' accumulators leave no registers for a second step in flight.
   static constexpr bool kPipelined = GM <= 8;
   float m_run = -__builtin_inff(), l_run = 0.f;  // head l16's running max (base 2) and sum
@@ -310,15 +320,15 @@ struct DecodeWave {
     }
   }
 
-  // Requests (non-temporal loads) the V rows (lane: dims lane*VPL ..) and the K operand rows of
-  // keys [c0, c0 + 16); keys at or past nvalid read key nvalid-1.  kr, vr:
-  // buffer resources over the block-head's K and V rows; ks_b: the key
-  // stride in bytes.  A V row's offset is the same in every lane (a scalar
-  // offset); each lane adds only its own dims.
-  __device__ __forceinline__ void issue(__amdgpu_buffer_rsrc_t kr, __amdgpu_buffer_rsrc_t vr, int ks_b, int nvalid,
-                                        int c0, uint32_t (&vreg)[SUB], bf16x8 (&ak)[KS]) const {
+  // Requests (non-temporal loads) the V rows (lane: dims lane*VPL ..) and,
+  // into the wave's LDS region `stage`, the K rows of keys [c0, c0 + 16);
+  // keys at or past nvalid read key nvalid-1.  kg: the block-head's first K
+  // row; vr: a buffer resource over its V rows; ks_b: the key stride in
+  // bytes.  A V row's offset is the same in every lane (a scalar offset);
+  // each lane adds only its own dims.
+  __device__ __forceinline__ void issue(const uint16_t* kg, __amdgpu_buffer_rsrc_t vr, int ks_b, int nvalid, int c0,
+                                        uint32_t (&vreg)[SUB], uint16_t* stage) const {
     const int lane = threadIdx.x & 63;
-    const int l16 = lane & 15, q16 = lane >> 4;
 #pragma unroll
     for (int kk = 0; kk < SUB; ++kk) {
       const int soff = min(c0 + kk, nvalid - 1) * ks_b;
@@ -327,12 +337,26 @@ struct DecodeWave {
       else
         vreg[kk] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(vr, lane * 2, soff, kLoadNT);
     }
-    const int koff = min(c0 + l16, nvalid - 1) * ks_b + q16 * 16;
+    const char* kb = reinterpret_cast<const char*>(kg);
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const auto x = __builtin_amdgcn_raw_buffer_load_b128(kr, koff + ks * 64, 0, kLoadNT);
-      ak[ks] = as_bf16x8(u32x4{x[0], x[1], x[2], x[3]});
+    for (int j = 0; j < SUB / RPI; ++j) {
+      const int r = j * RPI + lane / CPR;  // staged row; lane's chunk position lane % CPR
+      const int chunk = (lane % CPR) ^ swz(r);
+      __builtin_amdgcn_global_load_lds(static_cast<const void*>(kb + (int64_t)min(c0 + r, nvalid - 1) * ks_b + chunk * 16),
+                                       reinterpret_cast<__attribute__((address_space(3))) void*>(
+                                           reinterpret_cast<uintptr_t>(stage + j * 512)),
+                                       16, 0, kLoadNT);
     }
+  }
+
+  // The A operand of a staged step: lane (key l16, q16) takes logical chunk
+  // 4*ks + q16 of its key's row.
+  __device__ __forceinline__ void read_k(const uint16_t* stage, bf16x8 (&ak)[KS]) const {
+    const int lane = threadIdx.x & 63;
+    const int l16 = lane & 15, q16 = lane >> 4;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      ak[ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(&stage[l16 * D + (((4 * ks + q16) ^ swz(l16)) * 8)]));
   }
 
   // One step: scores of keys [c0, c0 + 16), the running softmax, and P.V.
@@ -400,35 +424,43 @@ struct DecodeWave {
 
   // Keys [0, nvalid) of the block whose head-g rows start at k + base / v + base
   // (1 <= nvalid <= 128).  p_w, alpha_w: this wave's LDS scratch for the P rows
-  // and the rescale factors.  PIPE: request the next step before the current
-  // one is multiplied (needs the second register set).
+  // and the rescale factors; stage: its LDS region of STAGE bf16 for the K
+  // rows.  PIPE: request the next step before the current one is multiplied
+  // (needs the second register set).  Every request has landed on return.
   template <bool PIPE = kPipelined>
   __device__ __forceinline__ void attend_block(const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
                                                int64_t base, int64_t key_stride, int nvalid, const bf16x8 (&bq)[KS],
-                                               float c, float (&p_w)[GM][SUB], float (&alpha_w)[GM]) {
+                                               float c, float (&p_w)[GM][SUB], float (&alpha_w)[GM], uint16_t* stage) {
     const int ks_b = (int)(key_stride * 2);
     const uint32_t bytes = (uint32_t)((kBlock - 1) * ks_b + D * 2);
-    const __amdgpu_buffer_rsrc_t kb = buffer_rsrc(k + base, bytes), vb = buffer_rsrc(v + base, bytes);
+    const __amdgpu_buffer_rsrc_t vb = buffer_rsrc(v + base, bytes);
+    const uint16_t* kg = k + base;
     if constexpr (PIPE) {
       uint32_t vreg[2][SUB];
-      bf16x8 ak[2][KS];
-      issue(kb, vb, ks_b, nvalid, 0, vreg[0], ak[0]);
+      issue(kg, vb, ks_b, nvalid, 0, vreg[0], stage);
 #pragma unroll
       for (int st = 0; st < NSTEP; ++st) {
         const int c0 = st * SUB;
         if (c0 >= nvalid) break;
-        if (st + 1 < NSTEP && c0 + SUB < nvalid)
-          issue(kb, vb, ks_b, nvalid, c0 + SUB, vreg[(st + 1) & 1], ak[(st + 1) & 1]);
-        step(nvalid, c0, vreg[st & 1], ak[st & 1], bq, c, p_w, alpha_w);
+        bf16x8 ak[KS];
+        __builtin_amdgcn_s_waitcnt(0);  // this step's K rows have landed (and its V rows)
+        read_k(stage, ak);
+        __builtin_amdgcn_s_waitcnt(0);  // read before the region is refilled
+        if (st + 1 < NSTEP && c0 + SUB < nvalid) issue(kg, vb, ks_b, nvalid, c0 + SUB, vreg[(st + 1) & 1], stage);
+        step(nvalid, c0, vreg[st & 1], ak, bq, c, p_w, alpha_w);
       }
     } else {
       for (int c0 = 0; c0 < nvalid; c0 += SUB) {
         uint32_t vreg[SUB];
         bf16x8 ak[KS];
-        issue(kb, vb, ks_b, nvalid, c0, vreg, ak);
+        issue(kg, vb, ks_b, nvalid, c0, vreg, stage);
+        __builtin_amdgcn_s_waitcnt(0);  // the K rows have landed
+        read_k(stage, ak);
+        __builtin_amdgcn_s_waitcnt(0);  // read before the region is refilled
         step(nvalid, c0, vreg, ak, bq, c, p_w, alpha_w);
       }
     }
+    __builtin_amdgcn_s_waitcnt(0);
   }
 
   // This wave's unnormalised output rows and softmax state into LDS for the

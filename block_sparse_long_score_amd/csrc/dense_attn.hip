@@ -292,7 +292,11 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void dense_decode_kernel(DenseDe
   __shared__ float p_s[kDecodeWaves][GM][W::SUB];
   __shared__ float alpha_s[kDecodeWaves][GM];
   __shared__ float m_s[kDecodeWaves][GM], l_s[kDecodeWaves][GM];
-  __shared__ float o_s[kDecodeWaves][GM][D];
+  __shared__ __attribute__((aligned(16))) float o_s[kDecodeWaves][GM][D];
+  // Each wave's K staging: inside its own o_s rows when they are large
+  // enough (they are written only after the wave's last block), else apart.
+  constexpr bool kStageInOut = GM * D * 4 >= W::STAGE * 2;
+  __shared__ __attribute__((aligned(16))) uint16_t kst_s[kStageInOut ? 1 : kDecodeWaves][kStageInOut ? 1 : W::STAGE];
   const Problem& p = a.p;
   const int G = p.group;
   const int split = blockIdx.x, g = blockIdx.y, s = blockIdx.z;
@@ -311,8 +315,9 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void dense_decode_kernel(DenseDe
     for (int b = b0 + w; b < b_end; b += kDecodeWaves) {
       const int phys = bt[b];
       if (phys < 0 || phys >= p.num_blocks) continue;  // absent blocks hold no keys
+      uint16_t* stage = kStageInOut ? reinterpret_cast<uint16_t*>(&o_s[w][0][0]) : &kst_s[kStageInOut ? 0 : w][0];
       st.template attend_block<false>(p.k, p.v, ((int64_t)phys * kBlock * p.hkv + g) * D, (int64_t)p.hkv * D,
-                                      min(kBlock, t - b * kBlock + 1), bq, p.scale_log2e, p_s[w], alpha_s[w]);
+                                      min(kBlock, t - b * kBlock + 1), bq, p.scale_log2e, p_s[w], alpha_s[w], stage);
     }
   }
   st.store(o_s[w], m_s[w], l_s[w]);
