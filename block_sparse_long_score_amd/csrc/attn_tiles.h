@@ -290,6 +290,7 @@ struct DecodeWave {
   static constexpr int CPR = D / 8;             // 16-byte chunks per K row
   static constexpr int RPI = 64 / CPR;          // K rows per load instruction
   static constexpr int STAGE = SUB * D;         // bf16 elements of a step's staged K rows
+  static_assert(SUB == 16, "the partial waits below are written as vmcnt(16)");
   // Chunk c of staged row r sits at chunk position c ^ swz(r): a step's 16
   // rows then cover every bank once for any one logical chunk.
   static __device__ __forceinline__ int swz(int r) { return (r / (256 / (D * 2))) & (CPR - 1); }  // D <= 128
@@ -320,23 +321,17 @@ struct DecodeWave {
     }
   }
 
-  // Requests (non-temporal loads) the V rows (lane: dims lane*VPL ..) and,
-  // into the wave's LDS region `stage`, the K rows of keys [c0, c0 + 16);
-  // keys at or past nvalid read key nvalid-1.  kg: the block-head's first K
+  // Requests (non-temporal loads), into the wave's LDS region `stage`, the K
+  // rows of keys [c0, c0 + 16) and then the V rows (lane: dims lane*VPL ..);
+  // keys at or past nvalid read key nvalid-1.  The K copies go first, so a
+  // wait for all but the last SUB (= 16, one per V row) memory operations of
+  // the wave covers them while the V rows may still be in flight.  kg: the block-head's first K
   // row; vr: a buffer resource over its V rows; ks_b: the key stride in
   // bytes.  A V row's offset is the same in every lane (a scalar offset);
   // each lane adds only its own dims.
   __device__ __forceinline__ void issue(const uint16_t* kg, __amdgpu_buffer_rsrc_t vr, int ks_b, int nvalid, int c0,
                                         uint32_t (&vreg)[SUB], uint16_t* stage) const {
     const int lane = threadIdx.x & 63;
-#pragma unroll
-    for (int kk = 0; kk < SUB; ++kk) {
-      const int soff = min(c0 + kk, nvalid - 1) * ks_b;
-      if constexpr (VPL == 2)
-        vreg[kk] = __builtin_amdgcn_raw_buffer_load_b32(vr, lane * 4, soff, kLoadNT);
-      else
-        vreg[kk] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(vr, lane * 2, soff, kLoadNT);
-    }
     const char* kb = reinterpret_cast<const char*>(kg);
 #pragma unroll
     for (int j = 0; j < SUB / RPI; ++j) {
@@ -346,6 +341,14 @@ struct DecodeWave {
                                        reinterpret_cast<__attribute__((address_space(3))) void*>(
                                            reinterpret_cast<uintptr_t>(stage + j * 512)),
                                        16, 0, kLoadNT);
+    }
+#pragma unroll
+    for (int kk = 0; kk < SUB; ++kk) {
+      const int soff = min(c0 + kk, nvalid - 1) * ks_b;
+      if constexpr (VPL == 2)
+        vreg[kk] = __builtin_amdgcn_raw_buffer_load_b32(vr, lane * 4, soff, kLoadNT);
+      else
+        vreg[kk] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(vr, lane * 2, soff, kLoadNT);
     }
   }
 
@@ -443,10 +446,10 @@ struct DecodeWave {
         const int c0 = st * SUB;
         if (c0 >= nvalid) break;
         bf16x8 ak[KS];
-        __builtin_amdgcn_s_waitcnt(0);  // this step's K rows have landed (and its V rows)
+        asm volatile("s_waitcnt vmcnt(16)" ::: "memory");  // this step's K rows have landed (its 16 V rows may not)
         read_k(stage, ak);
-        __builtin_amdgcn_s_waitcnt(0);  // read before the region is refilled
-        if (st + 1 < NSTEP && c0 + SUB < nvalid) issue(kg, vb, ks_b, nvalid, c0 + SUB, vreg[(st + 1) & 1], stage);
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // read before the region is refilled
+        if (st + 1 < NSTEP) issue(kg, vb, ks_b, nvalid, c0 + SUB, vreg[(st + 1) & 1], stage);
         step(nvalid, c0, vreg[st & 1], ak, bq, c, p_w, alpha_w);
       }
     } else {
@@ -454,9 +457,9 @@ struct DecodeWave {
         uint32_t vreg[SUB];
         bf16x8 ak[KS];
         issue(kg, vb, ks_b, nvalid, c0, vreg, stage);
-        __builtin_amdgcn_s_waitcnt(0);  // the K rows have landed
+        asm volatile("s_waitcnt vmcnt(16)" ::: "memory");  // the K rows have landed (the 16 V rows may not)
         read_k(stage, ak);
-        __builtin_amdgcn_s_waitcnt(0);  // read before the region is refilled
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // read before the region is refilled
         step(nvalid, c0, vreg, ak, bq, c, p_w, alpha_w);
       }
     }
