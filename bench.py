@@ -63,16 +63,42 @@ def algorithmic_work(w):
                 io_bytes=float(io_bytes), pooled_bytes=float(pooled_bytes), nblk=nblk)
 
 
+def _code_only(text: str) -> str:
+    """C++ source without its comments and blank space, so that a comment edit
+    leaves the hash of the code (and the profiles recorded for it) valid.
+    String and character literals are kept as they are."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        c = text[i]
+        if c in "\"'":
+            j = i + 1
+            while j < n and text[j] != c:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        elif text.startswith("//", i):
+            i = text.find("\n", i)
+            i = n if i < 0 else i
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+        else:
+            out.append(c)
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def kernel_source_hash() -> str:
-    """Hash of the HIP sources and headers the library is built from."""
+    """Hash of the code (comments and spacing aside) of the HIP sources and
+    headers the library is built from."""
     import hashlib
     h = hashlib.sha256()
     for d in (os.path.join(ROOT, "block_sparse_long_score_amd", "csrc"), os.path.join(ROOT, "include")):
         for f in sorted(os.listdir(d)):
             if f.endswith((".hip", ".h")):
                 h.update(f.encode())
-                with open(os.path.join(d, f), "rb") as fh:
-                    h.update(fh.read())
+                with open(os.path.join(d, f), encoding="utf-8") as fh:
+                    h.update(_code_only(fh.read()).encode())
     return h.hexdigest()[:16]
 
 

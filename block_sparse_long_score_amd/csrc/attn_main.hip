@@ -882,10 +882,11 @@ __global__ __launch_bounds__(256) void decode_step_block_kernel(KvOuterArgs a, S
 // wave w attends the query's G heads to the block of slot w, 32 keys at a
 // time with an online softmax, and the 16 waves' (max, sum, output) triples
 // are combined in LDS into the output row, so no partial rows are written.
-// Scores use the 16x16x32 bf16 MFMA with keys on M (K rows read straight
-// from the cache) and heads on N (padded to 16); P.V uses vector ALU math
-// with each lane owning D/64 output dims and P broadcast from LDS.
-// Layout of the 16x16x32 operands as in decode_block_kernel.
+// Scores use the 16x16x32 bf16 MFMA with keys on M (each step's K rows
+// staged whole in the wave's LDS region, DecodeWave) and heads on N (padded
+// to 16); P.V uses vector ALU math with each lane owning D/64 output dims and
+// P broadcast from LDS.  Layout of the 16x16x32 operands as in
+// decode_block_kernel.
 template <int D, int GM>
 __global__ __launch_bounds__(1024) void decode_fused_kernel(KvOuterArgs a) {
   using W = DecodeWave<D, GM>;

@@ -268,8 +268,8 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, 
 
 // One wave attends a decode query's G heads (G <= GM <= 16) to the keys of
 // one block after another, keeping a running softmax state.  Scores use the
-// 16x16x32 bf16 MFMA with 16 keys on M (K rows read straight from the cache)
-// and the heads on N (padded to 16); P.V uses vector ALU math with each lane
+// 16x16x32 bf16 MFMA with 16 keys on M (K rows staged in the wave's LDS
+// region) and the heads on N (padded to 16); P.V uses vector ALU math with each lane
 // owning D/64 output dims.  16x16x32 lane layout: A lane l holds
 // A[l%16][8*(l/16) .. +7], B lane l holds B[8*(l/16) .. +7][l%16], D lane l
 // register i holds D[4*(l/16) + i][l%16].
