@@ -630,7 +630,7 @@ def main():
                                   if mode == "decode" else "")},
         "step_calls": ("msa_decode_step (the append fused into the K_idx scan; then selection, attention and "
                        "merge in one kernel below 128 (sequence, group) pairs, else the top-k kernel and the "
-                       "one-workgroup-per-pair attention)" if mode == "decode" else
+                       "attention, two workgroups per pair below 256 pairs)" if mode == "decode" else
                        "msa_kv_append, then per chunk msa_index_score, msa_block_topk, msa_sparse_attn_prefill"),
         "higher_is_better": True,
         "scaling": "weak",

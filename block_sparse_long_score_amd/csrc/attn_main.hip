@@ -68,6 +68,10 @@ static int kv_chunk(const Problem& p) { return std::max(16, kKvMaxChunk / p.grou
 // 16-wave workgroup per pair (decode_fused_kernel, any G <= 16); smaller ones split each
 // pair over 16 workgroups (one per selected block) and merge.
 constexpr int64_t kFusedDecodeMinGroups = 128;
+// In the fused decode step, batches with fewer pairs than this (and at least
+// kFusedDecodeMinGroups) split each pair over two workgroups
+// (decode_fused_half_kernel), so that every CU streams.
+constexpr int64_t kFusedHalfMaxGroups = 256;
 
 // ---------------------------------------------------------------- workspace
 
@@ -115,10 +119,24 @@ size_t prefill_workspace_bytes(const Problem& p) {
 }
 size_t decode_workspace_bytes(const Problem& p) { return main_layout(p, true).part_total; }
 
+// The two-workgroup decode (decode_fused_half_kernel) keeps, at the start of
+// the partial region, each (pair, half)'s G x D output sums and G (max, mass)
+// pairs, then one counter per pair; this always fits in the region, which
+// holds 16 fp16 partial rows per (pair, head).
+static size_t decode_half_state_bytes(const Problem& p) {
+  return align256(sizeof(float) * (size_t)p.total_q * p.hkv * 2 * ((size_t)p.group * p.head_dim + 2 * p.group));
+}
+static bool decode_uses_half(const Problem& p) {
+  const int64_t pairs = (int64_t)p.num_seqs * p.hkv;
+  return pairs >= kFusedDecodeMinGroups && pairs < kFusedHalfMaxGroups;
+}
+
 // ------------------------------------------------- decode without allocation
 
 // The split decode (fewer than kFusedDecodeMinGroups (sequence, group) pairs)
-// keeps one partial row per (pair, slot, head) in scratch memory; larger
+// keeps one partial row per (pair, slot, head) in scratch memory; batches of
+// up to kFusedHalfMaxGroups pairs keep two halves' G x D sums per pair and a
+// counter (at most 255 * 2 * (16 * 128 + 32) floats, about 4.2 MB); larger
 // batches use decode_fused_kernel, which needs none.  So the scratch of the
 // largest split decode, 127 pairs at G = 16 and D = 128, serves every decode
 // batch: 127 * 16 * 16 partial rows of 128 fp16 values and 8 bytes of
@@ -136,6 +154,7 @@ static __device__ __align__(256) unsigned char scratch[kDecodeScratchBytes];
 size_t decode_scratch_capacity() { return kDecodeScratchBytes; }
 
 size_t decode_scratch_need(const Problem& p) {
+  if (decode_uses_half(p)) return decode_half_state_bytes(p) + sizeof(int32_t) * (size_t)p.total_q * p.hkv;
   return (int64_t)p.num_seqs * p.hkv >= kFusedDecodeMinGroups ? 0 : decode_workspace_bytes(p);
 }
 
@@ -927,6 +946,104 @@ __global__ __launch_bounds__(1024) void decode_fused_kernel(KvOuterArgs a) {
   }
 }
 
+__device__ __forceinline__ void swap_f(float& x, float& y) {
+  const float t = x;
+  x = y;
+  y = t;
+}
+
+// Decode step of a batch with fewer (sequence, group) pairs than the chip has
+// CUs (but enough for one workgroup each to pay): two 16-wave workgroups per
+// pair, each attending 8 of the 16 selected blocks with two waves per block
+// (64 keys each), so every CU streams about half as much.  Each workgroup
+// combines its waves in LDS as decode_fused_kernel does, stores its half's
+// (max, mass, unnormalised output) device-coherently in the step workspace,
+// and counts itself on the pair's counter (zero on entry: the step's scoring
+// kernel clears it); the second to arrive reads the other half with
+// device-coherent loads, combines the two, writes the bf16 output and clears
+// the counter.  One thread per (head, dim pair) item in both phases.
+template <int D, int GM>
+__global__ __launch_bounds__(1024) void decode_fused_half_kernel(KvOuterArgs a, StepArgs sa) {
+  using W = DecodeWave<D, GM>;
+  __shared__ float p_s[kTopK][GM][W::SUB];
+  __shared__ float alpha_s[kTopK][GM];
+  __shared__ float m_s[kTopK][GM], l_s[kTopK][GM];
+  __shared__ __attribute__((aligned(16))) float o_s[kTopK][GM][D];
+  constexpr bool kStageInOut = GM * D * 4 >= W::STAGE * 2;
+  __shared__ __attribute__((aligned(16))) uint16_t kst_s[kStageInOut ? 1 : kTopK][kStageInOut ? 1 : W::STAGE];
+  __shared__ int last_s;
+  const Problem& p = a.p;
+  const int G = p.group;
+  const int half = blockIdx.x & 1;
+  const int pair = blockIdx.x >> 1;
+  const int g = pair & ((1 << a.hkv_shift) - 1);
+  const int s = pair >> a.hkv_shift;
+  const int r = p.cu_q[s];
+  const int64_t R = ((int64_t)r << a.hkv_shift) + g;
+  const int t = p.seq_lens[s] - 1;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int slot = half * (kTopK / 2) + (w >> 1);
+  const int k_lo = (w & 1) * (kBlock / 2);  // this wave's half of the block's keys
+  const int b = a.sel[R * kTopK + slot];
+  W st;
+  if (entry_valid(p, s, b, t)) {
+    const int nvalid = min(kBlock, t - b * kBlock + 1) - k_lo;
+    if (nvalid > 0) {
+      const int phys = p.block_table[(int64_t)s * p.max_blocks_per_seq + b];
+      bf16x8 bq[W::KS];
+      st.load_q(a.q + ((int64_t)r * p.hq + g * G) * D, G, bq);
+      uint16_t* stage = kStageInOut ? reinterpret_cast<uint16_t*>(&o_s[w][0][0]) : &kst_s[kStageInOut ? 0 : w][0];
+      st.attend_block(p.k, p.v, ((int64_t)phys * kBlock * p.hkv + g) * D + (int64_t)k_lo * p.hkv * D,
+                      (int64_t)p.hkv * D, min(nvalid, kBlock / 2), bq, p.scale_log2e, p_s[w], alpha_s[w], stage);
+    }
+  }
+  st.store(o_s[w], m_s[w], l_s[w]);
+  __syncthreads();
+  // This half's state in the step workspace: per (pair, half), G x D output
+  // sums, then (max, mass) per head.
+  const int stride = G * D + 2 * G;
+  float* const mine = reinterpret_cast<float*>(a.part_o) + (R * 2 + half) * stride;
+  const float* const other = reinterpret_cast<const float*>(a.part_o) + (R * 2 + (half ^ 1)) * stride;
+  const int idx = threadIdx.x;  // G * D / 2 <= 1024 items, one per thread
+  const bool item = idx < G * (D / 2);
+  const int j = item ? idx / (D / 2) : 0, d = item ? (idx - j * (D / 2)) * 2 : 0;
+  float o0 = 0.f, o1 = 0.f, L = 0.f, M = -__builtin_inff();
+  if (item) {
+    combine_waves<D, GM, kTopK>(o_s, m_s, l_s, j, d, o0, o1, L, M);
+    coherent_store8(mine, (uint32_t)((j * D + d) * 4), u32x2{__float_as_uint(o0), __float_as_uint(o1)});
+    if (d == 0) coherent_store8(mine, (uint32_t)((G * D + 2 * j) * 4), u32x2{__float_as_uint(M), __float_as_uint(L)});
+  }
+  __builtin_amdgcn_s_waitcnt(0);  // this thread's stores have completed
+  __syncthreads();                // and every thread's, before the pair's counter is incremented
+  if (threadIdx.x == 0)
+    last_s = __hip_atomic_fetch_add(sa.counters + R, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 1;
+  __syncthreads();
+  if (!last_s) return;
+  if (item) {
+    const u32x2 ov = coherent_load8(other, (uint32_t)((j * D + d) * 4));
+    const u32x2 ml = coherent_load8(other, (uint32_t)((G * D + 2 * j) * 4));
+    // Combine in half order, whichever half arrived last, so the rounding
+    // (fused multiply-adds included) does not depend on the arrival order.
+    float ao0 = o0, ao1 = o1, aL = L, aM = M;
+    float bo0 = __uint_as_float(ov[0]), bo1 = __uint_as_float(ov[1]), bL = __uint_as_float(ml[1]),
+          bM = __uint_as_float(ml[0]);
+    if (half) {
+      swap_f(ao0, bo0);
+      swap_f(ao1, bo1);
+      swap_f(aL, bL);
+      swap_f(aM, bM);
+    }
+    const float Mx = fmaxf(aM, bM);
+    const float fa = aL > 0.f ? fast_exp2(aM - Mx) : 0.f;
+    const float fb = bL > 0.f ? fast_exp2(bM - Mx) : 0.f;
+    const float Lt = aL * fa + bL * fb;
+    const float inv = Lt > 0.f ? 1.0f / Lt : 0.f;  // no attended key: 0
+    const float y0 = (ao0 * fa + bo0 * fb) * inv, y1 = (ao1 * fa + bo1 * fb) * inv;
+    *reinterpret_cast<uint32_t*>(a.out_direct + ((int64_t)r * p.hq + g * G + j) * D + d) = pack_bf16x2(y0, y1);
+  }
+  if (threadIdx.x == 0) sa.counters[R] = 0;
+}
+
 // ----------------------------------------------------------------- merge
 
 struct MergeArgs {
@@ -1176,6 +1293,25 @@ static hipError_t launch_run_t(const Problem& p, const uint16_t* q, const int32_
   return launch_merge_t<D>(p, sel, reinterpret_cast<const int32_t*>(pb + w.entry_of), k.part_o, k.part_st, out, stream);
 }
 
+__global__ void clear_counters_kernel(int32_t* counters, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) counters[i] = 0;
+}
+
+template <int D>
+static hipError_t launch_half_t(const Problem& p, const KvOuterArgs& k, const StepArgs& sa, hipStream_t stream) {
+  const dim3 hgrid((unsigned)((int64_t)p.num_seqs * p.hkv * 2));
+  if (p.group <= 4)
+    hipLaunchKernelGGL((decode_fused_half_kernel<D, 4>), hgrid, dim3(1024), 0, stream, k, sa);
+  else if (p.group <= 6)
+    hipLaunchKernelGGL((decode_fused_half_kernel<D, 6>), hgrid, dim3(1024), 0, stream, k, sa);
+  else if (p.group <= 8)
+    hipLaunchKernelGGL((decode_fused_half_kernel<D, 8>), hgrid, dim3(1024), 0, stream, k, sa);
+  else
+    hipLaunchKernelGGL((decode_fused_half_kernel<D, 16>), hgrid, dim3(1024), 0, stream, k, sa);
+  return hipGetLastError();
+}
+
 template <int D>
 static hipError_t launch_decode_t(const Problem& p, const uint16_t* q, const int32_t* sel, uint16_t* out, void* ws,
                                   hipStream_t stream) {
@@ -1184,6 +1320,14 @@ static hipError_t launch_decode_t(const Problem& p, const uint16_t* q, const int
   KvOuterArgs k{p, q, sel, nullptr, nullptr, nullptr, nullptr,
                 reinterpret_cast<uint16_t*>(base + w.part_o), out, reinterpret_cast<float*>(base + w.part_st),
                 w.n_lists, hkv_shift_of(p), w.chunk};
+  if (decode_uses_half(p)) {
+    // Two workgroups per pair; their counters (after the halves' state) are
+    // cleared first by a small kernel, the workspace being the caller's.
+    int32_t* counters = reinterpret_cast<int32_t*>(base + w.part_o + decode_half_state_bytes(p));
+    const int n = p.total_q * p.hkv;
+    hipLaunchKernelGGL(clear_counters_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, counters, n);
+    return launch_half_t<D>(p, k, StepArgs{nullptr, 0, nullptr, counters}, stream);
+  }
   if ((int64_t)p.num_seqs * p.hkv >= kFusedDecodeMinGroups) {
     // Enough (sequence, group) pairs to fill the chip: one workgroup each, no merge pass.
     const unsigned n = (unsigned)(p.num_seqs * p.hkv);
@@ -1245,7 +1389,7 @@ size_t decode_step_workspace_bytes(const Problem& p) {
 }
 
 int32_t* decode_step_counters(const Problem& p, void* ws) {
-  if ((int64_t)p.num_seqs * p.hkv >= kFusedDecodeMinGroups) return nullptr;  // the fused path merges in LDS
+  if ((int64_t)p.num_seqs * p.hkv >= kFusedHalfMaxGroups) return nullptr;  // one workgroup per pair merges in LDS
   return reinterpret_cast<int32_t*>(static_cast<char*>(ws) + decode_workspace_bytes(p));
 }
 
@@ -1258,13 +1402,16 @@ static hipError_t launch_step_attn_t(const Problem& p, const uint16_t* q, const 
                 reinterpret_cast<uint16_t*>(base + w.part_o), out, reinterpret_cast<float*>(base + w.part_st),
                 w.n_lists, hkv_shift_of(p), w.chunk};
   const StepArgs sa{scores, ld, sel, decode_step_counters(p, ws)};
-  if (!sa.counters) {
-    // Batches that fill the chip with one workgroup per (sequence, group): the
-    // selection as its own short kernel (made inside each workgroup, it would
-    // delay every workgroup's attention by its latency), then the attention.
+  const int64_t pairs = (int64_t)p.num_seqs * p.hkv;
+  if (pairs >= kFusedDecodeMinGroups) {
+    // Batches that fill the chip with one or two workgroups per (sequence,
+    // group): the selection as its own short kernel (made inside each
+    // workgroup, it would delay every workgroup's attention by its latency),
+    // then the attention.
     const hipError_t e = launch_block_topk(p, scores, ld, sel, max_blocks, stream);
     if (e != hipSuccess) return e;
-    return launch_decode_t<D>(p, q, sel, out, ws, stream);
+    if (pairs >= kFusedHalfMaxGroups) return launch_decode_t<D>(p, q, sel, out, ws, stream);
+    return launch_half_t<D>(p, k, sa, stream);  // the step's counters, cleared by its scoring kernel
   }
   const dim3 dgrid(kTopK, p.hkv, p.num_seqs);
   if (p.group <= 4)

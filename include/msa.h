@@ -278,8 +278,11 @@ msa_status msa_sparse_attn_decode(const msa_dims* dims, const msa_cache* cache,
  * (sequence, group) pairs the block selection, the attention and the merge
  * of the 16 slots run as one kernel (the workgroup that finishes a row last
  * merges it; two kernels instead of five).  Larger batches run the top-k
- * and the one-workgroup-per-pair attention after the fused scan (three
- * instead of four).  Fewer launches shorten a step whose work is one
+ * and the attention after the fused scan (three kernels instead of four:
+ * from 128 to 255 pairs two workgroups per pair, the second to finish
+ * merging the two halves; from 256 on one workgroup per pair).  The
+ * attention kernels and their arithmetic are those of
+ * msa_sparse_attn_decode.  Fewer launches shorten a step whose work is one
  * HBM-bound scan followed by latency-bound tails.
  *   Requires cu_q[s+1] - cu_q[s] == 1 for every s (BAD_SHAPE otherwise).
  *   k_new, v_new, k_idx_new : as msa_kv_append
@@ -304,10 +307,10 @@ msa_status msa_decode_step(const msa_dims* dims, const msa_cache* cache, const m
  * computes exactly what msa_sparse_attn_decode computes (same kernels, same
  * results bit for bit).  Its scratch memory is a static array inside the
  * library: about 8.2 MB per GPU, held from the first call on that GPU until
- * the process ends, enough for every decode batch (batches of 128 or more
- * (sequence, group) pairs need none; smaller ones need
- * msa_workspace_size(..., MSA_CALL_SPARSE_ATTN_DECODE) bytes of it, at most
- * the array's size).  The call allocates nothing and calls no allocating
+ * the process ends, enough for every decode batch (batches of 256 or more
+ * (sequence, group) pairs need none, batches of 128 to 255 at most 4.3 MB;
+ * smaller ones need msa_workspace_size(..., MSA_CALL_SPARSE_ATTN_DECODE)
+ * bytes of it, at most the array's size).  The call allocates nothing and calls no allocating
  * routine.  Every call on one GPU shares that GPU's array: calls that overlap
  * in time on one GPU (on different streams, or from different threads without
  * ordering) race and may return wrong results; calls ordered on one stream are

@@ -118,14 +118,22 @@ def test_decode_batch_ragged_lengths():
 _RAGGED = [1, 128, 129, 2047, 2049, 5000, 16 * 128, 16 * 128 + 1, 300, 4097, 7777, 12000, 64, 1500, 2176, 9000]
 
 
-@pytest.mark.parametrize("shape", ["g6_d128", "g4_d128", "g8_d64"])
+@pytest.mark.parametrize("shape", ["g6_d128", "g4_d128", "g8_d64", "g16_256", "g6_256"])
 def test_decode_large_batch_one_workgroup_per_group(shape):
-    """Batches with >= 128 (sequence, group) pairs take the one-workgroup-per-pair decode kernel."""
+    """Batches with >= 128 (sequence, group) pairs take the fused decode kernels:
+    two workgroups per pair (each attending 8 slots, merged by the second to
+    finish) below 256 pairs, one workgroup per pair from 256 pairs on."""
     import dataclasses
     if shape == "g6_d128":
         w = M2.with_sizes("decode16", _RAGGED, [1] * 16, permuted_table=True)
     elif shape == "g4_d128":
         w = dataclasses.replace(M2, num_q_heads=32).with_sizes("decode16g4", _RAGGED, [1] * 16, permuted_table=True)
+    elif shape == "g16_256":  # 64 sequences x 4 groups at G = 16
+        lens = [_RAGGED[i % 16] + 11 * i for i in range(64)]
+        w = WORKLOADS["m3d"].with_sizes("decode64g16", lens, [1] * 64, permuted_table=True)
+    elif shape == "g6_256":  # 32 sequences x 8 groups
+        lens = [_RAGGED[i % 16] + 5 * i for i in range(32)]
+        w = M2.with_sizes("decode32", lens, [1] * 32, permuted_table=True)
     else:
         lens = [_RAGGED[i % 16] + 7 * (i // 16) for i in range(128)]
         w = WORKLOADS["c0"].with_sizes("decode128", lens, [1] * 128, permuted_table=True)
