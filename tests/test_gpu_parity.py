@@ -145,15 +145,21 @@ def test_decode_large_batch_one_workgroup_per_group(shape):
 
 
 @pytest.mark.parametrize("group", [3, 5, 7])
-@pytest.mark.parametrize("path", ["decode_fused", "decode_split", "prefill"])
+@pytest.mark.parametrize("path", ["decode_fused", "decode_fused_half", "decode_split", "prefill"])
 def test_group_sizes_between_instantiations(group, path):
     """Group sizes the kernels pad to the next instantiated head count
-    (3 -> 4, 5 -> 6, 7 -> 8): the padded heads must not leak into the output."""
+    (3 -> 4, 5 -> 6, 7 -> 8): the padded heads must not leak into the output.
+    Decode paths: one workgroup per (sequence, group) pair (256 pairs), two
+    per pair (128 pairs), one per (sequence, group, slot) (64 pairs)."""
     import dataclasses
     w0 = dataclasses.replace(M2, num_q_heads=8 * group)
     if path == "decode_fused":
-        w = w0.with_sizes(f"g{group}_fused", _RAGGED, [1] * 16, permuted_table=True)
-        assert w.num_seqs * w.num_kv_heads >= 128
+        lens = [_RAGGED[i % 16] + 3 * i for i in range(32)]
+        w = w0.with_sizes(f"g{group}_fused", lens, [1] * 32, permuted_table=True)
+        assert w.num_seqs * w.num_kv_heads >= 256
+    elif path == "decode_fused_half":
+        w = w0.with_sizes(f"g{group}_half", _RAGGED, [1] * 16, permuted_table=True)
+        assert 128 <= w.num_seqs * w.num_kv_heads < 256
     elif path == "decode_split":
         w = w0.with_sizes(f"g{group}_split", _RAGGED[:8], [1] * 8, permuted_table=True)
     else:
@@ -163,12 +169,14 @@ def test_group_sizes_between_instantiations(group, path):
     check_selection_invariants(runner)
 
 
-@pytest.mark.parametrize("case", ["decode_fused", "decode_split", "prefill"])
+@pytest.mark.parametrize("case", ["decode_fused", "decode_fused_half", "decode_split", "prefill"])
 def test_graph_replays_equal_eager_step(case):
     """A captured step replays to the eager step's results, replay after replay,
     with eager work and synchronisation in between."""
     if case == "decode_fused":
-        w = M2.with_sizes("g_fused", _RAGGED, [1] * 16, permuted_table=True)
+        w = M2.with_sizes("g_fused", [_RAGGED[i % 16] + 3 * i for i in range(32)], [1] * 32, permuted_table=True)
+    elif case == "decode_fused_half":
+        w = M2.with_sizes("g_half", _RAGGED, [1] * 16, permuted_table=True)
     elif case == "decode_split":
         w = M2.with_sizes("g_split", _RAGGED[:8], [1] * 8, permuted_table=True)
     else:
@@ -364,6 +372,8 @@ def test_prepared_step_equals_plain_calls(mode):
 _STEP_CASES = {
     "split_m2": lambda: M2.with_sizes("step_split", [9999, 130, 2049, 5000, 1, 70000], [1] * 6, permuted_table=True),
     "fused_m2": lambda: M2.with_sizes("step_fused", _RAGGED, [1] * 16, permuted_table=True),
+    "fused_m2_256": lambda: M2.with_sizes("step_fused256", [_RAGGED[i % 16] + 3 * i for i in range(32)], [1] * 32,
+                                          permuted_table=True),
     "split_g16": lambda: WORKLOADS["m3d"].with_sizes("step_g16", [_RAGGED[i % 16] + 13 * i for i in range(31)],
                                                      [1] * 31, permuted_table=True),
     "fused_g16": lambda: WORKLOADS["m3d"].with_sizes("step_g16f", [_RAGGED[i % 16] + 13 * i for i in range(32)],
