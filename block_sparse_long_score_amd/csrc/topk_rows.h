@@ -24,11 +24,15 @@ __device__ __forceinline__ void wave_lds_sync() {
 }
 
 // k-th largest of the 64 lane values (k <= 64): the largest T with
-// |{lanes : x >= T}| >= k, built from the top bit down.
+// |{lanes : x >= T}| >= k, built from the top bit down.  With LOW > 0 the
+// LOW lowest bits are not searched: the result is the k-th largest with those
+// bits cleared, a lower bound of it (the largest such T is at most the k-th
+// largest, and every value above the k-th largest has a count below k).
+template <int LOW = 0>
 __device__ __forceinline__ uint32_t kth_largest_lane(uint32_t x, int k) {
   uint32_t t = 0;
 #pragma unroll
-  for (int bit = 31; bit >= 0; --bit) {
+  for (int bit = 31; bit >= LOW; --bit) {
     const uint32_t cand = t | (1u << bit);
     if (__popcll(__ballot(x >= cand)) >= k) t = cand;
   }
@@ -73,7 +77,8 @@ __device__ void select_row(const float* __restrict__ row, int c, int32_t* __rest
 #pragma unroll
     for (int j = 0; j < NC; ++j) lmax = max(lmax, keys[j]);
   }
-  const uint32_t theta = kth_largest_lane(lmax, kKeep);
+  // A lower bound is all the compaction needs: the 16 high bits suffice.
+  const uint32_t theta = kth_largest_lane<16>(lmax, kKeep);
 
   // 2. compact survivors (key >= theta) in ascending block order.
   int count = 0;
