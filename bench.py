@@ -387,8 +387,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="run one device-to-device copy of this many MiB first (scales PMC byte counters)")
-    ap.add_argument("--chunk-rows", type=int, default=16384,
-                    help="prefill query rows per pipelined chunk (0: one chunk, no overlap)")
+    ap.add_argument("--chunk-rows", type=int, default=65536,
+                    help="prefill query rows per pipelined chunk (0: one chunk, no overlap); prefills of at "
+                         "most this many rows run unchunked")
     ap.add_argument("--quality-rows", type=int, default=64,
                     help="query rows (evenly spaced) on which to measure selection quality against dense attention; 0: skip")
     ap.add_argument("--dense-calls", type=int, default=3,
