@@ -56,7 +56,17 @@ __global__ __launch_bounds__(256) void block_topk_kernel(TopkArgs a) {
     return;
   }
   const float* row = a.scores + (R - a.r_base) * a.ld;
-  if (c <= kCached * 64)
+  // Registers sized to the row: a short row loads, keys and compacts only the
+  // groups of 64 candidates it has.
+  if (c <= 2 * 64)
+    select_row<true, true, 2>(row, c, out, surv_key[wave], surv_idx[wave]);
+  else if (c <= 4 * 64)
+    select_row<true, true, 4>(row, c, out, surv_key[wave], surv_idx[wave]);
+  else if (c <= 8 * 64)
+    select_row<true, true, 8>(row, c, out, surv_key[wave], surv_idx[wave]);
+  else if (c <= 12 * 64)
+    select_row<true, true, 12>(row, c, out, surv_key[wave], surv_idx[wave]);
+  else if (c <= kCached * 64)
     select_row<true>(row, c, out, surv_key[wave], surv_idx[wave]);
   else
     select_row<false>(row, c, out, surv_key[wave], surv_idx[wave]);

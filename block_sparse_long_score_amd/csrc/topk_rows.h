@@ -78,7 +78,8 @@ __device__ void select_row(const float* __restrict__ row, int c, int32_t* __rest
     for (int j = 0; j < NC; ++j) lmax = max(lmax, keys[j]);
   }
   // A lower bound is all the compaction needs: the 16 high bits suffice.
-  const uint32_t theta = kth_largest_lane<16>(lmax, kKeep);
+  // Key 0 marks a lane past the row, so the bound is at least 1.
+  const uint32_t theta = max(kth_largest_lane<16>(lmax, kKeep), 1u);
 
   // 2. compact survivors (key >= theta) in ascending block order.
   int count = 0;
@@ -86,7 +87,7 @@ __device__ void select_row(const float* __restrict__ row, int c, int32_t* __rest
     if constexpr (!CACHED) load_batch<NC>(row, c, j0, keys);
 #pragma unroll
     for (int j = 0; j < NC; ++j) {
-      const bool ok = keys[j] >= theta && keys[j] != 0u;
+      const bool ok = keys[j] >= theta;
       const uint64_t m = __ballot(ok);
       const int pos = count + lanes_below(m);
       if (ok && pos < 64) {
