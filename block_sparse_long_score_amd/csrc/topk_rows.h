@@ -89,12 +89,14 @@ __device__ void select_row(const float* __restrict__ row, int c, int32_t* __rest
     for (int j = 0; j < NC; ++j) {
       const bool ok = keys[j] >= theta;
       const uint64_t m = __ballot(ok);
-      const int pos = count + lanes_below(m);
-      if (ok && pos < 64) {
-        surv_key[pos] = keys[j];
-        surv_idx[pos] = (j0 + j) * 64 + lane;
+      if (m != 0) {  // most groups hold no survivor: a ballot is all they cost
+        const int pos = count + lanes_below(m);
+        if (ok && pos < 64) {
+          surv_key[pos] = keys[j];
+          surv_idx[pos] = (j0 + j) * 64 + lane;
+        }
+        count += __popcll(m);
       }
-      count += __popcll(m);
     }
   }
   wave_lds_sync();
