@@ -64,13 +64,14 @@ static int hkv_shift_of(const Problem& p) {
 constexpr int kKvMaxChunk = 3072;  // (entry, head) rows per kvouter workgroup, at most
 static int kv_chunk(const Problem& p) { return std::max(16, kKvMaxChunk / p.group); }
 
-// Decode batches with at least this many (sequence, group) pairs use one
-// 16-wave workgroup per pair (decode_fused_kernel, any G <= 16); smaller ones split each
-// pair over 16 workgroups (one per selected block) and merge.
+// Decode batches with at least this many (sequence, group) pairs give each
+// pair whole 16-wave workgroups (any G <= 16); smaller ones split each pair
+// over 16 workgroups (one per selected block) and merge.
 constexpr int64_t kFusedDecodeMinGroups = 128;
-// In the fused decode step, batches with fewer pairs than this (and at least
-// kFusedDecodeMinGroups) split each pair over two workgroups
-// (decode_fused_half_kernel), so that every CU streams.
+// Batches with fewer pairs than this (and at least kFusedDecodeMinGroups)
+// give each pair two workgroups (decode_fused_half_kernel), so that every CU
+// streams; larger ones one (decode_fused_kernel).  Both the decode call and
+// the fused decode step follow this split.
 constexpr int64_t kFusedHalfMaxGroups = 256;
 
 // ---------------------------------------------------------------- workspace
