@@ -63,8 +63,8 @@ __device__ __forceinline__ void load_batch(const float* __restrict__ row, int c,
 // 64 * NC (NC per lane).  out_key (optional): each kept block's order key,
 // beside its index in out.
 template <bool CACHED, bool WRITE_LOCAL = true, int NC = kCached>
-__device__ void select_row(const float* __restrict__ row, int c, int32_t* __restrict__ out, uint32_t* surv_key,
-                           int32_t* surv_idx, uint32_t* out_key = nullptr) {
+__device__ __forceinline__ void select_row(const float* __restrict__ row, int c, int32_t* __restrict__ out,
+                                           uint32_t* surv_key, int32_t* surv_idx, uint32_t* out_key = nullptr) {
   const int lane = threadIdx.x & 63;
   const int nj = (c + 63) / 64;
   uint32_t keys[NC];

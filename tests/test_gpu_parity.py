@@ -246,13 +246,15 @@ def test_decode_equals_prefill_last_row():
     compare_rows(runner_d, 0, [4499])
 
 
-@pytest.mark.parametrize("n_rows,ld", [(64, 8300), (1100, 8300), (1100, 10000)])
+@pytest.mark.parametrize("n_rows,ld", [(64, 8300), (1100, 8300), (1100, 10000), (2000, 1024)])
 def test_topk_on_oracle_scores_with_ties(n_rows, ld):
     """The selection kernel alone, fed block scores written by the oracle
     (real rows) and by hand (massive ties, +/-0, long rows past the register
     cache).  64 long rows take the split (16 waves per row) kernel, 1100 the
     four-waves-per-row kernel (rows over 1024 blocks, many rows), which holds
-    rows of up to 9216 blocks in registers and streams longer ones."""
+    rows of up to 9216 blocks in registers and streams longer ones; 2000 rows
+    of at most 1024 blocks the one-wave kernel, whose row lengths span all of
+    its register sizes (2 to 16 groups of 64 candidates)."""
     w = M2.with_sizes("topk", [9000], [9000])
     inp = make_inputs(w, "cuda")
     runner = MsaRunner(inp)
@@ -268,7 +270,7 @@ def test_topk_on_oracle_scores_with_ties(n_rows, ld):
     import oracle
     rng = np.random.default_rng(3)
     pos = np.sort(rng.integers(2048, ld * 128, size=n_rows)).astype(np.int64)
-    pos[:3] = [ld * 128 - 1, 1024 * 128 + 5, 1024 * 128 - 1]
+    pos[:3] = [ld * 128 - 1, 1024 * 128 + 5, 1024 * 128 - 1] if ld > 1024 else [ld * 128 - 1, 767 * 128 + 5, 512 * 128 - 1]
     pos[-6:] = [0, 130, 2047, 2100, 5000, 8191]  # short rows: every block kept, or candidates in one wave only
     vals = rng.integers(-3, 4, size=(n_rows, 1, ld)).astype(np.float32) / 4
     vals[0] = 0.0                      # every block ties
