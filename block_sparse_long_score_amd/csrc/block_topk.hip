@@ -42,7 +42,7 @@ __global__ __launch_bounds__(256) void block_topk_kernel(TopkArgs a) {
   __shared__ int32_t surv_idx[4][64];
   const Problem& p = a.p;
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // row values stay scalar
   const int64_t local = (int64_t)blockIdx.x * 4 + wave;
   if (local >= ((int64_t)p.total_q << a.hkv_shift)) return;
   const int64_t R = a.r_base + local;
