@@ -12,9 +12,10 @@
 // the row (c = the local block).  Scores are compared through a monotone
 // 32-bit key (order_key), which also makes -0 equal to +0.
 //   1. Each lane takes the maximum key of its strided candidates; the 15th
-//      largest of the 64 lane maxima, theta, bounds the answer from below:
-//      the 15 lanes above it each own a candidate >= theta, so every one of
-//      the 15 best candidates is >= theta.
+//      largest of the 64 lane maxima, with its low 16 bits cleared (only the
+//      high bits are searched), theta, bounds the answer from below: 15
+//      lanes each own a candidate >= theta, so every one of the 15 best
+//      candidates is >= theta.
 //   2. Candidates >= theta (usually a few dozen) are compacted into LDS in
 //      ascending block order; if more than 64 survive (massive ties), an
 //      exact search over all candidates is used instead.
