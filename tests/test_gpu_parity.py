@@ -218,6 +218,26 @@ def test_m3_shape_prefill_and_decode():
     check_selection_invariants(runner)
 
 
+@pytest.mark.parametrize("path", ["prefill", "decode_split", "decode_half", "decode_whole"])
+def test_d64_g16_every_path(path):
+    """D = 64 with G = 16 (32 query / 2 KV heads, d_idx = 32): the D = 64
+    instantiations of every Main Branch kernel at the largest group size,
+    prefill and the three decode shapes (40, 128 and 256 (sequence, group)
+    pairs)."""
+    import dataclasses
+    w0 = dataclasses.replace(WORKLOADS["c0"], num_q_heads=32, num_kv_heads=2)
+    if path == "prefill":
+        w = w0.with_sizes("d64g16_prefill", [2600, 700], [2600, 90], permuted_table=True)
+    else:
+        n = {"decode_split": 20, "decode_half": 64, "decode_whole": 128}[path]
+        lens = [_RAGGED[i % 16] % 6000 + 3 * i + 1 for i in range(n)]
+        w = w0.with_sizes(f"d64g16_{path}", lens, [1] * n, permuted_table=True)
+    _announce(f"D=64 G=16 {path}: num_seqs={w.num_seqs}")
+    runner = _run(w)
+    _all_rows(runner)
+    check_selection_invariants(runner)
+
+
 def test_m3_decode_large_batch():
     """32 sequences x 4 groups: 128 (sequence, group) pairs at G = 16."""
     lens = [_RAGGED[i % 16] + 11 * (i // 16) for i in range(32)]
