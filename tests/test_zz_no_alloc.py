@@ -3,8 +3,11 @@ static scratch, for callers that cannot allocate) against
 msa_sparse_attn_decode with a caller workspace: identical outputs, bit for
 bit, on two calls in a row (the second on a smaller batch, so it runs over
 what the first left in the scratch), for the split decode (fewer than 128
-(sequence, group) pairs, which uses the scratch) and the one-workgroup-per-pair
-decode (which needs none), including a batch near the scratch's capacity."""
+(sequence, group) pairs, which uses the scratch for partial rows), the
+two-workgroups-per-pair decode (128 to 255 pairs, which keeps the halves'
+state and the pair counters there) and the one-workgroup-per-pair decode
+(256 pairs or more, which needs none), including a batch near the scratch's
+capacity."""
 import sys
 
 import numpy as np
@@ -35,6 +38,12 @@ def _case(name):
     if name == "fused_then_split":
         return [M2.with_sizes("na_fused16", _LENS, [1] * 16, permuted_table=True),
                 M2.with_sizes("na_split2", [9999, 3000], [1, 1], permuted_table=True)]
+    if name == "whole_then_half":  # 256 pairs, then 192
+        return [M2.with_sizes("na_whole32", [_LENS[i % 16] + 3 * i for i in range(32)], [1] * 32, permuted_table=True),
+                M2.with_sizes("na_half24", [_LENS[i % 16] + 5 * i for i in range(24)], [1] * 24, permuted_table=True)]
+    if name == "half_then_half":  # 192 pairs, then 128 (the counters of the first must not leak into the second)
+        return [M2.with_sizes("na_half24b", [_LENS[i % 16] + 7 * i for i in range(24)], [1] * 24, permuted_table=True),
+                M2.with_sizes("na_half16", _LENS, [1] * 16, permuted_table=True)]
     # M3 shape (G = 16): 31 sequences x 4 groups = 124 pairs, close to the scratch's capacity
     m3 = WORKLOADS["m3d"]
     lens = [_LENS[i % 16] + 11 * i for i in range(31)]
@@ -42,7 +51,8 @@ def _case(name):
             m3.with_sizes("na_m3_5", lens[:5], [1] * 5, permuted_table=True)]
 
 
-@pytest.mark.parametrize("name", ["split_then_smaller", "fused_then_split", "near_capacity"])
+@pytest.mark.parametrize("name", ["split_then_smaller", "fused_then_split", "whole_then_half", "half_then_half",
+                                  "near_capacity"])
 def test_noalloc_decode_equals_workspace_decode(name):
     for i, w in enumerate(_case(name)):
         print(f"[gpu-case] {name} call {i}: {w.name} num_seqs={w.num_seqs} Hq={w.num_q_heads} Hkv={w.num_kv_heads}",
