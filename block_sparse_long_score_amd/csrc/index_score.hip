@@ -616,7 +616,7 @@ static hipError_t launch_index_impl(const Problem& p, const uint16_t* q_idx, flo
     // 16 halves it and the pipelined 128K prefill step is ~3% faster); short
     // contexts keep 16 so the grid still fills the chip.
     // (kc <= 64 always: the kernels hold a chunk's block-table entries one per lane.)
-    const int kc = max_blocks >= 2048 ? 64 : (max_blocks >= 512 ? 32 : 16);
+    const int kc = max_blocks >= 1024 ? 64 : (max_blocks >= 512 ? 32 : 16);
     IndexArgs a{p, q_idx, scores, ld, tq, hkv_shift, kc, first_row};
     dim3 grid((unsigned)max_tiles, (unsigned)((max_blocks + kc - 1) / kc), (unsigned)p.num_seqs);
     if (p.index_dim == 64)
