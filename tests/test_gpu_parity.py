@@ -292,6 +292,8 @@ def test_topk_on_oracle_scores_with_ties(n_rows, ld):
     pos = np.sort(rng.integers(2048, ld * 128, size=n_rows)).astype(np.int64)
     pos[:3] = [ld * 128 - 1, 1024 * 128 + 5, 1024 * 128 - 1] if ld > 1024 else [ld * 128 - 1, 767 * 128 + 5, 512 * 128 - 1]
     pos[-6:] = [0, 130, 2047, 2100, 5000, 8191]  # short rows: every block kept, or candidates in one wave only
+    if ld <= 1024:  # rows at the edges of the one-wave kernel's register sizes (c = 64 k and 64 k + 1 candidates)
+        pos[3:13] = [c * 128 + 77 for c in (128, 129, 256, 257, 512, 513, 768, 769, 1023, 65)]
     vals = rng.integers(-3, 4, size=(n_rows, 1, ld)).astype(np.float32) / 4
     vals[0] = 0.0                      # every block ties
     vals[1, 0, ::2] = -0.0             # signed zeros tie with +0
