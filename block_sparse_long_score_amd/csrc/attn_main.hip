@@ -953,16 +953,17 @@ __device__ __forceinline__ void swap_f(float& x, float& y) {
   y = t;
 }
 
-// Decode step of a batch with fewer (sequence, group) pairs than the chip has
-// CUs (but enough for one workgroup each to pay): two 16-wave workgroups per
+// Decode of a batch with fewer (sequence, group) pairs than the chip has CUs
+// (but enough for one workgroup each to pay): two 16-wave workgroups per
 // pair, each attending 8 of the 16 selected blocks with two waves per block
 // (64 keys each), so every CU streams about half as much.  Each workgroup
 // combines its waves in LDS as decode_fused_kernel does, stores its half's
-// (max, mass, unnormalised output) device-coherently in the step workspace,
-// and counts itself on the pair's counter (zero on entry: the step's scoring
-// kernel clears it); the second to arrive reads the other half with
-// device-coherent loads, combines the two, writes the bf16 output and clears
-// the counter.  One thread per (head, dim pair) item in both phases.
+// (max, mass, unnormalised output) device-coherently in the workspace, and
+// counts itself on the pair's counter (zero on entry: the decode step's
+// scoring kernel clears it, or a fill kernel before the decode call); the
+// second to arrive reads the other half with device-coherent loads, combines
+// the two in half order, writes the bf16 output and clears the counter.  One
+// thread per (head, dim pair) item in both phases.
 template <int D, int GM>
 __global__ __launch_bounds__(1024) void decode_fused_half_kernel(KvOuterArgs a, StepArgs sa) {
   using W = DecodeWave<D, GM>;
